@@ -1,0 +1,161 @@
+"""Plain double-precision CPU oracle of the S6 selective scan.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  It shares no
+code with the GPU library and the GPU library never calls it.
+
+The arithmetic lives in ``ssm_oracle.c`` (sequential definition, fp64, one
+thread per group of independent (batch, channel) chains).  This module only
+widens inputs to float64 exactly (bfloat16 and float32 values are exactly
+representable in float64), calls the C routine and returns numpy arrays.
+
+Definitions followed (page title, site, section):
+  * recurrence, readout and direct path -- "Mamba: Linear-Time Sequence
+    Modeling with Selective State Spaces" (abhik.ai), "Original paper,
+    equations and runnable CPU code", row 2 "Retain, write and read each
+    channel's state";
+  * softplus step and A = -exp(A_log) -- "mamba, from scratch" (khushi
+    keswani), "from ssm to selective ssm";
+  * silu(z) gate -- abhik.ai page, row 5 "Put the selective operator inside
+    the complete mixer";
+  * single-token update -- abhik.ai page, row 6 "Carry both buffers to the
+    next token".
+
+Parity status: every function here is pinned by closed forms, invariants and
+brute force in ``tests/test_oracle_pins.py``; none is "parity unpinned".
+"""
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(HERE, "libssm_oracle.so")
+_lib = None
+
+_dp = ctypes.POINTER(ctypes.c_double)
+
+
+def _load(path=None):
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    if path is None:
+        path = _LIB_PATH
+        if not os.path.exists(path):
+            from . import build as _build
+
+            _build.build()
+    lib = ctypes.CDLL(path)
+    lib.oracle_scan.restype = ctypes.c_int
+    lib.oracle_scan.argtypes = [_dp] * 8 + [ctypes.c_int, _dp, _dp, _dp, _dp] + [ctypes.c_int64] * 4 + [ctypes.c_int]
+    lib.oracle_state_update.restype = ctypes.c_int
+    lib.oracle_state_update.argtypes = [_dp] * 9 + [ctypes.c_int, _dp] + [ctypes.c_int64] * 3 + [ctypes.c_int]
+    lib.oracle_softplus_value.restype = ctypes.c_double
+    lib.oracle_softplus_value.argtypes = [ctypes.c_double]
+    lib.oracle_silu_value.restype = ctypes.c_double
+    lib.oracle_silu_value.argtypes = [ctypes.c_double]
+    _lib = lib
+    return lib
+
+
+def use_library(path=None):
+    """Point this module at another build of the oracle (mutation tests); None restores the default."""
+    global _lib
+    _lib = None
+    if path is not None:
+        _load(path)
+
+
+def default_threads() -> int:
+    """Host threads for the oracle: OMP_NUM_THREADS if set, else the CPU count, at most 16."""
+    env = os.environ.get("OMP_NUM_THREADS")
+    n = int(env) if env and env.isdigit() else (os.cpu_count() or 1)
+    return max(1, min(n, 16))
+
+
+def to_f64(x):
+    """Widen a numpy array or a (CPU or GPU) torch tensor to a contiguous float64 numpy array.
+
+    bfloat16 and float32 values widen exactly, so the oracle sees exactly the
+    numbers the GPU sees.
+    """
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # torch tensor
+        import torch
+
+        t = x.detach()
+        if t.dtype == torch.bfloat16 or t.dtype == torch.float16:
+            t = t.float()
+        x = t.cpu().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(_dp)
+
+
+def scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=False, h0=None,
+         return_states=False, threads=None):
+    """Sequential fp64 selective scan.
+
+    Shapes: u, delta, z [b, L, E]; A [E, N]; B, C [b, L, N]; D, delta_bias [E];
+    h0 [b, E, N] (None means a zero initial state).
+    Returns (y [b, L, E], last_state [b, E, N]) and, with return_states=True,
+    also every state [b, L, E, N].
+    """
+    lib = _load()
+    u, delta, A, B, C = (to_f64(v) for v in (u, delta, A, B, C))
+    D, z, delta_bias, h0 = (to_f64(v) for v in (D, z, delta_bias, h0))
+    b, L, E = u.shape
+    N = A.shape[1]
+    if delta.shape != (b, L, E) or A.shape != (E, N) or B.shape != (b, L, N) or C.shape != (b, L, N):
+        raise ValueError("oracle.scan: inconsistent shapes")
+    if z is not None and z.shape != (b, L, E):
+        raise ValueError("oracle.scan: z shape")
+    for v in (D, delta_bias):
+        if v is not None and v.shape != (E,):
+            raise ValueError("oracle.scan: D / delta_bias shape")
+    if h0 is not None and h0.shape != (b, E, N):
+        raise ValueError("oracle.scan: h0 shape")
+    y = np.empty((b, L, E), dtype=np.float64)
+    last = np.empty((b, E, N), dtype=np.float64)
+    states = np.empty((b, L, E, N), dtype=np.float64) if return_states else None
+    rc = lib.oracle_scan(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                         int(bool(softplus)), _ptr(h0), _ptr(y), _ptr(last), _ptr(states),
+                         b, L, E, N, threads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"oracle_scan failed with {rc}")
+    if return_states:
+        return y, last, states
+    return y, last
+
+
+def state_update(state, x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=False, threads=None):
+    """One recurrent step.  state [b, E, N] (not modified); x, delta, z [b, E]; B, C [b, N].
+
+    Returns (new_state [b, E, N], y [b, E]).
+    """
+    lib = _load()
+    s = to_f64(state).copy()
+    x, delta, A, B, C = (to_f64(v) for v in (x, delta, A, B, C))
+    D, z, delta_bias = (to_f64(v) for v in (D, z, delta_bias))
+    b, E, N = s.shape
+    if x.shape != (b, E) or delta.shape != (b, E) or A.shape != (E, N) or B.shape != (b, N) or C.shape != (b, N):
+        raise ValueError("oracle.state_update: inconsistent shapes")
+    y = np.empty((b, E), dtype=np.float64)
+    rc = lib.oracle_state_update(_ptr(s), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                 _ptr(delta_bias), int(bool(softplus)), _ptr(y), b, E, N,
+                                 threads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"oracle_state_update failed with {rc}")
+    return s, y
+
+
+def softplus_value(x: float) -> float:
+    return _load().oracle_softplus_value(float(x))
+
+
+def silu_value(z: float) -> float:
+    return _load().oracle_silu_value(float(z))

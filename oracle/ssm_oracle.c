@@ -1,0 +1,263 @@
+/*
+ * ssm_oracle.c -- plain, sequential, double-precision CPU reference of the
+ * Mamba-1 (S6) selective scan and of its single-token recurrent state update.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the correctness oracle for the GPU
+ * library.  Only the test suite, the package's smoke check and the benchmark's
+ * CPU-baseline leg may load it.  It shares no code, header, table or helper
+ * with the GPU path, and the GPU path never calls it.
+ *
+ * Pages cited (title, site):
+ *   [KK] "mamba, from scratch" (khushi keswani)
+ *   [AB] "Mamba: Linear-Time Sequence Modeling with Selective State Spaces" (abhik.ai)
+ *   [NC] "Mamba: Linear-Time Sequence Modeling with Selective State Spaces"
+ *        (nadeemcite research-papers summary)
+ *
+ * What is computed, for every batch row b and expanded channel e, with a state
+ * vector h[0..N-1] that starts at zero (or at a given h0):
+ *
+ *   d_t     = delta[b,t,e] + bias[e]                 bias added before the
+ *             then softplus(d_t) if requested         softplus ([NC] "Core Idea":
+ *                                                     the step is the softplus of a
+ *                                                     parameter plus a projection;
+ *                                                     [KK] "from ssm to selective ssm")
+ *   a_t,n   = exp(d_t * A[e,n])                       retention ([AB] "The input
+ *                                                     changes the coefficients";
+ *                                                     [KK] "from ssm to selective ssm")
+ *   h_t,n   = a_t,n * h_{t-1},n + d_t * B[b,t,n] * u[b,t,e]
+ *             (write term is step * B * x, not the exact zero-order-hold
+ *             integral: [AB] "Original paper, equations and runnable CPU code",
+ *             row 2 "Retain, write and read each channel's state")
+ *   y[b,t,e] = sum_n C[b,t,n] * h_t,n + D[e] * u[b,t,e]
+ *             (read after the update, then the direct D*x path: same row 2)
+ *   y[b,t,e] *= silu(z[b,t,e]) = z / (1 + exp(-z))   when a gate is given
+ *             ([AB] row 5 "Put the selective operator inside the complete
+ *             mixer": the z branch multiplies the scan result through SiLU)
+ *   last_state[b,e,n] = h_{L-1},n
+ *
+ * The single-token update applies the same body once to a given state
+ * ([AB] row 6 "Carry both buffers to the next token", the SSM half of `step`).
+ *
+ * Arithmetic: every input is widened to double before use; exp/log1p come
+ * from the C library; there is no blocking, fusion or reordering of the
+ * definition above.  Chains (b,e) are independent, so threads split chains,
+ * never time.  Build without -ffast-math and with floating-point contraction
+ * off so the arithmetic is the plain definition.
+ */
+#include <math.h>
+#include <pthread.h>
+
+/* ORACLE_MUTATION plants one deliberate mistake (test builds only; the
+ * default 0 is the oracle).  The mutation test compiles each variant on the
+ * CPU and requires every one of them to fail at least one pin. */
+#ifndef ORACLE_MUTATION
+#define ORACLE_MUTATION 0
+#endif
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* softplus(x) = log(1 + e^x), written so neither branch overflows. */
+static double oracle_softplus(double x) {
+#if ORACLE_MUTATION == 9
+  if (x > 0.0) return x + log1p(exp(x));
+#endif
+  if (x > 0.0) return x + log1p(exp(-x));
+  return log1p(exp(x));
+}
+
+/* silu(z) = z * sigmoid(z) = z / (1 + e^{-z}). */
+static double oracle_silu(double z) {
+#if ORACLE_MUTATION == 6
+  return 1.0 / (1.0 + exp(-z));
+#endif
+  return z / (1.0 + exp(-z));
+}
+
+typedef struct {
+  const double *u, *delta, *A, *B, *C, *D, *z, *bias, *h0;
+  double *y, *last_state, *states;
+  int64_t b, L, E, N;
+  int softplus;
+  int64_t chain_begin, chain_end; /* chains are flattened (b, e) */
+} scan_job;
+
+static void scan_chain(const scan_job* j, int64_t bi, int64_t e, double* h) {
+  const int64_t L = j->L, E = j->E, N = j->N;
+  for (int64_t n = 0; n < N; n++) h[n] = j->h0 ? j->h0[(bi * E + e) * N + n] : 0.0;
+  for (int64_t t = 0; t < L; t++) {
+    const int64_t xe = (bi * L + t) * E + e; /* index into [b, L, E] */
+    const int64_t xn = (bi * L + t) * N;     /* row index into [b, L, N] */
+    const double x = j->u[xe];
+    double d = j->delta[xe] + (j->bias ? j->bias[e] : 0.0);
+    if (j->softplus) d = oracle_softplus(d);
+#if ORACLE_MUTATION == 3
+    if (j->softplus && j->bias) d = oracle_softplus(j->delta[xe]) + j->bias[e];
+#endif
+    double acc = 0.0;
+    for (int64_t n = 0; n < N; n++) {
+#if ORACLE_MUTATION == 4
+      const double a = exp(-d * j->A[e * N + n]);
+#else
+      const double a = exp(d * j->A[e * N + n]);
+#endif
+#if ORACLE_MUTATION == 5
+      const double w = j->B[xn + n] * x;
+#elif ORACLE_MUTATION == 7
+      const double w = d * j->B[xn + (N - 1 - n)] * x;
+#else
+      const double w = d * j->B[xn + n] * x;
+#endif
+#if ORACLE_MUTATION == 1
+      acc += j->C[xn + n] * h[n];
+      h[n] = a * h[n] + w;
+#elif ORACLE_MUTATION == 8
+      h[n] = a * h[n] + w;
+      acc += j->C[(t > 0 ? xn - N : xn) + n] * h[n];
+#else
+      h[n] = a * h[n] + w;
+      acc += j->C[xn + n] * h[n];
+#endif
+      if (j->states) j->states[((bi * L + t) * E + e) * N + n] = h[n];
+    }
+#if ORACLE_MUTATION == 2
+    double yv = acc;
+#else
+    double yv = acc + (j->D ? j->D[e] * x : 0.0);
+#endif
+    if (j->z) yv *= oracle_silu(j->z[xe]);
+    j->y[xe] = yv;
+  }
+  if (j->last_state)
+    for (int64_t n = 0; n < N; n++) j->last_state[(bi * E + e) * N + n] = h[n];
+}
+
+static void* scan_worker(void* arg) {
+  const scan_job* j = (const scan_job*)arg;
+  double* h = (double*)malloc(sizeof(double) * (size_t)(j->N > 0 ? j->N : 1));
+  if (!h) return (void*)1;
+  for (int64_t c = j->chain_begin; c < j->chain_end; c++) scan_chain(j, c / j->E, c % j->E, h);
+  free(h);
+  return NULL;
+}
+
+/* Returns 0 on success, -1 on bad arguments, -2 on allocation/thread failure. */
+int oracle_scan(const double* u, const double* delta, const double* A, const double* B, const double* C,
+                const double* D, const double* z, const double* delta_bias, int softplus, const double* h0,
+                double* y, double* last_state, double* states, int64_t b, int64_t L, int64_t E, int64_t N,
+                int threads) {
+  if (b < 0 || L < 0 || E < 0 || N < 0) return -1;
+  if ((L > 0 && (!u || !delta || !B || !C || !y)) || (N > 0 && E > 0 && !A)) return -1;
+  const int64_t chains = b * E;
+  if (chains == 0) return 0;
+  if (threads < 1) threads = 1;
+  if (threads > chains) threads = (int)chains;
+  scan_job base;
+  memset(&base, 0, sizeof base);
+  base.u = u; base.delta = delta; base.A = A; base.B = B; base.C = C; base.D = D; base.z = z;
+  base.bias = delta_bias; base.h0 = h0; base.y = y; base.last_state = last_state; base.states = states;
+  base.b = b; base.L = L; base.E = E; base.N = N; base.softplus = softplus;
+  scan_job* jobs = (scan_job*)malloc(sizeof(scan_job) * (size_t)threads);
+  pthread_t* tid = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)threads);
+  if (!jobs || !tid) { free(jobs); free(tid); return -2; }
+  int rc = 0, started = 0;
+  for (int i = 0; i < threads; i++) {
+    jobs[i] = base;
+    jobs[i].chain_begin = chains * i / threads;
+    jobs[i].chain_end = chains * (i + 1) / threads;
+    if (threads == 1) {
+      if (scan_worker(&jobs[i])) rc = -2;
+    } else if (pthread_create(&tid[i], NULL, scan_worker, &jobs[i]) != 0) {
+      rc = -2;
+      break;
+    } else {
+      started++;
+    }
+  }
+  for (int i = 0; i < started; i++) {
+    void* ret = NULL;
+    pthread_join(tid[i], &ret);
+    if (ret) rc = -2;
+  }
+  free(jobs);
+  free(tid);
+  return rc;
+}
+
+typedef struct {
+  double* state;
+  const double *x, *delta, *A, *B, *C, *D, *z, *bias;
+  double* y;
+  int64_t b, E, N;
+  int softplus;
+  int64_t chain_begin, chain_end;
+} update_job;
+
+static void* update_worker(void* arg) {
+  const update_job* j = (const update_job*)arg;
+  const int64_t E = j->E, N = j->N;
+  for (int64_t c = j->chain_begin; c < j->chain_end; c++) {
+    const int64_t bi = c / E, e = c % E;
+    const double x = j->x[c];
+    double d = j->delta[c] + (j->bias ? j->bias[e] : 0.0);
+    if (j->softplus) d = oracle_softplus(d);
+    double acc = 0.0;
+    for (int64_t n = 0; n < N; n++) {
+      double* s = &j->state[c * N + n];
+#if ORACLE_MUTATION == 10
+      *s = exp(d * j->A[e * N + n]) * *s + d * j->C[bi * N + n] * x;
+      acc += j->B[bi * N + n] * *s;
+#else
+      *s = exp(d * j->A[e * N + n]) * *s + d * j->B[bi * N + n] * x;
+      acc += j->C[bi * N + n] * *s;
+#endif
+    }
+    double yv = acc + (j->D ? j->D[e] * x : 0.0);
+    if (j->z) yv *= oracle_silu(j->z[c]);
+    j->y[c] = yv;
+  }
+  return NULL;
+}
+
+/* One recurrent step for every (b, e): state [b,E,N] is updated in place,
+ * x, delta, z, y are [b,E], B and C are [b,N].  Returns 0, -1 or -2 as above. */
+int oracle_state_update(double* state, const double* x, const double* delta, const double* A, const double* B,
+                        const double* C, const double* D, const double* z, const double* delta_bias, int softplus,
+                        double* y, int64_t b, int64_t E, int64_t N, int threads) {
+  if (b < 0 || E < 0 || N < 0) return -1;
+  const int64_t chains = b * E;
+  if (chains == 0) return 0;
+  if (!x || !delta || !y || (N > 0 && (!state || !A || !B || !C))) return -1;
+  if (threads < 1) threads = 1;
+  if (threads > chains) threads = (int)chains;
+  update_job base;
+  memset(&base, 0, sizeof base);
+  base.state = state; base.x = x; base.delta = delta; base.A = A; base.B = B; base.C = C; base.D = D;
+  base.z = z; base.bias = delta_bias; base.y = y; base.b = b; base.E = E; base.N = N;
+  base.softplus = softplus;
+  update_job* jobs = (update_job*)malloc(sizeof(update_job) * (size_t)threads);
+  pthread_t* tid = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)threads);
+  if (!jobs || !tid) { free(jobs); free(tid); return -2; }
+  int rc = 0, started = 0;
+  for (int i = 0; i < threads; i++) {
+    jobs[i] = base;
+    jobs[i].chain_begin = chains * i / threads;
+    jobs[i].chain_end = chains * (i + 1) / threads;
+    if (threads == 1) {
+      update_worker(&jobs[i]);
+    } else if (pthread_create(&tid[i], NULL, update_worker, &jobs[i]) != 0) {
+      rc = -2;
+      break;
+    } else {
+      started++;
+    }
+  }
+  for (int i = 0; i < started; i++) pthread_join(tid[i], NULL);
+  free(jobs);
+  free(tid);
+  return rc;
+}
+
+/* Exposed for the softplus / gate pins: the scalar helpers exactly as used above. */
+double oracle_softplus_value(double x) { return oracle_softplus(x); }
+double oracle_silu_value(double z) { return oracle_silu(z); }
