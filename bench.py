@@ -1,0 +1,275 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X selective scan (Mamba-1 / S6 forward) on one GPU.
+
+One step = one ``ssm_scan_fwd`` call over the long-sequence workload
+(b=1, L=65536, E=5120, N=16, bf16 inputs/outputs, fp32 state, softplus step,
+silu gate, D skip), with inputs already resident in HBM.  That call runs the
+whole hot path: discretisation, recurrence, readout, gate and the last-state
+write.  The single-token state update is measured as well (128 successive
+updates of the generation workload b=256, E=5120, N=16) and reported in its
+own JSON object.
+
+Prints ONE JSON line on stdout:
+  value        b*L*E elements per second over the timed steps
+  roofline     HBM roofline of the dominant kernel (scan_main), its duration
+               measured with HIP events on the launch stream over the timed
+               region; traffic from the committed rocprofv3 PMC summary when
+               it was taken on the current kernel source, else null
+  cpu_baseline the fp64 oracle on a bounded channel sample of the same inputs
+               (channels are independent chains), timed on the host cores
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9  # 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz, non-packed fp32 issue
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def scan_bytes(b, L, E, N, s, gate=True, last_state=True):
+    """Algorithmic HBM bytes of one scan: u, delta (, z) in and y out at s bytes each; B and C rows;
+    A, D (and bias); the fp32 last state."""
+    streams_in = 3 if gate else 2
+    by = b * L * E * (streams_in + 1) * s + 2 * b * L * N * s + E * (N + 2) * 4
+    if last_state:
+        by += b * E * N * 4
+    return by
+
+
+def update_bytes(b, E, N, s, gate=True):
+    """Algorithmic bytes of one state update: fp32 state read + write, x, delta (, z) in, y out, B, C, A, D."""
+    return 8 * b * E * N + b * E * ((3 if gate else 2) + 1) * s + 2 * b * N * s + E * (N + 2) * 4
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in ("ssm_kernels.hip",):
+        with open(os.path.join(ROOT, "selective_state_space_35_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, workload):
+    """HBM traffic per launch from profiles/traffic_<kernel>_<workload>.json if taken on this source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None, "no PMC summary"
+    with open(path) as f:
+        doc = json.load(f)
+    if doc.get("source_hash") != source_hash():
+        return None, "kernel changed since the PMC counters were taken"
+    return doc.get("hbm_bytes_per_launch"), doc.get("note", "")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target wall time of the CPU baseline sample")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); the scan "
+              "shards over batch and channels with no communication, so there is no multi-GPU path to time.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import selective_state_space_35_amd as ssm
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        nbytes = 1 << 30
+        src = torch.full((nbytes,), 7, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": nbytes, "bytes_written": nbytes, "launches": 3}))
+        return
+
+    w = workloads.LONG
+    log(f"[bench] generating {w.description} (seed {args.seed}) on {torch.cuda.get_device_name(dev)}")
+    x = workloads.make_scan_inputs(w, seed=args.seed, device=dev, backend="torch")
+    y = torch.empty_like(x["u"])
+    last = torch.empty(w.b, w.E, w.N, dtype=torch.float32, device=dev)
+    chunk_len, n_chunks = ssm.ssm_scan_plan(w.b, w.L, w.E, w.N, w.dtype)
+
+    def step():
+        ssm.ssm_scan_fwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
+                         x["softplus"], y=y, last_state=last)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ssm.ssm_profile_read()  # drop anything recorded before the timed region
+    ssm.ssm_profile_enable(True)
+    stream = torch.cuda.current_stream(dev)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ssm.ssm_profile_enable(False)
+    per_kernel = ssm.ssm_profile_read()
+    total_ms = t0.elapsed_time(t1)
+    ms_per_step = total_ms / args.steps
+    elems = w.b * w.L * w.E
+    value = elems / (ms_per_step * 1e-3)
+    s = 2 if w.dtype == "bf16" else 4
+    algo = scan_bytes(w.b, w.L, w.E, w.N, s, gate=w.z is not None)
+    path_gbps = algo / (ms_per_step * 1e-3) / 1e9
+    kernels = {k: {"avg_us": round(1e3 * v[0] / v[1], 2), "launches": v[1]} for k, v in per_kernel.items() if v[1]}
+    main_ms, main_n = per_kernel["scan_main"]
+    main_avg_s = main_ms / max(main_n, 1) * 1e-3
+    achieved = algo / main_avg_s / 1e9
+    traffic, traffic_note = load_traffic("scan_main", w.name)
+    log(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step, {value:.4e} elem/s, path {path_gbps:.1f} GB/s; "
+        f"kernels {kernels}")
+
+    # ALU view: the recurrence needs per (t, e, n) one exp2 and four fp32 VALU ops (2 mul, 2 fma)
+    valu_ops = 5 * elems * w.N
+    alu = {"valu_lane_ops_per_step": valu_ops, "achieved_lane_ops_per_s": valu_ops / (ms_per_step * 1e-3),
+           "issue_peak_lane_ops_per_s": VALU_LANE_OPS,
+           "note": "counts the minimal 4 VALU + 1 v_exp_f32 per (t,e,n) of one pass; the chunked path adds a "
+                   "second pass over most elements"}
+
+    # state update (generation): 128 successive single-token updates, state carried in HBM
+    update = None
+    if not args.no_decode:
+        wd = workloads.DECODE
+        xd = workloads.make_decode_inputs(wd, seed=args.seed, device=dev, backend="torch")
+        st = xd["state0"].clone()
+        yd = torch.empty(wd.b, wd.E, dtype=torch.bfloat16, device=dev)
+
+        def decode_pass():
+            for k in range(wd.steps):
+                ssm.ssm_state_update(st, xd["x"][k], xd["delta"][k], xd["A"], xd["B"][k], xd["C"][k], xd["D"],
+                                     xd["z"][k], xd["delta_bias"], xd["softplus"], y=yd)
+
+        decode_pass()
+        torch.cuda.synchronize()
+        reps = 5
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ssm.ssm_profile_enable(True)
+        e0.record(stream)
+        for _ in range(reps):
+            st.zero_()
+            decode_pass()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ssm.ssm_profile_enable(False)
+        upd = ssm.ssm_profile_read()["state_update"]
+        per_call_us = 1e3 * upd[0] / upd[1]
+        ub = update_bytes(wd.b, wd.E, wd.N, 2)
+        update = {"workload": wd.description, "us_per_call": round(per_call_us, 3),
+                  "calls": upd[1], "wall_ms_per_128": round(e0.elapsed_time(e1) / reps, 4),
+                  "GBps": round(ub / (per_call_us * 1e-6) / 1e9, 1),
+                  "bytes_per_call": ub,
+                  "note": "the 84 MB fp32 state fits in the 256 MB Infinity Cache, so carried-state traffic "
+                          "can be served from it; GB/s is algorithmic bytes over kernel time"}
+        del xd, st, yd
+
+    # CPU baseline: the oracle on a bounded channel sample of the same inputs
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        threads = oracle.default_threads()
+        rng = np.random.default_rng(1)
+
+        def sample(nch):
+            ch = torch.from_numpy(np.sort(rng.choice(w.E, size=nch, replace=False))).to(dev)
+            sel = lambda t: None if t is None else t.index_select(2, ch)
+            args_ = (sel(x["u"]), sel(x["delta"]), x["A"].index_select(0, ch), x["B"], x["C"],
+                     None if x["D"] is None else x["D"].index_select(0, ch), sel(x["z"]),
+                     None if x["delta_bias"] is None else x["delta_bias"].index_select(0, ch))
+            return ch, [oracle.to_f64(a) for a in args_]
+
+        # calibrate on a small sample, then size the measured sample to about --cpu-seconds
+        ch, a = sample(threads)
+        c0 = time.perf_counter()
+        oracle.scan(*a, softplus=x["softplus"], threads=threads)
+        rate = threads * w.L / (time.perf_counter() - c0)  # channel-steps per second
+        nch = int(max(threads, min(w.E, args.cpu_seconds * rate / w.L)))
+        nch = max(threads, (nch // threads) * threads)
+        ch, a = sample(nch)
+        c0 = time.perf_counter()
+        y_ref, last_ref = oracle.scan(*a, softplus=x["softplus"], threads=threads)
+        cpu_s = time.perf_counter() - c0
+        cpu = {"value": w.b * w.L * nch / cpu_s, "unit": "elem/s", "cores": threads, "kind": "oracle",
+               "seconds": round(cpu_s, 2),
+               "sample": f"{nch} of {w.E} channels (independent chains), full L={w.L}, b={w.b}; "
+                         "fp64 sequential oracle, same inputs"}
+        yg = oracle.to_f64(y.index_select(2, ch))
+        lg = oracle.to_f64(last.index_select(1, ch))
+        err = lambda g, r: float(np.max(np.abs(g - r) / (1 + np.abs(r))))
+        parity = {"y_max_normalised_error": err(yg, y_ref), "last_state_max_normalised_error": err(lg, last_ref),
+                  "bound": 2e-2, "channels_checked": nch}
+        log(f"[bench] cpu baseline {cpu['value']:.3e} elem/s on {threads} threads; parity {parity}")
+
+    out = {
+        "metric": "selective-scan B·L·E elems/s and achieved HBM GB/s (% of MI355X peak)",
+        "value": value,
+        "unit": "elem/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "long-sequence selective scan b1 L65536 E5120 N16, bf16 I/O, fp32 state, "
+                               "softplus step, silu gate, D skip",
+                   "b": w.b, "L": w.L, "E": w.E, "N": w.N, "io_dtype": w.dtype,
+                   "chunk_len": chunk_len, "n_chunks": n_chunks, "parallelism": "single GPU"},
+        "hbm_GBps": path_gbps,
+        "hbm_frac": path_gbps / HBM_PEAK_GBPS,
+        "algorithmic_bytes_per_step": algo,
+        "roofline": {"bound": "hbm", "kernel": "scan_main", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "traffic_note": traffic_note,
+                     "kernel_avg_us": round(main_avg_s * 1e6, 2)},
+        "kernels": kernels,
+        "alu": alu,
+        "state_update": update,
+        "cpu_baseline": cpu,
+        "parity": parity,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

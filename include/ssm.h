@@ -1,0 +1,174 @@
+/*
+ * ssm.h -- C ABI of the MI355X (gfx950) selective-scan library (libssm.so).
+ *
+ * Two operations of the Mamba-1 (S6) selective state-space layer, forward
+ * only, on one GPU:
+ *
+ *   ssm_scan_fwd      the selective scan over a whole sequence
+ *   ssm_state_update  one recurrent step of the same recurrence (generation)
+ *
+ * Pages that define the operations (title, site):
+ *   [KK] "mamba, from scratch" (khushi keswani)
+ *   [AB] "Mamba: Linear-Time Sequence Modeling with Selective State Spaces" (abhik.ai)
+ *   [NC] "Mamba: Linear-Time Sequence Modeling with Selective State Spaces"
+ *        (nadeemcite research-papers summary)
+ *
+ * Conventions shared by every entry point
+ * ----------------------------------------
+ * Memory.  Every pointer is a DEVICE pointer on the current HIP device, owned
+ * by the caller.  Arrays are dense, row-major (last index fastest).  The
+ * library keeps no pointer after a call returns.
+ *
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL = the default
+ * stream).  Work is enqueued on it and the call returns without waiting;
+ * errors raised while the kernels run surface at the caller's next
+ * synchronisation.  The scan takes a temporary workspace from the
+ * stream-ordered allocator (hipMallocAsync / hipFreeAsync on `stream`), so
+ * concurrent calls on different streams do not share memory.
+ *
+ * Data types.  `dtype` (ssm_dtype) is the element type of the streamed
+ * tensors u/x, delta, B, C, z and y: SSM_F32 (float) or SSM_BF16 (bfloat16,
+ * raw 16-bit storage).  A, D, delta_bias and every state are always float.
+ * Arithmetic is float32 throughout; bf16 outputs are rounded to nearest-even.
+ *
+ * Sizes.  b (batch), L (sequence length), E (expanded channels) and
+ * N (state size per channel).  Supported: 1 <= N <= 16; b, L, E >= 0.
+ * b == 0 or E == 0 is a no-op.  L == 0 writes a zero last_state.
+ *
+ * Alignment.  Every array must be aligned to its element size; float arrays
+ * to 4 bytes, bf16 arrays to 2 bytes.  (Tensors from a PyTorch allocator
+ * always are.)
+ *
+ * Aliasing.  Outputs must not overlap inputs.
+ *
+ * Errors.  Argument errors are detected before anything is enqueued and
+ * reported as a negative ssm_status; nothing is written in that case.
+ * SSM_ERR_HIP reports a failed HIP launch or allocation (the HIP error is
+ * cleared and its text is available from ssm_last_hip_error()).
+ */
+#ifndef SSM_H_
+#define SSM_H_
+
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define SSM_API __attribute__((visibility("default")))
+#else
+#define SSM_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SSM_F32 = 0,
+  SSM_BF16 = 1
+} ssm_dtype;
+
+typedef enum {
+  SSM_OK = 0,
+  SSM_ERR_NULL = -1,          /* a required pointer is NULL */
+  SSM_ERR_DIM = -2,           /* a negative size, or a size product that overflows */
+  SSM_ERR_DTYPE = -3,         /* dtype is not an ssm_dtype value */
+  SSM_ERR_UNSUPPORTED_N = -4, /* N outside 1..16 */
+  SSM_ERR_ALIGN = -5,         /* an array is not aligned to its element size */
+  SSM_ERR_HIP = -6            /* HIP launch / allocation failure */
+} ssm_status;
+
+/*
+ * Selective scan, forward.
+ *
+ * For every batch row b, channel e and state n, starting from h = 0:
+ *   d      = delta[b,t,e] + delta_bias[e], then softplus(d) when softplus != 0
+ *            (bias added before the softplus: [NC] "Core Idea"; [KK] "from ssm
+ *            to selective ssm")
+ *   h[n]   = exp(d * A[e,n]) * h[n] + d * B[b,t,n] * u[b,t,e]
+ *            (retention exp(step*A) and write step*B*x: [AB] "Original paper,
+ *            equations and runnable CPU code", row 2 "Retain, write and read
+ *            each channel's state"; the write is not the exact zero-order-hold
+ *            integral)
+ *   y[b,t,e] = (sum_n C[b,t,n] * h[n] + D[e] * u[b,t,e]) * silu(z[b,t,e])
+ *            (read after the update, direct D*x path: same row 2; silu gate:
+ *            [AB] row 5 "Put the selective operator inside the complete mixer")
+ *   last_state[b,e,n] = h[n] after step L-1
+ * The recurrence is an associative affine composition
+ * ([KK] "the scan"; [AB] "Compose the updates instead of waiting for every
+ * state"), which is how the library splits long sequences across the GPU.
+ *
+ * Arguments (all device pointers):
+ *   u, delta, z, y   [b, L, E]  dtype       (z nullable: no gate)
+ *   A                [E, N]     float       (used as given; the usual
+ *                                            parameterisation is A = -exp(A_log))
+ *   B, C             [b, L, N]  dtype       (shared by all E channels)
+ *   D, delta_bias    [E]        float       (nullable: treated as zero)
+ *   softplus         0 or 1
+ *   last_state       [b, E, N]  float       (nullable: not written)
+ */
+SSM_API int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                 const float* D, const void* z, const float* delta_bias, int softplus,
+                 void* y, float* last_state,
+                 int64_t b, int64_t L, int64_t E, int64_t N, int dtype, void* stream);
+
+/*
+ * One recurrent step for every (b, e) -- the SSM half of the decode step of
+ * [AB] row 6 "Carry both buffers to the next token":
+ *   d          = delta[b,e] + delta_bias[e], softplus(d) when softplus != 0
+ *   state[b,e,n] = exp(d * A[e,n]) * state[b,e,n] + d * B[b,n] * x[b,e]   (in place)
+ *   y[b,e]     = (sum_n C[b,n] * state[b,e,n] + D[e] * x[b,e]) * silu(z[b,e])
+ *
+ * Arguments (all device pointers):
+ *   state            [b, E, N]  float       (read and written in place)
+ *   x, delta, z, y   [b, E]     dtype       (z nullable)
+ *   A                [E, N]     float
+ *   B, C             [b, N]     dtype
+ *   D, delta_bias    [E]        float       (nullable)
+ * Calling it L times on the token slices of a sequence reproduces
+ * ssm_scan_fwd (same recurrence, [AB] "What persists when the next token
+ * arrives").
+ */
+SSM_API int ssm_state_update(float* state, const void* x, const void* delta, const float* A,
+                     const void* B, const void* C, const float* D, const void* z,
+                     const float* delta_bias, int softplus, void* y,
+                     int64_t b, int64_t E, int64_t N, int dtype, void* stream);
+
+/*
+ * How ssm_scan_fwd will split a scan of this size along the sequence: it
+ * writes the chunk length (steps) and the number of chunks.  One chunk means
+ * a single pass; more chunks mean a chunk-aggregate pass, a carry pass over
+ * the chunk boundaries and a main pass (the affine composition of
+ * [KK] "the scan").  The split depends only on (b, L, E, dtype) and on the
+ * tuning variables SSM_SCAN_TARGET_WAVES / SSM_SCAN_MIN_CHUNK if set.
+ * Host-only: enqueues nothing.  Same argument checks as ssm_scan_fwd.
+ */
+SSM_API int ssm_scan_plan(int64_t b, int64_t L, int64_t E, int64_t N, int dtype,
+                          int64_t* chunk_len, int64_t* n_chunks);
+
+/*
+ * Kernel timing for benchmarks.  While enabled (on != 0), every kernel the
+ * library enqueues is bracketed by two HIP events recorded on the caller's
+ * stream.  ssm_profile_read() waits for those events, writes per-kind totals
+ * (milliseconds) and launch counts for kinds 0 .. n_kinds-1 and clears the
+ * record.  Kinds: 0 widen_rows (bf16 B/C rows to f32), 1 chunk_aggregate,
+ * 2 chunk_carry, 3 scan_main, 4 fill_zero, 5 state_update; names from
+ * ssm_profile_kind_name().  Off by default; the events add a few
+ * microseconds per launch.  Process-wide, thread-safe.
+ */
+SSM_API int ssm_profile_enable(int on);
+SSM_API int ssm_profile_read(double* total_ms, int64_t* launches, int n_kinds);
+SSM_API const char* ssm_profile_kind_name(int kind);
+
+/* Static text for an ssm_status value (never NULL). */
+SSM_API const char* ssm_status_string(int status);
+
+/* Text of the last HIP error that produced SSM_ERR_HIP in this thread ("" if none). */
+SSM_API const char* ssm_last_hip_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+SSM_API int ssm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_H_ */

@@ -1,0 +1,235 @@
+"""MI355X (gfx950) selective scan of Mamba-1 (S6): Python binding of ``libssm.so``.
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/ssm.h``; this module checks
+shapes, dtypes and devices, allocates outputs with PyTorch (device memory
+and streams are PyTorch's job here), and calls the library on the current
+PyTorch stream of the tensors' device.  There is no CPU fallback: if the
+library is missing or the tensors are not on a GPU, the call raises.
+
+Functions (same names as the C entry points):
+
+* ``ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
+  softplus=False, y=None, last_state=None, return_last_state=True)``
+  -> ``(y, last_state)``
+* ``ssm_state_update(state, x, delta, A, B, C, D=None, z=None,
+  delta_bias=None, softplus=False, y=None)`` -> ``y`` (``state`` is updated
+  in place)
+
+Shapes: u, delta, z, y [b, L, E]; A [E, N] (float32); B, C [b, L, N];
+D, delta_bias [E] (float32); state / last_state [b, E, N] (float32).
+Streamed tensors are all float32 or all bfloat16.
+"""
+import ctypes
+import os
+
+__all__ = [
+    "ssm_scan_fwd", "ssm_state_update", "ssm_scan_plan", "ssm_profile_enable", "ssm_profile_read",
+    "ssm_status_string", "library_path", "SSMError",
+    "SSM_F32", "SSM_BF16", "load_library",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libssm.so")
+_lib = None
+
+SSM_F32 = 0
+SSM_BF16 = 1
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+
+
+class SSMError(RuntimeError):
+    """A call into libssm.so returned a non-zero ssm_status."""
+
+    def __init__(self, fn, status, detail=""):
+        self.status = status
+        msg = f"{fn} failed: {ssm_status_string(status)} (status {status})"
+        if detail:
+            msg += f": {detail}"
+        super().__init__(msg)
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libssm.so (built in-tree by ``python -m selective_state_space_35_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is missing: build the HIP library first "
+            "(python -m selective_state_space_35_amd.build)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.ssm_scan_fwd.restype = _int
+    lib.ssm_scan_fwd.argtypes = [_vp] * 8 + [_int, _vp, _vp] + [_i64] * 4 + [_int, _vp]
+    lib.ssm_state_update.restype = _int
+    lib.ssm_state_update.argtypes = [_vp] * 9 + [_int, _vp] + [_i64] * 3 + [_int, _vp]
+    lib.ssm_status_string.restype = ctypes.c_char_p
+    lib.ssm_status_string.argtypes = [_int]
+    lib.ssm_last_hip_error.restype = ctypes.c_char_p
+    lib.ssm_last_hip_error.argtypes = []
+    lib.ssm_version.restype = _int
+    lib.ssm_version.argtypes = []
+    lib.ssm_profile_enable.restype = _int
+    lib.ssm_profile_enable.argtypes = [_int]
+    lib.ssm_profile_read.restype = _int
+    lib.ssm_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64), _int]
+    lib.ssm_profile_kind_name.restype = ctypes.c_char_p
+    lib.ssm_profile_kind_name.argtypes = [_int]
+    lib.ssm_scan_plan.restype = _int
+    lib.ssm_scan_plan.argtypes = [_i64, _i64, _i64, _i64, _int, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]
+    _lib = lib
+    return lib
+
+
+def ssm_status_string(status: int) -> str:
+    return load_library().ssm_status_string(int(status)).decode()
+
+
+def ssm_scan_plan(b, L, E, N, dtype="bf16"):
+    """(chunk_len, n_chunks) that ssm_scan_fwd uses for this size (host-only query)."""
+    code = {"f32": SSM_F32, "bf16": SSM_BF16}.get(dtype, dtype)
+    cl, nc = _i64(0), _i64(0)
+    status = load_library().ssm_scan_plan(int(b), int(L), int(E), int(N), int(code), ctypes.byref(cl),
+                                          ctypes.byref(nc))
+    _raise_on("ssm_scan_plan", status)
+    return cl.value, nc.value
+
+
+PROFILE_KINDS = 6
+
+
+def ssm_profile_enable(on=True):
+    """Bracket every library kernel with HIP events on its stream (benchmark timing)."""
+    load_library().ssm_profile_enable(int(bool(on)))
+
+
+def ssm_profile_read():
+    """Wait for the recorded events; return {kind name: (total ms, launches)} and clear the record."""
+    lib = load_library()
+    ms = (ctypes.c_double * PROFILE_KINDS)()
+    cnt = (_i64 * PROFILE_KINDS)()
+    _raise_on("ssm_profile_read", lib.ssm_profile_read(ms, cnt, PROFILE_KINDS))
+    return {lib.ssm_profile_kind_name(k).decode(): (ms[k], cnt[k]) for k in range(PROFILE_KINDS)}
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(torch, dt):
+    if dt == torch.float32:
+        return SSM_F32
+    if dt == torch.bfloat16:
+        return SSM_BF16
+    raise TypeError(f"streamed tensors must be float32 or bfloat16, got {dt}")
+
+
+def _check(torch, name, t, shape, dtype, device, optional=False):
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_of(torch, device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _raise_on(fn, status):
+    if status != 0:
+        detail = load_library().ssm_last_hip_error().decode() if status == -6 else ""
+        raise SSMError(fn, status, detail)
+
+
+def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=False, y=None,
+                 last_state=None, return_last_state=True):
+    """Selective scan forward on the GPU.  Returns ``(y, last_state)`` (last_state None if not requested)."""
+    import torch
+
+    lib = load_library()
+    if not isinstance(u, torch.Tensor) or u.dim() != 3:
+        raise ValueError("u must be a [b, L, E] tensor")
+    device = u.device
+    if device.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU device, got {device}")
+    b, L, E = u.shape
+    if not isinstance(A, torch.Tensor) or A.dim() != 2:
+        raise ValueError("A must be an [E, N] tensor")
+    N = A.shape[1]
+    io = u.dtype
+    code = _dtype_code(torch, io)
+    _check(torch, "delta", delta, (b, L, E), io, device)
+    _check(torch, "A", A, (E, N), torch.float32, device)
+    _check(torch, "B", B, (b, L, N), io, device)
+    _check(torch, "C", C, (b, L, N), io, device)
+    _check(torch, "D", D, (E,), torch.float32, device, optional=True)
+    _check(torch, "z", z, (b, L, E), io, device, optional=True)
+    _check(torch, "delta_bias", delta_bias, (E,), torch.float32, device, optional=True)
+    _check(torch, "u", u, (b, L, E), io, device)
+    if y is None:
+        y = torch.empty((b, L, E), dtype=io, device=device)
+    else:
+        _check(torch, "y", y, (b, L, E), io, device)
+    if last_state is None and return_last_state:
+        last_state = torch.empty((b, E, N), dtype=torch.float32, device=device)
+    elif last_state is not None:
+        _check(torch, "last_state", last_state, (b, E, N), torch.float32, device)
+    with torch.cuda.device(device):
+        status = lib.ssm_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                  _ptr(delta_bias), int(bool(softplus)), _ptr(y), _ptr(last_state),
+                                  b, L, E, N, code, _stream_of(torch, device))
+    _raise_on("ssm_scan_fwd", status)
+    return y, last_state
+
+
+def ssm_state_update(state, x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=False, y=None):
+    """One recurrent step on the GPU; ``state`` [b, E, N] float32 is updated in place.  Returns y [b, E]."""
+    import torch
+
+    lib = load_library()
+    if not isinstance(state, torch.Tensor) or state.dim() != 3:
+        raise ValueError("state must be a [b, E, N] tensor")
+    device = state.device
+    if device.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU device, got {device}")
+    b, E, N = state.shape
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("x must be a torch.Tensor")
+    io = x.dtype
+    code = _dtype_code(torch, io)
+    _check(torch, "state", state, (b, E, N), torch.float32, device)
+    _check(torch, "x", x, (b, E), io, device)
+    _check(torch, "delta", delta, (b, E), io, device)
+    _check(torch, "A", A, (E, N), torch.float32, device)
+    _check(torch, "B", B, (b, N), io, device)
+    _check(torch, "C", C, (b, N), io, device)
+    _check(torch, "D", D, (E,), torch.float32, device, optional=True)
+    _check(torch, "z", z, (b, E), io, device, optional=True)
+    _check(torch, "delta_bias", delta_bias, (E,), torch.float32, device, optional=True)
+    if y is None:
+        y = torch.empty((b, E), dtype=io, device=device)
+    else:
+        _check(torch, "y", y, (b, E), io, device)
+    with torch.cuda.device(device):
+        status = lib.ssm_state_update(_ptr(state), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                      _ptr(z), _ptr(delta_bias), int(bool(softplus)), _ptr(y), b, E, N, code,
+                                      _stream_of(torch, device))
+    _raise_on("ssm_state_update", status)
+    return y

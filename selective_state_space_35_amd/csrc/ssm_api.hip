@@ -1,0 +1,125 @@
+// ssm_api.hip -- the extern "C" entry points declared in include/ssm.h:
+// argument validation, status codes, and the hand-off to the launchers.
+// Every argument check runs before any HIP call, so an invalid call enqueues
+// nothing and also works on a host without a GPU.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cstring>
+
+#include "ssm.h"
+#include "ssm_internal.h"
+
+namespace {
+
+thread_local char g_last_hip_error[256] = "";
+
+int hip_status(hipError_t err) {
+  if (err == hipSuccess) return SSM_OK;
+  const char* s = hipGetErrorString(err);
+  std::strncpy(g_last_hip_error, s ? s : "unknown HIP error", sizeof(g_last_hip_error) - 1);
+  g_last_hip_error[sizeof(g_last_hip_error) - 1] = '\0';
+  (void)hipGetLastError();  // clear the sticky launch error
+  return SSM_ERR_HIP;
+}
+
+bool aligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
+
+// Common size / dtype checks.  `elems` receives b*L*E (or b*E).
+int check_sizes(int64_t b, int64_t L, int64_t E, int64_t N, int dtype) {
+  if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_DTYPE;
+  if (b < 0 || L < 0 || E < 0 || N < 0) return SSM_ERR_DIM;
+  if (N < 1 || N > 16) return SSM_ERR_UNSUPPORTED_N;
+  int64_t t = 0;
+  if (!mul_ok(b, L, &t) || !mul_ok(t, E, &t) || !mul_ok(t, 4, &t)) return SSM_ERR_DIM;
+  if (!mul_ok(b, L, &t) || !mul_ok(t, N, &t) || !mul_ok(t, 4, &t)) return SSM_ERR_DIM;
+  if (!mul_ok(b, E, &t) || !mul_ok(t, N, &t) || !mul_ok(t, 16, &t)) return SSM_ERR_DIM;
+  return SSM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C, const float* D,
+                 const void* z, const float* delta_bias, int softplus, void* y, float* last_state, int64_t b,
+                 int64_t L, int64_t E, int64_t N, int dtype, void* stream) {
+  int st = check_sizes(b, L, E, N, dtype);
+  if (st != SSM_OK) return st;
+  if (b == 0 || E == 0) return SSM_OK;
+  if (L > 0 && (!u || !delta || !A || !B || !C || !y)) return SSM_ERR_NULL;
+  const size_t es = dtype == SSM_F32 ? 4 : 2;
+  const void* streamed[] = {u, delta, B, C, z, y};
+  for (const void* p : streamed)
+    if (p && !aligned(p, es)) return SSM_ERR_ALIGN;
+  const void* fl[] = {A, D, delta_bias, last_state};
+  for (const void* p : fl)
+    if (p && !aligned(p, 4)) return SSM_ERR_ALIGN;
+  // with L > 0 the chunk count is bounded by L / 64 and the grid by b * E / 64 * chunks
+  const ssm::ScanPlan pl = ssm::plan_scan(b, L, E, int(es));
+  int64_t grid = 0;
+  if (pl.chunk_len <= 0 || !mul_ok(b * pl.e_blocks, pl.n_chunks, &grid) || grid > INT32_MAX) return SSM_ERR_DIM;
+
+  ssm::ScanArgs a;
+  a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias;
+  a.softplus = softplus ? 1 : 0; a.y = y; a.last_state = last_state;
+  a.b = b; a.L = L; a.E = E; a.N = N; a.dtype = dtype;
+  a.stream = static_cast<hipStream_t>(stream);
+  return hip_status(ssm::launch_scan(a));
+}
+
+int ssm_state_update(float* state, const void* x, const void* delta, const float* A, const void* B, const void* C,
+                     const float* D, const void* z, const float* delta_bias, int softplus, void* y, int64_t b,
+                     int64_t E, int64_t N, int dtype, void* stream) {
+  int st = check_sizes(b, 1, E, N, dtype);
+  if (st != SSM_OK) return st;
+  if (b == 0 || E == 0) return SSM_OK;
+  if (!state || !x || !delta || !A || !B || !C || !y) return SSM_ERR_NULL;
+  const size_t es = dtype == SSM_F32 ? 4 : 2;
+  const void* streamed[] = {x, delta, B, C, z, y};
+  for (const void* p : streamed)
+    if (p && !aligned(p, es)) return SSM_ERR_ALIGN;
+  const void* fl[] = {state, A, D, delta_bias};
+  for (const void* p : fl)
+    if (p && !aligned(p, 4)) return SSM_ERR_ALIGN;
+  int64_t threads = 0;
+  if (!mul_ok(b, E, &threads) || !mul_ok(threads, 4, &threads) || threads / 256 > INT32_MAX) return SSM_ERR_DIM;
+
+  ssm::UpdateArgs a;
+  a.state = state; a.x = x; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias;
+  a.softplus = softplus ? 1 : 0; a.y = y; a.b = b; a.E = E; a.N = N; a.dtype = dtype;
+  a.stream = static_cast<hipStream_t>(stream);
+  return hip_status(ssm::launch_state_update(a));
+}
+
+int ssm_scan_plan(int64_t b, int64_t L, int64_t E, int64_t N, int dtype, int64_t* chunk_len, int64_t* n_chunks) {
+  int st = check_sizes(b, L, E, N, dtype);
+  if (st != SSM_OK) return st;
+  if (!chunk_len || !n_chunks) return SSM_ERR_NULL;
+  const ssm::ScanPlan pl = ssm::plan_scan(b, L, E, dtype == SSM_F32 ? 4 : 2);
+  if (pl.chunk_len <= 0) return SSM_ERR_DIM;
+  *chunk_len = pl.chunk_len;
+  *n_chunks = pl.n_chunks;
+  return SSM_OK;
+}
+
+const char* ssm_status_string(int status) {
+  switch (status) {
+    case SSM_OK: return "ok";
+    case SSM_ERR_NULL: return "a required pointer is NULL";
+    case SSM_ERR_DIM: return "invalid or overflowing size";
+    case SSM_ERR_DTYPE: return "unknown dtype";
+    case SSM_ERR_UNSUPPORTED_N: return "state size N must be in 1..16";
+    case SSM_ERR_ALIGN: return "array not aligned to its element size";
+    case SSM_ERR_HIP: return "HIP launch or allocation failed";
+    default: return "unknown status";
+  }
+}
+
+const char* ssm_last_hip_error(void) { return g_last_hip_error; }
+
+int ssm_version(void) { return 10000; }
+
+}  // extern "C"

@@ -1,0 +1,59 @@
+// Internal interface between the C-ABI layer (ssm_api.hip) and the kernel
+// launchers (ssm_kernels.hip).  Arguments have already been validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+
+struct ScanArgs {
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;      // nullable
+  const void* z;       // nullable
+  const float* bias;   // nullable
+  int softplus;
+  void* y;
+  float* last_state;   // nullable
+  int64_t b, L, E, N;
+  int dtype;           // 0 = f32, 1 = bf16
+  hipStream_t stream;
+};
+
+struct UpdateArgs {
+  float* state;
+  const void* x;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;      // nullable
+  const void* z;       // nullable
+  const float* bias;   // nullable
+  int softplus;
+  void* y;
+  int64_t b, E, N;
+  int dtype;
+  hipStream_t stream;
+};
+
+// How a scan is split along the sequence: n_chunks chunks of chunk_len steps.
+struct ScanPlan {
+  int64_t chunk_len;
+  int n_chunks;
+  int e_blocks;  // ceil(E / 64): one 64-lane wave covers 64 channels
+};
+
+// elem_bytes: size of the streamed element type (4 for f32, 2 for bf16).
+// chunk_len == 0 means the row size is too large to address (rejected).
+ScanPlan plan_scan(int64_t b, int64_t L, int64_t E, int elem_bytes);
+
+// Both return hipSuccess or the first HIP error met while enqueueing.
+hipError_t launch_scan(const ScanArgs& a);
+hipError_t launch_state_update(const UpdateArgs& a);
+
+}  // namespace ssm

@@ -1,0 +1,652 @@
+// ssm_kernels.hip -- gfx950 (CDNA4) kernels of the S6 selective scan and of
+// the single-token state update, plus their host-side launchers.
+//
+// Pages that define the arithmetic (title, site):
+//   [KK] "mamba, from scratch" (khushi keswani)
+//   [AB] "Mamba: Linear-Time Sequence Modeling with Selective State Spaces" (abhik.ai)
+//
+// Per step t, channel e, state n (float32 throughout):
+//   d   = softplus(delta + bias)            [KK] "from ssm to selective ssm"
+//   h_n = exp(d*A_n) * h_n + (d*u) * B_n    [AB] "Original paper, equations and
+//                                           runnable CPU code", row 2
+//   y   = (sum_n C_n h_n + D*u) * silu(z)   same row 2; [AB] row 5
+//
+// Layout on the GPU
+// -----------------
+// One lane owns one channel and keeps all N (<= 16) states of it in VGPRs.
+// A 64-lane wave covers 64 consecutive channels, so every per-step load of
+// u/delta/z and store of y is one contiguous 128-byte (bf16) or 256-byte
+// (fp32) row segment.  B_t and C_t are shared by all channels of a batch
+// row, hence wave-uniform: they are fetched with scalar loads into SGPRs and
+// (bf16) widened on the scalar ALU, costing no VALU and no LDS.
+//
+// Splitting the sequence
+// ----------------------
+// The recurrence is an associative affine map per (channel, state)
+// ([KK] "the scan": (a2, b2) o (a1, b1) = (a2 a1, a2 b1 + b2); [AB] "Compose
+// the updates instead of waiting for every state").  When the batch x channel
+// count alone cannot fill the GPU (the long-sequence case has only 80 waves of
+// channels), the sequence is cut into chunks and processed in three launches:
+//   1. scan_chunk_agg_kernel: per chunk, the state reached from zero and the
+//      sum of the steps d (the product of the retentions over the chunk is
+//      exp(A_n * sum d), so its "a" half needs no per-state work);
+//   2. scan_carry_kernel: a sequential combine over the chunk aggregates,
+//      giving every chunk its incoming state;
+//   3. scan_main_kernel: every chunk rescans from its incoming state and
+//      writes y (and the last chunk writes last_state).
+// Only y and last_state are written to HBM besides the small per-chunk
+// workspace (b * chunks * E * (N + 1) floats).  Nothing here is a dense
+// contraction, so no MFMA is used.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <cstdlib>
+#include <type_traits>
+
+#include "ssm_internal.h"
+#include "ssm_profile.h"
+
+namespace ssm {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kWave = 64;
+
+typedef uint16_t bf16_bits;  // bfloat16 values are passed around as their raw 16 bits
+
+__device__ __forceinline__ float load_elem(const float* p) { return *p; }
+__device__ __forceinline__ float load_elem(const bf16_bits* p) { return __uint_as_float(uint32_t(*p) << 16); }
+__device__ __forceinline__ void store_elem(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_elem(bf16_bits* p, float v) {
+  *p = __builtin_bit_cast(bf16_bits, static_cast<__bf16>(v));  // v_cvt_pk_bf16_f32: round to nearest even
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// softplus(x) = log(1 + e^x) = max(x, 0) + log(1 + e^{-|x|}); both terms finite for every finite x.
+__device__ __forceinline__ float softplus(float x) {
+  const float e = exp2_fast(-fabsf(x) * kLog2e);
+  return fmaxf(x, 0.f) + __builtin_amdgcn_logf(1.f + e) * kLn2;
+}
+
+// silu(z) = z * sigmoid(z) = z / (1 + e^{-z})   ([AB] row 5)
+__device__ __forceinline__ float silu(float z) {
+  return z * __builtin_amdgcn_rcpf(1.f + exp2_fast(-z * kLog2e));
+}
+
+// Row of NS coefficients of B or C at one (batch, step), always float32 (bf16
+// rows are widened once by widen_rows_kernel).  The row address is
+// wave-uniform, so these are scalar loads into SGPRs.  EXACT means N == NS;
+// otherwise entries n >= N read as zero, which keeps padded states at zero.
+template <int NS, bool EXACT>
+__device__ __forceinline__ void load_row(const float* __restrict__ row, int N, float (&out)[NS]) {
+#pragma unroll
+  for (int n = 0; n < NS; n++) out[n] = (EXACT || n < N) ? row[n] : 0.f;
+}
+
+// bf16 -> f32 copy of the B and C rows (b*L*N values each), so the per-step
+// scalar loads of the scan kernels need no unpacking on the scalar ALU.
+__global__ __launch_bounds__(256) void widen_rows_kernel(const bf16_bits* __restrict__ B,
+                                                         const bf16_bits* __restrict__ C, float* __restrict__ Bf,
+                                                         float* __restrict__ Cf, int64_t n) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) {
+    Bf[i] = load_elem(B + i);
+    Cf[i] = load_elem(C + i);
+  }
+}
+
+// Steps per software-pipelined group: the inputs of the next group are in
+// flight while the current group computes.
+constexpr int kGroup = 8;
+
+// Raw buffer resource over a tensor region (CDNA buffer descriptor: 48-bit
+// base, no stride, 2 GiB range, dword3 as used for gfx9-family buffer ops).
+// Per-step loads then need one lane-offset VGPR shared by every stream and a
+// wave-uniform row offset in an SGPR, instead of one 64-bit address per load.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
+}
+__device__ __forceinline__ float buf_load(__amdgpu_buffer_rsrc_t r, int voff, int soff, float*) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+__device__ __forceinline__ float buf_load(__amdgpu_buffer_rsrc_t r, int voff, int soff, bf16_bits*) {
+  return __uint_as_float(uint32_t(__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0)) << 16);
+}
+__device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t r, int voff, int soff, float v, float*) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff, soff, 0);
+}
+__device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t r, int voff, int soff, float v, bf16_bits*) {
+  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(bf16_bits, static_cast<__bf16>(v)), r, voff, soff, 0);
+}
+
+struct BlockPos {
+  int64_t bi, e, ec, t0, t1, row0;  // row0: element index of (bi, t0, first channel of the block)
+  int c;
+  int lane_ld;                        // channel offset inside the block used for loads (clamped)
+  bool active;
+};
+
+// blockIdx.x enumerates (batch, chunk, channel block) with the channel block fastest,
+// so consecutive workgroups read neighbouring channels of the same rows.
+__device__ __forceinline__ BlockPos block_pos(int n_chunks, int e_blocks, int64_t E, int64_t L, int64_t chunk_len) {
+  BlockPos p;
+  const int eb = blockIdx.x % e_blocks;
+  const int rest = blockIdx.x / e_blocks;
+  p.c = rest % n_chunks;
+  p.bi = rest / n_chunks;
+  p.e = int64_t(eb) * kWave + threadIdx.x;
+  p.active = p.e < E;
+  p.ec = p.active ? p.e : E - 1;  // inactive lanes read a valid channel and store nothing
+  p.lane_ld = int(p.ec - int64_t(eb) * kWave);
+  p.t0 = int64_t(p.c) * chunk_len;
+  p.t1 = (p.t0 + chunk_len < L) ? p.t0 + chunk_len : L;
+  p.row0 = (p.bi * L + p.t0) * E + int64_t(eb) * kWave;
+  return p;
+}
+
+// ---------------------------------------------------------------------------
+// 1. chunk aggregates: state reached from zero over the chunk, and sum of d
+// ---------------------------------------------------------------------------
+template <typename T, int NS, bool EXACT, bool SOFTPLUS>
+__global__ __launch_bounds__(kWave) void scan_chunk_agg_kernel(
+    const T* __restrict__ u, const T* __restrict__ delta, const float* __restrict__ A,
+    const float* __restrict__ B, const float* __restrict__ bias, float* __restrict__ carry,
+    float* __restrict__ chunk_sum, int64_t L, int64_t E, int N, int64_t chunk_len, int n_chunks,
+    int agg_chunks, int e_blocks) {
+  // grid covers chunks 0 .. agg_chunks-1 (the last chunk's aggregate is never needed)
+  const BlockPos p = block_pos(agg_chunks, e_blocks, E, L, chunk_len);
+  float A2[NS];
+#pragma unroll
+  for (int n = 0; n < NS; n++) A2[n] = (EXACT || n < N) ? A[p.ec * N + n] * kLog2e : 0.f;
+  const float bv = bias ? bias[p.ec] : 0.f;
+  float h[NS];
+#pragma unroll
+  for (int n = 0; n < NS; n++) h[n] = 0.f;
+  double dsum = 0.0;  // sum of steps, kept in double so long chunks do not drift
+
+  const __amdgpu_buffer_rsrc_t ru = make_rsrc(u + p.row0);
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(delta + p.row0);
+  const int voff = p.lane_ld * int(sizeof(T));
+  const int row_bytes = int(E * int64_t(sizeof(T)));  // the plan keeps chunk_len * row_bytes < 2^31
+  const float* brow = B + (p.bi * L + p.t0) * int64_t(N);
+  float bn[NS];
+  load_row<NS, EXACT>(brow, N, bn);
+
+  int ks = 0;  // step index inside the chunk
+  const int n_steps = int(p.t1 - p.t0);
+  auto step = [&](float d, float x) {
+    d += bv;
+    if (SOFTPLUS) d = softplus(d);
+    float bcur[NS];
+#pragma unroll
+    for (int n = 0; n < NS; n++) bcur[n] = bn[n];
+    if (++ks < n_steps) brow += N;     // the last step re-reads its own row: never past the end of B
+    load_row<NS, EXACT>(brow, N, bn);  // next step's row, fetched while this step computes
+    const float dx = d * x;
+#pragma unroll
+    for (int n = 0; n < NS; n++) h[n] = fmaf(exp2_fast(d * A2[n]), h[n], dx * bcur[n]);
+    dsum += double(d);
+  };
+  const int n_groups = n_steps / kGroup;
+  float cu[kGroup], cd[kGroup];
+  int soff = 0;
+  if (n_groups > 0) {
+#pragma unroll
+    for (int k = 0; k < kGroup; k++) {
+      cu[k] = buf_load(ru, voff, k * row_bytes, (T*)nullptr);
+      cd[k] = buf_load(rd, voff, k * row_bytes, (T*)nullptr);
+    }
+  }
+  for (int g = 0; g < n_groups; ++g) {
+    const int nxt = (g + 1 < n_groups) ? soff + kGroup * row_bytes : soff;  // last group re-reads itself
+    float nu[kGroup], nd[kGroup];
+#pragma unroll
+    for (int k = 0; k < kGroup; k++) {
+      nu[k] = buf_load(ru, voff, nxt + k * row_bytes, (T*)nullptr);
+      nd[k] = buf_load(rd, voff, nxt + k * row_bytes, (T*)nullptr);
+    }
+#pragma unroll
+    for (int k = 0; k < kGroup; k++) step(cd[k], cu[k]);
+#pragma unroll
+    for (int k = 0; k < kGroup; k++) { cu[k] = nu[k]; cd[k] = nd[k]; }
+    soff += kGroup * row_bytes;
+  }
+  for (int k = n_groups * kGroup; k < n_steps; ++k) {
+    step(buf_load(rd, voff, soff, (T*)nullptr), buf_load(ru, voff, soff, (T*)nullptr));
+    soff += row_bytes;
+  }
+  if (p.active) {
+    float* dst = carry + ((p.bi * n_chunks + p.c) * E + p.e) * NS;
+#pragma unroll
+    for (int n = 0; n < NS; n++) dst[n] = h[n];
+    chunk_sum[(p.bi * n_chunks + p.c) * E + p.e] = float(dsum);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 2. carries: state at the end of chunk c = exp(A_n * sum_c d) * (state at the
+//    end of chunk c-1) + aggregate_c, written over aggregate_c.
+// ---------------------------------------------------------------------------
+template <int NS>
+__global__ __launch_bounds__(256) void scan_carry_kernel(const float* __restrict__ A, float* carry,
+                                                         const float* __restrict__ chunk_sum, int64_t b,
+                                                         int64_t E, int N, int n_chunks) {
+  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= b * E * NS) return;
+  const int n = int(gid % NS);
+  const int64_t ch = gid / NS;
+  const int64_t e = ch % E, bi = ch / E;
+  const float a2 = n < N ? A[e * N + n] * kLog2e : 0.f;
+  const int64_t stride = E;  // slots of consecutive chunks of one (batch, channel)
+  const int64_t first = bi * n_chunks * E + e;
+  constexpr int U = 8;  // aggregates of U chunks are loaded before the dependent combines run
+  float h = 0.f;
+  for (int c0 = 0; c0 + 1 < n_chunks; c0 += U) {
+    float Hs[U], Ss[U];
+#pragma unroll
+    for (int k = 0; k < U; k++) {
+      const int c = (c0 + k + 1 < n_chunks) ? c0 + k : c0;  // past the end: reload a valid slot, unused
+      Hs[k] = carry[(first + c * stride) * NS + n];
+      Ss[k] = chunk_sum[first + c * stride];
+    }
+#pragma unroll
+    for (int k = 0; k < U; k++) {
+      if (c0 + k + 1 < n_chunks) {
+        h = fmaf(exp2_fast(a2 * Ss[k]), h, Hs[k]);
+        carry[(first + (c0 + k) * stride) * NS + n] = h;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. main pass: rescan each chunk from its incoming state, write y
+// ---------------------------------------------------------------------------
+// FULL: every lane of every block is a real channel (E % 64 == 0), so the
+// per-step store needs no exec-mask branch.
+template <typename T, int NS, bool EXACT, bool SOFTPLUS, bool HAS_Z, bool FULL>
+__global__ __launch_bounds__(kWave) void scan_main_kernel(
+    const T* __restrict__ u, const T* __restrict__ delta, const float* __restrict__ A,
+    const float* __restrict__ B, const float* __restrict__ C, const float* __restrict__ D,
+    const T* __restrict__ z, const float* __restrict__ bias, T* __restrict__ y,
+    float* __restrict__ last_state, const float* __restrict__ carry, int64_t L, int64_t E, int N,
+    int64_t chunk_len, int n_chunks, int e_blocks) {
+  const BlockPos p = block_pos(n_chunks, e_blocks, E, L, chunk_len);
+  float A2[NS];
+#pragma unroll
+  for (int n = 0; n < NS; n++) A2[n] = (EXACT || n < N) ? A[p.ec * N + n] * kLog2e : 0.f;
+  const float Dv = D ? D[p.ec] : 0.f;
+  const float bv = bias ? bias[p.ec] : 0.f;
+  float h[NS];
+  if (p.c == 0) {
+#pragma unroll
+    for (int n = 0; n < NS; n++) h[n] = 0.f;
+  } else {
+    const float* src = carry + ((p.bi * n_chunks + p.c - 1) * E + p.ec) * NS;
+#pragma unroll
+    for (int n = 0; n < NS; n++) h[n] = src[n];
+  }
+
+  const __amdgpu_buffer_rsrc_t ru = make_rsrc(u + p.row0);
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(delta + p.row0);
+  const __amdgpu_buffer_rsrc_t rz = make_rsrc((HAS_Z ? z : u) + p.row0);
+  const __amdgpu_buffer_rsrc_t ry = make_rsrc(y + p.row0);
+  const int voff = p.lane_ld * int(sizeof(T));
+  const int row_bytes = int(E * int64_t(sizeof(T)));  // the plan keeps chunk_len * row_bytes < 2^31
+  const float* brow = B + (p.bi * L + p.t0) * int64_t(N);
+  const float* crow = C + (p.bi * L + p.t0) * int64_t(N);
+  float bn[NS], cn[NS];
+  load_row<NS, EXACT>(brow, N, bn);
+  load_row<NS, EXACT>(crow, N, cn);
+  int soff = 0;  // byte offset of the current step's row inside the chunk
+  int ks = 0;    // step index inside the chunk
+  const int n_steps = int(p.t1 - p.t0);
+
+  auto step = [&](float d, float x, float zz) {
+    d += bv;
+    if (SOFTPLUS) d = softplus(d);
+    float bcur[NS], ccur[NS];
+#pragma unroll
+    for (int n = 0; n < NS; n++) { bcur[n] = bn[n]; ccur[n] = cn[n]; }
+    if (++ks < n_steps) {  // the last step re-reads its own rows: never past the end of B / C
+      brow += N;
+      crow += N;
+    }
+    load_row<NS, EXACT>(brow, N, bn);  // next step's rows are fetched while this step computes
+    load_row<NS, EXACT>(crow, N, cn);
+    const float dx = d * x;
+    float acc0 = 0.f, acc1 = 0.f;  // two chains halve the dependent-FMA depth of the readout
+#pragma unroll
+    for (int n = 0; n < NS; n++) {
+      h[n] = fmaf(exp2_fast(d * A2[n]), h[n], dx * bcur[n]);
+      if (n % 2 == 0) acc0 = fmaf(ccur[n], h[n], acc0);
+      else acc1 = fmaf(ccur[n], h[n], acc1);
+    }
+    float out = fmaf(Dv, x, acc0 + acc1);
+    if (HAS_Z) out *= silu(zz);
+    if (FULL || p.active) buf_store(ry, voff, soff, out, (T*)nullptr);
+    soff += row_bytes;
+  };
+  const int n_groups = n_steps / kGroup;
+  float cu[kGroup], cd[kGroup], cz[kGroup];
+  if (n_groups > 0) {
+#pragma unroll
+    for (int k = 0; k < kGroup; k++) {
+      cu[k] = buf_load(ru, voff, k * row_bytes, (T*)nullptr);
+      cd[k] = buf_load(rd, voff, k * row_bytes, (T*)nullptr);
+      cz[k] = HAS_Z ? buf_load(rz, voff, k * row_bytes, (T*)nullptr) : 0.f;
+    }
+  }
+  for (int g = 0; g < n_groups; ++g) {
+    const int nxt = (g + 1 < n_groups) ? soff + kGroup * row_bytes : soff;  // last group re-reads itself
+    float nu[kGroup], nd[kGroup], nz[kGroup];
+#pragma unroll
+    for (int k = 0; k < kGroup; k++) {
+      nu[k] = buf_load(ru, voff, nxt + k * row_bytes, (T*)nullptr);
+      nd[k] = buf_load(rd, voff, nxt + k * row_bytes, (T*)nullptr);
+      nz[k] = HAS_Z ? buf_load(rz, voff, nxt + k * row_bytes, (T*)nullptr) : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < kGroup; k++) step(cd[k], cu[k], cz[k]);
+#pragma unroll
+    for (int k = 0; k < kGroup; k++) { cu[k] = nu[k]; cd[k] = nd[k]; cz[k] = nz[k]; }
+  }
+  for (int k = n_groups * kGroup; k < n_steps; ++k) {
+    const float x = buf_load(ru, voff, soff, (T*)nullptr);
+    const float d = buf_load(rd, voff, soff, (T*)nullptr);
+    const float zz = HAS_Z ? buf_load(rz, voff, soff, (T*)nullptr) : 0.f;
+    step(d, x, zz);
+  }
+  if (last_state && p.c == n_chunks - 1 && p.active) {
+    float* dst = last_state + (p.bi * E + p.e) * N;
+#pragma unroll
+    for (int n = 0; n < NS; n++)
+      if (EXACT || n < N) dst[n] = h[n];
+  }
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, int64_t n) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0.f;
+}
+
+// ---------------------------------------------------------------------------
+// single-token state update ([AB] row 6, the SSM half of `step`)
+// ---------------------------------------------------------------------------
+// LPC = NS / 4 lanes share one channel, each holding 4 consecutive states, so
+// a wave reads and writes the fp32 state as one contiguous 1 KiB block per
+// instruction.  The partial readouts are summed across the LPC lanes.
+template <typename T, int NS, bool VEC, bool SOFTPLUS, bool HAS_Z>
+__global__ __launch_bounds__(256) void state_update_kernel(
+    float* __restrict__ state, const T* __restrict__ x, const T* __restrict__ delta,
+    const float* __restrict__ A, const T* __restrict__ B, const T* __restrict__ C,
+    const float* __restrict__ D, const T* __restrict__ z, const float* __restrict__ bias,
+    T* __restrict__ y, int64_t n_ch, int64_t E, int N) {
+  constexpr int LPC = NS / 4;
+  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t ch = gid / LPC;
+  const int q = int(gid % LPC);
+  const bool active = ch < n_ch;
+  const int64_t cc = active ? ch : n_ch - 1;
+  const int64_t e = cc % E, bi = cc / E;
+  const int n0 = 4 * q;
+
+  float s[4], a[4], bn[4], cn[4];
+  if constexpr (VEC) {  // N == NS, state / A / B / C rows aligned for vector access
+    const float4 sv = *reinterpret_cast<const float4*>(state + cc * NS + n0);
+    const float4 av = *reinterpret_cast<const float4*>(A + e * NS + n0);
+    s[0] = sv.x; s[1] = sv.y; s[2] = sv.z; s[3] = sv.w;
+    a[0] = av.x; a[1] = av.y; a[2] = av.z; a[3] = av.w;
+    if constexpr (std::is_same<T, float>::value) {
+      const float4 b4 = *reinterpret_cast<const float4*>(B + bi * NS + n0);
+      const float4 c4 = *reinterpret_cast<const float4*>(C + bi * NS + n0);
+      bn[0] = b4.x; bn[1] = b4.y; bn[2] = b4.z; bn[3] = b4.w;
+      cn[0] = c4.x; cn[1] = c4.y; cn[2] = c4.z; cn[3] = c4.w;
+    } else {
+      const uint2 b2 = *reinterpret_cast<const uint2*>(B + bi * NS + n0);
+      const uint2 c2 = *reinterpret_cast<const uint2*>(C + bi * NS + n0);
+      bn[0] = __uint_as_float(b2.x << 16); bn[1] = __uint_as_float(b2.x & 0xffff0000u);
+      bn[2] = __uint_as_float(b2.y << 16); bn[3] = __uint_as_float(b2.y & 0xffff0000u);
+      cn[0] = __uint_as_float(c2.x << 16); cn[1] = __uint_as_float(c2.x & 0xffff0000u);
+      cn[2] = __uint_as_float(c2.y << 16); cn[3] = __uint_as_float(c2.y & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      const int n = n0 + k;
+      const bool in = n < N;
+      s[k] = in ? state[cc * N + n] : 0.f;
+      a[k] = in ? A[e * N + n] : 0.f;
+      bn[k] = in ? load_elem(B + bi * N + n) : 0.f;
+      cn[k] = in ? load_elem(C + bi * N + n) : 0.f;
+    }
+  }
+  float d = load_elem(delta + cc) + (bias ? bias[e] : 0.f);
+  if (SOFTPLUS) d = softplus(d);
+  const float xv = load_elem(x + cc);
+  const float dx = d * xv;
+  float acc = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    s[k] = fmaf(exp2_fast(d * a[k] * kLog2e), s[k], dx * bn[k]);
+    acc = fmaf(cn[k], s[k], acc);
+  }
+#pragma unroll
+  for (int off = LPC / 2; off >= 1; off /= 2) acc += __shfl_xor(acc, off, LPC);
+  if (active) {
+    if constexpr (VEC) {
+      *reinterpret_cast<float4*>(state + cc * NS + n0) = make_float4(s[0], s[1], s[2], s[3]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; k++)
+        if (n0 + k < N) state[cc * N + n0 + k] = s[k];
+    }
+    if (q == 0) {
+      float out = fmaf(D ? D[e] : 0.f, xv, acc);
+      if (HAS_Z) out *= silu(load_elem(z + cc));
+      store_elem(y + cc, out);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+// Every launch goes through here.  With profiling on, it is bracketed by two
+// HIP events on the launch stream (see ssm_profile_enable in ssm.h).
+template <typename Kern, typename... Args>
+hipError_t launch_kind(int kind, Kern k, int64_t blocks, int threads, hipStream_t s, Args... args) {
+  if (blocks <= 0) return hipSuccess;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  const bool prof = profile_begin(s, &ev0, &ev1);
+  hipLaunchKernelGGL(k, dim3(unsigned(blocks)), dim3(threads), 0, s, args...);
+  hipError_t err = hipGetLastError();
+  if (prof) profile_end(kind, s, ev0, ev1);
+  return err;
+}
+
+// Scan launch resources: float rows of B and C (the caller's arrays for fp32
+// I/O, widened copies for bf16) and the per-chunk workspace.
+struct ScanBufs {
+  const float* B;
+  const float* C;
+  float* carry;  // [b][n_chunks][E][NS] chunk aggregates, then incoming states
+  float* csum;   // [b][n_chunks][E] sum of steps per chunk
+};
+
+template <typename T, int NS, bool EXACT, bool SOFTPLUS, bool HAS_Z, bool FULL>
+hipError_t run_scan(const ScanArgs& a, const ScanPlan& pl, const ScanBufs& w) {
+  const T* u = static_cast<const T*>(a.u);
+  const T* dl = static_cast<const T*>(a.delta);
+  const T* z = static_cast<const T*>(a.z);
+  T* y = static_cast<T*>(a.y);
+  const int N = int(a.N);
+  hipError_t err = hipSuccess;
+  if (pl.n_chunks > 1) {
+    const int agg = pl.n_chunks - 1;
+    err = launch_kind(kKindAgg, scan_chunk_agg_kernel<T, NS, EXACT, SOFTPLUS>, a.b * agg * pl.e_blocks, kWave, a.stream, u, dl,
+                 a.A, w.B, a.bias, w.carry, w.csum, a.L, a.E, N, pl.chunk_len, pl.n_chunks, agg, pl.e_blocks);
+    if (err != hipSuccess) return err;
+    const int64_t lanes = a.b * a.E * NS;
+    err = launch_kind(kKindCarry, scan_carry_kernel<NS>, (lanes + 255) / 256, 256, a.stream, a.A, w.carry, (const float*)w.csum,
+                 a.b, a.E, N, pl.n_chunks);
+    if (err != hipSuccess) return err;
+  }
+  return launch_kind(kKindMain, scan_main_kernel<T, NS, EXACT, SOFTPLUS, HAS_Z, FULL>, a.b * pl.n_chunks * pl.e_blocks, kWave,
+                a.stream, u, dl, a.A, w.B, w.C, a.D, z, a.bias, y, a.last_state, (const float*)w.carry, a.L, a.E, N,
+                pl.chunk_len, pl.n_chunks, pl.e_blocks);
+}
+
+template <typename T, int NS, bool EXACT, bool FULL>
+hipError_t scan_flags(const ScanArgs& a, const ScanPlan& pl, const ScanBufs& w) {
+  const bool z = a.z != nullptr;
+  if (a.softplus) {
+    return z ? run_scan<T, NS, EXACT, true, true, FULL>(a, pl, w) : run_scan<T, NS, EXACT, true, false, FULL>(a, pl, w);
+  }
+  return z ? run_scan<T, NS, EXACT, false, true, FULL>(a, pl, w) : run_scan<T, NS, EXACT, false, false, FULL>(a, pl, w);
+}
+
+template <typename T, int NS, bool EXACT>
+hipError_t scan_full(const ScanArgs& a, const ScanPlan& pl, const ScanBufs& w) {
+  return (a.E % kWave == 0) ? scan_flags<T, NS, EXACT, true>(a, pl, w) : scan_flags<T, NS, EXACT, false>(a, pl, w);
+}
+
+// state slots per channel in the workspace: N for the exact-size kernels, 16 for the padded one
+int scan_states(int64_t N) { return (N == 4 || N == 8 || N == 16) ? int(N) : 16; }
+
+template <typename T>
+hipError_t scan_typed(const ScanArgs& a, const ScanPlan& pl, const ScanBufs& w) {
+  if (a.N == 16) return scan_full<T, 16, true>(a, pl, w);
+  if (a.N == 8) return scan_full<T, 8, true>(a, pl, w);
+  if (a.N == 4) return scan_full<T, 4, true>(a, pl, w);
+  return scan_full<T, 16, false>(a, pl, w);
+}
+
+template <typename T, int NS, bool VEC>
+hipError_t update_flags(const UpdateArgs& a) {
+  const T* x = static_cast<const T*>(a.x);
+  const T* dl = static_cast<const T*>(a.delta);
+  const T* B = static_cast<const T*>(a.B);
+  const T* C = static_cast<const T*>(a.C);
+  const T* z = static_cast<const T*>(a.z);
+  T* y = static_cast<T*>(a.y);
+  const int64_t n_ch = a.b * a.E;
+  const int64_t threads = n_ch * (NS / 4);
+  const int64_t blocks = (threads + 255) / 256;
+  const int N = int(a.N);
+#define SSM_UPDATE_LAUNCH(SP, HZ)                                                                            \
+  return launch_kind(kKindUpdate, state_update_kernel<T, NS, VEC, SP, HZ>, blocks, 256, a.stream, a.state, x, dl, a.A, B, C, a.D, \
+                z, a.bias, y, n_ch, a.E, N)
+  if (a.softplus) {
+    if (z) { SSM_UPDATE_LAUNCH(true, true); }
+    SSM_UPDATE_LAUNCH(true, false);
+  }
+  if (z) { SSM_UPDATE_LAUNCH(false, true); }
+  SSM_UPDATE_LAUNCH(false, false);
+#undef SSM_UPDATE_LAUNCH
+}
+
+template <typename T>
+hipError_t update_typed(const UpdateArgs& a) {
+  const size_t row_align = std::is_same<T, float>::value ? 16 : 8;
+  const bool vec = (a.N == 4 || a.N == 8 || a.N == 16) && reinterpret_cast<uintptr_t>(a.state) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(a.A) % 16 == 0 && reinterpret_cast<uintptr_t>(a.B) % row_align == 0 &&
+                   reinterpret_cast<uintptr_t>(a.C) % row_align == 0;
+  if (vec) {
+    if (a.N == 16) return update_flags<T, 16, true>(a);
+    if (a.N == 8) return update_flags<T, 8, true>(a);
+    return update_flags<T, 4, true>(a);
+  }
+  if (a.N <= 4) return update_flags<T, 4, false>(a);
+  if (a.N <= 8) return update_flags<T, 8, false>(a);
+  return update_flags<T, 16, false>(a);
+}
+
+}  // namespace
+
+ScanPlan plan_scan(int64_t b, int64_t L, int64_t E, int elem_bytes) {
+  ScanPlan pl;
+  pl.e_blocks = int((E + kWave - 1) / kWave);
+  // Enough waves that every SIMD of the 256 CUs sees several rounds of them
+  // (register use allows 4 resident per SIMD); measured best on the long
+  // sequence.  The sequence is cut only when batch x channel blocks alone
+  // cannot provide them.
+  int64_t target = 16384;
+  if (const char* s = std::getenv("SSM_SCAN_TARGET_WAVES")) {
+    const long v = std::strtol(s, nullptr, 10);
+    if (v > 0) target = v;
+  }
+  int64_t min_chunk = 64;
+  if (const char* s = std::getenv("SSM_SCAN_MIN_CHUNK")) {
+    const long v = std::strtol(s, nullptr, 10);
+    if (v > 0) min_chunk = v;
+  }
+  const int64_t base = b * pl.e_blocks;
+  pl.chunk_len = std::max<int64_t>(L, 1);
+  pl.n_chunks = 1;
+  if (base > 0 && base * 2 < target && L > min_chunk) {
+    const int64_t want = (target + base - 1) / base;
+    int64_t len = std::max<int64_t>(min_chunk, (L + want - 1) / want);
+    len = (len + 7) / 8 * 8;
+    pl.chunk_len = len;
+  }
+  // a chunk's rows are addressed with 32-bit buffer offsets: keep them below 2^31
+  const int64_t row_bytes = std::max<int64_t>(E, 1) * elem_bytes;
+  const int64_t max_len = (int64_t(0x7fffffff) - kWave * elem_bytes) / row_bytes;
+  if (max_len >= 1 && pl.chunk_len > max_len) pl.chunk_len = max_len;
+  if (max_len < 1) pl.chunk_len = 0;  // rejected by the caller
+  pl.n_chunks = pl.chunk_len > 0 ? int((std::max<int64_t>(L, 1) + pl.chunk_len - 1) / pl.chunk_len) : 0;
+  return pl;
+}
+
+hipError_t launch_scan(const ScanArgs& a) {
+  if (a.b == 0 || a.E == 0) return hipSuccess;
+  if (a.L == 0) {
+    if (!a.last_state) return hipSuccess;
+    const int64_t n = a.b * a.E * a.N;
+    return launch_kind(kKindFill, fill_zero_kernel, (n + 255) / 256, 256, a.stream, a.last_state, n);
+  }
+  const ScanPlan pl = plan_scan(a.b, a.L, a.E, a.dtype == 0 ? 4 : 2);
+  // workspace: [chunk aggregates | chunk step sums | widened B rows | widened C rows]
+  const size_t slots = pl.n_chunks > 1 ? size_t(a.b) * size_t(pl.n_chunks) * size_t(a.E) : 0;
+  const size_t n_agg = slots * size_t(scan_states(a.N));
+  const size_t n_rows = a.dtype == 0 ? 0 : size_t(a.b) * size_t(a.L) * size_t(a.N);
+  const size_t n_floats = n_agg + slots + 2 * n_rows;
+  void* ws = nullptr;
+  if (n_floats > 0) {
+    hipError_t err = hipMallocAsync(&ws, n_floats * sizeof(float), a.stream);
+    if (err != hipSuccess) return err;
+  }
+  float* f = static_cast<float*>(ws);
+  ScanBufs w;
+  w.carry = slots ? f : nullptr;
+  w.csum = slots ? f + n_agg : nullptr;
+  hipError_t err = hipSuccess;
+  if (a.dtype == 0) {
+    w.B = static_cast<const float*>(a.B);
+    w.C = static_cast<const float*>(a.C);
+  } else {
+    float* Bf = f + n_agg + slots;
+    float* Cf = Bf + n_rows;
+    err = launch_kind(kKindWiden, widen_rows_kernel, int64_t((n_rows + 255) / 256), 256, a.stream,
+                 static_cast<const bf16_bits*>(a.B), static_cast<const bf16_bits*>(a.C), Bf, Cf, int64_t(n_rows));
+    w.B = Bf;
+    w.C = Cf;
+  }
+  if (err == hipSuccess) err = a.dtype == 0 ? scan_typed<float>(a, pl, w) : scan_typed<bf16_bits>(a, pl, w);
+  if (ws) {
+    hipError_t ferr = hipFreeAsync(ws, a.stream);
+    if (err == hipSuccess) err = ferr;
+  }
+  return err;
+}
+
+hipError_t launch_state_update(const UpdateArgs& a) {
+  if (a.b == 0 || a.E == 0) return hipSuccess;
+  return a.dtype == 0 ? update_typed<float>(a) : update_typed<bf16_bits>(a);
+}
+
+}  // namespace ssm

@@ -1,0 +1,24 @@
+// Opt-in per-kernel timing with HIP events (benchmark support).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace ssm {
+
+// Kinds of kernels the library launches; indices of ssm_profile_read().
+enum : int {
+  kKindWiden = 0,   // bf16 -> f32 copy of the B / C rows
+  kKindAgg = 1,     // per-chunk aggregates
+  kKindCarry = 2,   // carries across chunk boundaries
+  kKindMain = 3,    // main scan pass
+  kKindFill = 4,    // zero last_state (L == 0)
+  kKindUpdate = 5,  // single-token state update
+  kNumKinds = 6
+};
+
+// When profiling is on, creates and records the start event on `s` and returns true.
+bool profile_begin(hipStream_t s, hipEvent_t* ev0, hipEvent_t* ev1);
+// Records the stop event and files the pair under `kind`.
+void profile_end(int kind, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+
+}  // namespace ssm

@@ -1,0 +1,159 @@
+"""Host-side checks of the C ABI: no GPU needed.
+
+* libssm.so loads and exports every function include/ssm.h declares;
+* status strings;
+* argument validation returns the documented ssm_status before anything is
+  enqueued (every call here is invalid or a no-op, so no HIP work happens);
+* the Python binding refuses CPU tensors (there is no CPU fallback) and
+  raises when the library is missing.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import selective_state_space_35_amd as ssm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssm.h")
+
+OK, ERR_NULL, ERR_DIM, ERR_DTYPE, ERR_N, ERR_ALIGN, ERR_HIP = 0, -1, -2, -3, -4, -5, -6
+FAKE = 0x10000  # a non-null, 64 KiB-aligned address that is never dereferenced by these calls
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return re.findall(r"SSM_API\s+[\w\s\*]+?\b(ssm_\w+)\s*\(", src)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ssm.library_path()):
+        pytest.skip("libssm.so not built")
+    return ssm.load_library()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    assert {"ssm_scan_fwd", "ssm_state_update", "ssm_status_string", "ssm_last_hip_error",
+            "ssm_version"} <= set(names)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in ssm.h but not exported"
+    out = os.popen(f"nm -D --defined-only {ssm.library_path()}").read()
+    exported = set(re.findall(r" T (\w+)", out))
+    assert set(declared_functions()) <= exported
+    # nothing else leaks out of the library's C namespace
+    assert {s for s in exported if s.startswith("ssm_")} == set(declared_functions())
+
+
+def test_status_strings(lib):
+    for code in (OK, ERR_NULL, ERR_DIM, ERR_DTYPE, ERR_N, ERR_ALIGN, ERR_HIP):
+        s = ssm.ssm_status_string(code)
+        assert s and s != "unknown status"
+    assert ssm.ssm_status_string(12345) == "unknown status"
+    assert lib.ssm_version() >= 10000
+
+
+def scan(lib, u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, bias=None, softplus=1, y=FAKE,
+         last=None, b=1, L=8, E=64, N=16, dtype=0):
+    return lib.ssm_scan_fwd(u, delta, A, B, C, D, z, bias, softplus, y, last, b, L, E, N, dtype, None)
+
+
+def update(lib, state=FAKE, x=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, bias=None, softplus=1,
+           y=FAKE, b=1, E=64, N=16, dtype=0):
+    return lib.ssm_state_update(state, x, delta, A, B, C, D, z, bias, softplus, y, b, E, N, dtype, None)
+
+
+def test_scan_validation(lib):
+    assert scan(lib, dtype=2) == ERR_DTYPE
+    assert scan(lib, dtype=-1) == ERR_DTYPE
+    assert scan(lib, b=-1) == ERR_DIM
+    assert scan(lib, L=-5) == ERR_DIM
+    assert scan(lib, E=-64) == ERR_DIM
+    assert scan(lib, N=0) == ERR_N
+    assert scan(lib, N=17) == ERR_N
+    assert scan(lib, u=None) == ERR_NULL
+    assert scan(lib, delta=None) == ERR_NULL
+    assert scan(lib, A=None) == ERR_NULL
+    assert scan(lib, B=None) == ERR_NULL
+    assert scan(lib, C=None) == ERR_NULL
+    assert scan(lib, y=None) == ERR_NULL
+    assert scan(lib, u=FAKE + 2, dtype=0) == ERR_ALIGN      # fp32 needs 4-byte alignment
+    assert scan(lib, u=FAKE + 1, dtype=1) == ERR_ALIGN      # bf16 needs 2-byte alignment
+    assert scan(lib, A=FAKE + 2) == ERR_ALIGN
+    assert scan(lib, last=FAKE + 1) == ERR_ALIGN
+    assert scan(lib, z=FAKE + 1, dtype=1) == ERR_ALIGN
+    assert scan(lib, b=1 << 40, L=1 << 20, E=1 << 10) == ERR_DIM  # b*L*E*4 overflows int64
+
+
+def test_scan_noop_sizes_return_ok_without_work(lib):
+    # b == 0 or E == 0: nothing to do, pointers are not even looked at
+    assert scan(lib, b=0, u=None, delta=None, A=None, B=None, C=None, y=None) == OK
+    assert scan(lib, E=0, u=None, delta=None, A=None, B=None, C=None, y=None) == OK
+
+
+def test_update_validation(lib):
+    assert update(lib, dtype=7) == ERR_DTYPE
+    assert update(lib, b=-2) == ERR_DIM
+    assert update(lib, N=0) == ERR_N
+    assert update(lib, N=32) == ERR_N
+    for k in ("state", "x", "delta", "A", "B", "C", "y"):
+        assert update(lib, **{k: None}) == ERR_NULL, k
+    assert update(lib, state=FAKE + 2) == ERR_ALIGN
+    assert update(lib, x=FAKE + 1, dtype=1) == ERR_ALIGN
+    assert update(lib, b=0, state=None) == OK
+
+
+def test_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    if not os.path.exists(ssm.library_path()):
+        pytest.skip("libssm.so not built")
+    b, L, E, N = 1, 4, 8, 4
+    u = torch.zeros(b, L, E)
+    A = -torch.ones(E, N)
+    BC = torch.zeros(b, L, N)
+    with pytest.raises(ValueError, match="GPU"):
+        ssm.ssm_scan_fwd(u, u, A, BC, BC)
+    with pytest.raises(ValueError, match="GPU"):
+        ssm.ssm_state_update(torch.zeros(b, E, N), torch.zeros(b, E), torch.zeros(b, E), A,
+                             torch.zeros(b, N), torch.zeros(b, N))
+
+
+def test_binding_raises_when_library_missing(monkeypatch):
+    monkeypatch.setattr(ssm, "_lib", None)
+    monkeypatch.setattr(ssm, "_LIB_PATH", "/nonexistent/libssm.so")
+    with pytest.raises(ImportError, match="build the HIP library"):
+        ssm.load_library()
+
+
+def test_scan_plan_query(lib, monkeypatch):
+    monkeypatch.delenv("SSM_SCAN_TARGET_WAVES", raising=False)
+    monkeypatch.delenv("SSM_SCAN_MIN_CHUNK", raising=False)
+    # a tiny problem is one chunk; big batch x channel counts need no split
+    assert ssm.ssm_scan_plan(1, 64, 16, 4, "f32") == (64, 1)
+    assert ssm.ssm_scan_plan(256, 4096, 8192, 16, "bf16")[1] == 1
+    for (b, L, E, N, dt) in [(32, 512, 512, 16, "f32"), (8, 2048, 1536, 16, "bf16"), (1, 65536, 5120, 16, "bf16"),
+                             (3, 1003, 70, 5, "bf16"), (1, 1 << 20, 64, 16, "f32")]:
+        cl, nc = ssm.ssm_scan_plan(b, L, E, N, dt)
+        assert cl >= 1 and nc >= 1
+        assert (nc - 1) * cl < L <= nc * cl, (b, L, E, cl, nc)  # chunks tile the sequence exactly
+        assert cl * E * (4 if dt == "f32" else 2) < 2 ** 31  # 32-bit buffer offsets inside a chunk
+    # the tuning variables are honoured
+    monkeypatch.setenv("SSM_SCAN_TARGET_WAVES", "100000")
+    monkeypatch.setenv("SSM_SCAN_MIN_CHUNK", "8")
+    assert ssm.ssm_scan_plan(3, 1003, 70, 16, "bf16") == (8, 126)
+    monkeypatch.setenv("SSM_SCAN_MIN_CHUNK", "1000")
+    assert ssm.ssm_scan_plan(3, 1003, 70, 16, "bf16") == (1000, 2)
+    # a row too wide for 32-bit offsets is rejected
+    with pytest.raises(ssm.SSMError):
+        ssm.ssm_scan_plan(1, 4, 1 << 31, 16, "f32")
+
+
+def test_profile_read_with_nothing_recorded(lib):
+    out = ssm.ssm_profile_read()
+    assert set(out) == {"widen_rows", "chunk_aggregate", "chunk_carry", "scan_main", "fill_zero", "state_update"}
+    assert all(v == (0.0, 0) for v in out.values())
