@@ -111,6 +111,22 @@ SSM_API int ssm_scan_fwd(const void* u, const void* delta, const float* A, const
                  int64_t b, int64_t L, int64_t E, int64_t N, int dtype, void* stream);
 
 /*
+ * Selective scan that continues from a given state: identical to
+ * ssm_scan_fwd except that the recurrence starts from initial_state
+ * [b, E, N] (float, device; NULL means zero) instead of zero.  An optional
+ * incoming state is part of the recurrence's definition ([AB] row 2: the loop
+ * continues an earlier prefix), so
+ *   scan(L1 + L2) == scan(L2, initial_state = last_state of scan(L1))
+ * and a prefill can hand its state to ssm_state_update for decoding.
+ * With L == 0, last_state receives a copy of initial_state.
+ * initial_state must not overlap last_state (or any other output).
+ */
+SSM_API int ssm_scan_fwd_from(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                              const float* D, const void* z, const float* delta_bias, int softplus,
+                              const float* initial_state, void* y, float* last_state,
+                              int64_t b, int64_t L, int64_t E, int64_t N, int dtype, void* stream);
+
+/*
  * One recurrent step for every (b, e) -- the SSM half of the decode step of
  * [AB] row 6 "Carry both buffers to the next token":
  *   d          = delta[b,e] + delta_bias[e], softplus(d) when softplus != 0
@@ -150,7 +166,7 @@ SSM_API int ssm_scan_plan(int64_t b, int64_t L, int64_t E, int64_t N, int dtype,
  * stream.  ssm_profile_read() waits for those events, writes per-kind totals
  * (milliseconds) and launch counts for kinds 0 .. n_kinds-1 and clears the
  * record.  Kinds: 0 widen_rows (bf16 B/C rows to f32), 1 chunk_aggregate,
- * 2 chunk_carry, 3 scan_main, 4 fill_zero, 5 state_update; names from
+ * 2 chunk_carry, 3 scan_main, 4 fill_state, 5 state_update; names from
  * ssm_profile_kind_name().  Off by default; the events add a few
  * microseconds per launch.  Process-wide, thread-safe.
  */

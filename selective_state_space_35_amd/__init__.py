@@ -24,7 +24,7 @@ import ctypes
 import os
 
 __all__ = [
-    "ssm_scan_fwd", "ssm_state_update", "ssm_scan_plan", "ssm_profile_enable", "ssm_profile_read",
+    "ssm_scan_fwd", "ssm_scan_fwd_from", "ssm_state_update", "ssm_scan_plan", "ssm_profile_enable", "ssm_profile_read",
     "ssm_status_string", "library_path", "SSMError",
     "SSM_F32", "SSM_BF16", "load_library",
 ]
@@ -68,6 +68,8 @@ def load_library():
     lib = ctypes.CDLL(_LIB_PATH)
     lib.ssm_scan_fwd.restype = _int
     lib.ssm_scan_fwd.argtypes = [_vp] * 8 + [_int, _vp, _vp] + [_i64] * 4 + [_int, _vp]
+    lib.ssm_scan_fwd_from.restype = _int
+    lib.ssm_scan_fwd_from.argtypes = [_vp] * 8 + [_int, _vp, _vp, _vp] + [_i64] * 4 + [_int, _vp]
     lib.ssm_state_update.restype = _int
     lib.ssm_state_update.argtypes = [_vp] * 9 + [_int, _vp] + [_i64] * 3 + [_int, _vp]
     lib.ssm_status_string.restype = ctypes.c_char_p
@@ -159,8 +161,12 @@ def _raise_on(fn, status):
 
 
 def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=False, y=None,
-                 last_state=None, return_last_state=True):
-    """Selective scan forward on the GPU.  Returns ``(y, last_state)`` (last_state None if not requested)."""
+                 last_state=None, return_last_state=True, initial_state=None):
+    """Selective scan forward on the GPU.  Returns ``(y, last_state)`` (last_state None if not requested).
+
+    ``initial_state`` [b, E, N] float32 continues the recurrence from that state
+    (the C entry point ``ssm_scan_fwd_from``); None starts from zero.
+    """
     import torch
 
     lib = load_library()
@@ -191,12 +197,27 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=Fa
         last_state = torch.empty((b, E, N), dtype=torch.float32, device=device)
     elif last_state is not None:
         _check(torch, "last_state", last_state, (b, E, N), torch.float32, device)
+    _check(torch, "initial_state", initial_state, (b, E, N), torch.float32, device, optional=True)
+    if initial_state is not None and last_state is not None and initial_state.data_ptr() == last_state.data_ptr():
+        raise ValueError("initial_state must not be the last_state buffer")
     with torch.cuda.device(device):
-        status = lib.ssm_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                                  _ptr(delta_bias), int(bool(softplus)), _ptr(y), _ptr(last_state),
-                                  b, L, E, N, code, _stream_of(torch, device))
-    _raise_on("ssm_scan_fwd", status)
+        if initial_state is None:
+            status = lib.ssm_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                      _ptr(delta_bias), int(bool(softplus)), _ptr(y), _ptr(last_state),
+                                      b, L, E, N, code, _stream_of(torch, device))
+        else:
+            status = lib.ssm_scan_fwd_from(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                           _ptr(delta_bias), int(bool(softplus)), _ptr(initial_state), _ptr(y),
+                                           _ptr(last_state), b, L, E, N, code, _stream_of(torch, device))
+    _raise_on("ssm_scan_fwd" if initial_state is None else "ssm_scan_fwd_from", status)
     return y, last_state
+
+
+def ssm_scan_fwd_from(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=False, initial_state=None,
+                      y=None, last_state=None, return_last_state=True):
+    """``ssm_scan_fwd`` continuing from ``initial_state`` (same name as the C entry point)."""
+    return ssm_scan_fwd(u, delta, A, B, C, D, z, delta_bias, softplus, y=y, last_state=last_state,
+                        return_last_state=return_last_state, initial_state=initial_state)
 
 
 def ssm_state_update(state, x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=False, y=None):

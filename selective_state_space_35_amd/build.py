@@ -40,21 +40,22 @@ def _run(cmd, verbose):
         print("\n".join(noise), flush=True)
 
 
-def build(verbose: bool = False) -> str:
-    objdir = os.path.join(PKG, "_build")
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Compile and link libssm.so.  ``defines`` (e.g. ["SSM_KGROUP=4"]) override tuning macros."""
+    objdir = os.path.join(PKG, "_build" if not defines else "_build_" + "_".join(d.replace("=", "") for d in defines))
     os.makedirs(objdir, exist_ok=True)
     objs = []
     cmds = []
     for src in SOURCES:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([HIPCC, *COMMON, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

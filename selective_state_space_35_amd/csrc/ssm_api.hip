@@ -46,6 +46,14 @@ extern "C" {
 int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C, const float* D,
                  const void* z, const float* delta_bias, int softplus, void* y, float* last_state, int64_t b,
                  int64_t L, int64_t E, int64_t N, int dtype, void* stream) {
+  return ssm_scan_fwd_from(u, delta, A, B, C, D, z, delta_bias, softplus, nullptr, y, last_state, b, L, E, N, dtype,
+                           stream);
+}
+
+int ssm_scan_fwd_from(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                      const float* D, const void* z, const float* delta_bias, int softplus,
+                      const float* initial_state, void* y, float* last_state, int64_t b, int64_t L, int64_t E,
+                      int64_t N, int dtype, void* stream) {
   int st = check_sizes(b, L, E, N, dtype);
   if (st != SSM_OK) return st;
   if (b == 0 || E == 0) return SSM_OK;
@@ -54,7 +62,7 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
   const void* streamed[] = {u, delta, B, C, z, y};
   for (const void* p : streamed)
     if (p && !aligned(p, es)) return SSM_ERR_ALIGN;
-  const void* fl[] = {A, D, delta_bias, last_state};
+  const void* fl[] = {A, D, delta_bias, last_state, initial_state};
   for (const void* p : fl)
     if (p && !aligned(p, 4)) return SSM_ERR_ALIGN;
   // with L > 0 the chunk count is bounded by L / 64 and the grid by b * E / 64 * chunks
@@ -64,7 +72,7 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
 
   ssm::ScanArgs a;
   a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias;
-  a.softplus = softplus ? 1 : 0; a.y = y; a.last_state = last_state;
+  a.softplus = softplus ? 1 : 0; a.y = y; a.last_state = last_state; a.h0 = initial_state;
   a.b = b; a.L = L; a.E = E; a.N = N; a.dtype = dtype;
   a.stream = static_cast<hipStream_t>(stream);
   return hip_status(ssm::launch_scan(a));
@@ -84,8 +92,10 @@ int ssm_state_update(float* state, const void* x, const void* delta, const float
   const void* fl[] = {state, A, D, delta_bias};
   for (const void* p : fl)
     if (p && !aligned(p, 4)) return SSM_ERR_ALIGN;
-  int64_t threads = 0;
-  if (!mul_ok(b, E, &threads) || !mul_ok(threads, 4, &threads) || threads / 256 > INT32_MAX) return SSM_ERR_DIM;
+  // one row of workgroups per batch row; channels and lanes use 32-bit indices
+  int64_t blocks = 0;
+  if (E > (int64_t(1) << 28) || b > INT32_MAX || !mul_ok(b, (E * 4 + 255) / 256, &blocks) || blocks > INT32_MAX)
+    return SSM_ERR_DIM;
 
   ssm::UpdateArgs a;
   a.state = state; a.x = x; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias;

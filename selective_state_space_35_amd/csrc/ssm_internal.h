@@ -19,6 +19,7 @@ struct ScanArgs {
   int softplus;
   void* y;
   float* last_state;   // nullable
+  const float* h0;     // nullable: incoming state [b, E, N] (zero when null)
   int64_t b, L, E, N;
   int dtype;           // 0 = f32, 1 = bf16
   hipStream_t stream;

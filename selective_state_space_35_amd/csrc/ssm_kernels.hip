@@ -100,7 +100,21 @@ __global__ __launch_bounds__(256) void widen_rows_kernel(const bf16_bits* __rest
 
 // Steps per software-pipelined group: the inputs of the next group are in
 // flight while the current group computes.
-constexpr int kGroup = 8;
+#ifndef SSM_KGROUP
+#define SSM_KGROUP 4
+#endif
+constexpr int kGroup = SSM_KGROUP;
+
+// Optional occupancy hint for the scan kernels (waves per SIMD the register
+// allocation must allow); 0 leaves the choice to the compiler.
+#ifndef SSM_SCAN_WAVES_PER_EU
+#define SSM_SCAN_WAVES_PER_EU 0
+#endif
+#if SSM_SCAN_WAVES_PER_EU > 0
+#define SSM_SCAN_OCCUPANCY __attribute__((amdgpu_waves_per_eu(SSM_SCAN_WAVES_PER_EU)))
+#else
+#define SSM_SCAN_OCCUPANCY
+#endif
 
 // Raw buffer resource over a tensor region (CDNA buffer descriptor: 48-bit
 // base, no stride, 2 GiB range, dword3 as used for gfx9-family buffer ops).
@@ -151,7 +165,7 @@ __device__ __forceinline__ BlockPos block_pos(int n_chunks, int e_blocks, int64_
 // 1. chunk aggregates: state reached from zero over the chunk, and sum of d
 // ---------------------------------------------------------------------------
 template <typename T, int NS, bool EXACT, bool SOFTPLUS>
-__global__ __launch_bounds__(kWave) void scan_chunk_agg_kernel(
+__global__ __launch_bounds__(kWave) SSM_SCAN_OCCUPANCY void scan_chunk_agg_kernel(
     const T* __restrict__ u, const T* __restrict__ delta, const float* __restrict__ A,
     const float* __restrict__ B, const float* __restrict__ bias, float* __restrict__ carry,
     float* __restrict__ chunk_sum, int64_t L, int64_t E, int N, int64_t chunk_len, int n_chunks,
@@ -230,33 +244,42 @@ __global__ __launch_bounds__(kWave) void scan_chunk_agg_kernel(
 // 2. carries: state at the end of chunk c = exp(A_n * sum_c d) * (state at the
 //    end of chunk c-1) + aggregate_c, written over aggregate_c.
 // ---------------------------------------------------------------------------
-template <int NS>
+template <int NS, int U>
 __global__ __launch_bounds__(256) void scan_carry_kernel(const float* __restrict__ A, float* carry,
-                                                         const float* __restrict__ chunk_sum, int64_t b,
-                                                         int64_t E, int N, int n_chunks) {
+                                                         const float* __restrict__ chunk_sum,
+                                                         const float* __restrict__ h0, int64_t b, int64_t E, int N,
+                                                         int n_chunks) {
   const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (gid >= b * E * NS) return;
   const int n = int(gid % NS);
   const int64_t ch = gid / NS;
   const int64_t e = ch % E, bi = ch / E;
   const float a2 = n < N ? A[e * N + n] * kLog2e : 0.f;
-  const int64_t stride = E;  // slots of consecutive chunks of one (batch, channel)
-  const int64_t first = bi * n_chunks * E + e;
-  constexpr int U = 8;  // aggregates of U chunks are loaded before the dependent combines run
-  float h = 0.f;
-  for (int c0 = 0; c0 + 1 < n_chunks; c0 += U) {
-    float Hs[U], Ss[U];
+  const int64_t first = bi * n_chunks * E + e;  // slot of chunk 0; chunk c is at first + c * E
+  const int n_comb = n_chunks - 1;              // chunks whose end state is needed
+  // The combines are a dependent chain, but their inputs are not: the
+  // aggregates of the next U chunks are loaded while the current U combine.
+  float Hs[U], Ss[U];
+  auto load = [&](int c0) {
 #pragma unroll
     for (int k = 0; k < U; k++) {
-      const int c = (c0 + k + 1 < n_chunks) ? c0 + k : c0;  // past the end: reload a valid slot, unused
-      Hs[k] = carry[(first + c * stride) * NS + n];
-      Ss[k] = chunk_sum[first + c * stride];
+      const int c = (c0 + k < n_comb) ? c0 + k : n_comb - 1;  // past the end: a valid slot, unused
+      Hs[k] = carry[(first + int64_t(c) * E) * NS + n];
+      Ss[k] = chunk_sum[first + int64_t(c) * E];
     }
+  };
+  float h = (h0 && n < N) ? h0[ch * N + n] : 0.f;  // incoming state of chunk 0
+  load(0);
+  for (int c0 = 0; c0 < n_comb; c0 += U) {
+    float Hc[U], Sc[U];
+#pragma unroll
+    for (int k = 0; k < U; k++) { Hc[k] = Hs[k]; Sc[k] = Ss[k]; }
+    if (c0 + U < n_comb) load(c0 + U);
 #pragma unroll
     for (int k = 0; k < U; k++) {
-      if (c0 + k + 1 < n_chunks) {
-        h = fmaf(exp2_fast(a2 * Ss[k]), h, Hs[k]);
-        carry[(first + (c0 + k) * stride) * NS + n] = h;
+      if (c0 + k < n_comb) {
+        h = fmaf(exp2_fast(a2 * Sc[k]), h, Hc[k]);
+        carry[(first + int64_t(c0 + k) * E) * NS + n] = h;
       }
     }
   }
@@ -268,12 +291,12 @@ __global__ __launch_bounds__(256) void scan_carry_kernel(const float* __restrict
 // FULL: every lane of every block is a real channel (E % 64 == 0), so the
 // per-step store needs no exec-mask branch.
 template <typename T, int NS, bool EXACT, bool SOFTPLUS, bool HAS_Z, bool FULL>
-__global__ __launch_bounds__(kWave) void scan_main_kernel(
+__global__ __launch_bounds__(kWave) SSM_SCAN_OCCUPANCY void scan_main_kernel(
     const T* __restrict__ u, const T* __restrict__ delta, const float* __restrict__ A,
     const float* __restrict__ B, const float* __restrict__ C, const float* __restrict__ D,
     const T* __restrict__ z, const float* __restrict__ bias, T* __restrict__ y,
-    float* __restrict__ last_state, const float* __restrict__ carry, int64_t L, int64_t E, int N,
-    int64_t chunk_len, int n_chunks, int e_blocks) {
+    float* __restrict__ last_state, const float* __restrict__ carry, const float* __restrict__ h0, int64_t L,
+    int64_t E, int N, int64_t chunk_len, int n_chunks, int e_blocks) {
   const BlockPos p = block_pos(n_chunks, e_blocks, E, L, chunk_len);
   float A2[NS];
 #pragma unroll
@@ -281,9 +304,10 @@ __global__ __launch_bounds__(kWave) void scan_main_kernel(
   const float Dv = D ? D[p.ec] : 0.f;
   const float bv = bias ? bias[p.ec] : 0.f;
   float h[NS];
-  if (p.c == 0) {
+  if (p.c == 0) {  // the incoming state of the sequence: given, or zero
+    const float* src = h0 ? h0 + (p.bi * E + p.ec) * N : nullptr;
 #pragma unroll
-    for (int n = 0; n < NS; n++) h[n] = 0.f;
+    for (int n = 0; n < NS; n++) h[n] = (src && (EXACT || n < N)) ? src[n] : 0.f;
   } else {
     const float* src = carry + ((p.bi * n_chunks + p.c - 1) * E + p.ec) * NS;
 #pragma unroll
@@ -368,9 +392,11 @@ __global__ __launch_bounds__(kWave) void scan_main_kernel(
   }
 }
 
-__global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, int64_t n) {
+// last_state of an empty sequence: a copy of the incoming state, or zeros
+__global__ __launch_bounds__(256) void fill_state_kernel(float* __restrict__ p, const float* __restrict__ src,
+                                                         int64_t n) {
   const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0.f;
+  if (i < n) p[i] = src ? src[i] : 0.f;
 }
 
 // ---------------------------------------------------------------------------
@@ -378,76 +404,119 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, i
 // ---------------------------------------------------------------------------
 // LPC = NS / 4 lanes share one channel, each holding 4 consecutive states, so
 // a wave reads and writes the fp32 state as one contiguous 1 KiB block per
-// instruction.  The partial readouts are summed across the LPC lanes.
+// instruction.  Workgroups are laid out per batch row (row_blocks of them per
+// row), so the row index is a per-workgroup scalar and the lane's channel is
+// plain 32-bit arithmetic.  The partial readouts of the LPC lanes are summed
+// with DPP quad permutes (no LDS traffic).
+__device__ __forceinline__ float quad_xor1(float v) {  // value of lane ^ 1 within the quad
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float quad_xor2(float v) {  // value of lane ^ 2 within the quad
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
+}
+
+#ifndef SSM_UPDATE_ROWS
+#define SSM_UPDATE_ROWS 4
+#endif
+// Each thread updates the same 4 states of one channel in kRows consecutive
+// batch rows: the channel's A slice and bias / D are loaded once and reused,
+// and all rows' state loads are issued before any arithmetic.
+constexpr int kRows = SSM_UPDATE_ROWS;
+
 template <typename T, int NS, bool VEC, bool SOFTPLUS, bool HAS_Z>
 __global__ __launch_bounds__(256) void state_update_kernel(
     float* __restrict__ state, const T* __restrict__ x, const T* __restrict__ delta,
     const float* __restrict__ A, const T* __restrict__ B, const T* __restrict__ C,
     const float* __restrict__ D, const T* __restrict__ z, const float* __restrict__ bias,
-    T* __restrict__ y, int64_t n_ch, int64_t E, int N) {
+    T* __restrict__ y, int b, int E, int N, int row_blocks) {
   constexpr int LPC = NS / 4;
-  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t ch = gid / LPC;
-  const int q = int(gid % LPC);
-  const bool active = ch < n_ch;
-  const int64_t cc = active ? ch : n_ch - 1;
-  const int64_t e = cc % E, bi = cc / E;
+  const int rb = blockIdx.x / row_blocks;  // group of kRows batch rows: uniform per workgroup
+  const int r = (blockIdx.x - rb * row_blocks) * 256 + threadIdx.x;
+  const int e_raw = r / LPC;
+  const int q = r % LPC;
+  const bool active = e_raw < E;
+  const int e = active ? e_raw : E - 1;
   const int n0 = 4 * q;
 
-  float s[4], a[4], bn[4], cn[4];
-  if constexpr (VEC) {  // N == NS, state / A / B / C rows aligned for vector access
-    const float4 sv = *reinterpret_cast<const float4*>(state + cc * NS + n0);
-    const float4 av = *reinterpret_cast<const float4*>(A + e * NS + n0);
-    s[0] = sv.x; s[1] = sv.y; s[2] = sv.z; s[3] = sv.w;
+  float a[4];
+  if constexpr (VEC) {
+    const float4 av = *reinterpret_cast<const float4*>(A + int64_t(e) * NS + n0);
     a[0] = av.x; a[1] = av.y; a[2] = av.z; a[3] = av.w;
-    if constexpr (std::is_same<T, float>::value) {
-      const float4 b4 = *reinterpret_cast<const float4*>(B + bi * NS + n0);
-      const float4 c4 = *reinterpret_cast<const float4*>(C + bi * NS + n0);
-      bn[0] = b4.x; bn[1] = b4.y; bn[2] = b4.z; bn[3] = b4.w;
-      cn[0] = c4.x; cn[1] = c4.y; cn[2] = c4.z; cn[3] = c4.w;
-    } else {
-      const uint2 b2 = *reinterpret_cast<const uint2*>(B + bi * NS + n0);
-      const uint2 c2 = *reinterpret_cast<const uint2*>(C + bi * NS + n0);
-      bn[0] = __uint_as_float(b2.x << 16); bn[1] = __uint_as_float(b2.x & 0xffff0000u);
-      bn[2] = __uint_as_float(b2.y << 16); bn[3] = __uint_as_float(b2.y & 0xffff0000u);
-      cn[0] = __uint_as_float(c2.x << 16); cn[1] = __uint_as_float(c2.x & 0xffff0000u);
-      cn[2] = __uint_as_float(c2.y << 16); cn[3] = __uint_as_float(c2.y & 0xffff0000u);
-    }
   } else {
 #pragma unroll
-    for (int k = 0; k < 4; k++) {
-      const int n = n0 + k;
-      const bool in = n < N;
-      s[k] = in ? state[cc * N + n] : 0.f;
-      a[k] = in ? A[e * N + n] : 0.f;
-      bn[k] = in ? load_elem(B + bi * N + n) : 0.f;
-      cn[k] = in ? load_elem(C + bi * N + n) : 0.f;
-    }
-  }
-  float d = load_elem(delta + cc) + (bias ? bias[e] : 0.f);
-  if (SOFTPLUS) d = softplus(d);
-  const float xv = load_elem(x + cc);
-  const float dx = d * xv;
-  float acc = 0.f;
-#pragma unroll
-  for (int k = 0; k < 4; k++) {
-    s[k] = fmaf(exp2_fast(d * a[k] * kLog2e), s[k], dx * bn[k]);
-    acc = fmaf(cn[k], s[k], acc);
+    for (int k = 0; k < 4; k++) a[k] = (n0 + k < N) ? A[int64_t(e) * N + n0 + k] : 0.f;
   }
 #pragma unroll
-  for (int off = LPC / 2; off >= 1; off /= 2) acc += __shfl_xor(acc, off, LPC);
-  if (active) {
-    if constexpr (VEC) {
-      *reinterpret_cast<float4*>(state + cc * NS + n0) = make_float4(s[0], s[1], s[2], s[3]);
+  for (int k = 0; k < 4; k++) a[k] *= kLog2e;
+  const float bv = bias ? bias[e] : 0.f;
+  const float Dv = D ? D[e] : 0.f;
+
+  float s[kRows][4], bn[kRows][4], cn[kRows][4];
+  float xv[kRows], dr[kRows], zz[kRows];
+  int64_t cc[kRows];
+  bool row_ok[kRows];
+#pragma unroll
+  for (int j = 0; j < kRows; j++) {
+    const int bi_raw = rb * kRows + j;
+    row_ok[j] = bi_raw < b;
+    const int bi = row_ok[j] ? bi_raw : b - 1;
+    cc[j] = int64_t(bi) * E + e;
+    if constexpr (VEC) {  // N == NS, state / B / C rows aligned for vector access
+      const float4 sv = *reinterpret_cast<const float4*>(state + cc[j] * NS + n0);
+      s[j][0] = sv.x; s[j][1] = sv.y; s[j][2] = sv.z; s[j][3] = sv.w;
+      if constexpr (std::is_same<T, float>::value) {
+        const float4 b4 = *reinterpret_cast<const float4*>(B + int64_t(bi) * NS + n0);
+        const float4 c4 = *reinterpret_cast<const float4*>(C + int64_t(bi) * NS + n0);
+        bn[j][0] = b4.x; bn[j][1] = b4.y; bn[j][2] = b4.z; bn[j][3] = b4.w;
+        cn[j][0] = c4.x; cn[j][1] = c4.y; cn[j][2] = c4.z; cn[j][3] = c4.w;
+      } else {
+        const uint2 b2 = *reinterpret_cast<const uint2*>(B + int64_t(bi) * NS + n0);
+        const uint2 c2 = *reinterpret_cast<const uint2*>(C + int64_t(bi) * NS + n0);
+        bn[j][0] = __uint_as_float(b2.x << 16); bn[j][1] = __uint_as_float(b2.x & 0xffff0000u);
+        bn[j][2] = __uint_as_float(b2.y << 16); bn[j][3] = __uint_as_float(b2.y & 0xffff0000u);
+        cn[j][0] = __uint_as_float(c2.x << 16); cn[j][1] = __uint_as_float(c2.x & 0xffff0000u);
+        cn[j][2] = __uint_as_float(c2.y << 16); cn[j][3] = __uint_as_float(c2.y & 0xffff0000u);
+      }
     } else {
 #pragma unroll
-      for (int k = 0; k < 4; k++)
-        if (n0 + k < N) state[cc * N + n0 + k] = s[k];
+      for (int k = 0; k < 4; k++) {
+        const int n = n0 + k;
+        const bool in = n < N;
+        s[j][k] = in ? state[cc[j] * N + n] : 0.f;
+        bn[j][k] = in ? load_elem(B + int64_t(bi) * N + n) : 0.f;
+        cn[j][k] = in ? load_elem(C + int64_t(bi) * N + n) : 0.f;
+      }
     }
-    if (q == 0) {
-      float out = fmaf(D ? D[e] : 0.f, xv, acc);
-      if (HAS_Z) out *= silu(load_elem(z + cc));
-      store_elem(y + cc, out);
+    xv[j] = load_elem(x + cc[j]);
+    dr[j] = load_elem(delta + cc[j]);
+    zz[j] = HAS_Z ? load_elem(z + cc[j]) : 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < kRows; j++) {
+    float d = dr[j] + bv;
+    if (SOFTPLUS) d = softplus(d);
+    const float dx = d * xv[j];
+    float acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      s[j][k] = fmaf(exp2_fast(d * a[k]), s[j][k], dx * bn[j][k]);
+      acc = fmaf(cn[j][k], s[j][k], acc);
+    }
+    if constexpr (LPC >= 2) acc += quad_xor1(acc);
+    if constexpr (LPC >= 4) acc += quad_xor2(acc);
+    if (active && row_ok[j]) {
+      if constexpr (VEC) {
+        *reinterpret_cast<float4*>(state + cc[j] * NS + n0) = make_float4(s[j][0], s[j][1], s[j][2], s[j][3]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; k++)
+          if (n0 + k < N) state[cc[j] * N + n0 + k] = s[j][k];
+      }
+      if (q == 0) {
+        float out = fmaf(Dv, xv[j], acc);
+        if (HAS_Z) out *= silu(zz[j]);
+        store_elem(y + cc[j], out);
+      }
     }
   }
 }
@@ -491,13 +560,17 @@ hipError_t run_scan(const ScanArgs& a, const ScanPlan& pl, const ScanBufs& w) {
                  a.A, w.B, a.bias, w.carry, w.csum, a.L, a.E, N, pl.chunk_len, pl.n_chunks, agg, pl.e_blocks);
     if (err != hipSuccess) return err;
     const int64_t lanes = a.b * a.E * NS;
-    err = launch_kind(kKindCarry, scan_carry_kernel<NS>, (lanes + 255) / 256, 256, a.stream, a.A, w.carry, (const float*)w.csum,
-                 a.b, a.E, N, pl.n_chunks);
+    // prefetch depth: 32 chunks for long chains, 8 when there are few chunks
+    err = pl.n_chunks > 33
+              ? launch_kind(kKindCarry, scan_carry_kernel<NS, 32>, (lanes + 255) / 256, 256, a.stream, a.A, w.carry,
+                            (const float*)w.csum, a.h0, a.b, a.E, N, pl.n_chunks)
+              : launch_kind(kKindCarry, scan_carry_kernel<NS, 8>, (lanes + 255) / 256, 256, a.stream, a.A, w.carry,
+                            (const float*)w.csum, a.h0, a.b, a.E, N, pl.n_chunks);
     if (err != hipSuccess) return err;
   }
   return launch_kind(kKindMain, scan_main_kernel<T, NS, EXACT, SOFTPLUS, HAS_Z, FULL>, a.b * pl.n_chunks * pl.e_blocks, kWave,
-                a.stream, u, dl, a.A, w.B, w.C, a.D, z, a.bias, y, a.last_state, (const float*)w.carry, a.L, a.E, N,
-                pl.chunk_len, pl.n_chunks, pl.e_blocks);
+                a.stream, u, dl, a.A, w.B, w.C, a.D, z, a.bias, y, a.last_state, (const float*)w.carry, a.h0, a.L,
+                a.E, N, pl.chunk_len, pl.n_chunks, pl.e_blocks);
 }
 
 template <typename T, int NS, bool EXACT, bool FULL>
@@ -533,13 +606,12 @@ hipError_t update_flags(const UpdateArgs& a) {
   const T* C = static_cast<const T*>(a.C);
   const T* z = static_cast<const T*>(a.z);
   T* y = static_cast<T*>(a.y);
-  const int64_t n_ch = a.b * a.E;
-  const int64_t threads = n_ch * (NS / 4);
-  const int64_t blocks = (threads + 255) / 256;
-  const int N = int(a.N);
-#define SSM_UPDATE_LAUNCH(SP, HZ)                                                                            \
-  return launch_kind(kKindUpdate, state_update_kernel<T, NS, VEC, SP, HZ>, blocks, 256, a.stream, a.state, x, dl, a.A, B, C, a.D, \
-                z, a.bias, y, n_ch, a.E, N)
+  const int row_blocks = int((a.E * (NS / 4) + 255) / 256);
+  const int64_t blocks = (a.b + kRows - 1) / kRows * row_blocks;
+  const int N = int(a.N), E = int(a.E);
+#define SSM_UPDATE_LAUNCH(SP, HZ)                                                                              \
+  return launch_kind(kKindUpdate, state_update_kernel<T, NS, VEC, SP, HZ>, blocks, 256, a.stream, a.state, x, dl, \
+                     a.A, B, C, a.D, z, a.bias, y, int(a.b), E, N, row_blocks)
   if (a.softplus) {
     if (z) { SSM_UPDATE_LAUNCH(true, true); }
     SSM_UPDATE_LAUNCH(true, false);
@@ -604,10 +676,10 @@ ScanPlan plan_scan(int64_t b, int64_t L, int64_t E, int elem_bytes) {
 
 hipError_t launch_scan(const ScanArgs& a) {
   if (a.b == 0 || a.E == 0) return hipSuccess;
-  if (a.L == 0) {
+  if (a.L == 0) {  // no step: the last state is the incoming one
     if (!a.last_state) return hipSuccess;
     const int64_t n = a.b * a.E * a.N;
-    return launch_kind(kKindFill, fill_zero_kernel, (n + 255) / 256, 256, a.stream, a.last_state, n);
+    return launch_kind(kKindFill, fill_state_kernel, (n + 255) / 256, 256, a.stream, a.last_state, a.h0, n);
   }
   const ScanPlan pl = plan_scan(a.b, a.L, a.E, a.dtype == 0 ? 4 : 2);
   // workspace: [chunk aggregates | chunk step sums | widened B rows | widened C rows]

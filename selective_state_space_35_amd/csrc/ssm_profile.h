@@ -11,7 +11,7 @@ enum : int {
   kKindAgg = 1,     // per-chunk aggregates
   kKindCarry = 2,   // carries across chunk boundaries
   kKindMain = 3,    // main scan pass
-  kKindFill = 4,    // zero last_state (L == 0)
+  kKindFill = 4,    // last_state of an empty sequence (L == 0)
   kKindUpdate = 5,  // single-token state update
   kNumKinds = 6
 };

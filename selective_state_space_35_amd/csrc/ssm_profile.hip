@@ -24,7 +24,7 @@ std::mutex g_mu;
 std::vector<Pending> g_pending;
 
 const char* const kNames[kNumKinds] = {"widen_rows", "chunk_aggregate", "chunk_carry",
-                                       "scan_main",  "fill_zero",       "state_update"};
+                                       "scan_main",  "fill_state",      "state_update"};
 
 }  // namespace
 

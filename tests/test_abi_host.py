@@ -96,6 +96,16 @@ def test_scan_noop_sizes_return_ok_without_work(lib):
     assert scan(lib, E=0, u=None, delta=None, A=None, B=None, C=None, y=None) == OK
 
 
+def test_scan_from_validation(lib):
+    f = lambda h0, **kw: lib.ssm_scan_fwd_from(kw.get("u", FAKE), FAKE, FAKE, FAKE, FAKE, None, None, None, 1, h0,
+                                               kw.get("y", FAKE), None, kw.get("b", 1), 8, 64, 16, 0, None)
+    assert f(FAKE + 2) == ERR_ALIGN
+    assert f(FAKE, u=None) == ERR_NULL
+    assert f(FAKE, y=None) == ERR_NULL
+    assert f(FAKE, b=-1) == ERR_DIM
+    assert f(None, b=0) == OK
+
+
 def test_update_validation(lib):
     assert update(lib, dtype=7) == ERR_DTYPE
     assert update(lib, b=-2) == ERR_DIM
@@ -155,5 +165,5 @@ def test_scan_plan_query(lib, monkeypatch):
 
 def test_profile_read_with_nothing_recorded(lib):
     out = ssm.ssm_profile_read()
-    assert set(out) == {"widen_rows", "chunk_aggregate", "chunk_carry", "scan_main", "fill_zero", "state_update"}
+    assert set(out) == {"widen_rows", "chunk_aggregate", "chunk_carry", "scan_main", "fill_state", "state_update"}
     assert all(v == (0.0, 0) for v in out.values())

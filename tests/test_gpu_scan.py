@@ -216,3 +216,112 @@ def test_full_long_no_D_no_gate_sampled():
     check_scan(x, "bf16", "long full no D / no gate (sampled)", channels=ch, y=y, last=last)
     del x, y, last
     torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------------------
+# continuation from a given state (ssm_scan_fwd_from)
+# ----------------------------------------------------------------------------
+def _h0(w, seed):
+    import torch
+
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    return torch.randn(w.b, w.E, w.N, generator=g).to("cuda")
+
+
+@pytest.mark.parametrize("kind,w", [("bf16", workloads.MID.with_shape(b=2, L=700, E=130)),
+                                    ("f32", workloads.BLOCK.with_shape(b=3, L=300, E=70, N=5))],
+                         ids=["bf16", "f32_N5"])
+def test_initial_state_parity(kind, w):
+    import torch
+
+    import selective_state_space_35_amd as ssm
+
+    say(f"initial state {kind}")
+    x = make(w, seed=11)
+    h0 = _h0(w, 12)
+    y, last = ssm.ssm_scan_fwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
+                               x["softplus"], initial_state=h0)
+    torch.cuda.synchronize()
+    y_ref, last_ref = oracle.scan(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
+                                  x["softplus"], h0=h0)
+    ey = max_err(y, y_ref)
+    el = max_err(last, last_ref)
+    print(f"[parity] initial state {kind}: y {ey:.3e} last {el:.3e}", flush=True)
+    assert ey <= TOL[kind] and el <= TOL[kind]
+
+
+def max_err(t, ref):
+    from tests.parity import max_normalised_error
+
+    return max_normalised_error(oracle.to_f64(t), ref)
+
+
+@pytest.mark.parametrize("min_chunk", [None, 16])
+def test_continuation_equals_whole_sequence(min_chunk, monkeypatch):
+    """scan(L1 + L2) == scan(L2, initial_state = last_state of scan(L1)), split inside a chunk."""
+    import torch
+
+    import selective_state_space_35_amd as ssm
+
+    if min_chunk:
+        monkeypatch.setenv("SSM_SCAN_MIN_CHUNK", str(min_chunk))
+        monkeypatch.setenv("SSM_SCAN_TARGET_WAVES", "100000")
+    say(f"continuation min_chunk={min_chunk}")
+    w = workloads.MID.with_shape(b=2, L=1500, E=96)
+    x = make(w, seed=13)
+    y_all, last_all = gpu_scan(x)
+    L1 = 611
+    part = lambda sl: {k: (v[:, sl].contiguous() if k in ("u", "delta", "z", "B", "C") else v) for k, v in x.items()}
+    p1, p2 = part(slice(0, L1)), part(slice(L1, None))
+    y1, last1 = gpu_scan(p1)
+    y2, last2 = ssm.ssm_scan_fwd(p2["u"], p2["delta"], p2["A"], p2["B"], p2["C"], p2["D"], p2["z"], p2["delta_bias"],
+                                 p2["softplus"], initial_state=last1)
+    torch.cuda.synchronize()
+    y_cat = torch.cat([y1, y2], dim=1)
+    y_ref, last_ref = oracle.scan(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"], True)
+    e_cat, e_last = max_err(y_cat, y_ref), max_err(last2, last_ref)
+    e_self = max_err(y_cat, oracle.to_f64(y_all))
+    print(f"[parity] continuation: y {e_cat:.3e} last {e_last:.3e} vs one call {e_self:.3e}", flush=True)
+    assert e_cat <= TOL["bf16"] and e_last <= TOL["bf16"] and e_self <= TOL["bf16"]
+    assert max_err(last2, oracle.to_f64(last_all)) <= 1e-4
+
+
+def test_prefill_then_decode():
+    """A prefill's last state handed to the token update continues the same recurrence."""
+    import torch
+
+    import selective_state_space_35_amd as ssm
+
+    say("prefill -> decode")
+    w = workloads.MID.with_shape(b=3, L=400, E=130)
+    x = make(w, seed=14)
+    L1 = 371
+    part = {k: (v[:, :L1].contiguous() if k in ("u", "delta", "z", "B", "C") else v) for k, v in x.items()}
+    _, st = gpu_scan(part)
+    ys = []
+    for t in range(L1, w.L):
+        ys.append(ssm.ssm_state_update(st, x["u"][:, t].contiguous(), x["delta"][:, t].contiguous(), x["A"],
+                                       x["B"][:, t].contiguous(), x["C"][:, t].contiguous(), x["D"],
+                                       x["z"][:, t].contiguous(), x["delta_bias"], x["softplus"]))
+    torch.cuda.synchronize()
+    y_ref, last_ref = oracle.scan(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"], True)
+    ey = max_err(torch.stack(ys, dim=1), y_ref[:, L1:])
+    el = max_err(st, last_ref)
+    print(f"[parity] prefill->decode: y {ey:.3e} state {el:.3e}", flush=True)
+    assert ey <= TOL["bf16"] and el <= TOL["bf16"]
+
+
+def test_empty_sequence_copies_initial_state():
+    import torch
+
+    import selective_state_space_35_amd as ssm
+
+    say("L=0 with initial state")
+    w = workloads.BLOCK.with_shape(b=2, L=0, E=70)
+    A = torch.from_numpy(workloads.a_matrix(70, 16)).to("cuda")
+    e = torch.empty(2, 0, 70, device="cuda")
+    bc = torch.empty(2, 0, 16, device="cuda")
+    h0 = _h0(w, 15)
+    _, last = ssm.ssm_scan_fwd(e, e, A, bc, bc, initial_state=h0)
+    torch.cuda.synchronize()
+    assert torch.equal(last, h0)
