@@ -7,7 +7,8 @@ silu gate, D skip), with inputs already resident in HBM.  That call runs the
 whole hot path: discretisation, recurrence, readout, gate and the last-state
 write.  The single-token state update is measured as well (128 successive
 updates of the generation workload b=256, E=5120, N=16) and reported in its
-own JSON object.
+own JSON object, and so is the causal convolution that precedes the scan
+(b1 L65536 E5120 K4 bf16, and its token step at b256 E5120 K4).
 
 Prints ONE JSON line on stdout:
   value        b*L*E elements per second over the timed steps
@@ -53,9 +54,19 @@ def update_bytes(b, E, N, s, gate=True):
     return 8 * b * E * N + b * E * ((3 if gate else 2) + 1) * s + 2 * b * N * s + E * (N + 2) * 4
 
 
+def conv_bytes(b, L, E, K, s, bias=True):
+    """Algorithmic bytes of one causal convolution: v in, x out, the weights (and bias), the K-sample state out."""
+    return 2 * b * L * E * s + E * K * 4 + (E * 4 if bias else 0) + b * E * K * s
+
+
+def conv_update_bytes(b, E, K, s, bias=True):
+    """Algorithmic bytes of one convolution token step: state read + write, v in, x out, weights (and bias)."""
+    return 2 * b * E * K * s + 2 * b * E * s + E * K * 4 + (E * 4 if bias else 0)
+
+
 def source_hash():
     h = hashlib.sha256()
-    for f in ("ssm_kernels.hip",):
+    for f in ("ssm_kernels.hip", "ssm_device.h"):
         with open(os.path.join(ROOT, "selective_state_space_35_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -82,6 +93,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target wall time of the CPU baseline sample")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-conv", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -199,6 +211,49 @@ def main():
                           "can be served from it; GB/s is algorithmic bytes over kernel time"}
         del xd, st, yd
 
+    # causal convolution in front of the scan (long workload) and its generation-time token step
+    conv = None
+    if not args.no_conv:
+        wc = workloads.CONV_LONG
+        xc = workloads.make_conv_inputs(wc, seed=args.seed, device=dev, backend="torch")
+        xo = torch.empty_like(xc["v"])
+        so = torch.empty((wc.b, wc.E, wc.K), dtype=xc["v"].dtype, device=dev)
+        for _ in range(3):
+            ssm.ssm_conv_fwd(xc["v"], xc["weight"], xc["conv_bias"], None, x=xo, state_out=so)
+        torch.cuda.synchronize()
+        ssm.ssm_profile_enable(True)
+        for _ in range(20):
+            ssm.ssm_conv_fwd(xc["v"], xc["weight"], xc["conv_bias"], None, x=xo, state_out=so)
+        torch.cuda.synchronize()
+        ssm.ssm_profile_enable(False)
+        cf = ssm.ssm_profile_read()["conv"]
+        cf_us = 1e3 * cf[0] / cf[1]
+        cb_ = conv_bytes(wc.b, wc.L, wc.E, wc.K, 2)
+        del xc, xo, so
+        wu = workloads.CONV_DECODE
+        xu = workloads.make_conv_inputs(wu, seed=args.seed, device=dev, backend="torch")
+        cst = xu["state_in"].clone()
+        v_t = xu["v"][:, 0].contiguous()
+        xt = torch.empty_like(v_t)
+        for _ in range(3):
+            ssm.ssm_conv_update(cst, v_t, xu["weight"], xu["conv_bias"], x=xt)
+        torch.cuda.synchronize()
+        ssm.ssm_profile_enable(True)
+        for _ in range(128):
+            ssm.ssm_conv_update(cst, v_t, xu["weight"], xu["conv_bias"], x=xt)
+        torch.cuda.synchronize()
+        ssm.ssm_profile_enable(False)
+        cu = ssm.ssm_profile_read()["conv_update"]
+        cu_us = 1e3 * cu[0] / cu[1]
+        ub_ = conv_update_bytes(wu.b, wu.E, wu.K, 2)
+        conv = {"sequence": {"workload": wc.description, "us_per_call": round(cf_us, 2), "calls": cf[1],
+                             "bytes_per_call": cb_, "GBps": round(cb_ / (cf_us * 1e-6) / 1e9, 1),
+                             "frac": round(cb_ / (cf_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)},
+                "token": {"workload": wu.description, "us_per_call": round(cu_us, 3), "calls": cu[1],
+                          "bytes_per_call": ub_, "GBps": round(ub_ / (cu_us * 1e-6) / 1e9, 1)}}
+        log(f"[bench] conv {conv}")
+        del xu, cst, v_t, xt
+
     # CPU baseline: the oracle on a bounded channel sample of the same inputs
     cpu = None
     parity = None
@@ -265,6 +320,7 @@ def main():
         "kernels": kernels,
         "alu": alu,
         "state_update": update,
+        "conv": conv,
         "cpu_baseline": cpu,
         "parity": parity,
     }

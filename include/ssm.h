@@ -149,6 +149,36 @@ SSM_API int ssm_state_update(float* state, const void* x, const void* delta, con
                      int64_t b, int64_t E, int64_t N, int dtype, void* stream);
 
 /*
+ * Causal depthwise convolution + SiLU, the step before the scan in the Mamba
+ * block ([AB] row 4 "Add causal local context before selecting coefficients"):
+ *   x[b,t,c] = silu(conv_bias[c] + sum_{k=0..K-1} q[c,k] * v[b, t-K+1+k, c])
+ * Samples before t = 0 come from state_in (the K most recent earlier samples,
+ * oldest first) or are zero when state_in is NULL (left zero padding).
+ *
+ * Arguments (device pointers):
+ *   v, x             [b, L, E]  dtype       (x must not overlap v)
+ *   q                [E, K]     float       (a depthwise Conv1d weight [E, 1, K])
+ *   conv_bias        [E]        float       (nullable: zero)
+ *   state_in         [b, E, K]  dtype       (nullable)
+ *   state_out        [b, E, K]  dtype       (nullable): the K most recent samples after the
+ *                                            last step, oldest first -- the state
+ *                                            ssm_conv_update continues from
+ *   1 <= K <= 8.  L == 0 copies state_in (or zeros) to state_out.
+ */
+SSM_API int ssm_conv_fwd(const void* v, const float* q, const float* conv_bias, const void* state_in, void* x,
+                         void* state_out, int64_t b, int64_t L, int64_t E, int64_t K, int dtype, void* stream);
+
+/*
+ * One token of the convolution ([AB] row 6 "Carry both buffers to the next
+ * token"): conv_state [b, E, K] (dtype, in place) is shifted left by one
+ * sample and v [b, E] is appended; then
+ *   x[b,c] = silu(conv_bias[c] + sum_k q[c,k] * conv_state[b,c,k]).
+ * Calling it L times reproduces ssm_conv_fwd over the L tokens.
+ */
+SSM_API int ssm_conv_update(void* conv_state, const void* v, const float* q, const float* conv_bias, void* x,
+                            int64_t b, int64_t E, int64_t K, int dtype, void* stream);
+
+/*
  * How ssm_scan_fwd will split a scan of this size along the sequence: it
  * writes the chunk length (steps) and the number of chunks.  One chunk means
  * a single pass; more chunks mean a chunk-aggregate pass, a carry pass over
@@ -166,7 +196,8 @@ SSM_API int ssm_scan_plan(int64_t b, int64_t L, int64_t E, int64_t N, int dtype,
  * stream.  ssm_profile_read() waits for those events, writes per-kind totals
  * (milliseconds) and launch counts for kinds 0 .. n_kinds-1 and clears the
  * record.  Kinds: 0 widen_rows (bf16 B/C rows to f32), 1 chunk_aggregate,
- * 2 chunk_carry, 3 scan_main, 4 fill_state, 5 state_update; names from
+ * 2 chunk_carry, 3 scan_main, 4 fill_state, 5 state_update, 6 conv,
+ * 7 conv_update; names from
  * ssm_profile_kind_name().  Off by default; the events add a few
  * microseconds per launch.  Process-wide, thread-safe.
  */

@@ -19,7 +19,10 @@ Definitions followed (page title, site, section):
   * silu(z) gate -- abhik.ai page, row 5 "Put the selective operator inside
     the complete mixer";
   * single-token update -- abhik.ai page, row 6 "Carry both buffers to the
-    next token".
+    next token";
+  * causal depthwise convolution + silu before the scan -- abhik.ai page,
+    row 4 "Add causal local context before selecting coefficients", and its
+    single-token form in row 6.
 
 Parity status: every function here is pinned by closed forms, invariants and
 brute force in ``tests/test_oracle_pins.py``; none is "parity unpinned".
@@ -51,6 +54,10 @@ def _load(path=None):
     lib.oracle_scan.argtypes = [_dp] * 8 + [ctypes.c_int, _dp, _dp, _dp, _dp] + [ctypes.c_int64] * 4 + [ctypes.c_int]
     lib.oracle_state_update.restype = ctypes.c_int
     lib.oracle_state_update.argtypes = [_dp] * 9 + [ctypes.c_int, _dp] + [ctypes.c_int64] * 3 + [ctypes.c_int]
+    lib.oracle_conv_fwd.restype = ctypes.c_int
+    lib.oracle_conv_fwd.argtypes = [_dp] * 6 + [ctypes.c_int64] * 4
+    lib.oracle_conv_update.restype = ctypes.c_int
+    lib.oracle_conv_update.argtypes = [_dp] * 5 + [ctypes.c_int64] * 3
     lib.oracle_softplus_value.restype = ctypes.c_double
     lib.oracle_softplus_value.argtypes = [ctypes.c_double]
     lib.oracle_silu_value.restype = ctypes.c_double
@@ -151,6 +158,42 @@ def state_update(state, x, delta, A, B, C, D=None, z=None, delta_bias=None, soft
     if rc != 0:
         raise RuntimeError(f"oracle_state_update failed with {rc}")
     return s, y
+
+
+def conv_fwd(v, q, cb=None, state_in=None):
+    """Causal depthwise convolution + silu: v [b, L, E], q [E, K], cb [E], state_in [b, E, K].
+
+    Returns (x [b, L, E], state_out [b, E, K]) where state_out holds the K most
+    recent samples (oldest first) -- the convolution state a decoder continues from.
+    """
+    lib = _load()
+    v, q, cb, state_in = (to_f64(a) for a in (v, q, cb, state_in))
+    b, L, E = v.shape
+    K = q.shape[1]
+    if q.shape != (E, K) or (cb is not None and cb.shape != (E,)) or (
+            state_in is not None and state_in.shape != (b, E, K)):
+        raise ValueError("oracle.conv_fwd: inconsistent shapes")
+    x = np.empty((b, L, E), dtype=np.float64)
+    st = np.empty((b, E, K), dtype=np.float64)
+    rc = lib.oracle_conv_fwd(_ptr(v), _ptr(q), _ptr(cb), _ptr(state_in), _ptr(x), _ptr(st), b, L, E, K)
+    if rc != 0:
+        raise RuntimeError(f"oracle_conv_fwd failed with {rc}")
+    return x, st
+
+
+def conv_update(state, v, q, cb=None):
+    """One token: returns (new state [b, E, K], x [b, E]); ``state`` is not modified."""
+    lib = _load()
+    st = to_f64(state).copy()
+    v, q, cb = (to_f64(a) for a in (v, q, cb))
+    b, E, K = st.shape
+    if v.shape != (b, E) or q.shape != (E, K):
+        raise ValueError("oracle.conv_update: inconsistent shapes")
+    x = np.empty((b, E), dtype=np.float64)
+    rc = lib.oracle_conv_update(_ptr(st), _ptr(v), _ptr(q), _ptr(cb), _ptr(x), b, E, K)
+    if rc != 0:
+        raise RuntimeError(f"oracle_conv_update failed with {rc}")
+    return st, x
 
 
 def softplus_value(x: float) -> float:

@@ -38,6 +38,14 @@
  * The single-token update applies the same body once to a given state
  * ([AB] row 6 "Carry both buffers to the next token", the SSM half of `step`).
  *
+ * The causal depthwise convolution that precedes the scan in the block
+ * ([AB] row 4 "Add causal local context before selecting coefficients"):
+ *   x[b,t,c] = silu(cb[c] + sum_{k=0..K-1} q[c,k] * v[b, t-K+1+k, c])
+ * with samples before t = 0 taken from an incoming convolution state
+ * (the K most recent earlier samples, oldest first) or zero (left padding).
+ * Its single-token form shifts the K-sample state left by one, appends the
+ * new sample and evaluates the same sum ([AB] row 6, the convolution half).
+ *
  * Arithmetic: every input is widened to double before use; exp/log1p come
  * from the C library; there is no blocking, fusion or reordering of the
  * definition above.  Chains (b,e) are independent, so threads split chains,
@@ -256,6 +264,65 @@ int oracle_state_update(double* state, const double* x, const double* delta, con
   free(jobs);
   free(tid);
   return rc;
+}
+
+/* Causal depthwise convolution + silu over a sequence.
+ * v, x [b, L, E]; q [E, K]; cb [E] (nullable: zero); state_in [b, E, K] (nullable: zero history);
+ * state_out [b, E, K] (nullable): the K most recent samples after the last step, oldest first. */
+int oracle_conv_fwd(const double* v, const double* q, const double* cb, const double* state_in, double* x,
+                    double* state_out, int64_t b, int64_t L, int64_t E, int64_t K) {
+  if (b < 0 || L < 0 || E < 0 || K < 1) return -1;
+  for (int64_t bi = 0; bi < b; bi++) {
+    for (int64_t c = 0; c < E; c++) {
+      for (int64_t t = 0; t < L; t++) {
+        double acc = cb ? cb[c] : 0.0;
+        for (int64_t k = 0; k < K; k++) {
+          const int64_t s = t - K + 1 + k; /* time index of this tap */
+          double sample;
+          if (s >= 0) sample = v[(bi * L + s) * E + c];
+          else sample = state_in ? state_in[(bi * E + c) * K + (K + s)] : 0.0;
+          acc += q[c * K + k] * sample;
+        }
+#if ORACLE_MUTATION == 11
+        x[(bi * L + t) * E + c] = acc;
+#else
+        x[(bi * L + t) * E + c] = oracle_silu(acc);
+#endif
+      }
+      if (state_out) {
+        for (int64_t k = 0; k < K; k++) {
+          const int64_t s = L - K + k;
+          double sample;
+          if (s >= 0) sample = v[(bi * L + s) * E + c];
+          else sample = state_in ? state_in[(bi * E + c) * K + (K + s)] : 0.0;
+          state_out[(bi * E + c) * K + k] = sample;
+        }
+      }
+    }
+  }
+  return 0;
+}
+
+/* One token: state [b, E, K] shifted left by one with v [b, E] appended (in place), then
+ * x [b, E] = silu(cb + sum_k q[c,k] * state[b,c,k]). */
+int oracle_conv_update(double* state, const double* v, const double* q, const double* cb, double* x, int64_t b,
+                       int64_t E, int64_t K) {
+  if (b < 0 || E < 0 || K < 1) return -1;
+  for (int64_t bi = 0; bi < b; bi++) {
+    for (int64_t c = 0; c < E; c++) {
+      double* st = state + (bi * E + c) * K;
+      for (int64_t k = 0; k + 1 < K; k++) st[k] = st[k + 1];
+      st[K - 1] = v[bi * E + c];
+      double acc = cb ? cb[c] : 0.0;
+#if ORACLE_MUTATION == 12
+      for (int64_t k = 0; k < K; k++) acc += q[c * K + (K - 1 - k)] * st[k];
+#else
+      for (int64_t k = 0; k < K; k++) acc += q[c * K + k] * st[k];
+#endif
+      x[bi * E + c] = oracle_silu(acc);
+    }
+  }
+  return 0;
 }
 
 /* Exposed for the softplus / gate pins: the scalar helpers exactly as used above. */

@@ -15,16 +15,23 @@ Functions (same names as the C entry points):
 * ``ssm_state_update(state, x, delta, A, B, C, D=None, z=None,
   delta_bias=None, softplus=False, y=None)`` -> ``y`` (``state`` is updated
   in place)
+* ``ssm_conv_fwd(v, weight, conv_bias=None, state_in=None, x=None,
+  state_out=None, return_state=True)`` -> ``(x, state_out)``: causal depthwise
+  convolution + SiLU over the sequence
+* ``ssm_conv_update(conv_state, v, weight, conv_bias=None, x=None)`` -> ``x``
+  (``conv_state`` is shifted and appended to in place)
 
 Shapes: u, delta, z, y [b, L, E]; A [E, N] (float32); B, C [b, L, N];
 D, delta_bias [E] (float32); state / last_state [b, E, N] (float32).
-Streamed tensors are all float32 or all bfloat16.
+Convolution: v, x [b, L, E]; weight [E, K] float32 (1 <= K <= 8); conv_bias
+[E] float32; convolution state [b, E, K] in the streamed dtype, oldest sample
+first.  Streamed tensors are all float32 or all bfloat16.
 """
 import ctypes
 import os
 
 __all__ = [
-    "ssm_scan_fwd", "ssm_scan_fwd_from", "ssm_state_update", "ssm_scan_plan", "ssm_profile_enable", "ssm_profile_read",
+    "ssm_scan_fwd", "ssm_scan_fwd_from", "ssm_state_update", "ssm_conv_fwd", "ssm_conv_update", "ssm_scan_plan", "ssm_profile_enable", "ssm_profile_read",
     "ssm_status_string", "library_path", "SSMError",
     "SSM_F32", "SSM_BF16", "load_library",
 ]
@@ -72,6 +79,10 @@ def load_library():
     lib.ssm_scan_fwd_from.argtypes = [_vp] * 8 + [_int, _vp, _vp, _vp] + [_i64] * 4 + [_int, _vp]
     lib.ssm_state_update.restype = _int
     lib.ssm_state_update.argtypes = [_vp] * 9 + [_int, _vp] + [_i64] * 3 + [_int, _vp]
+    lib.ssm_conv_fwd.restype = _int
+    lib.ssm_conv_fwd.argtypes = [_vp] * 6 + [_i64] * 4 + [_int, _vp]
+    lib.ssm_conv_update.restype = _int
+    lib.ssm_conv_update.argtypes = [_vp] * 5 + [_i64] * 3 + [_int, _vp]
     lib.ssm_status_string.restype = ctypes.c_char_p
     lib.ssm_status_string.argtypes = [_int]
     lib.ssm_last_hip_error.restype = ctypes.c_char_p
@@ -104,7 +115,7 @@ def ssm_scan_plan(b, L, E, N, dtype="bf16"):
     return cl.value, nc.value
 
 
-PROFILE_KINDS = 6
+PROFILE_KINDS = 8
 
 
 def ssm_profile_enable(on=True):
@@ -254,3 +265,72 @@ def ssm_state_update(state, x, delta, A, B, C, D=None, z=None, delta_bias=None, 
                                       _stream_of(torch, device))
     _raise_on("ssm_state_update", status)
     return y
+
+
+def ssm_conv_fwd(v, weight, conv_bias=None, state_in=None, x=None, state_out=None, return_state=True):
+    """Causal depthwise convolution + SiLU over [b, L, E] on the GPU.  Returns ``(x, state_out)``.
+
+    ``state_in`` [b, E, K] holds the K samples before the sequence (oldest first);
+    None pads with zeros.  ``state_out`` receives the K most recent samples.
+    """
+    import torch
+
+    lib = load_library()
+    if not isinstance(v, torch.Tensor) or v.dim() != 3:
+        raise ValueError("v must be a [b, L, E] tensor")
+    device = v.device
+    if device.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU device, got {device}")
+    b, L, E = v.shape
+    if not isinstance(weight, torch.Tensor) or weight.dim() != 2:
+        raise ValueError("weight must be an [E, K] tensor")
+    K = weight.shape[1]
+    io = v.dtype
+    code = _dtype_code(torch, io)
+    _check(torch, "v", v, (b, L, E), io, device)
+    _check(torch, "weight", weight, (E, K), torch.float32, device)
+    _check(torch, "conv_bias", conv_bias, (E,), torch.float32, device, optional=True)
+    _check(torch, "state_in", state_in, (b, E, K), io, device, optional=True)
+    if x is None:
+        x = torch.empty((b, L, E), dtype=io, device=device)
+    else:
+        _check(torch, "x", x, (b, L, E), io, device)
+    if state_out is None and return_state:
+        state_out = torch.empty((b, E, K), dtype=io, device=device)
+    elif state_out is not None:
+        _check(torch, "state_out", state_out, (b, E, K), io, device)
+    if state_in is not None and state_out is not None and state_in.data_ptr() == state_out.data_ptr():
+        raise ValueError("state_in must not be the state_out buffer")
+    with torch.cuda.device(device):
+        status = lib.ssm_conv_fwd(_ptr(v), _ptr(weight), _ptr(conv_bias), _ptr(state_in), _ptr(x), _ptr(state_out),
+                                  b, L, E, K, code, _stream_of(torch, device))
+    _raise_on("ssm_conv_fwd", status)
+    return x, state_out
+
+
+def ssm_conv_update(conv_state, v, weight, conv_bias=None, x=None):
+    """One token of the convolution; ``conv_state`` [b, E, K] is updated in place.  Returns x [b, E]."""
+    import torch
+
+    lib = load_library()
+    if not isinstance(conv_state, torch.Tensor) or conv_state.dim() != 3:
+        raise ValueError("conv_state must be a [b, E, K] tensor")
+    device = conv_state.device
+    if device.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU device, got {device}")
+    b, E, K = conv_state.shape
+    io = conv_state.dtype
+    code = _dtype_code(torch, io)
+    _check(torch, "conv_state", conv_state, (b, E, K), io, device)
+    _check(torch, "v", v, (b, E), io, device)
+    _check(torch, "weight", weight, (E, K), torch.float32, device)
+    _check(torch, "conv_bias", conv_bias, (E,), torch.float32, device, optional=True)
+    if x is None:
+        x = torch.empty((b, E), dtype=io, device=device)
+    else:
+        _check(torch, "x", x, (b, E), io, device)
+    with torch.cuda.device(device):
+        status = lib.ssm_conv_update(_ptr(conv_state), _ptr(v), _ptr(weight), _ptr(conv_bias), _ptr(x), b, E, K, code,
+                                     _stream_of(torch, device))
+    _raise_on("ssm_conv_update", status)
+    return x

@@ -115,6 +115,52 @@ int ssm_scan_plan(int64_t b, int64_t L, int64_t E, int64_t N, int dtype, int64_t
   return SSM_OK;
 }
 
+int ssm_conv_fwd(const void* v, const float* q, const float* conv_bias, const void* state_in, void* x,
+                 void* state_out, int64_t b, int64_t L, int64_t E, int64_t K, int dtype, void* stream) {
+  if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_DTYPE;
+  if (b < 0 || L < 0 || E < 0 || K < 1 || K > ssm::kMaxConvK) return SSM_ERR_DIM;
+  int64_t t = 0;
+  if (!mul_ok(b, L, &t) || !mul_ok(t, E, &t) || !mul_ok(t, 4, &t)) return SSM_ERR_DIM;
+  if (!mul_ok(b, E, &t) || !mul_ok(t, K, &t) || !mul_ok(t, 4, &t)) return SSM_ERR_DIM;
+  if (b == 0 || E == 0) return SSM_OK;
+  if ((L > 0 && (!v || !x)) || !q) return SSM_ERR_NULL;
+  const size_t es = dtype == SSM_F32 ? 4 : 2;
+  const void* streamed[] = {v, x, state_in, state_out};
+  for (const void* p : streamed)
+    if (p && !aligned(p, es)) return SSM_ERR_ALIGN;
+  if (!aligned(q, 4) || (conv_bias && !aligned(conv_bias, 4))) return SSM_ERR_ALIGN;
+  // one wave covers 64 channels of a conv_chunk_steps() row band; offsets inside it are 32-bit
+  const int64_t e_blocks = (E + 63) / 64, chunks = (L + ssm::conv_chunk_steps() - 1) / ssm::conv_chunk_steps();
+  if (E * int64_t(es) * ssm::conv_chunk_steps() > INT32_MAX) return SSM_ERR_DIM;
+  int64_t grid = 0;
+  if (!mul_ok(b, e_blocks, &grid) || !mul_ok(grid, chunks, &grid) || grid > INT32_MAX) return SSM_ERR_DIM;
+  ssm::ConvArgs a;
+  a.v = v; a.q = q; a.cb = conv_bias; a.state_in = state_in; a.x = x; a.state_out = state_out;
+  a.b = b; a.L = L; a.E = E; a.K = K; a.dtype = dtype; a.stream = static_cast<hipStream_t>(stream);
+  return hip_status(ssm::launch_conv_fwd(a));
+}
+
+int ssm_conv_update(void* conv_state, const void* v, const float* q, const float* conv_bias, void* x, int64_t b,
+                    int64_t E, int64_t K, int dtype, void* stream) {
+  if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_DTYPE;
+  if (b < 0 || E < 0 || K < 1 || K > ssm::kMaxConvK) return SSM_ERR_DIM;
+  int64_t t = 0;
+  if (!mul_ok(b, E, &t) || !mul_ok(t, K, &t) || !mul_ok(t, 4, &t)) return SSM_ERR_DIM;
+  if (b == 0 || E == 0) return SSM_OK;
+  if (!conv_state || !v || !q || !x) return SSM_ERR_NULL;
+  const size_t es = dtype == SSM_F32 ? 4 : 2;
+  const void* streamed[] = {conv_state, v, x};
+  for (const void* p : streamed)
+    if (!aligned(p, es)) return SSM_ERR_ALIGN;
+  if (!aligned(q, 4) || (conv_bias && !aligned(conv_bias, 4))) return SSM_ERR_ALIGN;
+  int64_t blocks = 0;
+  if (E > INT32_MAX || b > INT32_MAX || !mul_ok(b, (E + 255) / 256, &blocks) || blocks > INT32_MAX) return SSM_ERR_DIM;
+  ssm::ConvArgs a;
+  a.v = v; a.q = q; a.cb = conv_bias; a.state_in = nullptr; a.x = x; a.state_out = conv_state;
+  a.b = b; a.L = 1; a.E = E; a.K = K; a.dtype = dtype; a.stream = static_cast<hipStream_t>(stream);
+  return hip_status(ssm::launch_conv_update(a));
+}
+
 const char* ssm_status_string(int status) {
   switch (status) {
     case SSM_OK: return "ok";

@@ -1,0 +1,207 @@
+// ssm_conv.hip -- causal depthwise convolution + SiLU that precedes the scan
+// in the Mamba block, and its single-token form used while generating.
+//
+// Page defining the operation: "Mamba: Linear-Time Sequence Modeling with
+// Selective State Spaces" (abhik.ai), section "Original paper, equations and
+// runnable CPU code":
+//   row 4 "Add causal local context before selecting coefficients":
+//     x[t,c] = silu(cb[c] + sum_{k=0..K-1} q[c,k] * v[t-K+1+k, c]), left zero padding;
+//   row 6 "Carry both buffers to the next token": the convolution state keeps
+//     the K most recent samples (the latest included), shifted left by one
+//     and appended to before the same sum.
+//
+// Layout: v, x [b, L, E] (channels fastest, like the scan's inputs);
+// q [E, K] float; cb [E] float; convolution state [b, E, K] in the I/O dtype,
+// oldest sample first.
+//
+// conv_fwd_kernel: one lane per channel, 64 channels per wave (one contiguous
+// row segment per load), a chunk of kConvChunk steps per wave.  The K-1
+// previous samples live in registers and slide along; the chunk's first
+// window reads the K-1 rows before it (or the incoming state / zeros).  Each
+// input and output element crosses HBM once: an HBM-bound kernel.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "ssm_device.h"
+#include "ssm_internal.h"
+#include "ssm_profile.h"
+
+namespace ssm {
+namespace {
+
+constexpr int kConvChunk = 64;  // steps per wave
+constexpr int kConvGroup = 8;   // loads issued together
+
+template <typename T, int K>
+__global__ __launch_bounds__(kWave) void conv_fwd_kernel(const T* __restrict__ v, const float* __restrict__ q,
+                                                         const float* __restrict__ cb,
+                                                         const T* __restrict__ state_in, T* __restrict__ x,
+                                                         T* __restrict__ state_out, int64_t L, int64_t E,
+                                                         int n_chunks, int e_blocks) {
+  const int eb = blockIdx.x % e_blocks;
+  const int rest = blockIdx.x / e_blocks;
+  const int c = rest % n_chunks;
+  const int64_t bi = rest / n_chunks;
+  const int64_t e = int64_t(eb) * kWave + threadIdx.x;
+  const bool active = e < E;
+  const int64_t ec = active ? e : E - 1;
+  const int64_t t0 = int64_t(c) * kConvChunk;
+  const int64_t t1 = (t0 + kConvChunk < L) ? t0 + kConvChunk : L;
+
+  float w[K];
+#pragma unroll
+  for (int k = 0; k < K; k++) w[k] = q[ec * K + k];
+  const float bias = cb ? cb[ec] : 0.f;
+  // hist[j] = sample at time t0 - (K-1) + j, j < K-1
+  float hist[K > 1 ? K - 1 : 1];
+#pragma unroll
+  for (int j = 0; j < K - 1; j++) {
+    const int64_t s = t0 - (K - 1) + j;
+    if (s >= 0) hist[j] = load_elem(v + (bi * L + s) * E + ec);
+    else hist[j] = state_in ? load_elem(state_in + (bi * E + ec) * K + (K + s)) : 0.f;
+  }
+
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + (bi * L + t0) * E + int64_t(eb) * kWave);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + (bi * L + t0) * E + int64_t(eb) * kWave);
+  const int voff = int(ec - int64_t(eb) * kWave) * int(sizeof(T));
+  const int row_bytes = int(E * int64_t(sizeof(T)));  // kConvChunk * row_bytes < 2^31 is checked by the caller
+  const int n_steps = int(t1 - t0);
+  float last = 0.f;     // newest sample seen
+  float dropped = 0.f;  // sample that last left the window (the oldest of the K most recent)
+  for (int g0 = 0; g0 < n_steps; g0 += kConvGroup) {
+    float vs[kConvGroup];
+#pragma unroll
+    for (int k = 0; k < kConvGroup; k++) {
+      const int kk = (g0 + k < n_steps) ? g0 + k : n_steps - 1;  // past the end: a valid row, unused
+      vs[k] = buf_load(rv, voff, kk * row_bytes, (T*)nullptr);
+    }
+#pragma unroll
+    for (int k = 0; k < kConvGroup; k++) {
+      if (g0 + k < n_steps) {
+        float acc = bias;
+#pragma unroll
+        for (int j = 0; j < K - 1; j++) acc = fmaf(w[j], hist[j], acc);
+        acc = fmaf(w[K - 1], vs[k], acc);
+        if (active) buf_store(rx, voff, (g0 + k) * row_bytes, silu(acc), (T*)nullptr);
+        if (K > 1) dropped = hist[0];
+#pragma unroll
+        for (int j = 0; j + 1 < K - 1; j++) hist[j] = hist[j + 1];
+        if (K > 1) hist[K - 2] = vs[k];
+        last = vs[k];
+      }
+    }
+  }
+  if (state_out && c == n_chunks - 1 && active) {
+    T* dst = state_out + (bi * E + e) * K;
+    // the K most recent samples, oldest first: the one that just left the window,
+    // then the window (whose newest entry is the last sample)
+    if (K == 1) {
+      store_elem(dst, last);
+    } else {
+      store_elem(dst, dropped);
+#pragma unroll
+      for (int j = 0; j < K - 1; j++) store_elem(dst + 1 + j, hist[j]);
+    }
+  }
+}
+
+// last convolution state of an empty sequence: the incoming one, or zeros
+template <typename T>
+__global__ __launch_bounds__(256) void conv_state_copy_kernel(const T* __restrict__ src, T* __restrict__ dst,
+                                                              int64_t n) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) store_elem(dst + i, src ? load_elem(src + i) : 0.f);
+}
+
+// One token for every (b, e): shift the K-sample state left, append v, x = silu(cb + q . state).
+template <typename T, int K>
+__global__ __launch_bounds__(256) void conv_update_kernel(T* __restrict__ state, const T* __restrict__ v,
+                                                          const float* __restrict__ q, const float* __restrict__ cb,
+                                                          T* __restrict__ x, int E, int row_blocks) {
+  const int bi = blockIdx.x / row_blocks;  // batch row: uniform per workgroup
+  const int e = (blockIdx.x - bi * row_blocks) * 256 + threadIdx.x;
+  if (e >= E) return;
+  const int64_t cc = int64_t(bi) * E + e;
+  T* st = state + cc * K;
+  float s[K];
+#pragma unroll
+  for (int k = 0; k < K; k++) s[k] = load_elem(st + k);
+  const float vt = load_elem(v + cc);
+  float acc = cb ? cb[e] : 0.f;
+#pragma unroll
+  for (int k = 0; k < K; k++) {
+    const float sk = (k + 1 < K) ? s[k + 1] : vt;  // shifted state: oldest dropped, newest appended
+    acc = fmaf(q[int64_t(e) * K + k], sk, acc);
+    store_elem(st + k, sk);
+  }
+  store_elem(x + cc, silu(acc));
+}
+
+template <typename T, int K>
+hipError_t conv_fwd_k(const ConvArgs& a) {
+  const int e_blocks = int((a.E + kWave - 1) / kWave);
+  const int n_chunks = int((a.L + kConvChunk - 1) / kConvChunk);
+  return launch_kind(kKindConv, conv_fwd_kernel<T, K>, a.b * n_chunks * e_blocks, kWave, a.stream,
+                     static_cast<const T*>(a.v), a.q, a.cb, static_cast<const T*>(a.state_in), static_cast<T*>(a.x),
+                     static_cast<T*>(a.state_out), a.L, a.E, n_chunks, e_blocks);
+}
+
+template <typename T, int K>
+hipError_t conv_update_k(const ConvArgs& a) {
+  const int row_blocks = int((a.E + 255) / 256);
+  return launch_kind(kKindConvUpdate, conv_update_kernel<T, K>, a.b * row_blocks, 256, a.stream,
+                     static_cast<T*>(a.state_out), static_cast<const T*>(a.v), a.q, a.cb, static_cast<T*>(a.x),
+                     int(a.E), row_blocks);
+}
+
+// Dispatch on the kernel width K (1..kMaxConvK) as a compile-time constant.
+template <typename T, template <typename, int> class F>
+struct ByK {
+  static hipError_t run(const ConvArgs& a) {
+    switch (a.K) {
+      case 1: return F<T, 1>::run(a);
+      case 2: return F<T, 2>::run(a);
+      case 3: return F<T, 3>::run(a);
+      case 4: return F<T, 4>::run(a);
+      case 5: return F<T, 5>::run(a);
+      case 6: return F<T, 6>::run(a);
+      case 7: return F<T, 7>::run(a);
+      default: return F<T, 8>::run(a);
+    }
+  }
+};
+template <typename T, int K>
+struct FwdK {
+  static hipError_t run(const ConvArgs& a) { return conv_fwd_k<T, K>(a); }
+};
+template <typename T, int K>
+struct UpdK {
+  static hipError_t run(const ConvArgs& a) { return conv_update_k<T, K>(a); }
+};
+
+}  // namespace
+
+int64_t conv_chunk_steps() { return kConvChunk; }
+
+hipError_t launch_conv_fwd(const ConvArgs& a) {
+  if (a.b == 0 || a.E == 0) return hipSuccess;
+  if (a.L == 0) {
+    if (!a.state_out) return hipSuccess;
+    const int64_t n = a.b * a.E * a.K;
+    return a.dtype == 0
+               ? launch_kind(kKindConv, conv_state_copy_kernel<float>, (n + 255) / 256, 256, a.stream,
+                             static_cast<const float*>(a.state_in), static_cast<float*>(a.state_out), n)
+               : launch_kind(kKindConv, conv_state_copy_kernel<bf16_bits>, (n + 255) / 256, 256, a.stream,
+                             static_cast<const bf16_bits*>(a.state_in), static_cast<bf16_bits*>(a.state_out), n);
+  }
+  return a.dtype == 0 ? ByK<float, FwdK>::run(a) : ByK<bf16_bits, FwdK>::run(a);
+}
+
+hipError_t launch_conv_update(const ConvArgs& a) {
+  if (a.b == 0 || a.E == 0) return hipSuccess;
+  return a.dtype == 0 ? ByK<float, UpdK>::run(a) : ByK<bf16_bits, UpdK>::run(a);
+}
+
+}  // namespace ssm

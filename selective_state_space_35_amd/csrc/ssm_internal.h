@@ -42,6 +42,24 @@ struct UpdateArgs {
   hipStream_t stream;
 };
 
+// Causal depthwise convolution (sequence form and token form).
+struct ConvArgs {
+  const void* v;         // [b, L, E] (sequence) or [b, E] (token)
+  const float* q;        // [E, K]
+  const float* cb;       // [E], nullable
+  const void* state_in;  // [b, E, K], nullable (sequence form)
+  void* x;               // output, same shape as v
+  void* state_out;       // [b, E, K]: written (sequence form, nullable) / updated in place (token form)
+  int64_t b, L, E, K;
+  int dtype;
+  hipStream_t stream;
+};
+
+constexpr int kMaxConvK = 8;
+int64_t conv_chunk_steps();  // steps per wave of the sequence kernel
+hipError_t launch_conv_fwd(const ConvArgs& a);
+hipError_t launch_conv_update(const ConvArgs& a);
+
 // How a scan is split along the sequence: n_chunks chunks of chunk_len steps.
 struct ScanPlan {
   int64_t chunk_len;

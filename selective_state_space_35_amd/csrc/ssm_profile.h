@@ -13,7 +13,9 @@ enum : int {
   kKindMain = 3,    // main scan pass
   kKindFill = 4,    // last_state of an empty sequence (L == 0)
   kKindUpdate = 5,  // single-token state update
-  kNumKinds = 6
+  kKindConv = 6,    // causal depthwise convolution over a sequence
+  kKindConvUpdate = 7,  // single-token convolution-state update
+  kNumKinds = 8
 };
 
 // When profiling is on, creates and records the start event on `s` and returns true.

@@ -118,6 +118,47 @@ def test_update_validation(lib):
     assert update(lib, b=0, state=None) == OK
 
 
+def conv(lib, v=FAKE, q=FAKE, cb=None, sin=None, x=FAKE, sout=None, b=1, L=8, E=64, K=4, dtype=0):
+    return lib.ssm_conv_fwd(v, q, cb, sin, x, sout, b, L, E, K, dtype, None)
+
+
+def conv_update(lib, state=FAKE, v=FAKE, q=FAKE, cb=None, x=FAKE, b=1, E=64, K=4, dtype=0):
+    return lib.ssm_conv_update(state, v, q, cb, x, b, E, K, dtype, None)
+
+
+def test_conv_validation(lib):
+    assert conv(lib, dtype=3) == ERR_DTYPE
+    assert conv(lib, K=0) == ERR_DIM
+    assert conv(lib, K=9) == ERR_DIM
+    assert conv(lib, L=-1) == ERR_DIM
+    assert conv(lib, b=-1) == ERR_DIM
+    assert conv(lib, v=None) == ERR_NULL
+    assert conv(lib, x=None) == ERR_NULL
+    assert conv(lib, q=None) == ERR_NULL
+    assert conv(lib, v=FAKE + 2) == ERR_ALIGN
+    assert conv(lib, x=FAKE + 1, dtype=1) == ERR_ALIGN
+    assert conv(lib, q=FAKE + 2) == ERR_ALIGN
+    assert conv(lib, cb=FAKE + 1) == ERR_ALIGN
+    assert conv(lib, sin=FAKE + 1, dtype=1) == ERR_ALIGN
+    assert conv(lib, sout=FAKE + 2) == ERR_ALIGN
+    assert conv(lib, E=1 << 30) == ERR_DIM  # 64 rows of this width overflow 32-bit offsets
+    assert conv(lib, b=0, v=None, q=None, x=None) == OK
+    assert conv(lib, E=0, v=None, q=None, x=None) == OK
+
+
+def test_conv_update_validation(lib):
+    assert conv_update(lib, dtype=-1) == ERR_DTYPE
+    assert conv_update(lib, K=0) == ERR_DIM
+    assert conv_update(lib, K=9) == ERR_DIM
+    assert conv_update(lib, E=-1) == ERR_DIM
+    for k in ("state", "v", "q", "x"):
+        assert conv_update(lib, **{k: None}) == ERR_NULL, k
+    assert conv_update(lib, state=FAKE + 1, dtype=1) == ERR_ALIGN
+    assert conv_update(lib, v=FAKE + 2) == ERR_ALIGN
+    assert conv_update(lib, cb=FAKE + 2) == ERR_ALIGN
+    assert conv_update(lib, b=0, state=None) == OK
+
+
 def test_binding_refuses_cpu_tensors():
     torch = pytest.importorskip("torch")
     if not os.path.exists(ssm.library_path()):
@@ -131,6 +172,10 @@ def test_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError, match="GPU"):
         ssm.ssm_state_update(torch.zeros(b, E, N), torch.zeros(b, E), torch.zeros(b, E), A,
                              torch.zeros(b, N), torch.zeros(b, N))
+    with pytest.raises(ValueError, match="GPU"):
+        ssm.ssm_conv_fwd(u, torch.zeros(E, 4))
+    with pytest.raises(ValueError, match="GPU"):
+        ssm.ssm_conv_update(torch.zeros(b, E, 4), torch.zeros(b, E), torch.zeros(E, 4))
 
 
 def test_binding_raises_when_library_missing(monkeypatch):
@@ -165,5 +210,6 @@ def test_scan_plan_query(lib, monkeypatch):
 
 def test_profile_read_with_nothing_recorded(lib):
     out = ssm.ssm_profile_read()
-    assert set(out) == {"widen_rows", "chunk_aggregate", "chunk_carry", "scan_main", "fill_state", "state_update"}
+    assert set(out) == {"widen_rows", "chunk_aggregate", "chunk_carry", "scan_main", "fill_state", "state_update",
+                        "conv", "conv_update"}
     assert all(v == (0.0, 0) for v in out.values())

@@ -1,12 +1,9 @@
 """The oracle's pins must catch plausible mistakes.
 
 Each mutant is the oracle C source built with one planted mistake
-(``-DORACLE_MUTATION=k``, CPU only): readout before the update, a dropped
-D*x term, the bias added after the softplus, a flipped sign of A, a write
-term missing the step, a gate missing its z factor, a reversed state index
-on B, C read one step late, B and C swapped in the token update, a softplus
-sign error.  Every mutant must fail at least one pin in
-``test_oracle_pins.py``.
+(``-DORACLE_MUTATION=k``, CPU only); see MUTANTS for the list (scan,
+token update and convolution mistakes).  Every mutant must fail at least
+one pin in ``test_oracle_pins.py``, and the unmutated build must pass them.
 """
 import os
 
@@ -27,6 +24,8 @@ MUTANTS = {
     8: "C read one step late",
     9: "softplus sign error",
     10: "B and C swapped in the token update",
+    11: "convolution without its silu",
+    12: "reversed taps in the convolution token update",
 }
 
 # cheap pins first; each mutant stops at its first failing pin
@@ -45,6 +44,8 @@ PIN_CALLS = [
     pins.test_p4_large_step_resets_state,
     pins.test_p1_quadratic_closed_form_L64,
     pins.test_p1_hand_unrolled_L5_in_50_digits,
+    lambda: pins.test_conv_matches_numpy_convolve(4),
+    pins.test_conv_token_steps_equal_sequence,
 ]
 
 

@@ -383,3 +383,55 @@ def test_nan_propagates_along_its_channel_only():
     y, last = run(p)
     assert np.all(np.isnan(y[0, 7:, 2])) and not np.any(np.isnan(y[0, :7, 2]))
     assert not np.any(np.isnan(np.delete(y, 2, axis=2)))
+
+
+# ----------------------------------------------------------------------------
+# causal depthwise convolution + silu ([AB] row 4) and its token form ([AB] row 6)
+# ----------------------------------------------------------------------------
+def conv_problem(b, L, E, K, seed):
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((b, L, E)), rng.standard_normal((E, K)), rng.standard_normal(E)
+
+
+@pytest.mark.parametrize("K", [1, 2, 3, 4, 7])
+def test_conv_matches_numpy_convolve(K):
+    """x[t] = silu(cb + sum_k q[k] v[t-K+1+k]) with left zero padding == numpy.convolve with reversed taps."""
+    v, q, cb = conv_problem(2, 29, 5, K, seed=30 + K)
+    x, st = oracle.conv_fwd(v, q, cb)
+    for bi in range(2):
+        for c in range(5):
+            pre = cb[c] + np.convolve(v[bi, :, c], q[c, ::-1])[:29]
+            np.testing.assert_allclose(x[bi, :, c], pre * scipy.special.expit(pre), rtol=1e-13, atol=1e-14)
+            # the returned state is the K most recent samples, oldest first (zeros before t = 0)
+            tail = np.concatenate([np.zeros(K), v[bi, :, c]])[-K:]
+            np.testing.assert_array_equal(st[bi, c], tail)
+
+
+def test_conv_token_steps_equal_sequence():
+    """Shifting the K-sample state and appending each token reproduces the sequence form ([AB] self-check)."""
+    v, q, cb = conv_problem(3, 17, 6, 4, seed=40)
+    x, st_out = oracle.conv_fwd(v, q, cb)
+    st = np.zeros((3, 6, 4))
+    for t in range(17):
+        st, xt = oracle.conv_update(st, v[:, t], q, cb)
+        np.testing.assert_allclose(xt, x[:, t], rtol=1e-14, atol=1e-15)
+    np.testing.assert_array_equal(st, st_out)
+
+
+def test_conv_continuation_and_short_sequences():
+    v, q, cb = conv_problem(2, 23, 4, 4, seed=41)
+    x, st = oracle.conv_fwd(v, q, cb)
+    for L1 in (1, 2, 3, 9, 22):  # includes a first part shorter than K
+        x1, st1 = oracle.conv_fwd(v[:, :L1], q, cb)
+        x2, st2 = oracle.conv_fwd(v[:, L1:], q, cb, state_in=st1)
+        np.testing.assert_array_equal(np.concatenate([x1, x2], axis=1), x)
+        np.testing.assert_array_equal(st2, st)
+
+
+def test_conv_is_causal():
+    v, q, cb = conv_problem(1, 30, 3, 4, seed=42)
+    x0, _ = oracle.conv_fwd(v, q, cb)
+    v2 = v.copy()
+    v2[:, 13:] += 1.0
+    x1, _ = oracle.conv_fwd(v2, q, cb)
+    assert np.array_equal(x0[:, :13], x1[:, :13]) and not np.array_equal(x0[:, 13:], x1[:, 13:])

@@ -115,6 +115,32 @@ DECODE = DecodeWorkload(
 SCAN_WORKLOADS = {w.name: w for w in (TINY, BLOCK, MID, LONG)}
 
 
+@dataclass(frozen=True)
+class ConvWorkload:
+    """Causal depthwise convolution before the scan: v [b, L, E], weight [E, K]."""
+    name: str
+    b: int
+    L: int
+    E: int
+    K: int
+    dtype: str
+    bias: bool = True
+    state_in: bool = False
+    description: str = ""
+
+    def with_shape(self, **kw) -> "ConvWorkload":
+        d = dict(self.__dict__)
+        d.update(kw)
+        return ConvWorkload(**d)
+
+
+# the convolution in front of the long-sequence scan and of the generation step
+CONV_LONG = ConvWorkload("conv_long", b=1, L=65536, E=5120, K=4, dtype="bf16",
+                         description="convolution before the long scan: b1 L65536 E5120 K4 bf16")
+CONV_DECODE = ConvWorkload("conv_decode", b=256, L=1, E=5120, K=4, dtype="bf16", state_in=True,
+                           description="generation-time convolution state update: b256 E5120 K4 bf16")
+
+
 def a_matrix(E: int, N: int) -> np.ndarray:
     """A[e, n] = -exp(A_log[e, n]) with A_log[e, n] = log(n + 1), in float32, shape [E, N]."""
     a_log = np.log(np.arange(1, N + 1, dtype=np.float64)).astype(np.float32)
@@ -247,4 +273,25 @@ def make_decode_inputs(w: DecodeWorkload, seed: int = 0, device="cpu", backend: 
     out["A"] = torch.from_numpy(a_matrix(w.E, w.N)).to(device)
     out["state0"] = torch.zeros((w.b, w.E, w.N), dtype=torch.float32, device=device)
     out["softplus"] = w.softplus
+    return out
+
+
+def make_conv_inputs(w: ConvWorkload, seed: int = 0, device="cpu", backend: str = "numpy") -> dict:
+    """Inputs of one convolution call.
+
+    Keys: v [b, L, E] (N(0,1)); weight [E, K] float32, N(0, 1/K) like a fan-in
+    scaled initialisation; conv_bias [E] float32 N(0, 0.1^2) or None; state_in
+    [b, E, K] (N(0,1), the streamed dtype) or None.  Draw order: v, weight,
+    conv_bias, state_in.
+    """
+    import torch
+
+    drawer = _NumpyDraw(seed) if backend == "numpy" else _TorchDraw(seed, device)
+    io = _torch_dtype(w.dtype)
+    out = {}
+    out["v"] = drawer.finish(drawer.normal((w.b, w.L, w.E), 0.0, 1.0), io, device)
+    out["weight"] = drawer.finish(drawer.normal((w.E, w.K), 0.0, 1.0 / np.sqrt(w.K)), torch.float32, device)
+    out["conv_bias"] = drawer.finish(drawer.normal((w.E,), 0.0, 0.1), torch.float32, device) if w.bias else None
+    out["state_in"] = (drawer.finish(drawer.normal((w.b, w.E, w.K), 0.0, 1.0), io, device)
+                       if w.state_in else None)
     return out
