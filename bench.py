@@ -12,10 +12,13 @@ own JSON object, and so is the causal convolution that precedes the scan
 
 Prints ONE JSON line on stdout:
   value        b*L*E elements per second over the timed steps
-  roofline     HBM roofline of the dominant kernel (scan_main), its duration
-               measured with HIP events on the launch stream over the timed
-               region; traffic from the committed rocprofv3 PMC summary when
-               it was taken on the current kernel source, else null
+  roofline     ALU roofline of the dominant kernel (scan_main): algorithmic fp32
+               VALU lane-slots of one pass (a transcendental counts 4) over its
+               duration, measured with HIP events on the launch stream over the
+               timed region, against the 78.6e12 slot/s issue peak; traffic (HBM
+               bytes per launch) from the committed rocprofv3 PMC summary when it
+               was taken on the current kernel source, else null
+  roofline_hbm the same kernel's algorithmic bytes over its duration vs 8 TB/s
   cpu_baseline the fp64 oracle on a bounded channel sample of the same inputs
                (channels are independent chains), timed on the host cores
 
@@ -32,7 +35,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
-VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9  # 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz, non-packed fp32 issue
+# fp32 VALU issue peak in lane-slots/s: 157.3 TFLOP/s of fp32 vector FMA = 78.6e12 FMA lane-ops/s
+# (256 CUs x 4 SIMDs x 32 lanes x 2.4 GHz).  A transcendental (exp2, log2, rcp) issues at a quarter
+# of that rate, so it occupies 4 slots.
+VALU_SLOT_PEAK = 256 * 4 * 32 * 2.4e9
+TRANS_SLOTS = 4
 
 
 def log(*a):
@@ -47,6 +54,23 @@ def scan_bytes(b, L, E, N, s, gate=True, last_state=True):
     if last_state:
         by += b * E * N * 4
     return by
+
+
+def scan_slots(b, L, E, N, softplus=True, gate=True, has_d=True, has_bias=False, bf16=True):
+    """Algorithmic fp32 VALU lane-slots of one scan pass (the minimal single pass).
+
+    Per (t, e, n): d*A2 (1), exp2 (4), du*B (1), a*h + w (1), C*h + acc (1)          -> 8
+    Per (t, e):    delta + bias (1); softplus: 2 transcendentals + 4 VALU (12);
+                   d*u (1); D*u (1); silu gate: 2 transcendentals + 3 VALU, and the
+                   product (12); bf16 widening of each streamed input and rounding of y (1 each)
+    """
+    per_te = 1  # d * u
+    per_te += 1 if has_bias else 0
+    per_te += 2 * TRANS_SLOTS + 4 if softplus else 0
+    per_te += 1 if has_d else 0
+    per_te += 2 * TRANS_SLOTS + 4 if gate else 0
+    per_te += (3 if gate else 2) + 1 if bf16 else 0
+    return b * L * E * (8 * N + per_te)
 
 
 def update_bytes(b, E, N, s, gate=True):
@@ -168,12 +192,15 @@ def main():
     log(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step, {value:.4e} elem/s, path {path_gbps:.1f} GB/s; "
         f"kernels {kernels}")
 
-    # ALU view: the recurrence needs per (t, e, n) one exp2 and four fp32 VALU ops (2 mul, 2 fma)
-    valu_ops = 5 * elems * w.N
-    alu = {"valu_lane_ops_per_step": valu_ops, "achieved_lane_ops_per_s": valu_ops / (ms_per_step * 1e-3),
-           "issue_peak_lane_ops_per_s": VALU_LANE_OPS,
-           "note": "counts the minimal 4 VALU + 1 v_exp_f32 per (t,e,n) of one pass; the chunked path adds a "
-                   "second pass over most elements"}
+    # ALU view (the bound that holds): algorithmic VALU lane-slots of one pass over the scan
+    slots = scan_slots(w.b, w.L, w.E, w.N, softplus=w.softplus, gate=w.z is not None, has_d=w.D is not None,
+                       has_bias=w.delta_bias is not None, bf16=(w.dtype == "bf16"))
+    main_tslots = slots / main_avg_s / 1e12
+    path_tslots = slots / (ms_per_step * 1e-3) / 1e12
+    alu = {"slots_per_step": slots, "path_Tslot_per_s": path_tslots,
+           "path_frac": path_tslots * 1e12 / VALU_SLOT_PEAK,
+           "note": "one slot = one fp32 VALU lane-op issue; a transcendental takes 4. The sequence split runs a "
+                   "second (aggregate) pass over all but the last chunk; its slots are not algorithmic"}
 
     # state update (generation): 128 successive single-token updates, state carried in HBM
     update = None
@@ -313,10 +340,12 @@ def main():
         "hbm_GBps": path_gbps,
         "hbm_frac": path_gbps / HBM_PEAK_GBPS,
         "algorithmic_bytes_per_step": algo,
-        "roofline": {"bound": "hbm", "kernel": "scan_main", "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "traffic_note": traffic_note,
-                     "kernel_avg_us": round(main_avg_s * 1e6, 2)},
+        "roofline": {"bound": "alu", "kernel": "scan_main", "achieved": main_tslots,
+                     "peak": VALU_SLOT_PEAK / 1e12, "unit": "Tslot/s", "frac": main_tslots * 1e12 / VALU_SLOT_PEAK,
+                     "traffic": traffic, "traffic_note": traffic_note, "algorithmic_bytes": algo,
+                     "algorithmic_slots": slots, "kernel_avg_us": round(main_avg_s * 1e6, 2)},
+        "roofline_hbm": {"bound": "hbm", "kernel": "scan_main", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS},
         "kernels": kernels,
         "alu": alu,
         "state_update": update,

@@ -22,10 +22,15 @@ Definitions followed (page title, site, section):
     next token";
   * causal depthwise convolution + silu before the scan -- abhik.ai page,
     row 4 "Add causal local context before selecting coefficients", and its
-    single-token form in row 6.
+    single-token form in row 6;
+  * backward of the scan (gradients of every input by the chain rule of the
+    definition; the pages train the block end to end and recompute states in
+    the backward pass) -- nadeemcite summary, "Core Idea"; abhik.ai page,
+    "Compose the updates instead of waiting for every state".
 
 Parity status: every function here is pinned by closed forms, invariants and
-brute force in ``tests/test_oracle_pins.py``; none is "parity unpinned".
+brute force in ``tests/test_oracle_pins.py`` (the backward by central finite
+differences of the pinned forward); none is "parity unpinned".
 """
 import ctypes
 import os
@@ -58,6 +63,8 @@ def _load(path=None):
     lib.oracle_conv_fwd.argtypes = [_dp] * 6 + [ctypes.c_int64] * 4
     lib.oracle_conv_update.restype = ctypes.c_int
     lib.oracle_conv_update.argtypes = [_dp] * 5 + [ctypes.c_int64] * 3
+    lib.oracle_scan_bwd.restype = ctypes.c_int
+    lib.oracle_scan_bwd.argtypes = [_dp] * 8 + [ctypes.c_int] + [_dp] * 12 + [ctypes.c_int64] * 4 + [ctypes.c_int]
     lib.oracle_softplus_value.restype = ctypes.c_double
     lib.oracle_softplus_value.argtypes = [ctypes.c_double]
     lib.oracle_silu_value.restype = ctypes.c_double
@@ -137,6 +144,38 @@ def scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=False, h0=
     if return_states:
         return y, last, states
     return y, last
+
+
+def scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=False, h0=None, dy=None, dlast=None,
+             threads=None):
+    """Gradients of loss = sum(dy * y) + sum(dlast * last_state) for the scan above.
+
+    Returns a dict with du, ddelta [b, L, E]; dA [E, N]; dB, dC [b, L, N]; dh0 [b, E, N];
+    and dD [E], dz [b, L, E], d_delta_bias [E] when D, z, delta_bias are given (else None).
+    """
+    lib = _load()
+    u, delta, A, B, C, dy = (to_f64(v) for v in (u, delta, A, B, C, dy))
+    D, z, delta_bias, h0, dlast = (to_f64(v) for v in (D, z, delta_bias, h0, dlast))
+    b, L, E = u.shape
+    N = A.shape[1]
+    if (delta.shape != (b, L, E) or dy.shape != (b, L, E) or A.shape != (E, N) or B.shape != (b, L, N)
+            or C.shape != (b, L, N)):
+        raise ValueError("oracle.scan_bwd: inconsistent shapes")
+    for v, shp in ((z, (b, L, E)), (D, (E,)), (delta_bias, (E,)), (h0, (b, E, N)), (dlast, (b, E, N))):
+        if v is not None and v.shape != shp:
+            raise ValueError("oracle.scan_bwd: optional input shape")
+    out = {"du": np.empty((b, L, E)), "ddelta": np.empty((b, L, E)), "dA": np.empty((E, N)),
+           "dB": np.empty((b, L, N)), "dC": np.empty((b, L, N)), "dh0": np.empty((b, E, N)),
+           "dD": np.empty(E) if D is not None else None, "dz": np.empty((b, L, E)) if z is not None else None,
+           "d_delta_bias": np.empty(E) if delta_bias is not None else None}
+    rc = lib.oracle_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                             int(bool(softplus)), _ptr(h0), _ptr(dy), _ptr(dlast), _ptr(out["du"]),
+                             _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]),
+                             _ptr(out["dz"]), _ptr(out["d_delta_bias"]), _ptr(out["dh0"]), b, L, E, N,
+                             threads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"oracle_scan_bwd failed with {rc}")
+    return out
 
 
 def state_update(state, x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=False, threads=None):

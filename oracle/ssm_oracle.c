@@ -1,6 +1,7 @@
 /*
  * ssm_oracle.c -- plain, sequential, double-precision CPU reference of the
- * Mamba-1 (S6) selective scan and of its single-token recurrent state update.
+ * Mamba-1 (S6) selective scan, its backward (gradients of every input), its
+ * single-token recurrent state update, and the causal convolution before it.
  *
  * TEST INFRASTRUCTURE ONLY.  This file is the correctness oracle for the GPU
  * library.  Only the test suite, the package's smoke check and the benchmark's
@@ -323,6 +324,207 @@ int oracle_conv_update(double* state, const double* v, const double* q, const do
     }
   }
   return 0;
+}
+
+/* ------------------------------------------------------------------------
+ * Backward of the scan: the gradient of a scalar loss
+ *     loss = sum dy[b,t,e] * y[b,t,e] + sum d_last[b,e,n] * last_state[b,e,n]
+ * with respect to every input, by the chain rule applied to the definition
+ * above.  The pages train the block end to end and recompute the states in
+ * the backward pass instead of storing them ([NC] "Core Idea"; [AB] "Compose
+ * the updates instead of waiting for every state"); the oracle simply keeps
+ * every state of a chain in memory.
+ *
+ * Per chain, walking t from L-1 down to 0 with X = dloss/dh_t coming from
+ * the future (X = d_last at t = L-1):
+ *   g   = silu(z_t) (1 without a gate);  dq = dy_t * g
+ *   dz_t = dy_t * q_t * silu'(z_t),  silu'(z) = s(z) * (1 + z * (1 - s(z))),  s the logistic
+ *   dD  += dq * u_t;   du_t = dq * D
+ *   G_n = X_n + dq * C[t,n]                       (total dloss/dh_t,n)
+ *   dC[t,n] += dq * h_t,n ;  dB[t,n] += G_n * d_t * u_t
+ *   du_t += G_n * d_t * B[t,n];  dd += G_n * u_t * B[t,n] + G_n * h_{t-1},n * a_t,n * A[n]
+ *   dA[n] += G_n * h_{t-1},n * a_t,n * d_t;   X_n = a_t,n * G_n   (dloss/dh_{t-1})
+ *   ddelta_t = dd * s(delta_t + bias) with softplus (dd without);  dbias += ddelta_t
+ * and dloss/dh0 = X after t = 0.  B and C are shared by every channel of a
+ * batch row, A, D and bias by every batch row and step, so their gradients
+ * are sums over chains.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  const double *u, *delta, *A, *B, *C, *D, *z, *bias, *h0, *dy, *dlast;
+  double *du, *ddelta, *dz, *dh0;
+  double *dA, *dB, *dC, *dD, *dbias; /* this thread's private sums */
+  int64_t b, L, E, N;
+  int softplus;
+  int64_t chain_begin, chain_end;
+} bwd_job;
+
+static double oracle_sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+static void bwd_chain(const bwd_job* j, int64_t bi, int64_t e, double* hist, double* q, double* X) {
+  const int64_t L = j->L, E = j->E, N = j->N;
+  /* forward, keeping every state: hist[(t + 1) * N + n] = h_t,n, hist[n] = h_{-1},n */
+  for (int64_t n = 0; n < N; n++) hist[n] = j->h0 ? j->h0[(bi * E + e) * N + n] : 0.0;
+  for (int64_t t = 0; t < L; t++) {
+    const int64_t xe = (bi * L + t) * E + e, xn = (bi * L + t) * N;
+    double d = j->delta[xe] + (j->bias ? j->bias[e] : 0.0);
+    if (j->softplus) d = oracle_softplus(d);
+    double acc = 0.0;
+    for (int64_t n = 0; n < N; n++) {
+      const double h = exp(d * j->A[e * N + n]) * hist[t * N + n] + d * j->B[xn + n] * j->u[xe];
+      hist[(t + 1) * N + n] = h;
+      acc += j->C[xn + n] * h;
+    }
+    q[t] = acc + (j->D ? j->D[e] * j->u[xe] : 0.0);
+  }
+  /* backward */
+  for (int64_t n = 0; n < N; n++) X[n] = j->dlast ? j->dlast[(bi * E + e) * N + n] : 0.0;
+#if ORACLE_MUTATION == 19
+  for (int64_t n = 0; n < N; n++) X[n] = 0.0;
+#endif
+  for (int64_t t = L - 1; t >= 0; t--) {
+    const int64_t xe = (bi * L + t) * E + e, xn = (bi * L + t) * N;
+    const double x = j->u[xe];
+    const double raw = j->delta[xe] + (j->bias ? j->bias[e] : 0.0);
+    const double d = j->softplus ? oracle_softplus(raw) : raw;
+    double dq = j->dy[xe];
+    if (j->z) {
+      const double zz = j->z[xe], sg = oracle_sigmoid(zz);
+#if ORACLE_MUTATION == 17
+      j->dz[xe] = j->dy[xe] * q[t] * sg;
+#else
+      j->dz[xe] = j->dy[xe] * q[t] * sg * (1.0 + zz * (1.0 - sg));
+#endif
+      dq *= oracle_silu(zz);
+    }
+    double dut = 0.0, dd = 0.0;
+    if (j->D) {
+      j->dD[e] += dq * x;
+      dut = dq * j->D[e];
+    }
+    for (int64_t n = 0; n < N; n++) {
+      const double G = X[n] + dq * j->C[xn + n];
+      const double h_t = hist[(t + 1) * N + n], h_prev = hist[t * N + n];
+      const double a = exp(d * j->A[e * N + n]);
+#if ORACLE_MUTATION == 16
+      j->dC[xn + n] += dq * h_prev;
+#else
+      j->dC[xn + n] += dq * h_t;
+#endif
+#if ORACLE_MUTATION == 18
+      j->dB[xn + n] += G * x;
+#else
+      j->dB[xn + n] += G * d * x;
+#endif
+      dut += G * d * j->B[xn + n];
+#if ORACLE_MUTATION == 13
+      const double ha = h_t * a;
+#else
+      const double ha = h_prev * a;
+#endif
+      dd += G * x * j->B[xn + n] + G * ha * j->A[e * N + n];
+      j->dA[e * N + n] += G * ha * d;
+#if ORACLE_MUTATION == 14
+      X[n] = G;
+#else
+      X[n] = a * G;
+#endif
+    }
+    j->du[xe] = dut;
+#if ORACLE_MUTATION == 15
+    const double ddelta = dd;
+#else
+    const double ddelta = j->softplus ? dd * oracle_sigmoid(raw) : dd;
+#endif
+    j->ddelta[xe] = ddelta;
+    if (j->bias) j->dbias[e] += ddelta;
+  }
+  if (j->dh0)
+    for (int64_t n = 0; n < N; n++) j->dh0[(bi * E + e) * N + n] = X[n];
+}
+
+static void* bwd_worker(void* arg) {
+  const bwd_job* j = (const bwd_job*)arg;
+  const int64_t N = j->N > 0 ? j->N : 1;
+  double* hist = (double*)malloc(sizeof(double) * (size_t)((j->L + 1) * N));
+  double* q = (double*)malloc(sizeof(double) * (size_t)(j->L > 0 ? j->L : 1));
+  double* X = (double*)malloc(sizeof(double) * (size_t)N);
+  if (!hist || !q || !X) {
+    free(hist); free(q); free(X);
+    return (void*)1;
+  }
+  for (int64_t c = j->chain_begin; c < j->chain_end; c++) bwd_chain(j, c / j->E, c % j->E, hist, q, X);
+  free(hist); free(q); free(X);
+  return NULL;
+}
+
+/* Gradients of the scan.  Outputs: du, ddelta [b,L,E]; dz [b,L,E] (when z is given);
+ * dA [E,N]; dB, dC [b,L,N]; dD [E] (when D is given); dbias [E] (when a bias is given);
+ * dh0 [b,E,N] (nullable).  dlast [b,E,N] is nullable (zero).  Returns 0, -1 on bad
+ * arguments, -2 on allocation or thread failure. */
+int oracle_scan_bwd(const double* u, const double* delta, const double* A, const double* B, const double* C,
+                    const double* D, const double* z, const double* delta_bias, int softplus, const double* h0,
+                    const double* dy, const double* dlast, double* du, double* ddelta, double* dA, double* dB,
+                    double* dC, double* dD, double* dz, double* dbias, double* dh0, int64_t b, int64_t L, int64_t E,
+                    int64_t N, int threads) {
+  if (b < 0 || L < 0 || E < 0 || N < 0) return -1;
+  if (!A || !dA || !dB || !dC || (L > 0 && (!u || !delta || !B || !C || !dy || !du || !ddelta)) ||
+      (z && !dz) || (D && !dD) || (delta_bias && !dbias))
+    return -1;
+  memset(dA, 0, sizeof(double) * (size_t)(E * N));
+  memset(dB, 0, sizeof(double) * (size_t)(b * L * N));
+  memset(dC, 0, sizeof(double) * (size_t)(b * L * N));
+  if (dD) memset(dD, 0, sizeof(double) * (size_t)E);
+  if (dbias) memset(dbias, 0, sizeof(double) * (size_t)E);
+  const int64_t chains = b * E;
+  if (chains == 0) return 0;
+  if (threads < 1) threads = 1;
+  if (threads > chains) threads = (int)chains;
+  /* private sums per thread: dA [E,N], dB, dC [b,L,N], dD, dbias [E] */
+  const int64_t per = E * N + 2 * b * L * N + 2 * E;
+  double* priv = (double*)calloc((size_t)(per * threads), sizeof(double));
+  bwd_job* jobs = (bwd_job*)malloc(sizeof(bwd_job) * (size_t)threads);
+  pthread_t* tid = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)threads);
+  if (!priv || !jobs || !tid) { free(priv); free(jobs); free(tid); return -2; }
+  int rc = 0, started = 0;
+  for (int i = 0; i < threads; i++) {
+    bwd_job* jb = &jobs[i];
+    memset(jb, 0, sizeof *jb);
+    jb->u = u; jb->delta = delta; jb->A = A; jb->B = B; jb->C = C; jb->D = D; jb->z = z; jb->bias = delta_bias;
+    jb->h0 = h0; jb->dy = dy; jb->dlast = dlast; jb->du = du; jb->ddelta = ddelta; jb->dz = dz; jb->dh0 = dh0;
+    double* base = priv + per * i;
+    jb->dA = base; jb->dB = base + E * N; jb->dC = jb->dB + b * L * N; jb->dD = jb->dC + b * L * N;
+    jb->dbias = jb->dD + E;
+    jb->b = b; jb->L = L; jb->E = E; jb->N = N; jb->softplus = softplus;
+    jb->chain_begin = chains * i / threads;
+    jb->chain_end = chains * (i + 1) / threads;
+    if (threads == 1) {
+      if (bwd_worker(jb)) rc = -2;
+    } else if (pthread_create(&tid[i], NULL, bwd_worker, jb) != 0) {
+      rc = -2;
+      break;
+    } else {
+      started++;
+    }
+  }
+  for (int i = 0; i < started; i++) {
+    void* ret = NULL;
+    pthread_join(tid[i], &ret);
+    if (ret) rc = -2;
+  }
+  if (rc == 0) {
+    /* add the private sums in thread order */
+    for (int i = 0; i < threads; i++) {
+      const bwd_job* jb = &jobs[i];
+      for (int64_t k = 0; k < E * N; k++) dA[k] += jb->dA[k];
+      for (int64_t k = 0; k < b * L * N; k++) { dB[k] += jb->dB[k]; dC[k] += jb->dC[k]; }
+      if (dD) for (int64_t k = 0; k < E; k++) dD[k] += jb->dD[k];
+      if (dbias) for (int64_t k = 0; k < E; k++) dbias[k] += jb->dbias[k];
+    }
+  }
+  free(priv);
+  free(jobs);
+  free(tid);
+  return rc;
 }
 
 /* Exposed for the softplus / gate pins: the scalar helpers exactly as used above. */

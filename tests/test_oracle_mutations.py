@@ -2,7 +2,7 @@
 
 Each mutant is the oracle C source built with one planted mistake
 (``-DORACLE_MUTATION=k``, CPU only); see MUTANTS for the list (scan,
-token update and convolution mistakes).  Every mutant must fail at least
+token update, convolution and backward mistakes).  Every mutant must fail at least
 one pin in ``test_oracle_pins.py``, and the unmutated build must pass them.
 """
 import os
@@ -26,6 +26,13 @@ MUTANTS = {
     10: "B and C swapped in the token update",
     11: "convolution without its silu",
     12: "reversed taps in the convolution token update",
+    13: "backward: retention gradient uses h_t instead of h_{t-1}",
+    14: "backward: state gradient not decayed by the retention",
+    15: "backward: step gradient without the softplus derivative",
+    16: "backward: C gradient uses h_{t-1}",
+    17: "backward: gate gradient uses the logistic instead of the silu derivative",
+    18: "backward: B gradient without the step",
+    19: "backward: gradient of the last state ignored",
 }
 
 # cheap pins first; each mutant stops at its first failing pin
@@ -46,6 +53,7 @@ PIN_CALLS = [
     pins.test_p1_hand_unrolled_L5_in_50_digits,
     lambda: pins.test_conv_matches_numpy_convolve(4),
     pins.test_conv_token_steps_equal_sequence,
+    lambda: pins.test_bwd_matches_finite_differences(True, True, True, True, True, True),
 ]
 
 

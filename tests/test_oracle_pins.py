@@ -435,3 +435,119 @@ def test_conv_is_causal():
     v2[:, 13:] += 1.0
     x1, _ = oracle.conv_fwd(v2, q, cb)
     assert np.array_equal(x0[:, :13], x1[:, :13]) and not np.array_equal(x0[:, 13:], x1[:, 13:])
+
+
+# ----------------------------------------------------------------------------
+# backward: the gradient of the scan against central finite differences of the
+# (pinned) forward oracle.  The pages train the block end to end and recompute
+# states in the backward pass ([NC] "Core Idea"); the gradient itself is fixed
+# by the forward definition, so differentiating the forward numerically pins it.
+# ----------------------------------------------------------------------------
+GRAD_INPUTS = ("u", "delta", "A", "B", "C", "D", "z", "delta_bias", "h0")
+GRAD_NAMES = {"u": "du", "delta": "ddelta", "A": "dA", "B": "dB", "C": "dC", "D": "dD", "z": "dz",
+              "delta_bias": "d_delta_bias", "h0": "dh0"}
+
+
+def bwd_problem(seed, softplus=True, gate=True, with_D=True, with_bias=True, with_h0=True, with_dlast=True,
+                b=2, L=7, E=3, N=4):
+    p = rand_problem(b, L, E, N, seed, softplus=softplus, gate=gate, with_D=with_D, with_bias=with_bias)
+    rng = np.random.default_rng(seed + 1000)
+    if not softplus:  # a positive step keeps every retention below one
+        p["delta"] = rng.uniform(0.05, 0.8, (b, L, E))
+    p["h0"] = rng.standard_normal((b, E, N)) if with_h0 else None
+    p["dy"] = rng.standard_normal((b, L, E))
+    p["dlast"] = rng.standard_normal((b, E, N)) if with_dlast else None
+    return p
+
+
+def loss_of(p):
+    y, last = oracle.scan(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["delta_bias"],
+                          p["softplus"], h0=p["h0"], threads=1)
+    total = float(np.sum(p["dy"] * y))
+    if p["dlast"] is not None:
+        total += float(np.sum(p["dlast"] * last))
+    return total
+
+
+def grads_of(p):
+    return oracle.scan_bwd(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["delta_bias"],
+                           p["softplus"], h0=p["h0"], dy=p["dy"], dlast=p["dlast"], threads=2)
+
+
+def finite_difference(p, name, eps=1e-6):
+    base = p[name]
+    g = np.empty_like(base)
+    for idx in np.ndindex(base.shape):
+        old = base[idx]
+        h = eps * max(1.0, abs(old))
+        base[idx] = old + h
+        fp = loss_of(p)
+        base[idx] = old - h
+        fm = loss_of(p)
+        base[idx] = old
+        g[idx] = (fp - fm) / (2 * h)
+    return g
+
+
+@pytest.mark.parametrize("softplus,gate,with_D,with_bias,with_h0,with_dlast", [
+    (True, True, True, True, True, True),
+    (False, False, False, False, False, False),
+    (True, False, True, False, True, False),
+    (False, True, False, True, False, True),
+])
+def test_bwd_matches_finite_differences(softplus, gate, with_D, with_bias, with_h0, with_dlast):
+    p = bwd_problem(seed=51, softplus=softplus, gate=gate, with_D=with_D, with_bias=with_bias, with_h0=with_h0,
+                    with_dlast=with_dlast)
+    g = grads_of(p)
+    for name in GRAD_INPUTS:
+        if p[name] is None:
+            assert name in ("h0",) or g[GRAD_NAMES[name]] is None
+            continue
+        fd = finite_difference(p, name)
+        err = np.max(np.abs(g[GRAD_NAMES[name]] - fd) / (1.0 + np.abs(fd)))
+        assert err < 1e-6, f"{GRAD_NAMES[name]}: max error {err:.2e} against finite differences"
+
+
+def test_bwd_zero_initial_state_gradient_is_defined():
+    """Without h0 the gradient with respect to the (zero) initial state is still reported."""
+    p = bwd_problem(seed=52, with_h0=False)
+    g = grads_of(p)
+    p["h0"] = np.zeros((2, 3, 4))
+    fd = finite_difference(p, "h0")
+    assert np.max(np.abs(g["dh0"] - fd) / (1.0 + np.abs(fd))) < 1e-6
+
+
+def test_bwd_threads_do_not_change_results():
+    p = bwd_problem(seed=53, b=3, L=40, E=9, N=5)
+    g1 = oracle.scan_bwd(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["delta_bias"], True,
+                         h0=p["h0"], dy=p["dy"], dlast=p["dlast"], threads=1)
+    g4 = oracle.scan_bwd(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["delta_bias"], True,
+                         h0=p["h0"], dy=p["dy"], dlast=p["dlast"], threads=4)
+    for k, v in g1.items():
+        if v is None:
+            continue
+        if k in ("du", "ddelta", "dz", "dh0"):  # per-chain results do not depend on the split
+            assert np.array_equal(v, g4[k]), k
+        else:  # sums over chains: same terms, another addition order
+            np.testing.assert_allclose(v, g4[k], rtol=1e-12, atol=1e-12)
+
+
+def test_bwd_split_sequence_chains_through_the_state():
+    """Gradients of a sequence cut in two, with the state and its gradient passed across the cut,
+    equal those of the whole sequence (the backward of the continuation used for chunked training)."""
+    p = bwd_problem(seed=54, L=12)
+    g = grads_of(p)
+    L1 = 5
+    part = lambda k, sl: None if p[k] is None else p[k][:, sl]
+    first = {k: (part(k, slice(0, L1)) if k in ("u", "delta", "z", "B", "C", "dy") else p[k]) for k in p}
+    second = {k: (part(k, slice(L1, None)) if k in ("u", "delta", "z", "B", "C", "dy") else p[k]) for k in p}
+    _, mid = oracle.scan(first["u"], first["delta"], p["A"], first["B"], first["C"], p["D"], first["z"],
+                         p["delta_bias"], p["softplus"], h0=p["h0"])
+    second["h0"] = mid
+    g2 = grads_of(second)
+    first["dlast"] = g2["dh0"]
+    g1 = grads_of(first)
+    np.testing.assert_allclose(np.concatenate([g1["du"], g2["du"]], 1), g["du"], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(np.concatenate([g1["dB"], g2["dB"]], 1), g["dB"], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(g1["dA"] + g2["dA"], g["dA"], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(g1["dh0"], g["dh0"], rtol=1e-10, atol=1e-12)
