@@ -78,6 +78,13 @@ def update_bytes(b, E, N, s, gate=True):
     return 8 * b * E * N + b * E * ((3 if gate else 2) + 1) * s + 2 * b * N * s + E * (N + 2) * 4
 
 
+def bwd_bytes(b, L, E, N, s, gate=True):
+    """Algorithmic bytes of one backward call: u, delta (, z), dy and B, C read; du, ddelta (, dz) written
+    in the I/O dtype; dB, dC [b, L, N] and dA, dD, dbias written in float32; A, D, bias read."""
+    streams = (4 if gate else 3) + (3 if gate else 2)
+    return b * L * E * streams * s + 2 * b * L * N * s + 2 * b * L * N * 4 + 2 * E * (N + 2) * 4
+
+
 def conv_bytes(b, L, E, K, s, bias=True):
     """Algorithmic bytes of one causal convolution: v in, x out, the weights (and bias), the K-sample state out."""
     return 2 * b * L * E * s + E * K * 4 + (E * 4 if bias else 0) + b * E * K * s
@@ -118,6 +125,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target wall time of the CPU baseline sample")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-conv", action="store_true")
+    ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -238,6 +246,43 @@ def main():
                           "can be served from it; GB/s is algorithmic bytes over kernel time"}
         del xd, st, yd
 
+    # backward of the scan on the same workload (gradients of every input, states recomputed)
+    bwd = None
+    if not args.no_bwd:
+        gen = torch.Generator(device=dev).manual_seed(args.seed + 11)
+        dy = torch.randn(x["u"].shape, generator=gen, device=dev).to(x["u"].dtype)
+
+        def bwd_step():
+            return ssm.ssm_scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], dy, x["D"], x["z"],
+                                    x["delta_bias"], x["softplus"])
+
+        for _ in range(2):
+            g = bwd_step()
+        del g
+        torch.cuda.synchronize()
+        ssm.ssm_profile_read()
+        ssm.ssm_profile_enable(True)
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(3, args.steps // 5)
+        b0.record(stream)
+        for _ in range(reps):
+            g = bwd_step()
+        b1.record(stream)
+        torch.cuda.synchronize()
+        ssm.ssm_profile_enable(False)
+        del g
+        prof = ssm.ssm_profile_read()
+        bwd_ms = b0.elapsed_time(b1) / reps
+        bb = bwd_bytes(w.b, w.L, w.E, w.N, s, gate=w.z is not None)
+        bwd = {"workload": "backward of the long-sequence scan (same inputs, dy ~ N(0,1) bf16)",
+               "ms_per_call": round(bwd_ms, 4), "elem_per_s": elems / (bwd_ms * 1e-3),
+               "algorithmic_bytes": bb, "GBps": round(bb / (bwd_ms * 1e-3) / 1e9, 1),
+               "kernels": {k: {"avg_us": round(1e3 * v[0] / v[1], 2), "launches": v[1]}
+                           for k, v in prof.items() if v[1]},
+               "note": "includes the workspace allocation and the forward chunk-state passes it reruns"}
+        log(f"[bench] backward {bwd}")
+        del dy
+
     # causal convolution in front of the scan (long workload) and its generation-time token step
     conv = None
     if not args.no_conv:
@@ -350,6 +395,7 @@ def main():
         "alu": alu,
         "state_update": update,
         "conv": conv,
+        "backward": bwd,
         "cpu_baseline": cpu,
         "parity": parity,
     }

@@ -149,6 +149,41 @@ SSM_API int ssm_state_update(float* state, const void* x, const void* delta, con
                      int64_t b, int64_t E, int64_t N, int dtype, void* stream);
 
 /*
+ * Backward of the scan: gradients of
+ *   loss = sum dy[b,t,e] * y[b,t,e] + sum d_last_state[b,e,n] * last_state[b,e,n]
+ * with respect to every input of ssm_scan_fwd_from.  The gradients are the
+ * chain rule of the forward definition above; the states are recomputed from
+ * per-chunk incoming states instead of being stored ("Mamba: Linear-Time
+ * Sequence Modeling with Selective State Spaces", nadeemcite summary, "Core
+ * Idea"; abhik.ai page, "Compose the updates instead of waiting for every
+ * state").
+ *
+ * Inputs: the forward's arguments (same layouts and dtypes; initial_state
+ * nullable = zero), dy [b, L, E] (dtype), d_last_state [b, E, N] float
+ * (nullable = zero).
+ * Outputs (device pointers, fully overwritten, never accumulated into):
+ *   du, ddelta      [b, L, E]  dtype
+ *   dz              [b, L, E]  dtype   (required when z is given, ignored otherwise)
+ *   dA              [E, N]     float
+ *   dB, dC          [b, L, N]  float   (sums over the channels)
+ *   dD              [E]        float   (nullable; written when D is given)
+ *   d_delta_bias    [E]        float   (nullable; written when delta_bias is given)
+ *   d_initial_state [b, E, N]  float   (nullable; the gradient reaching the
+ *                                       initial state, also when it is zero)
+ * ddelta is the gradient with respect to the raw step (before bias and softplus).
+ * Results are deterministic: every sum over chunks or channel blocks is added
+ * in a fixed order.  The call takes a workspace of about
+ * 1.3 * b * L * E + 34 * b * L floats from the stream-ordered allocator on
+ * `stream`.  Sizes: 64 * E * sizeof(dtype) < 2^31.
+ */
+SSM_API int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                         const float* D, const void* z, const float* delta_bias, int softplus,
+                         const float* initial_state, const void* dy, const float* d_last_state, void* du,
+                         void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz, float* d_delta_bias,
+                         float* d_initial_state, int64_t b, int64_t L, int64_t E, int64_t N, int dtype,
+                         void* stream);
+
+/*
  * Causal depthwise convolution + SiLU, the step before the scan in the Mamba
  * block ([AB] row 4 "Add causal local context before selecting coefficients"):
  *   x[b,t,c] = silu(conv_bias[c] + sum_{k=0..K-1} q[c,k] * v[b, t-K+1+k, c])
@@ -197,7 +232,8 @@ SSM_API int ssm_scan_plan(int64_t b, int64_t L, int64_t E, int64_t N, int dtype,
  * (milliseconds) and launch counts for kinds 0 .. n_kinds-1 and clears the
  * record.  Kinds: 0 widen_rows (bf16 B/C rows to f32), 1 chunk_aggregate,
  * 2 chunk_carry, 3 scan_main, 4 fill_state, 5 state_update, 6 conv,
- * 7 conv_update; names from
+ * 7 conv_update, 8 bwd_rows, 9 bwd_aggregate, 10 bwd_carry, 11 bwd_main,
+ * 12 bwd_reduce; names from
  * ssm_profile_kind_name().  Off by default; the events add a few
  * microseconds per launch.  Process-wide, thread-safe.
  */

@@ -15,6 +15,9 @@ Functions (same names as the C entry points):
 * ``ssm_state_update(state, x, delta, A, B, C, D=None, z=None,
   delta_bias=None, softplus=False, y=None)`` -> ``y`` (``state`` is updated
   in place)
+* ``ssm_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None,
+  softplus=False, initial_state=None, d_last_state=None)`` -> dict of
+  gradients (du, ddelta, dA, dB, dC, dD, dz, d_delta_bias, d_initial_state)
 * ``ssm_conv_fwd(v, weight, conv_bias=None, state_in=None, x=None,
   state_out=None, return_state=True)`` -> ``(x, state_out)``: causal depthwise
   convolution + SiLU over the sequence
@@ -31,7 +34,7 @@ import ctypes
 import os
 
 __all__ = [
-    "ssm_scan_fwd", "ssm_scan_fwd_from", "ssm_state_update", "ssm_conv_fwd", "ssm_conv_update", "ssm_scan_plan", "ssm_profile_enable", "ssm_profile_read",
+    "ssm_scan_fwd", "ssm_scan_fwd_from", "ssm_scan_bwd", "ssm_state_update", "ssm_conv_fwd", "ssm_conv_update", "ssm_scan_plan", "ssm_profile_enable", "ssm_profile_read",
     "ssm_status_string", "library_path", "SSMError",
     "SSM_F32", "SSM_BF16", "load_library",
 ]
@@ -79,6 +82,8 @@ def load_library():
     lib.ssm_scan_fwd_from.argtypes = [_vp] * 8 + [_int, _vp, _vp, _vp] + [_i64] * 4 + [_int, _vp]
     lib.ssm_state_update.restype = _int
     lib.ssm_state_update.argtypes = [_vp] * 9 + [_int, _vp] + [_i64] * 3 + [_int, _vp]
+    lib.ssm_scan_bwd.restype = _int
+    lib.ssm_scan_bwd.argtypes = [_vp] * 8 + [_int] + [_vp] * 12 + [_i64] * 4 + [_int, _vp]
     lib.ssm_conv_fwd.restype = _int
     lib.ssm_conv_fwd.argtypes = [_vp] * 6 + [_i64] * 4 + [_int, _vp]
     lib.ssm_conv_update.restype = _int
@@ -115,7 +120,7 @@ def ssm_scan_plan(b, L, E, N, dtype="bf16"):
     return cl.value, nc.value
 
 
-PROFILE_KINDS = 8
+PROFILE_KINDS = 13
 
 
 def ssm_profile_enable(on=True):
@@ -229,6 +234,61 @@ def ssm_scan_fwd_from(u, delta, A, B, C, D=None, z=None, delta_bias=None, softpl
     """``ssm_scan_fwd`` continuing from ``initial_state`` (same name as the C entry point)."""
     return ssm_scan_fwd(u, delta, A, B, C, D, z, delta_bias, softplus, y=y, last_state=last_state,
                         return_last_state=return_last_state, initial_state=initial_state)
+
+
+def ssm_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=False, initial_state=None,
+                 d_last_state=None):
+    """Gradients of sum(dy * y) + sum(d_last_state * last_state) for ``ssm_scan_fwd_from``'s arguments.
+
+    Returns a dict: du, ddelta (and dz when z is given) [b, L, E] in the streamed dtype;
+    dA [E, N], dB and dC [b, L, N], d_initial_state [b, E, N], dD and d_delta_bias [E]
+    (None when D / delta_bias are None), all float32.
+    """
+    import torch
+
+    lib = load_library()
+    if not isinstance(u, torch.Tensor) or u.dim() != 3:
+        raise ValueError("u must be a [b, L, E] tensor")
+    device = u.device
+    if device.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU device, got {device}")
+    b, L, E = u.shape
+    if not isinstance(A, torch.Tensor) or A.dim() != 2:
+        raise ValueError("A must be an [E, N] tensor")
+    N = A.shape[1]
+    io = u.dtype
+    code = _dtype_code(torch, io)
+    f32 = torch.float32
+    _check(torch, "u", u, (b, L, E), io, device)
+    _check(torch, "delta", delta, (b, L, E), io, device)
+    _check(torch, "A", A, (E, N), f32, device)
+    _check(torch, "B", B, (b, L, N), io, device)
+    _check(torch, "C", C, (b, L, N), io, device)
+    _check(torch, "dy", dy, (b, L, E), io, device)
+    _check(torch, "D", D, (E,), f32, device, optional=True)
+    _check(torch, "z", z, (b, L, E), io, device, optional=True)
+    _check(torch, "delta_bias", delta_bias, (E,), f32, device, optional=True)
+    _check(torch, "initial_state", initial_state, (b, E, N), f32, device, optional=True)
+    _check(torch, "d_last_state", d_last_state, (b, E, N), f32, device, optional=True)
+    g = {
+        "du": torch.empty((b, L, E), dtype=io, device=device),
+        "ddelta": torch.empty((b, L, E), dtype=io, device=device),
+        "dz": torch.empty((b, L, E), dtype=io, device=device) if z is not None else None,
+        "dA": torch.empty((E, N), dtype=f32, device=device),
+        "dB": torch.empty((b, L, N), dtype=f32, device=device),
+        "dC": torch.empty((b, L, N), dtype=f32, device=device),
+        "dD": torch.empty((E,), dtype=f32, device=device) if D is not None else None,
+        "d_delta_bias": torch.empty((E,), dtype=f32, device=device) if delta_bias is not None else None,
+        "d_initial_state": torch.empty((b, E, N), dtype=f32, device=device),
+    }
+    with torch.cuda.device(device):
+        status = lib.ssm_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                                  int(bool(softplus)), _ptr(initial_state), _ptr(dy), _ptr(d_last_state), _ptr(g["du"]),
+                                  _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]),
+                                  _ptr(g["dz"]), _ptr(g["d_delta_bias"]), _ptr(g["d_initial_state"]), b, L, E, N, code,
+                                  _stream_of(torch, device))
+    _raise_on("ssm_scan_bwd", status)
+    return g
 
 
 def ssm_state_update(state, x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=False, y=None):

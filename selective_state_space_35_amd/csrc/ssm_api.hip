@@ -104,6 +104,42 @@ int ssm_state_update(float* state, const void* x, const void* delta, const float
   return hip_status(ssm::launch_state_update(a));
 }
 
+int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C, const float* D,
+                 const void* z, const float* delta_bias, int softplus, const float* initial_state, const void* dy,
+                 const float* d_last_state, void* du, void* ddelta, float* dA, float* dB, float* dC, float* dD,
+                 void* dz, float* d_delta_bias, float* d_initial_state, int64_t b, int64_t L, int64_t E, int64_t N,
+                 int dtype, void* stream) {
+  int st = check_sizes(b, L, E, N, dtype);
+  if (st != SSM_OK) return st;
+  int64_t bl = 0, ble = 0;
+  if (!mul_ok(b, L, &bl) || !mul_ok(bl, E, &ble)) return SSM_ERR_DIM;
+  if (E > 0 && (!A || !dA)) return SSM_ERR_NULL;
+  if (bl > 0 && (!dB || !dC)) return SSM_ERR_NULL;
+  if (ble > 0 && (!u || !delta || !B || !C || !dy || !du || !ddelta || (z && !dz))) return SSM_ERR_NULL;
+  const size_t es = dtype == SSM_F32 ? 4 : 2;
+  const void* streamed[] = {u, delta, B, C, z, dy, du, ddelta, dz};
+  for (const void* p : streamed)
+    if (p && !aligned(p, es)) return SSM_ERR_ALIGN;
+  const void* fl[] = {A, D, delta_bias, initial_state, d_last_state, dA, dB, dC, dD, d_delta_bias, d_initial_state};
+  for (const void* p : fl)
+    if (p && !aligned(p, 4)) return SSM_ERR_ALIGN;
+  // a chunk's rows are addressed with 32-bit offsets; grids stay below 2^31 workgroups
+  if (E * int64_t(es) * ssm::bwd_chunk_steps() > INT32_MAX) return SSM_ERR_DIM;
+  const int64_t chunks = (L + ssm::bwd_chunk_steps() - 1) / ssm::bwd_chunk_steps();
+  int64_t grid = 0;
+  if (!mul_ok(b, (E + 63) / 64, &grid) || !mul_ok(grid, chunks, &grid) || grid > INT32_MAX) return SSM_ERR_DIM;
+  if (b * E * 16 / 256 > INT32_MAX || bl * 32 / 256 > INT32_MAX) return SSM_ERR_DIM;
+
+  ssm::BwdArgs a;
+  a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias;
+  a.softplus = softplus ? 1 : 0; a.h0 = initial_state; a.dy = dy; a.dlast = d_last_state;
+  a.du = du; a.ddelta = ddelta; a.dA = dA; a.dB = dB; a.dC = dC; a.dD = D ? dD : nullptr; a.dz = z ? dz : nullptr;
+  a.dbias = delta_bias ? d_delta_bias : nullptr; a.dh0 = d_initial_state;
+  a.b = b; a.L = L; a.E = E; a.N = N; a.dtype = dtype;
+  a.stream = static_cast<hipStream_t>(stream);
+  return hip_status(ssm::launch_scan_bwd(a));
+}
+
 int ssm_scan_plan(int64_t b, int64_t L, int64_t E, int64_t N, int dtype, int64_t* chunk_len, int64_t* n_chunks) {
   int st = check_sizes(b, L, E, N, dtype);
   if (st != SSM_OK) return st;

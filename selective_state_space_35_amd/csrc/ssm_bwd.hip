@@ -1,0 +1,659 @@
+// ssm_bwd.hip -- backward of the selective scan: the gradient of a scalar loss
+// with respect to u, delta, A, B, C, D, z, the step bias and the initial state,
+// given dloss/dy and (optionally) dloss/dlast_state.  States are recomputed,
+// never stored for the whole sequence (pages: "Mamba: Linear-Time Sequence
+// Modeling with Selective State Spaces", nadeemcite summary, "Core Idea": the
+// backward pass recomputes the states; abhik.ai page, "Compose the updates
+// instead of waiting for every state": the affine composition that lets the
+// sequence be cut into chunks, used here in both time directions).
+//
+// Per chain, with G_t = dloss/dh_t and X the gradient arriving from later steps:
+//   dq_t = dy_t * silu(z_t);  G_t = X + dq_t * C_t;  X <- a_t * G_t  (dloss/dh_{t-1})
+//   dB_t += G_t * d_t * u_t;  dC_t += dq_t * h_t;  dA += G_t * a_t * h_{t-1} * d_t
+//   du_t = dq_t * D + d_t * sum_n G_t B_t;  dd_t = u_t * sum_n G_t B_t + sum_n G_t a_t h_{t-1} A
+//   ddelta_t = dd_t * sigmoid(delta_t + bias) (softplus) ;  dz_t = dy_t * q_t * silu'(z_t)
+//
+// Passes (one call):
+//   1. forward chunk states: the forward's aggregate + carry passes over chunks
+//      of kBwdChunk steps give the state entering every chunk;
+//   2. bwd_chunk_agg_kernel: per chunk, the state gradient reached from zero
+//      walking the chunk backwards (the reverse-time aggregate);
+//   3. bwd_carry_kernel: the chain of those aggregates from the last chunk to
+//      the first, started from dlast: the gradient entering every chunk from
+//      its end (the decay of a chunk is exp(A * sum of its steps), as forward);
+//   4. bwd_main_kernel: per chunk, states recomputed from the chunk's incoming
+//      state (checkpoints every kSub steps, then each sub-block's states in
+//      registers), the reverse walk, every gradient;
+//   5. bwd_reduce_*: sums of the partial gradients over channel blocks (dB, dC)
+//      and over batch rows and chunks (dA, dD, dbias), in a fixed order.
+//
+// Layout of the main kernel: a quad of lanes per channel, 4 state coordinates
+// per lane (N padded to 16), 16 channels per wave, 4 waves per workgroup.  The
+// sums over channels for dB and dC go through lane swaps and DPP inside the
+// wave, then through LDS across the workgroup's 4 waves.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "ssm_device.h"
+#include "ssm_internal.h"
+#include "ssm_profile.h"
+
+namespace ssm {
+namespace {
+
+constexpr int kBwdChunk = 64;                          // steps per chunk
+constexpr int kSub = 8;                                // steps whose states a sub-block keeps in registers
+constexpr int kNSub = kBwdChunk / kSub;                // checkpoints per chunk
+constexpr int kBwdWaves = 4;                           // waves per workgroup of the main kernel
+constexpr int kChPerWave = kWave / 4;                  // a quad of lanes per channel
+constexpr int kChPerBlock = kBwdWaves * kChPerWave;    // 64 channels per workgroup
+constexpr int kS = 16;                                 // state slots per channel (N padded)
+constexpr int kRed = 2 * kS;                           // dB and dC values per (step, channel block)
+
+// B and C rows as float, padded with zeros to 16 states: [b, L, 16].
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_rows_kernel(const T* __restrict__ B, const T* __restrict__ C,
+                                                       float* __restrict__ B16, float* __restrict__ C16, int64_t rows,
+                                                       int N) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= rows * kS) return;
+  const int64_t r = i / kS;
+  const int n = int(i % kS);
+  B16[i] = n < N ? load_elem(B + r * N + n) : 0.f;
+  C16[i] = n < N ? load_elem(C + r * N + n) : 0.f;
+}
+
+// ---------------------------------------------------------------------------
+// 2. reverse-time chunk aggregate: walking chunk c (c >= 1) from its last step
+//    to its first with X = 0 at the end, X <- a_t * (X + dq_t * C_t); also the
+//    chunk's sum of steps.  One lane per channel, 16 states in registers.
+// ---------------------------------------------------------------------------
+template <typename T, bool SOFTPLUS, bool HAS_Z>
+__global__ __launch_bounds__(kWave) void bwd_chunk_agg_kernel(
+    const T* __restrict__ delta, const T* __restrict__ dy, const T* __restrict__ z, const float* __restrict__ A,
+    const float* __restrict__ C16, const float* __restrict__ bias, float* __restrict__ xagg,
+    float* __restrict__ xsum, int64_t L, int64_t E, int N, int n_chunks, int e_blocks) {
+  const int eb = blockIdx.x % e_blocks;
+  const int rest = blockIdx.x / e_blocks;
+  const int c = 1 + rest % (n_chunks - 1);
+  const int64_t bi = rest / (n_chunks - 1);
+  const int64_t e = int64_t(eb) * kWave + threadIdx.x;
+  const bool active = e < E;
+  const int64_t ec = active ? e : E - 1;
+  const int64_t t0 = int64_t(c) * kBwdChunk;
+  const int n_steps = int(std::min<int64_t>(L - t0, kBwdChunk));
+
+  float A2[kS];
+#pragma unroll
+  for (int n = 0; n < kS; n++) A2[n] = n < N ? A[ec * N + n] * kLog2e : 0.f;
+  const float bv = bias ? bias[ec] : 0.f;
+  float X[kS];
+#pragma unroll
+  for (int n = 0; n < kS; n++) X[n] = 0.f;
+  double dsum = 0.0;
+
+  const int64_t row0 = (bi * L + t0) * E + int64_t(eb) * kWave;
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(delta + row0);
+  const __amdgpu_buffer_rsrc_t ry = make_rsrc(dy + row0);
+  const __amdgpu_buffer_rsrc_t rz = make_rsrc(HAS_Z ? z + row0 : delta + row0);
+  const int voff = int(ec - int64_t(eb) * kWave) * int(sizeof(T));
+  const int row_bytes = int(E * int64_t(sizeof(T)));  // kBwdChunk * row_bytes < 2^31 is checked by the caller
+  const float* crow0 = C16 + (bi * L + t0) * kS;
+
+  for (int k = n_steps - 1; k >= 0; --k) {
+    const int so = k * row_bytes;
+    float d = buf_load(rd, voff, so, (T*)nullptr) + bv;
+    float dq = buf_load(ry, voff, so, (T*)nullptr);
+    if (HAS_Z) dq *= silu(buf_load(rz, voff, so, (T*)nullptr));
+    if (SOFTPLUS) d = softplus(d);
+    const float* crow = crow0 + k * kS;  // wave-uniform: scalar loads
+#pragma unroll
+    for (int n = 0; n < kS; n++) X[n] = exp2_fast(d * A2[n]) * fmaf(dq, crow[n], X[n]);
+    dsum += double(d);
+  }
+  if (active) {
+    float* dst = xagg + ((bi * n_chunks + c) * E + e) * kS;
+#pragma unroll
+    for (int n = 0; n < kS; n++) dst[n] = X[n];
+    xsum[(bi * n_chunks + c) * E + e] = float(dsum);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. reverse carry: per (b, e, n), X = dlast; for c = last .. 1:
+//    slot c <- X (gradient entering chunk c from its end);
+//    X <- exp(A * sum_c d) * X + aggregate_c;   finally slot 0 <- X.
+// ---------------------------------------------------------------------------
+template <int U>
+__global__ __launch_bounds__(256) void bwd_carry_kernel(const float* __restrict__ A, float* xagg,
+                                                        const float* __restrict__ xsum,
+                                                        const float* __restrict__ dlast, int64_t b, int64_t E, int N,
+                                                        int n_chunks) {
+  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= b * E * kS) return;
+  const int n = int(gid % kS);
+  const int64_t ch = gid / kS;
+  const int64_t e = ch % E, bi = ch / E;
+  const float a2 = n < N ? A[e * N + n] * kLog2e : 0.f;
+  const int64_t first = bi * n_chunks * E + e;  // slot of chunk 0; chunk c is at first + c * E
+  float X = (dlast && n < N) ? dlast[ch * N + n] : 0.f;
+  // chunks n_chunks-1 .. 1, U at a time; the aggregates of the next U are in flight meanwhile
+  float Rs[U], Ss[U];
+  auto load = [&](int c0) {  // c0: the highest chunk of the group
+#pragma unroll
+    for (int k = 0; k < U; k++) {
+      const int c = (c0 - k >= 1) ? c0 - k : 1;  // below chunk 1: a valid slot, unused
+      Rs[k] = xagg[(first + int64_t(c) * E) * kS + n];
+      Ss[k] = xsum[first + int64_t(c) * E];
+    }
+  };
+  if (n_chunks > 1) load(n_chunks - 1);
+  for (int c0 = n_chunks - 1; c0 >= 1; c0 -= U) {
+    float Rc[U], Sc[U];
+#pragma unroll
+    for (int k = 0; k < U; k++) { Rc[k] = Rs[k]; Sc[k] = Ss[k]; }
+    if (c0 - U >= 1) load(c0 - U);
+#pragma unroll
+    for (int k = 0; k < U; k++) {
+      if (c0 - k >= 1) {
+        xagg[(first + int64_t(c0 - k) * E) * kS + n] = X;
+        X = fmaf(exp2_fast(a2 * Sc[k]), X, Rc[k]);
+      }
+    }
+  }
+  xagg[first * kS + n] = X;
+}
+
+// Sum over the 16 channels of a wave (lane = 4 * channel + quarter) of four
+// values per lane, one per state of the lane's quarter; the 16 sums of the
+// wave (state 4 * quarter + k) are written to dst[4 * quarter + k] by 16 lanes.
+// Lane swaps across the wave halves and rows, then DPP rotations inside rows.
+__device__ __forceinline__ void sum_channels(float v0, float v1, float v2, float v3, float* dst) {
+  auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v0), __float_as_uint(v1), false, false);
+  const float w01 = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);  // lanes < 32: v0, else v1
+  sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v2), __float_as_uint(v3), false, false);
+  const float w23 = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);  // lanes < 32: v2, else v3
+  sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(w01), __float_as_uint(w23), false, false);
+  float x = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);  // rows 0..3 hold v0, v2, v1, v3
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false));  // row_ror:8
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xF, 0xF, false));  // row_ror:4
+  const int l = threadIdx.x & (kWave - 1);
+  if ((l & 12) == 4) {  // complete in lanes 4..7 of each row
+    const int r = l >> 4;
+    const int k = (r == 0) ? 0 : (r == 1) ? 2 : (r == 2) ? 1 : 3;
+    dst[4 * (l & 3) + k] = x;
+  }
+}
+
+struct StepIn {
+  float x, d, dyv, zv, sg;
+};
+
+// Streams of one chunk staged in LDS: [stream][step][channel of the block].
+// Slots u, delta and z receive du, ddelta and dz once their inputs are dead.
+enum { kSu = 0, kSd = 1, kSy = 2, kSz = 3 };
+
+// ---------------------------------------------------------------------------
+// 4. main backward pass over one chunk of one 64-channel block
+// ---------------------------------------------------------------------------
+template <typename T, bool SOFTPLUS, bool HAS_Z, bool HAS_D>
+__global__ __launch_bounds__(kBwdWaves * kWave) void bwd_main_kernel(
+    const T* __restrict__ u, const T* __restrict__ delta, const float* __restrict__ A,
+    const float* __restrict__ B16, const float* __restrict__ C16, const float* __restrict__ D,
+    const T* __restrict__ z, const float* __restrict__ bias, const T* __restrict__ dy, const float* __restrict__ h0,
+    const float* __restrict__ fcarry, int fslots, const float* __restrict__ xin, T* __restrict__ du,
+    T* __restrict__ ddelta, T* __restrict__ dz, float* __restrict__ dh0, float* __restrict__ dA_part,
+    float* __restrict__ dDb_part, float* __restrict__ dbc_part, int64_t L, int64_t E, int N, int n_chunks,
+    int e_blocks) {
+  constexpr int kStreams = HAS_Z ? 4 : 3;
+  __shared__ T sio[kStreams][kBwdChunk][kChPerBlock];
+  __shared__ float4 srow[2][kBwdChunk][kS / 4];  // B and C rows of the chunk
+  __shared__ float red[kBwdWaves][kSub][kRed];
+  const int eb = blockIdx.x % e_blocks;
+  const int rest = blockIdx.x / e_blocks;
+  const int c = rest % n_chunks;
+  const int64_t bi = rest / n_chunks;
+  const int wv = threadIdx.x / kWave;
+  const int l = threadIdx.x % kWave;
+  const int q = l & 3;
+  const int chl = wv * kChPerWave + (l >> 2);  // channel inside the block
+  const int64_t e = int64_t(eb) * kChPerBlock + chl;
+  const bool active = e < E;
+  const int64_t ec = active ? e : E - 1;
+  const int64_t t0 = int64_t(c) * kBwdChunk;
+  const int n_steps = int(std::min<int64_t>(L - t0, kBwdChunk));
+  const bool lead = (q == 0) && active;  // the lane that writes the channel's per-step gradients
+
+  // stage the chunk: thread (row group g, channel k) moves rows g, g + 4, ... of every stream
+  const int64_t row0 = (bi * L + t0) * E + int64_t(eb) * kChPerBlock;
+  const int row_bytes = int(E * int64_t(sizeof(T)));  // kBwdChunk * row_bytes < 2^31 is checked by the caller
+  {
+    const int k = threadIdx.x % kChPerBlock, g = threadIdx.x / kChPerBlock;
+    const bool col_ok = int64_t(eb) * kChPerBlock + k < E;
+    const int voff = (col_ok ? k : 0) * int(sizeof(T));
+    const __amdgpu_buffer_rsrc_t rs[4] = {make_rsrc(u + row0), make_rsrc(delta + row0), make_rsrc(dy + row0),
+                                          make_rsrc(HAS_Z ? z + row0 : u + row0)};
+#pragma unroll
+    for (int st = 0; st < kStreams; st++) {
+      float v[kBwdChunk / kBwdWaves];
+#pragma unroll
+      for (int j = 0; j < kBwdChunk / kBwdWaves; j++) {
+        const int r = g + kBwdWaves * j;
+        v[j] = buf_load(rs[st], voff, std::min(r, n_steps - 1) * row_bytes, (T*)nullptr);
+      }
+      // a column past the last channel keeps the block's first channel's step (so its
+      // retentions stay those of a real channel) and zero u and dy (so it adds nothing)
+      const bool keep = st == kSd || st == kSz || col_ok;
+#pragma unroll
+      for (int j = 0; j < kBwdChunk / kBwdWaves; j++) {
+        const int r = g + kBwdWaves * j;
+        store_elem(&sio[st][r][k], (keep && r < n_steps) ? v[j] : 0.f);
+      }
+    }
+    // B and C rows: 2 * 64 rows of 4 float4 = 512 float4, two per thread
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+      const int idx = threadIdx.x + j * kBwdWaves * kWave;  // 0 .. 511
+      const int which = idx / (kBwdChunk * 4), r = (idx / 4) % kBwdChunk, p = idx % 4;
+      const float* src = (which ? C16 : B16) + (bi * L + t0 + std::min(r, n_steps - 1)) * kS + 4 * p;
+      srow[which][r][p] = *reinterpret_cast<const float4*>(src);
+    }
+  }
+
+  float Ar[4], A2[4];
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    const int n = 4 * q + k;
+    Ar[k] = n < N ? A[ec * N + n] : 0.f;
+    A2[k] = Ar[k] * kLog2e;
+  }
+  const float bv = bias ? bias[ec] : 0.f;
+  const float Dv = HAS_D ? D[ec] : 0.f;
+
+  float h[4], X[4];
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    const int n = 4 * q + k;
+    if (c == 0)
+      h[k] = (h0 && n < N) ? h0[(bi * E + ec) * N + n] : 0.f;
+    else
+      h[k] = n < N ? fcarry[((bi * n_chunks + c - 1) * E + ec) * fslots + n] : 0.f;
+    X[k] = xin[((bi * n_chunks + c) * E + ec) * kS + n];
+  }
+  __syncthreads();
+
+  // step inputs from LDS; lanes past the last channel read u = dy = 0, so they add nothing to dB and dC
+  auto load_step = [&](int i, bool with_grad) {
+    StepIn s;
+    s.x = load_elem(&sio[kSu][i][chl]);
+    const float raw = load_elem(&sio[kSd][i][chl]) + bv;
+    s.d = SOFTPLUS ? softplus(raw) : raw;
+    s.sg = SOFTPLUS ? sigmoid(raw) : 1.f;
+    s.dyv = with_grad ? load_elem(&sio[kSy][i][chl]) : 0.f;
+    s.zv = (with_grad && HAS_Z) ? load_elem(&sio[HAS_Z ? kSz : kSu][i][chl]) : 0.f;
+    return s;
+  };
+  auto brow = [&](int i) {
+    const float4 v = srow[0][i][q];
+    return v;
+  };
+  auto crow = [&](int i) {
+    const float4 v = srow[1][i][q];
+    return v;
+  };
+
+  // pass A: checkpoints (state entering each sub-block)
+  float ck[kNSub][4];
+#pragma unroll
+  for (int sb = 0; sb < kNSub; sb++) {
+#pragma unroll
+    for (int k = 0; k < 4; k++) ck[sb][k] = h[k];
+    if (sb < kNSub - 1) {
+      for (int i = sb * kSub; i < std::min(n_steps, (sb + 1) * kSub); i++) {
+        const StepIn s = load_step(i, false);
+        const float4 b4 = brow(i);
+        const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+        const float dx = s.d * s.x;
+#pragma unroll
+        for (int k = 0; k < 4; k++) h[k] = fmaf(exp2_fast(s.d * A2[k]), h[k], dx * bb[k]);
+      }
+    }
+  }
+
+  // pass B: sub-blocks from the last to the first
+  float dAacc[4] = {0.f, 0.f, 0.f, 0.f};
+  float dDacc = 0.f, dbacc = 0.f;
+  float* redw = &red[wv][0][0];
+#pragma unroll
+  for (int sb = kNSub - 1; sb >= 0; sb--) {
+    const int base = sb * kSub;
+    if (base >= n_steps) continue;  // uniform over the workgroup
+    const int cnt = std::min(kSub, n_steps - base);
+    float hs[kSub][4];
+    float cd[kSub], cx[kSub], cq[kSub], cs[kSub];
+#pragma unroll
+    for (int k = 0; k < 4; k++) h[k] = ck[sb][k];
+    // forward over the sub-block: states, readout (for dz), dC
+#pragma unroll
+    for (int i = 0; i < kSub; i++) {
+      if (i < cnt) {
+        const StepIn s = load_step(base + i, true);
+        const float4 b4 = brow(base + i);
+        const float4 c4 = crow(base + i);
+        const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+        const float cc[4] = {c4.x, c4.y, c4.z, c4.w};
+        const float dx = s.d * s.x;
+        float qp = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+          h[k] = fmaf(exp2_fast(s.d * A2[k]), h[k], dx * bb[k]);
+          hs[i][k] = h[k];
+          qp = fmaf(cc[k], h[k], qp);
+        }
+        float dq = s.dyv;
+        if (HAS_Z) {
+          qp += quad_xor1(qp);
+          qp += quad_xor2(qp);
+          const float qt = HAS_D ? fmaf(Dv, s.x, qp) : qp;
+          const float zs = sigmoid(s.zv);
+          dq = s.dyv * s.zv * zs;
+          const float dzv = s.dyv * qt * zs * fmaf(s.zv, 1.f - zs, 1.f);
+          if (lead) store_elem(&sio[HAS_Z ? kSz : kSu][base + i][chl], dzv);  // z of this step is dead now
+        }
+        if (HAS_D) dDacc = fmaf(dq, s.x, dDacc);
+        sum_channels(dq * h[0], dq * h[1], dq * h[2], dq * h[3], redw + i * kRed + kS);
+        cd[i] = s.d;
+        cx[i] = s.x;
+        cq[i] = dq;
+        cs[i] = s.sg;
+      }
+    }
+    // reverse over the sub-block
+#pragma unroll
+    for (int i = kSub - 1; i >= 0; i--) {
+      if (i < cnt) {
+        const float4 b4 = brow(base + i);
+        const float4 c4 = crow(base + i);
+        const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+        const float cc[4] = {c4.x, c4.y, c4.z, c4.w};
+        const float d = cd[i], x = cx[i], dq = cq[i];
+        const float dx = d * x;
+        float s1 = 0.f, ddp = 0.f, gb[4];
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+          const float G = fmaf(dq, cc[k], X[k]);
+          const float a = exp2_fast(d * A2[k]);
+          const float hp = (i > 0) ? hs[i > 0 ? i - 1 : 0][k] : ck[sb][k];
+          const float gha = G * a * hp;
+          dAacc[k] = fmaf(gha, d, dAacc[k]);
+          ddp = fmaf(gha, Ar[k], ddp);
+          s1 = fmaf(G, bb[k], s1);
+          gb[k] = G * dx;
+          X[k] = a * G;
+        }
+        s1 += quad_xor1(s1);
+        s1 += quad_xor2(s1);
+        ddp += quad_xor1(ddp);
+        ddp += quad_xor2(ddp);
+        const float dut = fmaf(s1, d, HAS_D ? dq * Dv : 0.f);
+        const float ddv = fmaf(s1, x, ddp) * cs[i];
+        if (lead) {  // u and delta of this step are dead now
+          store_elem(&sio[kSu][base + i][chl], dut);
+          store_elem(&sio[kSd][base + i][chl], ddv);
+        }
+        dbacc += ddv;
+        sum_channels(gb[0], gb[1], gb[2], gb[3], redw + i * kRed);
+      }
+    }
+    // dB / dC of the sub-block: the four waves' sums added in a fixed order
+    __syncthreads();
+    {
+      const int i = threadIdx.x / kRed, v = threadIdx.x % kRed;  // 256 threads = kSub * kRed
+      if (i < cnt)
+        dbc_part[((bi * L + t0 + base + i) * e_blocks + eb) * kRed + v] =
+            red[0][i][v] + red[1][i][v] + red[2][i][v] + red[3][i][v];
+    }
+    __syncthreads();
+  }
+
+  // per-step gradients of the chunk, from LDS to HBM in whole rows
+  {
+    const int k = threadIdx.x % kChPerBlock, g = threadIdx.x / kChPerBlock;
+    const bool col_ok = int64_t(eb) * kChPerBlock + k < E;
+    T* outs[3] = {du, ddelta, dz};
+    const int slots[3] = {kSu, kSd, HAS_Z ? kSz : kSu};
+#pragma unroll
+    for (int o = 0; o < (HAS_Z ? 3 : 2); o++) {
+      const __amdgpu_buffer_rsrc_t ro = make_rsrc(outs[o] + row0);
+#pragma unroll
+      for (int j = 0; j < kBwdChunk / kBwdWaves; j++) {
+        const int r = g + kBwdWaves * j;
+        if (col_ok && r < n_steps) buf_store(ro, k * int(sizeof(T)), r * row_bytes, load_elem(&sio[slots[o]][r][k]),
+                                             (T*)nullptr);
+      }
+    }
+  }
+
+  if (active) {
+    float* pa = dA_part + ((bi * n_chunks + c) * E + e) * kS + 4 * q;
+#pragma unroll
+    for (int k = 0; k < 4; k++) pa[k] = dAacc[k];
+    if (q == 0) {
+      dDb_part[((bi * n_chunks + c) * E + e) * 2 + 0] = dDacc;
+      dDb_part[((bi * n_chunks + c) * E + e) * 2 + 1] = dbacc;
+    }
+    if (c == 0 && dh0) {
+#pragma unroll
+      for (int k = 0; k < 4; k++)
+        if (4 * q + k < N) dh0[(bi * E + e) * N + 4 * q + k] = X[k];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 5. sums of the partials, each in a fixed order
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restrict__ part, float* __restrict__ dB,
+                                                            float* __restrict__ dC, int64_t rows, int e_blocks,
+                                                            int N) {
+  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= rows * kRed) return;
+  const int64_t r = gid / kRed;
+  const int v = int(gid % kRed);
+  const float* p = part + r * e_blocks * kRed + v;
+  float s = 0.f;
+  for (int k = 0; k < e_blocks; k++) s += p[int64_t(k) * kRed];
+  const int n = v % kS;
+  if (n < N) (v < kS ? dB : dC)[r * N + n] = s;
+}
+
+__global__ __launch_bounds__(256) void bwd_reduce_chan_kernel(const float* __restrict__ dA_part,
+                                                              const float* __restrict__ dDb_part,
+                                                              float* __restrict__ dA, float* __restrict__ dD,
+                                                              float* __restrict__ dbias, int64_t parts, int64_t E,
+                                                              int N) {
+  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= E * kS) return;
+  const int64_t e = gid / kS;
+  const int n = int(gid % kS);
+  constexpr int U = 8;
+  float acc[U];
+#pragma unroll
+  for (int k = 0; k < U; k++) acc[k] = 0.f;
+  int64_t p = 0;
+  for (; p + U <= parts; p += U) {
+#pragma unroll
+    for (int k = 0; k < U; k++) acc[k] += dA_part[((p + k) * E + e) * kS + n];
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < U; k++) s += acc[k];
+  for (; p < parts; p++) s += dA_part[(p * E + e) * kS + n];
+  if (n < N) dA[e * N + n] = s;
+  if ((n == 0 && dD) || (n == 1 && dbias)) {
+    float t = 0.f;
+    for (int64_t k = 0; k < parts; k++) t += dDb_part[(k * E + e) * 2 + n];
+    (n == 0 ? dD : dbias)[e] = t;
+  }
+}
+
+// fill n floats with src (or zero when src is null)
+__global__ __launch_bounds__(256) void bwd_fill_kernel(float* __restrict__ dst, const float* __restrict__ src,
+                                                       int64_t n) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = src ? src[i] : 0.f;
+}
+
+hipError_t fill(float* dst, const float* src, int64_t n, hipStream_t s) {
+  if (!dst || n <= 0) return hipSuccess;
+  return launch_kind(kKindBwdReduce, bwd_fill_kernel, (n + 255) / 256, 256, s, dst, src, n);
+}
+
+template <typename T, bool SOFTPLUS, bool HAS_Z, bool HAS_D>
+hipError_t run_main(const BwdArgs& a, int n_chunks, int e_blocks, const float* B16, const float* C16,
+                    const float* fcarry, int fslots, const float* xin, float* dA_part, float* dDb_part,
+                    float* dbc_part) {
+  return launch_kind(kKindBwdMain, bwd_main_kernel<T, SOFTPLUS, HAS_Z, HAS_D>, a.b * n_chunks * e_blocks,
+                     kBwdWaves * kWave, a.stream, static_cast<const T*>(a.u), static_cast<const T*>(a.delta), a.A, B16,
+                     C16, a.D, static_cast<const T*>(a.z), a.bias, static_cast<const T*>(a.dy), a.h0, fcarry, fslots,
+                     xin, static_cast<T*>(a.du), static_cast<T*>(a.ddelta), static_cast<T*>(a.dz), a.dh0, dA_part,
+                     dDb_part, dbc_part, a.L, a.E, int(a.N), n_chunks, e_blocks);
+}
+
+template <typename T>
+hipError_t bwd_typed(const BwdArgs& a, int n_chunks, const float* B16, const float* C16, const float* fcarry,
+                     int fslots, float* xagg, float* xsum, float* dA_part, float* dDb_part, float* dbc_part) {
+  const int N = int(a.N);
+  const int eb_agg = int((a.E + kWave - 1) / kWave);
+  hipError_t err = hipSuccess;
+  if (n_chunks > 1) {
+    const int64_t blocks = a.b * (n_chunks - 1) * eb_agg;
+    const T* dl = static_cast<const T*>(a.delta);
+    const T* dyp = static_cast<const T*>(a.dy);
+    const T* zp = static_cast<const T*>(a.z);
+#define SSM_BWD_AGG(SP, HZ)                                                                                       \
+  err = launch_kind(kKindBwdAgg, bwd_chunk_agg_kernel<T, SP, HZ>, blocks, kWave, a.stream, dl, dyp, zp, a.A, C16, \
+                    a.bias, xagg, xsum, a.L, a.E, N, n_chunks, eb_agg)
+    if (a.softplus) {
+      if (a.z) SSM_BWD_AGG(true, true); else SSM_BWD_AGG(true, false);
+    } else {
+      if (a.z) SSM_BWD_AGG(false, true); else SSM_BWD_AGG(false, false);
+    }
+#undef SSM_BWD_AGG
+    if (err != hipSuccess) return err;
+  }
+  const int64_t lanes = a.b * a.E * kS;
+  err = n_chunks > 33 ? launch_kind(kKindBwdCarry, bwd_carry_kernel<32>, (lanes + 255) / 256, 256, a.stream, a.A,
+                                    xagg, (const float*)xsum, a.dlast, a.b, a.E, N, n_chunks)
+                      : launch_kind(kKindBwdCarry, bwd_carry_kernel<8>, (lanes + 255) / 256, 256, a.stream, a.A, xagg,
+                                    (const float*)xsum, a.dlast, a.b, a.E, N, n_chunks);
+  if (err != hipSuccess) return err;
+  const int e_blocks = int((a.E + kChPerBlock - 1) / kChPerBlock);
+#define SSM_BWD_MAIN(SP, HZ, HD) \
+  return run_main<T, SP, HZ, HD>(a, n_chunks, e_blocks, B16, C16, fcarry, fslots, xagg, dA_part, dDb_part, dbc_part)
+  const bool hz = a.z != nullptr, hd = a.D != nullptr;
+  if (a.softplus) {
+    if (hz) { if (hd) SSM_BWD_MAIN(true, true, true); else SSM_BWD_MAIN(true, true, false); }
+    if (hd) SSM_BWD_MAIN(true, false, true);
+    SSM_BWD_MAIN(true, false, false);
+  }
+  if (hz) { if (hd) SSM_BWD_MAIN(false, true, true); else SSM_BWD_MAIN(false, true, false); }
+  if (hd) SSM_BWD_MAIN(false, false, true);
+  SSM_BWD_MAIN(false, false, false);
+#undef SSM_BWD_MAIN
+}
+
+}  // namespace
+
+int64_t bwd_chunk_steps() { return kBwdChunk; }
+
+hipError_t launch_scan_bwd(const BwdArgs& a) {
+  const int64_t b = a.b, L = a.L, E = a.E, N = a.N;
+  if (E == 0) {  // no channel: B and C receive nothing
+    hipError_t err = fill(a.dB, nullptr, b * L * N, a.stream);
+    return err == hipSuccess ? fill(a.dC, nullptr, b * L * N, a.stream) : err;
+  }
+  if (b == 0 || L == 0) {  // nothing flows through a step: parameter gradients are zero
+    hipError_t err = fill(a.dA, nullptr, E * N, a.stream);
+    if (err == hipSuccess) err = fill(a.dD, nullptr, a.D ? E : 0, a.stream);
+    if (err == hipSuccess) err = fill(a.dbias, nullptr, a.bias ? E : 0, a.stream);
+    if (err == hipSuccess) err = fill(a.dh0, a.dlast, b * E * N, a.stream);
+    return err;
+  }
+  const int n_chunks = int((L + kBwdChunk - 1) / kBwdChunk);
+  const int e_blocks = int((E + kChPerBlock - 1) / kChPerBlock);
+  const int fslots = chunk_state_slots(N);
+  // workspace (floats): [widened rows | B16 | C16 | forward carries | forward sums | reverse carries |
+  //                      reverse sums | dB/dC partials | dA partials | dD/dbias partials]
+  const size_t nb = size_t(b), nL = size_t(L), nE = size_t(E), nc = size_t(n_chunks);
+  const size_t n_rows = a.dtype == 0 ? 0 : 2 * nb * nL * size_t(N);
+  const size_t n_row16 = nb * nL * kS;
+  const size_t n_fc = n_chunks > 1 ? nb * nc * nE * size_t(fslots) : 0;
+  const size_t n_fs = n_chunks > 1 ? nb * nc * nE : 0;
+  const size_t n_xa = nb * nc * nE * kS;
+  const size_t n_xs = nb * nc * nE;
+  const size_t n_bc = nb * nL * size_t(e_blocks) * kRed;
+  const size_t n_da = nb * nc * nE * kS;
+  const size_t n_dd = nb * nc * nE * 2;
+  // every segment starts on a 256-byte boundary (the main kernel reads rows as float4)
+  const size_t sizes[10] = {n_rows, n_row16, n_row16, n_fc, n_fs, n_xa, n_xs, n_bc, n_da, n_dd};
+  size_t offs[10], total = 0;
+  for (int i = 0; i < 10; i++) {
+    offs[i] = total;
+    total += (sizes[i] + 63) / 64 * 64;
+  }
+  void* ws = nullptr;
+  hipError_t err = hipMallocAsync(&ws, total * sizeof(float), a.stream);
+  if (err != hipSuccess) return err;
+  float* f = static_cast<float*>(ws);
+  float* rows = f + offs[0];
+  float* B16 = f + offs[1];
+  float* C16 = f + offs[2];
+  float* fcarry = f + offs[3];
+  float* fsum = f + offs[4];
+  float* xagg = f + offs[5];
+  float* xsum = f + offs[6];
+  float* dbc = f + offs[7];
+  float* dA_part = f + offs[8];
+  float* dDb_part = f + offs[9];
+
+  const int64_t nr16 = b * L * kS;
+  err = a.dtype == 0 ? launch_kind(kKindBwdRows, bwd_rows_kernel<float>, (nr16 + 255) / 256, 256, a.stream,
+                                   static_cast<const float*>(a.B), static_cast<const float*>(a.C), B16, C16, b * L,
+                                   int(N))
+                     : launch_kind(kKindBwdRows, bwd_rows_kernel<bf16_bits>, (nr16 + 255) / 256, 256, a.stream,
+                                   static_cast<const bf16_bits*>(a.B), static_cast<const bf16_bits*>(a.C), B16, C16,
+                                   b * L, int(N));
+  if (err == hipSuccess && n_chunks > 1) {
+    ScanArgs s{};
+    s.u = a.u; s.delta = a.delta; s.A = a.A; s.B = a.B; s.C = a.C; s.D = a.D; s.z = a.z; s.bias = a.bias;
+    s.softplus = a.softplus; s.y = nullptr; s.last_state = nullptr; s.h0 = a.h0;
+    s.b = b; s.L = L; s.E = E; s.N = N; s.dtype = a.dtype; s.stream = a.stream;
+    ScanPlan pl;
+    pl.chunk_len = kBwdChunk;
+    pl.n_chunks = n_chunks;
+    pl.e_blocks = int((E + kWave - 1) / kWave);
+    err = launch_chunk_states(s, pl, rows, fcarry, fsum);
+  }
+  if (err == hipSuccess)
+    err = a.dtype == 0 ? bwd_typed<float>(a, n_chunks, B16, C16, fcarry, fslots, xagg, xsum, dA_part, dDb_part, dbc)
+                       : bwd_typed<bf16_bits>(a, n_chunks, B16, C16, fcarry, fslots, xagg, xsum, dA_part, dDb_part,
+                                              dbc);
+  if (err == hipSuccess) {
+    const int64_t n = b * L * kRed;
+    err = launch_kind(kKindBwdReduce, bwd_reduce_bc_kernel, (n + 255) / 256, 256, a.stream, (const float*)dbc, a.dB,
+                      a.dC, b * L, e_blocks, int(N));
+  }
+  if (err == hipSuccess) {
+    const int64_t n = E * kS;
+    err = launch_kind(kKindBwdReduce, bwd_reduce_chan_kernel, (n + 255) / 256, 256, a.stream, (const float*)dA_part,
+                      (const float*)dDb_part, a.dA, a.D ? a.dD : nullptr, a.bias ? a.dbias : nullptr,
+                      b * int64_t(n_chunks), E, int(N));
+  }
+  hipError_t ferr = hipFreeAsync(ws, a.stream);
+  return err != hipSuccess ? err : ferr;
+}
+
+}  // namespace ssm

@@ -35,6 +35,16 @@ __device__ __forceinline__ float silu(float z) {
   return z * __builtin_amdgcn_rcpf(1.f + exp2_fast(-z * kLog2e));
 }
 
+__device__ __forceinline__ float sigmoid(float x) { return __builtin_amdgcn_rcpf(1.f + exp2_fast(-x * kLog2e)); }
+
+// Cross-lane reads inside a quad of lanes (DPP quad_perm).
+__device__ __forceinline__ float quad_xor1(float v) {  // value of lane ^ 1 within the quad
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float quad_xor2(float v) {  // value of lane ^ 2 within the quad
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
+}
+
 // Raw buffer resource over a tensor region (CDNA buffer descriptor: 48-bit
 // base, no stride, 2 GiB range, dword3 as used for gfx9-family buffer ops).
 // Per-step loads then need one lane-offset VGPR shared by every stream and a

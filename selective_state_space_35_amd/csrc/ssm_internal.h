@@ -71,6 +71,45 @@ struct ScanPlan {
 // chunk_len == 0 means the row size is too large to address (rejected).
 ScanPlan plan_scan(int64_t b, int64_t L, int64_t E, int elem_bytes);
 
+// State slots per channel in the chunk-state buffers (N, or 16 when N is not 4, 8 or 16).
+int chunk_state_slots(int64_t N);
+// Incoming state of every chunk of the scan described by `a` cut as `pl` says:
+// afterwards carry[(b * n_chunks + c) * E + e][slots] holds the state at the end
+// of chunk c (c < n_chunks - 1) and csum the sum of steps of chunk c.  `rows`
+// (2 * b * L * N floats) is scratch for widened bf16 rows.  y / last_state are
+// not touched.
+hipError_t launch_chunk_states(const ScanArgs& a, const ScanPlan& pl, float* rows, float* carry, float* csum);
+
+// Backward of the scan (gradients of every input).
+struct BwdArgs {
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;      // nullable
+  const void* z;       // nullable
+  const float* bias;   // nullable
+  int softplus;
+  const float* h0;     // nullable
+  const void* dy;
+  const float* dlast;  // nullable
+  void* du;
+  void* ddelta;
+  float* dA;
+  float* dB;
+  float* dC;
+  float* dD;           // nullable
+  void* dz;            // required when z is given
+  float* dbias;        // nullable
+  float* dh0;          // nullable
+  int64_t b, L, E, N;
+  int dtype;
+  hipStream_t stream;
+};
+int64_t bwd_chunk_steps();  // steps per chunk of the backward
+hipError_t launch_scan_bwd(const BwdArgs& a);
+
 // Both return hipSuccess or the first HIP error met while enqueueing.
 hipError_t launch_scan(const ScanArgs& a);
 hipError_t launch_state_update(const UpdateArgs& a);

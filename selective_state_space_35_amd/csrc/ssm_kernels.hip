@@ -363,12 +363,6 @@ __global__ __launch_bounds__(256) void fill_state_kernel(float* __restrict__ p, 
 // row), so the row index is a per-workgroup scalar and the lane's channel is
 // plain 32-bit arithmetic.  The partial readouts of the LPC lanes are summed
 // with DPP quad permutes (no LDS traffic).
-__device__ __forceinline__ float quad_xor1(float v) {  // value of lane ^ 1 within the quad
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
-}
-__device__ __forceinline__ float quad_xor2(float v) {  // value of lane ^ 2 within the quad
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
-}
 
 #ifndef SSM_UPDATE_ROWS
 #define SSM_UPDATE_ROWS 4
@@ -488,6 +482,26 @@ struct ScanBufs {
   float* csum;   // [b][n_chunks][E] sum of steps per chunk
 };
 
+// Chunk aggregates, then the carry chain: afterwards carry slot c holds the
+// state at the end of chunk c (the incoming state of chunk c + 1).
+template <typename T, int NS, bool EXACT, bool SOFTPLUS>
+hipError_t run_carries(const ScanArgs& a, const ScanPlan& pl, const ScanBufs& w) {
+  if (pl.n_chunks <= 1) return hipSuccess;
+  const int N = int(a.N);
+  const int agg = pl.n_chunks - 1;
+  hipError_t err = launch_kind(kKindAgg, scan_chunk_agg_kernel<T, NS, EXACT, SOFTPLUS>, a.b * agg * pl.e_blocks, kWave,
+                               a.stream, static_cast<const T*>(a.u), static_cast<const T*>(a.delta), a.A, w.B, a.bias,
+                               w.carry, w.csum, a.L, a.E, N, pl.chunk_len, pl.n_chunks, agg, pl.e_blocks);
+  if (err != hipSuccess) return err;
+  const int64_t lanes = a.b * a.E * NS;
+  // prefetch depth: 32 chunks for long chains, 8 when there are few chunks
+  return pl.n_chunks > 33
+             ? launch_kind(kKindCarry, scan_carry_kernel<NS, 32>, (lanes + 255) / 256, 256, a.stream, a.A, w.carry,
+                           (const float*)w.csum, a.h0, a.b, a.E, N, pl.n_chunks)
+             : launch_kind(kKindCarry, scan_carry_kernel<NS, 8>, (lanes + 255) / 256, 256, a.stream, a.A, w.carry,
+                           (const float*)w.csum, a.h0, a.b, a.E, N, pl.n_chunks);
+}
+
 template <typename T, int NS, bool EXACT, bool SOFTPLUS, bool HAS_Z, bool FULL>
 hipError_t run_scan(const ScanArgs& a, const ScanPlan& pl, const ScanBufs& w) {
   const T* u = static_cast<const T*>(a.u);
@@ -495,21 +509,8 @@ hipError_t run_scan(const ScanArgs& a, const ScanPlan& pl, const ScanBufs& w) {
   const T* z = static_cast<const T*>(a.z);
   T* y = static_cast<T*>(a.y);
   const int N = int(a.N);
-  hipError_t err = hipSuccess;
-  if (pl.n_chunks > 1) {
-    const int agg = pl.n_chunks - 1;
-    err = launch_kind(kKindAgg, scan_chunk_agg_kernel<T, NS, EXACT, SOFTPLUS>, a.b * agg * pl.e_blocks, kWave, a.stream, u, dl,
-                 a.A, w.B, a.bias, w.carry, w.csum, a.L, a.E, N, pl.chunk_len, pl.n_chunks, agg, pl.e_blocks);
-    if (err != hipSuccess) return err;
-    const int64_t lanes = a.b * a.E * NS;
-    // prefetch depth: 32 chunks for long chains, 8 when there are few chunks
-    err = pl.n_chunks > 33
-              ? launch_kind(kKindCarry, scan_carry_kernel<NS, 32>, (lanes + 255) / 256, 256, a.stream, a.A, w.carry,
-                            (const float*)w.csum, a.h0, a.b, a.E, N, pl.n_chunks)
-              : launch_kind(kKindCarry, scan_carry_kernel<NS, 8>, (lanes + 255) / 256, 256, a.stream, a.A, w.carry,
-                            (const float*)w.csum, a.h0, a.b, a.E, N, pl.n_chunks);
-    if (err != hipSuccess) return err;
-  }
+  hipError_t err = run_carries<T, NS, EXACT, SOFTPLUS>(a, pl, w);
+  if (err != hipSuccess) return err;
   return launch_kind(kKindMain, scan_main_kernel<T, NS, EXACT, SOFTPLUS, HAS_Z, FULL>, a.b * pl.n_chunks * pl.e_blocks, kWave,
                 a.stream, u, dl, a.A, w.B, w.C, a.D, z, a.bias, y, a.last_state, (const float*)w.carry, a.h0, a.L,
                 a.E, N, pl.chunk_len, pl.n_chunks, pl.e_blocks);
@@ -538,6 +539,17 @@ hipError_t scan_typed(const ScanArgs& a, const ScanPlan& pl, const ScanBufs& w) 
   if (a.N == 8) return scan_full<T, 8, true>(a, pl, w);
   if (a.N == 4) return scan_full<T, 4, true>(a, pl, w);
   return scan_full<T, 16, false>(a, pl, w);
+}
+
+template <typename T>
+hipError_t carries_typed(const ScanArgs& a, const ScanPlan& pl, const ScanBufs& w) {
+#define SSM_CARRIES(NS, EX) \
+  return a.softplus ? run_carries<T, NS, EX, true>(a, pl, w) : run_carries<T, NS, EX, false>(a, pl, w)
+  if (a.N == 16) { SSM_CARRIES(16, true); }
+  if (a.N == 8) { SSM_CARRIES(8, true); }
+  if (a.N == 4) { SSM_CARRIES(4, true); }
+  SSM_CARRIES(16, false);
+#undef SSM_CARRIES
 }
 
 template <typename T, int NS, bool VEC>
@@ -656,6 +668,27 @@ hipError_t launch_scan(const ScanArgs& a) {
     if (err == hipSuccess) err = ferr;
   }
   return err;
+}
+
+int chunk_state_slots(int64_t N) { return scan_states(N); }
+
+hipError_t launch_chunk_states(const ScanArgs& a, const ScanPlan& pl, float* rows, float* carry, float* csum) {
+  if (a.b == 0 || a.E == 0 || pl.n_chunks <= 1) return hipSuccess;
+  ScanBufs w;
+  w.carry = carry;
+  w.csum = csum;
+  w.C = nullptr;
+  if (a.dtype == 0) {
+    w.B = static_cast<const float*>(a.B);
+    return carries_typed<float>(a, pl, w);
+  }
+  const int64_t n_rows = a.b * a.L * a.N;
+  hipError_t err = launch_kind(kKindWiden, widen_rows_kernel, (n_rows + 255) / 256, 256, a.stream,
+                               static_cast<const bf16_bits*>(a.B), static_cast<const bf16_bits*>(a.C), rows,
+                               rows + n_rows, n_rows);
+  if (err != hipSuccess) return err;
+  w.B = rows;
+  return carries_typed<bf16_bits>(a, pl, w);
 }
 
 hipError_t launch_state_update(const UpdateArgs& a) {

@@ -15,7 +15,12 @@ enum : int {
   kKindUpdate = 5,  // single-token state update
   kKindConv = 6,    // causal depthwise convolution over a sequence
   kKindConvUpdate = 7,  // single-token convolution-state update
-  kNumKinds = 8
+  kKindBwdRows = 8,     // backward: B / C rows padded to 16 states
+  kKindBwdAgg = 9,      // backward: per-chunk aggregate of the state gradient (reverse in time)
+  kKindBwdCarry = 10,   // backward: chain of the state gradient across chunks
+  kKindBwdMain = 11,    // backward: recompute states, gradients of every input
+  kKindBwdReduce = 12,  // backward: sums of the per-chunk / per-block partial gradients
+  kNumKinds = 13
 };
 
 // When profiling is on, creates and records the start event on `s` and returns true.

@@ -23,8 +23,10 @@ std::atomic<bool> g_enabled{false};
 std::mutex g_mu;
 std::vector<Pending> g_pending;
 
-const char* const kNames[kNumKinds] = {"widen_rows", "chunk_aggregate", "chunk_carry", "scan_main",
-                                       "fill_state", "state_update",    "conv",        "conv_update"};
+const char* const kNames[kNumKinds] = {"widen_rows",  "chunk_aggregate", "chunk_carry",   "scan_main",
+                                       "fill_state",  "state_update",    "conv",          "conv_update",
+                                       "bwd_rows",    "bwd_aggregate",   "bwd_carry",     "bwd_main",
+                                       "bwd_reduce"};
 
 }  // namespace
 

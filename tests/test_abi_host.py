@@ -159,6 +159,34 @@ def test_conv_update_validation(lib):
     assert conv_update(lib, b=0, state=None) == OK
 
 
+def bwd(lib, **kw):
+    args = dict(u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, bias=None, softplus=1, h0=None, dy=FAKE,
+                dlast=None, du=FAKE, ddelta=FAKE, dA=FAKE, dB=FAKE, dC=FAKE, dD=None, dz=None, dbias=None, dh0=None,
+                b=1, L=8, E=64, N=16, dtype=0)
+    args.update(kw)
+    a = args
+    return lib.ssm_scan_bwd(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], a["softplus"],
+                            a["h0"], a["dy"], a["dlast"], a["du"], a["ddelta"], a["dA"], a["dB"], a["dC"], a["dD"],
+                            a["dz"], a["dbias"], a["dh0"], a["b"], a["L"], a["E"], a["N"], a["dtype"], None)
+
+
+def test_bwd_validation(lib):
+    assert bwd(lib, dtype=5) == ERR_DTYPE
+    assert bwd(lib, N=0) == ERR_N
+    assert bwd(lib, N=17) == ERR_N
+    assert bwd(lib, L=-1) == ERR_DIM
+    for k in ("u", "delta", "A", "B", "C", "dy", "du", "ddelta", "dA", "dB", "dC"):
+        assert bwd(lib, **{k: None}) == ERR_NULL, k
+    assert bwd(lib, z=FAKE) == ERR_NULL  # a gate needs its gradient buffer
+    assert bwd(lib, du=FAKE + 2) == ERR_ALIGN
+    assert bwd(lib, dz=FAKE + 1, z=FAKE, dtype=1) == ERR_ALIGN
+    assert bwd(lib, dA=FAKE + 2) == ERR_ALIGN
+    assert bwd(lib, dh0=FAKE + 1) == ERR_ALIGN
+    assert bwd(lib, E=1 << 26) == ERR_DIM  # 64 rows of this width overflow 32-bit offsets
+    assert bwd(lib, b=0, E=0, u=None, delta=None, A=None, B=None, C=None, dy=None, du=None, ddelta=None, dA=None,
+               dB=None, dC=None) == OK
+
+
 def test_binding_refuses_cpu_tensors():
     torch = pytest.importorskip("torch")
     if not os.path.exists(ssm.library_path()):
@@ -172,6 +200,8 @@ def test_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError, match="GPU"):
         ssm.ssm_state_update(torch.zeros(b, E, N), torch.zeros(b, E), torch.zeros(b, E), A,
                              torch.zeros(b, N), torch.zeros(b, N))
+    with pytest.raises(ValueError, match="GPU"):
+        ssm.ssm_scan_bwd(u, u, A, BC, BC, u)
     with pytest.raises(ValueError, match="GPU"):
         ssm.ssm_conv_fwd(u, torch.zeros(E, 4))
     with pytest.raises(ValueError, match="GPU"):
@@ -211,5 +241,5 @@ def test_scan_plan_query(lib, monkeypatch):
 def test_profile_read_with_nothing_recorded(lib):
     out = ssm.ssm_profile_read()
     assert set(out) == {"widen_rows", "chunk_aggregate", "chunk_carry", "scan_main", "fill_state", "state_update",
-                        "conv", "conv_update"}
+                        "conv", "conv_update", "bwd_rows", "bwd_aggregate", "bwd_carry", "bwd_main", "bwd_reduce"}
     assert all(v == (0.0, 0) for v in out.values())
