@@ -199,7 +199,7 @@ enum { kSu = 0, kSd = 1, kSy = 2, kSz = 3 };
 // 4. main backward pass over one chunk of one 64-channel block
 // ---------------------------------------------------------------------------
 template <typename T, bool SOFTPLUS, bool HAS_Z, bool HAS_D>
-__global__ __launch_bounds__(kBwdWaves * kWave) void bwd_main_kernel(
+__global__ __launch_bounds__(kBwdWaves * kWave) __attribute__((amdgpu_waves_per_eu(3))) void bwd_main_kernel(
     const T* __restrict__ u, const T* __restrict__ delta, const float* __restrict__ A,
     const float* __restrict__ B16, const float* __restrict__ C16, const float* __restrict__ D,
     const T* __restrict__ z, const float* __restrict__ bias, const T* __restrict__ dy, const float* __restrict__ h0,
@@ -241,7 +241,8 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void bwd_main_kernel(
 #pragma unroll
       for (int j = 0; j < kBwdChunk / kBwdWaves; j++) {
         const int r = g + kBwdWaves * j;
-        v[j] = buf_load(rs[st], voff, std::min(r, n_steps - 1) * row_bytes, (T*)nullptr);
+        // the row term goes into the lane offset: g is per wave but not provably uniform
+        v[j] = buf_load(rs[st], voff + std::min(r, n_steps - 1) * row_bytes, 0, (T*)nullptr);
       }
       // a column past the last channel keeps the block's first channel's step (so its
       // retentions stay those of a real channel) and zero u and dy (so it adds nothing)
@@ -304,14 +305,25 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void bwd_main_kernel(
     return v;
   };
 
-  // pass A: checkpoints (state entering each sub-block)
-  float ck[kNSub][4];
+  // pass A: checkpoints (state entering each sub-block).  The sub-block loops
+  // stay rolled so the kernel's code fits the instruction cache; the
+  // checkpoint slot (a wave-uniform index) is picked by comparison.
+  typedef float ck_vec __attribute__((ext_vector_type(kNSub)));
+  ck_vec ck[4];  // ck[k][sb]: state coordinate k entering sub-block sb
+  auto ck_put = [&](int sb) {
 #pragma unroll
-  for (int sb = 0; sb < kNSub; sb++) {
+    for (int k = 0; k < 4; k++) ck[k][sb] = h[k];
+  };
+  auto ck_get = [&](int sb, float (&out)[4]) {
 #pragma unroll
-    for (int k = 0; k < 4; k++) ck[sb][k] = h[k];
-    if (sb < kNSub - 1) {
-      for (int i = sb * kSub; i < std::min(n_steps, (sb + 1) * kSub); i++) {
+    for (int k = 0; k < 4; k++) out[k] = ck[k][sb];
+  };
+  const int n_sub = (n_steps + kSub - 1) / kSub;
+#pragma unroll 1
+  for (int sb = 0; sb < n_sub; sb++) {
+    ck_put(sb);
+    if (sb < n_sub - 1) {
+      for (int i = sb * kSub; i < (sb + 1) * kSub; i++) {
         const StepIn s = load_step(i, false);
         const float4 b4 = brow(i);
         const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
@@ -326,15 +338,16 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void bwd_main_kernel(
   float dAacc[4] = {0.f, 0.f, 0.f, 0.f};
   float dDacc = 0.f, dbacc = 0.f;
   float* redw = &red[wv][0][0];
-#pragma unroll
-  for (int sb = kNSub - 1; sb >= 0; sb--) {
+#pragma unroll 1
+  for (int sb = n_sub - 1; sb >= 0; sb--) {
     const int base = sb * kSub;
-    if (base >= n_steps) continue;  // uniform over the workgroup
     const int cnt = std::min(kSub, n_steps - base);
     float hs[kSub][4];
     float cd[kSub], cx[kSub], cq[kSub], cs[kSub];
+    float h_in[4];
+    ck_get(sb, h_in);
 #pragma unroll
-    for (int k = 0; k < 4; k++) h[k] = ck[sb][k];
+    for (int k = 0; k < 4; k++) h[k] = h_in[k];
     // forward over the sub-block: states, readout (for dz), dC
 #pragma unroll
     for (int i = 0; i < kSub; i++) {
@@ -385,7 +398,7 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void bwd_main_kernel(
         for (int k = 0; k < 4; k++) {
           const float G = fmaf(dq, cc[k], X[k]);
           const float a = exp2_fast(d * A2[k]);
-          const float hp = (i > 0) ? hs[i > 0 ? i - 1 : 0][k] : ck[sb][k];
+          const float hp = (i > 0) ? hs[i > 0 ? i - 1 : 0][k] : h_in[k];
           const float gha = G * a * hp;
           dAacc[k] = fmaf(gha, d, dAacc[k]);
           ddp = fmaf(gha, Ar[k], ddp);
@@ -430,8 +443,8 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void bwd_main_kernel(
 #pragma unroll
       for (int j = 0; j < kBwdChunk / kBwdWaves; j++) {
         const int r = g + kBwdWaves * j;
-        if (col_ok && r < n_steps) buf_store(ro, k * int(sizeof(T)), r * row_bytes, load_elem(&sio[slots[o]][r][k]),
-                                             (T*)nullptr);
+        if (col_ok && r < n_steps)
+          buf_store(ro, k * int(sizeof(T)) + r * row_bytes, 0, load_elem(&sio[slots[o]][r][k]), (T*)nullptr);
       }
     }
   }
@@ -463,11 +476,25 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restr
   const int64_t r = gid / kRed;
   const int v = int(gid % kRed);
   const float* p = part + r * e_blocks * kRed + v;
+  constexpr int U = 8;  // independent partial sums, added in a fixed order at the end
+  float acc[U];
+#pragma unroll
+  for (int k = 0; k < U; k++) acc[k] = 0.f;
+  int k0 = 0;
+  for (; k0 + U <= e_blocks; k0 += U) {
+#pragma unroll
+    for (int k = 0; k < U; k++) acc[k] += p[int64_t(k0 + k) * kRed];
+  }
   float s = 0.f;
-  for (int k = 0; k < e_blocks; k++) s += p[int64_t(k) * kRed];
+#pragma unroll
+  for (int k = 0; k < U; k++) s += acc[k];
+  for (; k0 < e_blocks; k0++) s += p[int64_t(k0) * kRed];
   const int n = v % kS;
   if (n < N) (v < kS ? dB : dC)[r * N + n] = s;
 }
+
+// Per channel: slots 0..15 sum dA over (batch, chunk), slot 16 dD, slot 17 dbias.
+constexpr int kChanSlots = kS + 2;
 
 __global__ __launch_bounds__(256) void bwd_reduce_chan_kernel(const float* __restrict__ dA_part,
                                                               const float* __restrict__ dDb_part,
@@ -475,9 +502,15 @@ __global__ __launch_bounds__(256) void bwd_reduce_chan_kernel(const float* __res
                                                               float* __restrict__ dbias, int64_t parts, int64_t E,
                                                               int N) {
   const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (gid >= E * kS) return;
-  const int64_t e = gid / kS;
-  const int n = int(gid % kS);
+  if (gid >= E * kChanSlots) return;
+  const int64_t e = gid / kChanSlots;
+  const int n = int(gid % kChanSlots);
+  float* out = n < kS ? (n < N ? dA + e * N + n : nullptr) : (n == kS ? dD : dbias);
+  if (!out) return;
+  if (n >= kS) out += e;
+  // slot stride and first element of part p: dA [parts][E][16], dD / dbias [parts][E][2]
+  const float* base = n < kS ? dA_part + e * kS + n : dDb_part + e * 2 + (n - kS);
+  const int64_t stride = n < kS ? E * kS : E * 2;
   constexpr int U = 8;
   float acc[U];
 #pragma unroll
@@ -485,18 +518,13 @@ __global__ __launch_bounds__(256) void bwd_reduce_chan_kernel(const float* __res
   int64_t p = 0;
   for (; p + U <= parts; p += U) {
 #pragma unroll
-    for (int k = 0; k < U; k++) acc[k] += dA_part[((p + k) * E + e) * kS + n];
+    for (int k = 0; k < U; k++) acc[k] += base[(p + k) * stride];
   }
   float s = 0.f;
 #pragma unroll
   for (int k = 0; k < U; k++) s += acc[k];
-  for (; p < parts; p++) s += dA_part[(p * E + e) * kS + n];
-  if (n < N) dA[e * N + n] = s;
-  if ((n == 0 && dD) || (n == 1 && dbias)) {
-    float t = 0.f;
-    for (int64_t k = 0; k < parts; k++) t += dDb_part[(k * E + e) * 2 + n];
-    (n == 0 ? dD : dbias)[e] = t;
-  }
+  for (; p < parts; p++) s += base[p * stride];
+  *out = s;
 }
 
 // fill n floats with src (or zero when src is null)
@@ -647,7 +675,7 @@ hipError_t launch_scan_bwd(const BwdArgs& a) {
                       a.dC, b * L, e_blocks, int(N));
   }
   if (err == hipSuccess) {
-    const int64_t n = E * kS;
+    const int64_t n = E * kChanSlots;
     err = launch_kind(kKindBwdReduce, bwd_reduce_chan_kernel, (n + 255) / 256, 256, a.stream, (const float*)dA_part,
                       (const float*)dDb_part, a.dA, a.D ? a.dD : nullptr, a.bias ? a.dbias : nullptr,
                       b * int64_t(n_chunks), E, int(N));
