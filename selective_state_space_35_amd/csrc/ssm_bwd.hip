@@ -187,9 +187,17 @@ __device__ __forceinline__ void sum_channels(float v0, float v1, float v2, float
   }
 }
 
-struct StepIn {
-  float x, d, dyv, zv, sg;
-};
+// value of quad lane j, for every lane of the quad (DPP quad_perm [j, j, j, j]);
+// j is a constant once the calling loop is unrolled, so the switch folds away
+__device__ __forceinline__ float quad_bcast(float v, int j) {
+  const int b = __float_as_int(v);
+  switch (j) {
+    case 0: return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x00, 0xF, 0xF, false));
+    case 1: return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x55, 0xF, 0xF, false));
+    case 2: return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0xAA, 0xF, 0xF, false));
+    default: return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0xFF, 0xF, 0xF, false));
+  }
+}
 
 // Streams of one chunk staged in LDS: [stream][step][channel of the block].
 // Slots u, delta and z receive du, ddelta and dz once their inputs are dead.
@@ -208,7 +216,10 @@ __global__ __launch_bounds__(kBwdWaves * kWave) __attribute__((amdgpu_waves_per_
     float* __restrict__ dDb_part, float* __restrict__ dbc_part, int64_t L, int64_t E, int N, int n_chunks,
     int e_blocks) {
   constexpr int kStreams = HAS_Z ? 4 : 3;
-  __shared__ T sio[kStreams][kBwdChunk][kChPerBlock];
+  // rows padded by one 32-bit word so that the four lanes of a quad, reading four
+  // different steps of one channel, fall into different LDS banks
+  constexpr int kRowPad = kChPerBlock + 4 / int(sizeof(T));
+  __shared__ T sio[kStreams][kBwdChunk][kRowPad];
   __shared__ float4 srow[2][kBwdChunk][kS / 4];  // B and C rows of the chunk
   __shared__ float red[kBwdWaves][kSub][kRed];
   const int eb = blockIdx.x % e_blocks;
@@ -285,16 +296,33 @@ __global__ __launch_bounds__(kBwdWaves * kWave) __attribute__((amdgpu_waves_per_
   }
   __syncthreads();
 
-  // step inputs from LDS; lanes past the last channel read u = dy = 0, so they add nothing to dB and dC
-  auto load_step = [&](int i, bool with_grad) {
-    StepIn s;
-    s.x = load_elem(&sio[kSu][i][chl]);
+  // Per-step scalars (step, gate and their derivatives) are computed once per
+  // channel: in a group of four steps, quad lane q works out step g0 + q and the
+  // quad shares the results through DPP broadcasts.  Lanes past the last
+  // channel read u = dy = 0, so they add nothing to dB and dC.
+  struct Scal {
+    float d, x, dq, sg, gz;
+  };
+  auto own_scalars = [&](int i, bool with_grad) {  // i: this lane's step (rows past the end hold zeros)
+    Scal r;
+    r.x = load_elem(&sio[kSu][i][chl]);
     const float raw = load_elem(&sio[kSd][i][chl]) + bv;
-    s.d = SOFTPLUS ? softplus(raw) : raw;
-    s.sg = SOFTPLUS ? sigmoid(raw) : 1.f;
-    s.dyv = with_grad ? load_elem(&sio[kSy][i][chl]) : 0.f;
-    s.zv = (with_grad && HAS_Z) ? load_elem(&sio[HAS_Z ? kSz : kSu][i][chl]) : 0.f;
-    return s;
+    r.d = SOFTPLUS ? softplus(raw) : raw;
+    r.sg = 1.f;
+    r.dq = 0.f;
+    r.gz = 0.f;
+    if (with_grad) {
+      if (SOFTPLUS) r.sg = sigmoid(raw);
+      const float dyv = load_elem(&sio[kSy][i][chl]);
+      r.dq = dyv;
+      if (HAS_Z) {
+        const float zv = load_elem(&sio[HAS_Z ? kSz : kSu][i][chl]);
+        const float zs = sigmoid(zv);
+        r.dq = dyv * zv * zs;                         // dy * silu(z)
+        r.gz = dyv * zs * fmaf(zv, 1.f - zs, 1.f);   // dz = q * gz
+      }
+    }
+    return r;
   };
   auto brow = [&](int i) {
     const float4 v = srow[0][i][q];
@@ -322,14 +350,19 @@ __global__ __launch_bounds__(kBwdWaves * kWave) __attribute__((amdgpu_waves_per_
 #pragma unroll 1
   for (int sb = 0; sb < n_sub; sb++) {
     ck_put(sb);
-    if (sb < n_sub - 1) {
-      for (int i = sb * kSub; i < (sb + 1) * kSub; i++) {
-        const StepIn s = load_step(i, false);
-        const float4 b4 = brow(i);
-        const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
-        const float dx = s.d * s.x;
+    if (sb < n_sub - 1) {  // a full sub-block
 #pragma unroll
-        for (int k = 0; k < 4; k++) h[k] = fmaf(exp2_fast(s.d * A2[k]), h[k], dx * bb[k]);
+      for (int g0 = sb * kSub; g0 < (sb + 1) * kSub; g0 += 4) {
+        const Scal own = own_scalars(g0 + q, false);
+        const float own_dx = own.d * own.x;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const float d = quad_bcast(own.d, j), dx = quad_bcast(own_dx, j);
+          const float4 b4 = brow(g0 + j);
+          const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+          for (int k = 0; k < 4; k++) h[k] = fmaf(exp2_fast(d * A2[k]), h[k], dx * bb[k]);
+        }
       }
     }
   }
@@ -350,37 +383,41 @@ __global__ __launch_bounds__(kBwdWaves * kWave) __attribute__((amdgpu_waves_per_
     for (int k = 0; k < 4; k++) h[k] = h_in[k];
     // forward over the sub-block: states, readout (for dz), dC
 #pragma unroll
-    for (int i = 0; i < kSub; i++) {
-      if (i < cnt) {
-        const StepIn s = load_step(base + i, true);
-        const float4 b4 = brow(base + i);
-        const float4 c4 = crow(base + i);
-        const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
-        const float cc[4] = {c4.x, c4.y, c4.z, c4.w};
-        const float dx = s.d * s.x;
-        float qp = 0.f;
+    for (int g = 0; g < kSub; g += 4) {
+      if (g < cnt) {
+        const Scal own = own_scalars(base + g + q, true);
 #pragma unroll
-        for (int k = 0; k < 4; k++) {
-          h[k] = fmaf(exp2_fast(s.d * A2[k]), h[k], dx * bb[k]);
-          hs[i][k] = h[k];
-          qp = fmaf(cc[k], h[k], qp);
+        for (int j = 0; j < 4; j++) {
+          const int i = g + j;
+          if (i < cnt) {
+            const float d = quad_bcast(own.d, j), x = quad_bcast(own.x, j), dq = quad_bcast(own.dq, j);
+            const float4 b4 = brow(base + i);
+            const float4 c4 = crow(base + i);
+            const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+            const float cc[4] = {c4.x, c4.y, c4.z, c4.w};
+            const float dx = d * x;
+            float qp = 0.f;
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+              h[k] = fmaf(exp2_fast(d * A2[k]), h[k], dx * bb[k]);
+              hs[i][k] = h[k];
+              qp = fmaf(cc[k], h[k], qp);
+            }
+            if (HAS_Z) {
+              qp += quad_xor1(qp);
+              qp += quad_xor2(qp);
+              const float qt = HAS_D ? fmaf(Dv, x, qp) : qp;
+              const float dzv = qt * quad_bcast(own.gz, j);
+              if (lead) store_elem(&sio[HAS_Z ? kSz : kSu][base + i][chl], dzv);  // z of this step is dead now
+            }
+            if (HAS_D) dDacc = fmaf(dq, x, dDacc);
+            sum_channels(dq * h[0], dq * h[1], dq * h[2], dq * h[3], redw + i * kRed + kS);
+            cd[i] = d;
+            cx[i] = x;
+            cq[i] = dq;
+            cs[i] = SOFTPLUS ? quad_bcast(own.sg, j) : 1.f;
+          }
         }
-        float dq = s.dyv;
-        if (HAS_Z) {
-          qp += quad_xor1(qp);
-          qp += quad_xor2(qp);
-          const float qt = HAS_D ? fmaf(Dv, s.x, qp) : qp;
-          const float zs = sigmoid(s.zv);
-          dq = s.dyv * s.zv * zs;
-          const float dzv = s.dyv * qt * zs * fmaf(s.zv, 1.f - zs, 1.f);
-          if (lead) store_elem(&sio[HAS_Z ? kSz : kSu][base + i][chl], dzv);  // z of this step is dead now
-        }
-        if (HAS_D) dDacc = fmaf(dq, s.x, dDacc);
-        sum_channels(dq * h[0], dq * h[1], dq * h[2], dq * h[3], redw + i * kRed + kS);
-        cd[i] = s.d;
-        cx[i] = s.x;
-        cq[i] = dq;
-        cs[i] = s.sg;
       }
     }
     // reverse over the sub-block
