@@ -14,11 +14,14 @@
 // q [E, K] float; cb [E] float; convolution state [b, E, K] in the I/O dtype,
 // oldest sample first.
 //
-// conv_fwd_kernel: one lane per channel, 64 channels per wave (one contiguous
-// row segment per load), a chunk of kConvChunk steps per wave.  The K-1
-// previous samples live in registers and slide along; the chunk's first
-// window reads the K-1 rows before it (or the incoming state / zeros).  Each
-// input and output element crosses HBM once: an HBM-bound kernel.
+// conv_fwd_vec_kernel (E a multiple of 8 bf16 / 4 f32 channels, 16-byte aligned
+// rows): each lane owns 16 bytes of a row, so a wave moves 1 KiB per load and
+// per store; kConvVGroup rows are in flight.  conv_fwd_kernel (any E and
+// alignment): one lane per channel.  Both give a wave a chunk of kConvChunk
+// steps; the K-1 previous samples live in registers and slide along, and the
+// chunk's first window reads the K-1 rows before it (or the incoming state /
+// zeros).  Each input and output element crosses HBM once, apart from those
+// K-1 rows per chunk: an HBM-bound kernel.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -31,8 +34,15 @@
 namespace ssm {
 namespace {
 
-constexpr int kConvChunk = 64;  // steps per wave
-constexpr int kConvGroup = 8;   // loads issued together
+#ifndef SSM_CONV_CHUNK
+#define SSM_CONV_CHUNK 32
+#endif
+#ifndef SSM_CONV_VGROUP
+#define SSM_CONV_VGROUP 8
+#endif
+constexpr int kConvChunk = SSM_CONV_CHUNK;    // steps per wave
+constexpr int kConvGroup = 8;                 // loads issued together (one channel per lane)
+constexpr int kConvVGroup = SSM_CONV_VGROUP;  // 16-byte rows in flight (vector kernel)
 
 template <typename T, int K>
 __global__ __launch_bounds__(kWave) void conv_fwd_kernel(const T* __restrict__ v, const float* __restrict__ q,
@@ -107,6 +117,149 @@ __global__ __launch_bounds__(kWave) void conv_fwd_kernel(const T* __restrict__ v
   }
 }
 
+// 16 bytes of a row: 8 bf16 or 4 f32 channels, widened to f32
+template <typename T>
+struct Vec16 {
+  static constexpr int V = 16 / int(sizeof(T));
+  float v[V];
+};
+__device__ __forceinline__ Vec16<float> unpack16(uint32_t a, uint32_t b, uint32_t c, uint32_t d, float*) {
+  Vec16<float> r;
+  r.v[0] = __uint_as_float(a); r.v[1] = __uint_as_float(b); r.v[2] = __uint_as_float(c); r.v[3] = __uint_as_float(d);
+  return r;
+}
+__device__ __forceinline__ Vec16<bf16_bits> unpack16(uint32_t a, uint32_t b, uint32_t c, uint32_t d, bf16_bits*) {
+  Vec16<bf16_bits> r;
+  const uint32_t w[4] = {a, b, c, d};
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    r.v[2 * i] = __uint_as_float(w[i] << 16);
+    r.v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+  return r;
+}
+template <typename T>
+__device__ __forceinline__ Vec16<T> load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  const auto u = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return unpack16(u[0], u[1], u[2], u[3], (T*)nullptr);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return uint32_t(__builtin_bit_cast(bf16_bits, static_cast<__bf16>(lo))) |
+         (uint32_t(__builtin_bit_cast(bf16_bits, static_cast<__bf16>(hi))) << 16);
+}
+template <typename T>
+__device__ __forceinline__ void store16(__amdgpu_buffer_rsrc_t r, int voff, int soff, const float (&v)[Vec16<T>::V]) {
+  typedef __attribute__((ext_vector_type(4))) uint32_t u4;
+  u4 w;
+  if constexpr (sizeof(T) == 4) {
+    w = u4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+  } else {
+    w = u4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+  }
+  __builtin_amdgcn_raw_buffer_store_b128(w, r, voff, soff, 0);
+}
+
+// Same operation as conv_fwd_kernel with 16-byte accesses: each lane owns V
+// consecutive channels (V = 8 for bf16, 4 for f32), so a wave moves 1 KiB of a
+// row per load.  Needs E % V == 0 and 16-byte aligned rows (checked by the launcher).
+template <typename T, int K>
+__global__ __launch_bounds__(kWave) void conv_fwd_vec_kernel(const T* __restrict__ v, const float* __restrict__ q,
+                                                             const float* __restrict__ cb,
+                                                             const T* __restrict__ state_in, T* __restrict__ x,
+                                                             T* __restrict__ state_out, int64_t L, int64_t E,
+                                                             int n_chunks, int e_blocks) {
+  constexpr int V = Vec16<T>::V;
+  const int eb = blockIdx.x % e_blocks;
+  const int rest = blockIdx.x / e_blocks;
+  const int c = rest % n_chunks;
+  const int64_t bi = rest / n_chunks;
+  const int64_t e0 = (int64_t(eb) * kWave + threadIdx.x) * V;  // first channel of the lane
+  const bool active = e0 < E;
+  const int64_t ec0 = active ? e0 : E - V;                      // inactive lanes read a valid vector
+  const int64_t t0 = int64_t(c) * kConvChunk;
+  const int64_t t1 = (t0 + kConvChunk < L) ? t0 + kConvChunk : L;
+
+  float w[V][K], bias[V];
+#pragma unroll
+  for (int j = 0; j < V; j++) {
+#pragma unroll
+    for (int k = 0; k < K; k++) w[j][k] = q[(ec0 + j) * K + k];
+    bias[j] = cb ? cb[ec0 + j] : 0.f;
+  }
+  const int64_t row_base = bi * L * E;
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + row_base + t0 * E);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + row_base + t0 * E);
+  const int voff = int(ec0) * int(sizeof(T));
+  const int row_bytes = int(E * int64_t(sizeof(T)));  // kConvChunk * row_bytes < 2^31 is checked by the caller
+
+  // hist[i][j] = sample at time t0 - (K-1) + i of channel ec0 + j
+  float hist[K > 1 ? K - 1 : 1][V];
+#pragma unroll
+  for (int i = 0; i < K - 1; i++) {
+    const int64_t s = t0 - (K - 1) + i;
+    if (s >= 0) {
+      const __amdgpu_buffer_rsrc_t rp = make_rsrc(v + row_base + s * E);
+      const Vec16<T> r = load16<T>(rp, voff, 0);
+#pragma unroll
+      for (int j = 0; j < V; j++) hist[i][j] = r.v[j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < V; j++)
+        hist[i][j] = state_in ? load_elem(state_in + (bi * E + ec0 + j) * K + (K + s)) : 0.f;
+    }
+  }
+
+  const int n_steps = int(t1 - t0);
+  float dropped[V];
+#pragma unroll
+  for (int j = 0; j < V; j++) dropped[j] = 0.f;
+  float last[V];
+#pragma unroll
+  for (int j = 0; j < V; j++) last[j] = 0.f;
+  constexpr int G = kConvVGroup;
+  for (int g0 = 0; g0 < n_steps; g0 += G) {
+    Vec16<T> in[G];
+#pragma unroll
+    for (int k = 0; k < G; k++) {
+      const int kk = (g0 + k < n_steps) ? g0 + k : n_steps - 1;  // past the end: a valid row, unused
+      in[k] = load16<T>(rv, voff, kk * row_bytes);
+    }
+#pragma unroll
+    for (int k = 0; k < G; k++) {
+      if (g0 + k < n_steps) {
+        float out[V];
+#pragma unroll
+        for (int j = 0; j < V; j++) {
+          float acc = bias[j];
+#pragma unroll
+          for (int i = 0; i < K - 1; i++) acc = fmaf(w[j][i], hist[i][j], acc);
+          acc = fmaf(w[j][K - 1], in[k].v[j], acc);
+          out[j] = silu(acc);
+          if (K > 1) dropped[j] = hist[0][j];
+#pragma unroll
+          for (int i = 0; i + 1 < K - 1; i++) hist[i][j] = hist[i + 1][j];
+          if (K > 1) hist[K - 2][j] = in[k].v[j];
+          last[j] = in[k].v[j];
+        }
+        if (active) store16<T>(rx, voff, (g0 + k) * row_bytes, out);
+      }
+    }
+  }
+  if (state_out && c == n_chunks - 1 && active) {
+#pragma unroll
+    for (int j = 0; j < V; j++) {
+      T* dst = state_out + (bi * E + e0 + j) * K;
+      if (K == 1) {
+        store_elem(dst, last[j]);
+      } else {
+        store_elem(dst, dropped[j]);
+#pragma unroll
+        for (int i = 0; i < K - 1; i++) store_elem(dst + 1 + i, hist[i][j]);
+      }
+    }
+  }
+}
+
 // last convolution state of an empty sequence: the incoming one, or zeros
 template <typename T>
 __global__ __launch_bounds__(256) void conv_state_copy_kernel(const T* __restrict__ src, T* __restrict__ dst,
@@ -141,8 +294,17 @@ __global__ __launch_bounds__(256) void conv_update_kernel(T* __restrict__ state,
 
 template <typename T, int K>
 hipError_t conv_fwd_k(const ConvArgs& a) {
-  const int e_blocks = int((a.E + kWave - 1) / kWave);
   const int n_chunks = int((a.L + kConvChunk - 1) / kConvChunk);
+  constexpr int V = Vec16<T>::V;
+  const bool vec = a.E % V == 0 && reinterpret_cast<uintptr_t>(a.v) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(a.x) % 16 == 0;
+  if (vec) {
+    const int e_blocks = int((a.E / V + kWave - 1) / kWave);
+    return launch_kind(kKindConv, conv_fwd_vec_kernel<T, K>, a.b * n_chunks * e_blocks, kWave, a.stream,
+                       static_cast<const T*>(a.v), a.q, a.cb, static_cast<const T*>(a.state_in), static_cast<T*>(a.x),
+                       static_cast<T*>(a.state_out), a.L, a.E, n_chunks, e_blocks);
+  }
+  const int e_blocks = int((a.E + kWave - 1) / kWave);
   return launch_kind(kKindConv, conv_fwd_kernel<T, K>, a.b * n_chunks * e_blocks, kWave, a.stream,
                      static_cast<const T*>(a.v), a.q, a.cb, static_cast<const T*>(a.state_in), static_cast<T*>(a.x),
                      static_cast<T*>(a.state_out), a.L, a.E, n_chunks, e_blocks);

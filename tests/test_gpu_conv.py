@@ -75,11 +75,20 @@ def test_bias_and_state_flags(bias, state_in):
     check(make(w, seed=3), "f32", f"conv bias={bias} state_in={state_in}")
 
 
+@pytest.mark.parametrize("E", [70, 128])  # 70: one channel per lane; 128: 16-byte vectors per lane
 @pytest.mark.parametrize("L", [1, 2, 3, 5, 63, 64, 65, 128])
-def test_short_and_boundary_lengths(L):
-    w = BASE.with_shape(L=L, E=70, K=4, state_in=True)
-    say(f"conv L={L}")
-    check(make(w, seed=L), "f32", f"conv L={L}")
+def test_short_and_boundary_lengths(L, E):
+    w = BASE.with_shape(L=L, E=E, K=4, state_in=True)
+    say(f"conv L={L} E={E}")
+    check(make(w, seed=L), "f32", f"conv L={L} E={E}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("E", [8, 1032])  # one vector; a partial second wave
+def test_vector_path_edges(E, dtype):
+    w = BASE.with_shape(L=70, E=E, K=3, dtype=dtype, state_in=True)
+    say(f"conv vector path E={E} {dtype}")
+    check(make(w, seed=E), dtype, f"conv vector E={E} {dtype}")
 
 
 def test_empty_sequence_copies_state():
