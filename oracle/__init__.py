@@ -23,6 +23,11 @@ Definitions followed (page title, site, section):
   * causal depthwise convolution + silu before the scan -- abhik.ai page,
     row 4 "Add causal local context before selecting coefficients", and its
     single-token form in row 6;
+  * the scan with a scalar transition per head (structured state-space
+    duality, computed by the GPU in chunks of matrix products) -- abhik.ai
+    page, "Key takeaways" and "Related reading" (Mamba-2: a restricted state
+    update turned into a structured mixing matrix and a chunked algorithm);
+    "mamba-from-scratch" README (Mamba-2 / SSD: chunked parallel scan);
   * backward of the scan (gradients of every input by the chain rule of the
     definition; the pages train the block end to end and recompute states in
     the backward pass) -- nadeemcite summary, "Core Idea"; abhik.ai page,
@@ -176,6 +181,26 @@ def scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=False,
     if rc != 0:
         raise RuntimeError(f"oracle_scan_bwd failed with {rc}")
     return out
+
+
+def ssd(x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=False, h0=None, threads=None):
+    """The scan with the transition restricted to a scalar per head (structured state-space duality).
+
+    x, z [b, L, H*P] (channel e = h*P + p); delta [b, L, H]; A, D, delta_bias [H];
+    B, C [b, L, N]; h0 [b, H*P, N].  Every channel of head h uses the head's step,
+    A, D and bias, identical over the N states: the scan above on broadcast inputs.
+    Returns (y [b, L, H*P], last_state [b, H*P, N]).
+    """
+    x, delta, A = to_f64(x), to_f64(delta), to_f64(A)
+    b, L, E = x.shape
+    H = delta.shape[2]
+    N = to_f64(B).shape[2]
+    if E % H or A.shape != (H,):
+        raise ValueError("oracle.ssd: channels must split evenly into heads")
+    P = E // H
+    rep = lambda v: None if v is None else np.repeat(to_f64(v), P, axis=-1)
+    A_full = np.repeat(A, P)[:, None] * np.ones((1, N))
+    return scan(x, rep(delta), A_full, B, C, rep(D), z, rep(delta_bias), softplus, h0=h0, threads=threads)
 
 
 def state_update(state, x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=False, threads=None):

@@ -551,3 +551,73 @@ def test_bwd_split_sequence_chains_through_the_state():
     np.testing.assert_allclose(np.concatenate([g1["dB"], g2["dB"]], 1), g["dB"], rtol=1e-10, atol=1e-12)
     np.testing.assert_allclose(g1["dA"] + g2["dA"], g["dA"], rtol=1e-10, atol=1e-12)
     np.testing.assert_allclose(g1["dh0"], g["dh0"], rtol=1e-10, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# scalar transition per head (structured state-space duality).  With a_t the same
+# for every state of a head, the scan is a lower-triangular mixing matrix applied
+# to the inputs: y_t = sum_{s<=t} (C_t . B_s) exp(A (S_t - S_s)) d_s x_s
+# + (C_t . h0) exp(A S_t) + D x_t, with S_t the running sum of steps ([AB] "Key
+# takeaways": a restricted state update becomes a structured mixing matrix;
+# [MS] Mamba-2 / SSD, the chunked attention view).  The dense matrix is built here
+# directly from that closed form and compared with the recurrence.
+# ----------------------------------------------------------------------------
+def ssd_problem(seed, b=2, L=23, H=3, P=4, N=5, gate=True, with_h0=True):
+    rng = np.random.default_rng(seed)
+    return dict(x=rng.standard_normal((b, L, H * P)), delta=rng.normal(-1.0, 0.8, (b, L, H)),
+                A=-np.exp(rng.normal(0.3, 0.5, H)), B=rng.standard_normal((b, L, N)),
+                C=rng.standard_normal((b, L, N)), D=rng.standard_normal(H),
+                z=rng.standard_normal((b, L, H * P)) if gate else None,
+                delta_bias=rng.normal(0.0, 0.3, H), h0=rng.standard_normal((b, H * P, N)) if with_h0 else None)
+
+
+def ssd_dense(p, softplus=True):
+    x, B, C, A, D = p["x"], p["B"], p["C"], p["A"], p["D"]
+    b, L, E = x.shape
+    H = p["delta"].shape[2]
+    P = E // H
+    raw = p["delta"] + p["delta_bias"]
+    d = np.logaddexp(0.0, raw) if softplus else raw            # [b, L, H]
+    S = np.cumsum(d, axis=1)                                     # running sum of steps
+    y = np.zeros((b, L, E))
+    for bi in range(b):
+        G = C[bi] @ B[bi].T                                      # [L, L]: C_t . B_s
+        for h in range(H):
+            decay = np.exp(A[h] * (S[bi, :, h][:, None] - S[bi, :, h][None, :]))
+            M = np.tril(G * decay) * d[bi, :, h][None, :]
+            xs = x[bi, :, h * P:(h + 1) * P]
+            yh = M @ xs + D[h] * xs
+            if p["h0"] is not None:
+                h0 = p["h0"][bi, h * P:(h + 1) * P, :]           # [P, N]
+                yh += np.exp(A[h] * S[bi, :, h])[:, None] * (C[bi] @ h0.T)
+            y[bi, :, h * P:(h + 1) * P] = yh
+    if p["z"] is not None:
+        y = y * p["z"] / (1.0 + np.exp(-p["z"]))
+    return y
+
+
+@pytest.mark.parametrize("gate,with_h0,softplus", [(True, True, True), (False, False, True), (True, False, False)])
+def test_ssd_recurrence_equals_structured_matrix(gate, with_h0, softplus):
+    p = ssd_problem(61, gate=gate, with_h0=with_h0)
+    if not softplus:
+        p["delta"] = np.abs(p["delta"]) * 0.3 + 0.05
+        p["delta_bias"] = np.zeros_like(p["delta_bias"])
+    y, _ = oracle.ssd(p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["delta_bias"], softplus, h0=p["h0"])
+    np.testing.assert_allclose(y, ssd_dense(p, softplus), rtol=1e-10, atol=1e-10)
+
+
+def test_ssd_last_state_closed_form():
+    """last_state[e, n] = sum_s exp(A (S_L - S_s)) d_s B_s[n] x_s[e] + exp(A S_L) h0[e, n]."""
+    p = ssd_problem(62)
+    _, last = oracle.ssd(p["x"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["delta_bias"], True, h0=p["h0"])
+    b, L, E = p["x"].shape
+    H = p["delta"].shape[2]
+    P = E // H
+    d = np.logaddexp(0.0, p["delta"] + p["delta_bias"])
+    S = np.cumsum(d, axis=1)
+    for bi in range(b):
+        for h in range(H):
+            w = np.exp(p["A"][h] * (S[bi, -1, h] - S[bi, :, h])) * d[bi, :, h]     # [L]
+            xs = p["x"][bi, :, h * P:(h + 1) * P]                                    # [L, P]
+            ref = (xs * w[:, None]).T @ p["B"][bi] + np.exp(p["A"][h] * S[bi, -1, h]) * p["h0"][bi, h * P:(h + 1) * P]
+            np.testing.assert_allclose(last[bi, h * P:(h + 1) * P], ref, rtol=1e-10, atol=1e-10)
