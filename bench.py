@@ -7,8 +7,10 @@ silu gate, D skip), with inputs already resident in HBM.  That call runs the
 whole hot path: discretisation, recurrence, readout, gate and the last-state
 write.  The single-token state update is measured as well (128 successive
 updates of the generation workload b=256, E=5120, N=16) and reported in its
-own JSON object, and so is the causal convolution that precedes the scan
-(b1 L65536 E5120 K4 bf16, and its token step at b256 E5120 K4).
+own JSON object, and so are the causal convolution that precedes the scan
+(b1 L65536 E5120 K4 bf16, and its token step at b256 E5120 K4), the scan's
+backward on the long workload, and the scan with a scalar transition per head
+(b1 L65536 H80 P64 N64 bf16, chunked MFMA form).
 
 Prints ONE JSON line on stdout:
   value        b*L*E elements per second over the timed steps
@@ -85,6 +87,19 @@ def bwd_bytes(b, L, E, N, s, gate=True):
     return b * L * E * streams * s + 2 * b * L * N * s + 2 * b * L * N * 4 + 2 * E * (N + 2) * 4
 
 
+def ssd_bytes(b, L, H, P, N, s, gate=True):
+    """Algorithmic bytes of one scalar-per-head scan: x (, z) in and y out; delta; B, C; A, D; the last state."""
+    E = H * P
+    return b * L * E * ((2 if gate else 1) + 1) * s + b * L * H * s + 2 * b * L * N * s + 2 * H * 4 + b * E * N * 4
+
+
+def ssd_flops(b, L, H, P, N, Q=64):
+    """Matrix-product flops of the chunked form: C B^T (causal half), L o (C B^T) X (causal half), C S_in, B^T (w o X)."""
+    chunks = (L + Q - 1) // Q
+    per = Q * Q * N + Q * Q * P + 2 * Q * N * P  # multiply-adds per (chunk, head), causal halves counted
+    return 2 * b * H * chunks * per
+
+
 def conv_bytes(b, L, E, K, s, bias=True):
     """Algorithmic bytes of one causal convolution: v in, x out, the weights (and bias), the K-sample state out."""
     return 2 * b * L * E * s + E * K * 4 + (E * 4 if bias else 0) + b * E * K * s
@@ -126,6 +141,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-conv", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
+    ap.add_argument("--no-ssd", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -283,6 +299,42 @@ def main():
         log(f"[bench] backward {bwd}")
         del dy
 
+    # the scan with a scalar transition per head, in chunks of MFMA matrix products
+    ssd = None
+    if not args.no_ssd:
+        ws = workloads.SSD_LONG
+        xs = workloads.make_ssd_inputs(ws, seed=args.seed, device=dev, backend="torch")
+        ys = torch.empty_like(xs["x"])
+        ls = torch.empty((ws.b, ws.E, ws.N), dtype=torch.float32, device=dev)
+
+        def ssd_step():
+            ssm.ssm_ssd_fwd(xs["x"], xs["delta"], xs["A"], xs["B"], xs["C"], xs["D"], xs["z"], xs["delta_bias"],
+                            xs["softplus"], y=ys, last_state=ls)
+
+        for _ in range(3):
+            ssd_step()
+        torch.cuda.synchronize()
+        ssm.ssm_profile_read()
+        ssm.ssm_profile_enable(True)
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        for _ in range(20):
+            ssd_step()
+        s1.record(stream)
+        torch.cuda.synchronize()
+        ssm.ssm_profile_enable(False)
+        prof = ssm.ssm_profile_read()
+        ssd_ms = s0.elapsed_time(s1) / 20
+        sb = ssd_bytes(ws.b, ws.L, ws.H, ws.P, ws.N, 2, gate=ws.gate)
+        sf = ssd_flops(ws.b, ws.L, ws.H, ws.P, ws.N)
+        ssd = {"workload": ws.description, "ms_per_call": round(ssd_ms, 4),
+               "elem_per_s": ws.b * ws.L * ws.E / (ssd_ms * 1e-3), "algorithmic_bytes": sb,
+               "GBps": round(sb / (ssd_ms * 1e-3) / 1e9, 1), "matrix_TFLOPs": round(sf / (ssd_ms * 1e-3) / 1e12, 2),
+               "kernels": {k: {"avg_us": round(1e3 * v[0] / v[1], 2), "launches": v[1]}
+                           for k, v in prof.items() if v[1]}}
+        log(f"[bench] ssd {ssd}")
+        del xs, ys, ls
+
     # causal convolution in front of the scan (long workload) and its generation-time token step
     conv = None
     if not args.no_conv:
@@ -396,6 +448,7 @@ def main():
         "state_update": update,
         "conv": conv,
         "backward": bwd,
+        "ssd": ssd,
         "cpu_baseline": cpu,
         "parity": parity,
     }

@@ -184,6 +184,35 @@ SSM_API int ssm_scan_bwd(const void* u, const void* delta, const float* A, const
                          void* stream);
 
 /*
+ * The scan with a scalar transition per head -- structured state-space
+ * duality -- computed in chunks of matrix products on the MFMA units ("Mamba:
+ * Linear-Time Sequence Modeling with Selective State Spaces", abhik.ai, "Key
+ * takeaways" / "Related reading": a restricted state update becomes a
+ * structured mixing matrix computed in chunks; "mamba-from-scratch" README,
+ * Mamba-2 / SSD).  The result is ssm_scan_fwd_from's for E = H * P channels
+ * where channel e = h * P + p uses the head's step delta[b,t,h], A[h] (the same
+ * for every state), D[h] and delta_bias[h]:
+ *   y[t,e] = sum_{s<=t} (C_t . B_s) exp(A_h (S_t - S_s)) d_s x[s,e] + D_h x[t,e]
+ *            (+ the initial state's part), times silu(z[t,e]);  S_t = d_0 + ... + d_t
+ *
+ * Arguments (device pointers):
+ *   x, z, y         [b, L, H*P]  bf16   (z nullable; x, z, y 16-byte aligned)
+ *   delta           [b, L, H]    bf16
+ *   A, D, delta_bias [H]         float  (D, delta_bias nullable)
+ *   B, C            [b, L, N]    bf16   (16-byte aligned)
+ *   initial_state, last_state [b, H*P, N] float (nullable)
+ *   P == 64; N a multiple of 16 in 16..128 (else SSM_ERR_DIM / SSM_ERR_UNSUPPORTED_N);
+ *   dtype must be SSM_BF16 (the matrix products take bf16 operands and
+ *   accumulate in fp32; SSM_F32 returns SSM_ERR_DTYPE).
+ * Takes a workspace of b * ceil(L/64) * H * (64 * N + 1) floats from the
+ * stream-ordered allocator on `stream`.
+ */
+SSM_API int ssm_ssd_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                        const float* D, const void* z, const float* delta_bias, int softplus,
+                        const float* initial_state, void* y, float* last_state, int64_t b, int64_t L, int64_t H,
+                        int64_t P, int64_t N, int dtype, void* stream);
+
+/*
  * Causal depthwise convolution + SiLU, the step before the scan in the Mamba
  * block ([AB] row 4 "Add causal local context before selecting coefficients"):
  *   x[b,t,c] = silu(conv_bias[c] + sum_{k=0..K-1} q[c,k] * v[b, t-K+1+k, c])
@@ -233,7 +262,7 @@ SSM_API int ssm_scan_plan(int64_t b, int64_t L, int64_t E, int64_t N, int dtype,
  * record.  Kinds: 0 widen_rows (bf16 B/C rows to f32), 1 chunk_aggregate,
  * 2 chunk_carry, 3 scan_main, 4 fill_state, 5 state_update, 6 conv,
  * 7 conv_update, 8 bwd_rows, 9 bwd_aggregate, 10 bwd_carry, 11 bwd_main,
- * 12 bwd_reduce; names from
+ * 12 bwd_reduce, 13 ssd_state, 14 ssd_carry, 15 ssd_scan; names from
  * ssm_profile_kind_name().  Off by default; the events add a few
  * microseconds per launch.  Process-wide, thread-safe.
  */

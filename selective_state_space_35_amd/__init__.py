@@ -18,6 +18,11 @@ Functions (same names as the C entry points):
 * ``ssm_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None,
   softplus=False, initial_state=None, d_last_state=None)`` -> dict of
   gradients (du, ddelta, dA, dB, dC, dD, dz, d_delta_bias, d_initial_state)
+* ``ssm_ssd_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None,
+  softplus=False, initial_state=None, y=None, last_state=None,
+  return_last_state=True)`` -> ``(y, last_state)``: the scan with a scalar
+  transition per head (x [b, L, H*64], delta [b, L, H], A, D, delta_bias [H]),
+  bf16 only
 * ``ssm_conv_fwd(v, weight, conv_bias=None, state_in=None, x=None,
   state_out=None, return_state=True)`` -> ``(x, state_out)``: causal depthwise
   convolution + SiLU over the sequence
@@ -34,7 +39,7 @@ import ctypes
 import os
 
 __all__ = [
-    "ssm_scan_fwd", "ssm_scan_fwd_from", "ssm_scan_bwd", "ssm_state_update", "ssm_conv_fwd", "ssm_conv_update", "ssm_scan_plan", "ssm_profile_enable", "ssm_profile_read",
+    "ssm_scan_fwd", "ssm_scan_fwd_from", "ssm_scan_bwd", "ssm_ssd_fwd", "ssm_state_update", "ssm_conv_fwd", "ssm_conv_update", "ssm_scan_plan", "ssm_profile_enable", "ssm_profile_read",
     "ssm_status_string", "library_path", "SSMError",
     "SSM_F32", "SSM_BF16", "load_library",
 ]
@@ -84,6 +89,8 @@ def load_library():
     lib.ssm_state_update.argtypes = [_vp] * 9 + [_int, _vp] + [_i64] * 3 + [_int, _vp]
     lib.ssm_scan_bwd.restype = _int
     lib.ssm_scan_bwd.argtypes = [_vp] * 8 + [_int] + [_vp] * 12 + [_i64] * 4 + [_int, _vp]
+    lib.ssm_ssd_fwd.restype = _int
+    lib.ssm_ssd_fwd.argtypes = [_vp] * 8 + [_int] + [_vp] * 3 + [_i64] * 5 + [_int, _vp]
     lib.ssm_conv_fwd.restype = _int
     lib.ssm_conv_fwd.argtypes = [_vp] * 6 + [_i64] * 4 + [_int, _vp]
     lib.ssm_conv_update.restype = _int
@@ -120,7 +127,7 @@ def ssm_scan_plan(b, L, E, N, dtype="bf16"):
     return cl.value, nc.value
 
 
-PROFILE_KINDS = 13
+PROFILE_KINDS = 16
 
 
 def ssm_profile_enable(on=True):
@@ -289,6 +296,53 @@ def ssm_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplu
                                   _stream_of(torch, device))
     _raise_on("ssm_scan_bwd", status)
     return g
+
+
+def ssm_ssd_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=False, initial_state=None, y=None,
+                last_state=None, return_last_state=True):
+    """The scan with a scalar transition per head on the GPU (bf16).  Returns ``(y, last_state)``."""
+    import torch
+
+    lib = load_library()
+    if not isinstance(x, torch.Tensor) or x.dim() != 3:
+        raise ValueError("x must be a [b, L, H*P] tensor")
+    device = x.device
+    if device.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU device, got {device}")
+    if not isinstance(delta, torch.Tensor) or delta.dim() != 3:
+        raise ValueError("delta must be a [b, L, H] tensor")
+    b, L, E = x.shape
+    H = delta.shape[2]
+    if H == 0 or E % H:
+        raise ValueError("the channels of x must split evenly into the heads of delta")
+    P = E // H
+    N = B.shape[2] if isinstance(B, torch.Tensor) and B.dim() == 3 else -1
+    io = x.dtype
+    code = _dtype_code(torch, io)
+    f32 = torch.float32
+    _check(torch, "x", x, (b, L, E), io, device)
+    _check(torch, "delta", delta, (b, L, H), io, device)
+    _check(torch, "A", A, (H,), f32, device)
+    _check(torch, "B", B, (b, L, N), io, device)
+    _check(torch, "C", C, (b, L, N), io, device)
+    _check(torch, "D", D, (H,), f32, device, optional=True)
+    _check(torch, "z", z, (b, L, E), io, device, optional=True)
+    _check(torch, "delta_bias", delta_bias, (H,), f32, device, optional=True)
+    _check(torch, "initial_state", initial_state, (b, E, N), f32, device, optional=True)
+    if y is None:
+        y = torch.empty((b, L, E), dtype=io, device=device)
+    else:
+        _check(torch, "y", y, (b, L, E), io, device)
+    if last_state is None and return_last_state:
+        last_state = torch.empty((b, E, N), dtype=f32, device=device)
+    elif last_state is not None:
+        _check(torch, "last_state", last_state, (b, E, N), f32, device)
+    with torch.cuda.device(device):
+        status = lib.ssm_ssd_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                                 int(bool(softplus)), _ptr(initial_state), _ptr(y), _ptr(last_state), b, L, H, P, N,
+                                 code, _stream_of(torch, device))
+    _raise_on("ssm_ssd_fwd", status)
+    return y, last_state
 
 
 def ssm_state_update(state, x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=False, y=None):

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libssm.so")
-SOURCES = ["ssm_kernels.hip", "ssm_conv.hip", "ssm_bwd.hip", "ssm_api.hip", "ssm_profile.hip"]
+SOURCES = ["ssm_kernels.hip", "ssm_conv.hip", "ssm_bwd.hip", "ssm_ssd.hip", "ssm_api.hip", "ssm_profile.hip"]
 ARCH = os.environ.get("SSM_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

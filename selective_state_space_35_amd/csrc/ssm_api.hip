@@ -140,6 +140,37 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
   return hip_status(ssm::launch_scan_bwd(a));
 }
 
+int ssm_ssd_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
+                const void* z, const float* delta_bias, int softplus, const float* initial_state, void* y,
+                float* last_state, int64_t b, int64_t L, int64_t H, int64_t P, int64_t N, int dtype, void* stream) {
+  if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_DTYPE;
+  if (dtype != SSM_BF16) return SSM_ERR_DTYPE;  // the matrix products take bf16 operands
+  if (b < 0 || L < 0 || H < 0 || P != ssm::ssd_head_dim()) return SSM_ERR_DIM;
+  if (N < 16 || N > 128 || N % 16 != 0) return SSM_ERR_UNSUPPORTED_N;
+  int64_t E = 0, t = 0;
+  if (!mul_ok(H, P, &E) || !mul_ok(b, L, &t) || !mul_ok(t, E, &t) || !mul_ok(t, 4, &t)) return SSM_ERR_DIM;
+  if (!mul_ok(b, E, &t) || !mul_ok(t, N, &t) || !mul_ok(t, 4, &t)) return SSM_ERR_DIM;
+  if (b == 0 || H == 0) return SSM_OK;
+  if (L > 0 && (!x || !delta || !A || !B || !C || !y)) return SSM_ERR_NULL;
+  // rows of x, z, y, B and C are read and written 16 bytes at a time
+  const void* vec[] = {x, z, y, B, C};
+  for (const void* p : vec)
+    if (p && !aligned(p, 16)) return SSM_ERR_ALIGN;
+  if (delta && !aligned(delta, 2)) return SSM_ERR_ALIGN;
+  const void* fl[] = {A, D, delta_bias, initial_state, last_state};
+  for (const void* p : fl)
+    if (p && !aligned(p, 4)) return SSM_ERR_ALIGN;
+  const int64_t chunks = (L + ssm::ssd_chunk_steps() - 1) / ssm::ssd_chunk_steps();
+  int64_t grid = 0;
+  if (!mul_ok(b * chunks, H, &grid) || grid > INT32_MAX) return SSM_ERR_DIM;
+  if (b * E * N / 256 > INT32_MAX) return SSM_ERR_DIM;
+  ssm::SsdArgs a;
+  a.x = x; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias;
+  a.softplus = softplus ? 1 : 0; a.h0 = initial_state; a.y = y; a.last_state = last_state;
+  a.b = b; a.L = L; a.H = H; a.N = N; a.stream = static_cast<hipStream_t>(stream);
+  return hip_status(ssm::launch_ssd(a));
+}
+
 int ssm_scan_plan(int64_t b, int64_t L, int64_t E, int64_t N, int dtype, int64_t* chunk_len, int64_t* n_chunks) {
   int st = check_sizes(b, L, E, N, dtype);
   if (st != SSM_OK) return st;

@@ -110,6 +110,27 @@ struct BwdArgs {
 int64_t bwd_chunk_steps();  // steps per chunk of the backward
 hipError_t launch_scan_bwd(const BwdArgs& a);
 
+// The scan with a scalar transition per head, in chunks of matrix products (bf16 I/O).
+struct SsdArgs {
+  const void* x;       // [b, L, H * P]
+  const void* delta;   // [b, L, H]
+  const float* A;      // [H]
+  const void* B;       // [b, L, N]
+  const void* C;       // [b, L, N]
+  const float* D;      // [H], nullable
+  const void* z;       // [b, L, H * P], nullable
+  const float* bias;   // [H], nullable
+  int softplus;
+  const float* h0;     // [b, H * P, N], nullable
+  void* y;             // [b, L, H * P]
+  float* last_state;   // [b, H * P, N], nullable
+  int64_t b, L, H, N;
+  hipStream_t stream;
+};
+int64_t ssd_chunk_steps();  // steps per chunk
+int64_t ssd_head_dim();     // channels per head (P)
+hipError_t launch_ssd(const SsdArgs& a);
+
 // Both return hipSuccess or the first HIP error met while enqueueing.
 hipError_t launch_scan(const ScanArgs& a);
 hipError_t launch_state_update(const UpdateArgs& a);

@@ -20,7 +20,10 @@ enum : int {
   kKindBwdCarry = 10,   // backward: chain of the state gradient across chunks
   kKindBwdMain = 11,    // backward: recompute states, gradients of every input
   kKindBwdReduce = 12,  // backward: sums of the per-chunk / per-block partial gradients
-  kNumKinds = 13
+  kKindSsdState = 13,   // scalar-per-head scan: chunk states (matrix products)
+  kKindSsdCarry = 14,   // scalar-per-head scan: chain of chunk states
+  kKindSsdScan = 15,    // scalar-per-head scan: chunk outputs (matrix products)
+  kNumKinds = 16
 };
 
 // When profiling is on, creates and records the start event on `s` and returns true.

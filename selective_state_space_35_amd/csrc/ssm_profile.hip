@@ -26,7 +26,7 @@ std::vector<Pending> g_pending;
 const char* const kNames[kNumKinds] = {"widen_rows",  "chunk_aggregate", "chunk_carry",   "scan_main",
                                        "fill_state",  "state_update",    "conv",          "conv_update",
                                        "bwd_rows",    "bwd_aggregate",   "bwd_carry",     "bwd_main",
-                                       "bwd_reduce"};
+                                       "bwd_reduce",  "ssd_state",       "ssd_carry",     "ssd_scan"};
 
 }  // namespace
 

@@ -187,6 +187,27 @@ def test_bwd_validation(lib):
                dB=None, dC=None) == OK
 
 
+def ssd(lib, x=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, bias=None, h0=None, y=FAKE, last=None,
+        b=1, L=8, H=2, P=64, N=16, dtype=1):
+    return lib.ssm_ssd_fwd(x, delta, A, B, C, D, z, bias, 1, h0, y, last, b, L, H, P, N, dtype, None)
+
+
+def test_ssd_validation(lib):
+    assert ssd(lib, dtype=0) == ERR_DTYPE      # bf16 only
+    assert ssd(lib, dtype=4) == ERR_DTYPE
+    assert ssd(lib, P=32) == ERR_DIM
+    assert ssd(lib, L=-1) == ERR_DIM
+    for n in (0, 8, 24, 144):
+        assert ssd(lib, N=n) == ERR_N, n
+    for k in ("x", "delta", "A", "B", "C", "y"):
+        assert ssd(lib, **{k: None}) == ERR_NULL, k
+    assert ssd(lib, x=FAKE + 8) == ERR_ALIGN    # 16-byte rows
+    assert ssd(lib, B=FAKE + 2) == ERR_ALIGN
+    assert ssd(lib, delta=FAKE + 1) == ERR_ALIGN
+    assert ssd(lib, last=FAKE + 2) == ERR_ALIGN
+    assert ssd(lib, b=0, x=None, delta=None, A=None, B=None, C=None, y=None) == OK
+
+
 def test_binding_refuses_cpu_tensors():
     torch = pytest.importorskip("torch")
     if not os.path.exists(ssm.library_path()):
@@ -241,5 +262,5 @@ def test_scan_plan_query(lib, monkeypatch):
 def test_profile_read_with_nothing_recorded(lib):
     out = ssm.ssm_profile_read()
     assert set(out) == {"widen_rows", "chunk_aggregate", "chunk_carry", "scan_main", "fill_state", "state_update",
-                        "conv", "conv_update", "bwd_rows", "bwd_aggregate", "bwd_carry", "bwd_main", "bwd_reduce"}
+                        "conv", "conv_update", "bwd_rows", "bwd_aggregate", "bwd_carry", "bwd_main", "bwd_reduce", "ssd_state", "ssd_carry", "ssd_scan"}
     assert all(v == (0.0, 0) for v in out.values())

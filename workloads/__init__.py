@@ -141,6 +141,45 @@ CONV_DECODE = ConvWorkload("conv_decode", b=256, L=1, E=5120, K=4, dtype="bf16",
                            description="generation-time convolution state update: b256 E5120 K4 bf16")
 
 
+@dataclass(frozen=True)
+class SsdWorkload:
+    """The scan with a scalar transition per head: x [b, L, H*P], delta [b, L, H], B, C [b, L, N]."""
+    name: str
+    b: int
+    L: int
+    H: int
+    N: int
+    P: int = 64
+    dtype: str = "bf16"
+    gate: bool = True
+    with_D: bool = True
+    with_bias: bool = False
+    softplus: bool = True
+    description: str = ""
+
+    @property
+    def E(self) -> int:
+        return self.H * self.P
+
+    def with_shape(self, **kw) -> "SsdWorkload":
+        d = dict(self.__dict__)
+        d.update(kw)
+        return SsdWorkload(**d)
+
+
+# a long sequence through a layer of 80 heads of 64 channels (5120 channels, as the long scan) with 64 states
+SSD_LONG = SsdWorkload("ssd_long", b=1, L=65536, H=80, N=64,
+                       description="scalar-per-head scan: b1 L65536 H80 P64 (E5120) N64 bf16, gate, D")
+SSD_MID = SsdWorkload("ssd_mid", b=4, L=2048, H=24, N=64,
+                      description="scalar-per-head scan: b4 L2048 H24 P64 (E1536) N64 bf16, gate, D")
+
+
+def ssd_a(H: int) -> np.ndarray:
+    """A[h] = -exp(A_log[h]) with A_log[h] = log(1 + 15 h / max(H - 1, 1)): decay rates spread over 1..16, float32."""
+    a_log = np.log(1.0 + 15.0 * np.arange(H, dtype=np.float64) / max(H - 1, 1)).astype(np.float32)
+    return (-np.exp(a_log)).astype(np.float32)
+
+
 def a_matrix(E: int, N: int) -> np.ndarray:
     """A[e, n] = -exp(A_log[e, n]) with A_log[e, n] = log(n + 1), in float32, shape [E, N]."""
     a_log = np.log(np.arange(1, N + 1, dtype=np.float64)).astype(np.float32)
@@ -294,4 +333,30 @@ def make_conv_inputs(w: ConvWorkload, seed: int = 0, device="cpu", backend: str 
     out["conv_bias"] = drawer.finish(drawer.normal((w.E,), 0.0, 0.1), torch.float32, device) if w.bias else None
     out["state_in"] = (drawer.finish(drawer.normal((w.b, w.E, w.K), 0.0, 1.0), io, device)
                        if w.state_in else None)
+    return out
+
+
+def make_ssd_inputs(w: SsdWorkload, seed: int = 0, device="cpu", backend: str = "numpy") -> dict:
+    """Inputs of one scalar-per-head scan call.
+
+    Keys: x [b, L, H*P] N(0,1); delta [b, L, H] raw step N(-3, 1) (softplus applied by
+    the operator); B, C [b, L, N] N(0, 0.25^2); A [H] from ssd_a; D [H] N(0,1) or None;
+    z [b, L, H*P] N(0,1) or None; delta_bias [H] N(0, 0.3^2) or None; softplus.
+    Draw order: x, delta, z, B, C, D, delta_bias.
+    """
+    import torch
+
+    drawer = _NumpyDraw(seed) if backend == "numpy" else _TorchDraw(seed, device)
+    io = _torch_dtype(w.dtype)
+    out = {}
+    out["x"] = drawer.finish(drawer.normal((w.b, w.L, w.E), 0.0, 1.0), io, device)
+    out["delta"] = drawer.finish(drawer.normal((w.b, w.L, w.H), -3.0, 1.0), io, device)
+    out["z"] = drawer.finish(drawer.normal((w.b, w.L, w.E), 0.0, 1.0), io, device) if w.gate else None
+    out["B"] = drawer.finish(drawer.normal((w.b, w.L, w.N), 0.0, 0.25), io, device)
+    out["C"] = drawer.finish(drawer.normal((w.b, w.L, w.N), 0.0, 0.25), io, device)
+    out["D"] = drawer.finish(drawer.normal((w.H,), 0.0, 1.0), torch.float32, device) if w.with_D else None
+    out["delta_bias"] = (drawer.finish(drawer.normal((w.H,), 0.0, 0.3), torch.float32, device)
+                         if w.with_bias else None)
+    out["A"] = torch.from_numpy(ssd_a(w.H)).to(device)
+    out["softplus"] = w.softplus
     return out
