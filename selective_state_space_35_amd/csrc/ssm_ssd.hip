@@ -16,9 +16,10 @@
 //   Y   = diag(exp(cum)) (C S_in)  +  (L o (C B^T)) X,   L[t,s] = exp(cum_t - cum_s) d_s for s <= t
 //   S_out = exp(cum_last) S_in + B^T (w o X),            w_s = exp(cum_last - cum_s) d_s
 //
-// Kernels (bf16 I/O; matrix products take bf16 operands and accumulate in fp32):
-//   ssd_state_kernel  per (batch, chunk, head): B^T (w o X) -> chunk state [N, P]
-//   ssd_carry_kernel  per (batch, head, n, p): chain of chunk states -> state entering each chunk
+// Kernels (bf16 I/O; matrix products take bf16 operands and accumulate in fp32;
+// chunk states are handed between kernels in bf16, laid out [p][n]):
+//   ssd_state_kernel  per (batch, chunk, head): (w o X)^T B -> chunk state [P, N]
+//   ssd_carry_kernel  per (batch, head, p, n): chain of chunk states (fp32 in registers) -> state entering each chunk
 //   ssd_scan_kernel   per (batch, chunk, head): Y as above, + D x, gate, store
 // MFMA: v_mfma_f32_16x16x32_bf16.  Lane l of a wave holds A-operand row l % 16,
 // k = 8 (l / 16) .. +7; B-operand column l % 16, same k; result rows
@@ -90,12 +91,12 @@ __device__ __forceinline__ void stage_rows(const bf16_bits* __restrict__ src, in
 }
 
 // ---------------------------------------------------------------------------
-// chunk state: S_c[n, p] = sum_s B[s, n] w_s X[s, p]
+// chunk state, transposed: S_c[p, n] = sum_s (w o X)[s, p] B[s, n]  (bf16 out)
 // ---------------------------------------------------------------------------
 template <int NK, bool SOFTPLUS>  // NK: the state size padded to a multiple of 32, in units of 32
 __global__ __launch_bounds__(kSsdThreads) void ssd_state_kernel(
     const bf16_bits* __restrict__ x, const bf16_bits* __restrict__ delta, const float* __restrict__ A,
-    const bf16_bits* __restrict__ B, const float* __restrict__ bias, float* __restrict__ states,
+    const bf16_bits* __restrict__ B, const float* __restrict__ bias, bf16_bits* __restrict__ states,
     float* __restrict__ cum_last, int64_t L, int H, int N, int n_chunks) {
   constexpr int NP = NK * 32;
   __shared__ float d_s[kQ], cum_s[kQ];
@@ -109,15 +110,21 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_state_kernel(
   const int n_steps = int(std::min<int64_t>(kQ, L - t0));
   const int64_t row0 = bi * L + t0;
   const int64_t E = int64_t(H) * kP;
-  const float Ah = A[h];
-  chunk_steps<SOFTPLUS>(delta, bias, Ah, row0, H, h, n_steps, d_s, cum_s);
+  chunk_steps<SOFTPLUS>(delta, bias, A[h], row0, H, h, n_steps, d_s, cum_s);
+  // B^T: 16-byte row reads, transposed writes
+  for (int i = threadIdx.x; i < kQ * (NP / 8); i += kSsdThreads) {
+    const int s = i / (NP / 8), n8 = (i % (NP / 8)) * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (s < n_steps && n8 < N) v = *reinterpret_cast<const uint4*>(B + (row0 + s) * N + n8);
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      Bt[n8 + 2 * j][s] = bf16_bits(u[j] & 0xffff);
+      Bt[n8 + 2 * j + 1][s] = bf16_bits(u[j] >> 16);
+    }
+  }
   __syncthreads();
   const float last = cum_s[kQ - 1];
-  // B^T and (w o X)^T into LDS
-  for (int i = threadIdx.x; i < kQ * NP; i += kSsdThreads) {
-    const int s = i / NP, n = i % NP;
-    Bt[n][s] = (s < n_steps && n < N) ? B[(row0 + s) * N + n] : bf16_bits(0);
-  }
   for (int i = threadIdx.x; i < kQ * (kP / 8); i += kSsdThreads) {
     const int s = i / (kP / 8), p8 = (i % (kP / 8)) * 8;
     uint4 v = make_uint4(0, 0, 0, 0);
@@ -131,52 +138,51 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_state_kernel(
     }
   }
   __syncthreads();
-  // wave w: columns p in [16 w, 16 w + 16), every 16-row block of n
+  // wave w: rows p in [16 w, 16 w + 16), every 16-column block of n
   const int wv = threadIdx.x / kWave, l = threadIdx.x % kWave;
   const int lr = l % 16, lk = 8 * (l / 16);
-  float* out = states + ((bi * n_chunks + c) * H + h) * int64_t(N) * kP;
+  bf16_bits* out = states + ((bi * n_chunks + c) * H + h) * int64_t(kP) * N;  // [p][n]
+  bf16x8 xf[kQ / 32];
 #pragma unroll
-  for (int rb = 0; rb < NP / 16; rb++) {
-    if (rb * 16 >= N) break;
+  for (int kk = 0; kk < kQ / 32; kk++) xf[kk] = lds8(&Xw[wv * 16 + lr][kk * 32 + lk]);
+#pragma unroll
+  for (int nb = 0; nb < NP / 16; nb++) {
+    if (nb * 16 >= N) break;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < kQ / 32; kk++)
-      acc = mfma(lds8(&Bt[rb * 16 + lr][kk * 32 + lk]), lds8(&Xw[wv * 16 + lr][kk * 32 + lk]), acc);
+    for (int kk = 0; kk < kQ / 32; kk++) acc = mfma(xf[kk], lds8(&Bt[nb * 16 + lr][kk * 32 + lk]), acc);
 #pragma unroll
-    for (int r = 0; r < 4; r++) {
-      const int n = rb * 16 + 4 * (l / 16) + r;
-      if (n < N) out[int64_t(n) * kP + wv * 16 + lr] = acc[r];
-    }
+    for (int r = 0; r < 4; r++) out[int64_t(wv * 16 + 4 * (l / 16) + r) * N + nb * 16 + lr] = to_bf16(acc[r]);
   }
   if (threadIdx.x == 0) cum_last[(bi * n_chunks + c) * H + h] = last;
 }
 
 // ---------------------------------------------------------------------------
-// carry: per (batch, head, n, p), state entering chunk c, in place of S_c;
-// the state after the last chunk goes to last_state [b, E, N]
+// carry: per (batch, head, p, n), state entering chunk c (bf16, in place of
+// S_c; the chain itself is kept in fp32); the state after the last chunk goes
+// to last_state [b, E, N] in fp32
 // ---------------------------------------------------------------------------
 template <int U>
-__global__ __launch_bounds__(256) void ssd_carry_kernel(float* states, const float* __restrict__ cum_last,
+__global__ __launch_bounds__(256) void ssd_carry_kernel(bf16_bits* states, const float* __restrict__ cum_last,
                                                         const float* __restrict__ h0, float* __restrict__ last_state,
                                                         int64_t b, int H, int N, int n_chunks) {
   const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t per_head = int64_t(N) * kP;
   if (gid >= b * H * per_head) return;
-  const int64_t within = gid % per_head;  // n * P + p
-  const int n = int(within / kP), p = int(within % kP);
+  const int64_t within = gid % per_head;  // p * N + n
   const int64_t bh = gid / per_head;
   const int h = int(bh % H);
   const int64_t bi = bh / H;
   const int64_t E = int64_t(H) * kP;
-  const int64_t e = int64_t(h) * kP + p;
-  float S = h0 ? h0[(bi * E + e) * N + n] : 0.f;
+  const int64_t st = (bi * E + int64_t(h) * kP) * N + within;  // [b][e = h P + p][n]
+  float S = h0 ? h0[st] : 0.f;
   auto slot = [&](int c) { return ((bi * n_chunks + c) * H + h) * per_head + within; };
   float Ss[U], Ls[U];
   auto load = [&](int c0) {
 #pragma unroll
     for (int k = 0; k < U; k++) {
       const int cc = (c0 + k < n_chunks) ? c0 + k : n_chunks - 1;  // past the end: a valid slot, unused
-      Ss[k] = states[slot(cc)];
+      Ss[k] = from_bf16(states[slot(cc)]);
       Ls[k] = cum_last[(bi * n_chunks + cc) * H + h];
     }
   };
@@ -189,30 +195,33 @@ __global__ __launch_bounds__(256) void ssd_carry_kernel(float* states, const flo
 #pragma unroll
     for (int k = 0; k < U; k++) {
       if (c0 + k < n_chunks) {
-        states[slot(c0 + k)] = S;
+        states[slot(c0 + k)] = to_bf16(S);
         S = fmaf(exp2_fast(Lc[k] * kLog2e), S, Sc[k]);
       }
     }
   }
-  if (last_state) last_state[(bi * E + e) * N + n] = S;
+  if (last_state) last_state[st] = S;
 }
 
 // ---------------------------------------------------------------------------
-// outputs of a chunk
+// outputs of a chunk.  Wave w owns steps t in [16 w, 16 w + 16).  The mixing
+// matrix is built transposed (rows s, columns t) so that each lane ends with
+// its own step t in registers: those values are the A operand of the next
+// product directly, with the contraction index s in the order the transposed
+// tiles give it (s = 4 g + r and 16 + 4 g + r for lane group g); X is read in
+// the same order.
 // ---------------------------------------------------------------------------
 template <int NK, bool SOFTPLUS, bool HAS_Z, bool HAS_D>
 __global__ __launch_bounds__(kSsdThreads) void ssd_scan_kernel(
     const bf16_bits* __restrict__ x, const bf16_bits* __restrict__ delta, const float* __restrict__ A,
     const bf16_bits* __restrict__ B, const bf16_bits* __restrict__ C, const float* __restrict__ D,
-    const bf16_bits* __restrict__ z, const float* __restrict__ bias, const float* __restrict__ states,
+    const bf16_bits* __restrict__ z, const float* __restrict__ bias, const bf16_bits* __restrict__ states,
     bf16_bits* __restrict__ y, int64_t L, int H, int N, int n_chunks) {
   constexpr int NP = NK * 32;
   __shared__ float d_s[kQ], cum_s[kQ];
   __shared__ __attribute__((aligned(16))) bf16_bits Cs[kQ][NP + kPad];    // C rows [t][n]
   __shared__ __attribute__((aligned(16))) bf16_bits Bs[kQ][NP + kPad];    // B rows [s][n]
   __shared__ __attribute__((aligned(16))) bf16_bits Xt[kP][kQ + kPad];    // X transposed [p][s]
-  __shared__ __attribute__((aligned(16))) bf16_bits St[kP][NP + kPad];    // incoming state transposed [p][n]
-  __shared__ __attribute__((aligned(16))) bf16_bits Ms[kQ][kQ + kPad];    // mixing matrix [t][s]
   const int h = blockIdx.x % H;
   const int rest = blockIdx.x / H;
   const int c = rest % n_chunks;
@@ -221,6 +230,36 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_scan_kernel(
   const int n_steps = int(std::min<int64_t>(kQ, L - t0));
   const int64_t row0 = bi * L + t0;
   const int64_t E = int64_t(H) * kP;
+  const int wv = threadIdx.x / kWave, l = threadIdx.x % kWave;
+  const int lr = l % 16, lg = l / 16, lk = 8 * lg, lq = 4 * lg;
+  const int tb = wv;                 // this wave's step block
+  const int t_own = tb * 16 + lr;    // the step this lane carries through the mixing product
+  // Global reads this lane needs later are issued first, so their latency overlaps
+  // the staging and the mixing matrix: the gate of its outputs and the incoming
+  // state's fragments ([p][n] bf16).
+  float zv[kP / 16][4];
+  if (HAS_Z) {
+#pragma unroll
+    for (int pb = 0; pb < kP / 16; pb++)
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const int t = tb * 16 + lq + r;
+        zv[pb][r] = t < n_steps ? from_bf16(z[(row0 + t) * E + int64_t(h) * kP + pb * 16 + lr]) : 0.f;
+      }
+  }
+  const bf16_bits* Sin = states + ((bi * n_chunks + c) * H + h) * int64_t(kP) * N;
+  bf16x8 sfr[kP / 16][NK];
+#pragma unroll
+  for (int pb = 0; pb < kP / 16; pb++)
+#pragma unroll
+    for (int kk = 0; kk < NK; kk++) {
+      if (kk * 32 + lk < N) {
+        sfr[pb][kk] = *reinterpret_cast<const bf16x8*>(Sin + int64_t(pb * 16 + lr) * N + kk * 32 + lk);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; j++) sfr[pb][kk][j] = static_cast<__bf16>(0.f);
+      }
+    }
   chunk_steps<SOFTPLUS>(delta, bias, A[h], row0, H, h, n_steps, d_s, cum_s);
   stage_rows(C + row0 * N, N, kQ, n_steps, NP, N, &Cs[0][0], NP + kPad);
   stage_rows(B + row0 * N, N, kQ, n_steps, NP, N, &Bs[0][0], NP + kPad);
@@ -235,76 +274,73 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_scan_kernel(
       Xt[p8 + 2 * j + 1][s] = bf16_bits(u[j] >> 16);
     }
   }
-  {
-    const float* Sin = states + ((bi * n_chunks + c) * H + h) * int64_t(N) * kP;  // [n][p]
-    for (int i = threadIdx.x; i < NP * kP; i += kSsdThreads) {
-      const int n = i / kP, p = i % kP;
-      St[p][n] = n < N ? to_bf16(Sin[int64_t(n) * kP + p]) : bf16_bits(0);
-    }
-  }
   __syncthreads();
 
-  const int wv = threadIdx.x / kWave, l = threadIdx.x % kWave;
-  const int lr = l % 16, lk = 8 * (l / 16), lq = 4 * (l / 16);
-  const int trow = wv * 16;  // this wave's 16 steps
-  // C fragments of this wave's rows, reused by both products
-  bf16x8 cf[NK];
+  const float cum_t = cum_s[t_own];
+  bf16x8 cf[NK];                     // C rows of this wave's steps, as the operand [k = n][column t]
 #pragma unroll
-  for (int kk = 0; kk < NK; kk++) cf[kk] = lds8(&Cs[trow + lr][kk * 32 + lk]);
+  for (int kk = 0; kk < NK; kk++) cf[kk] = lds8(&Cs[tb * 16 + lr][kk * 32 + lk]);
 
-  // mixing matrix rows trow .. trow + 15: (C B^T) o L
+  // mixing matrix, transposed tiles (rows s, column t): m[sb][r] = M[t_own][16 sb + 4 g + r]
+  float m[kQ / 16][4];
 #pragma unroll
-  for (int cb = 0; cb < kQ / 16; cb++) {
-    if (cb * 16 > trow + 15) break;  // above the diagonal: L is zero
-    f32x4 g = {0.f, 0.f, 0.f, 0.f};
+  for (int sb = 0; sb < kQ / 16; sb++) {
 #pragma unroll
-    for (int kk = 0; kk < NK; kk++) g = mfma(cf[kk], lds8(&Bs[cb * 16 + lr][kk * 32 + lk]), g);
-    const int s = cb * 16 + lr;
-    const float cs = cum_s[s], ds = d_s[s];
+    for (int r = 0; r < 4; r++) m[sb][r] = 0.f;
+    if (sb <= tb) {  // blocks above the diagonal are zero
+      f32x4 g = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < NK; kk++) g = mfma(lds8(&Bs[sb * 16 + lr][kk * 32 + lk]), cf[kk], g);
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const int s = sb * 16 + lq + r;
+        m[sb][r] = (s <= t_own) ? g[r] * exp2_fast((cum_t - cum_s[s]) * kLog2e) * d_s[s] : 0.f;
+      }
+    }
+  }
+  // A operands of the in-chunk product: K block kk covers s in [32 kk, 32 kk + 32) in the order
+  // (4 g + r, 16 + 4 g + r), r = 0..3
+  bf16x8 mf[kQ / 32];
+#pragma unroll
+  for (int kk = 0; kk < kQ / 32; kk++) {
 #pragma unroll
     for (int r = 0; r < 4; r++) {
-      const int t = trow + lq + r;
-      const float m = (s <= t) ? g[r] * exp2_fast((cum_s[t] - cs) * kLog2e) * ds : 0.f;
-      Ms[t][s] = to_bf16(m);
+      mf[kk][r] = static_cast<__bf16>(m[2 * kk][r]);
+      mf[kk][4 + r] = static_cast<__bf16>(m[2 * kk + 1][r]);
     }
   }
-  // columns above the diagonal block row stay zero
-#pragma unroll
-  for (int cb = 0; cb < kQ / 16; cb++) {
-    if (cb * 16 > trow + 15) {
-#pragma unroll
-      for (int r = 0; r < 4; r++) Ms[trow + lq + r][cb * 16 + lr] = bf16_bits(0);
-    }
-  }
-  // the wave reads back rows of the mixing matrix written by its other lanes
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
   const float Dh = HAS_D ? D[h] : 0.f;
+  float row_scale[4];  // exp(cum_t) of this lane's output rows
+#pragma unroll
+  for (int r = 0; r < 4; r++) row_scale[r] = exp2_fast(cum_s[tb * 16 + lq + r] * kLog2e);
 #pragma unroll
   for (int pb = 0; pb < kP / 16; pb++) {
-    // incoming-state part, then scaled by exp(cum_t)
+    const int p = pb * 16 + lr;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // incoming-state part: [t][n] x [n][p]; rows scaled by exp(cum_t)
 #pragma unroll
-    for (int kk = 0; kk < NK; kk++) acc = mfma(cf[kk], lds8(&St[pb * 16 + lr][kk * 32 + lk]), acc);
+    for (int kk = 0; kk < NK; kk++)
+      acc = mfma(cf[kk], sfr[pb][kk], acc);  // the C fragment serves as the A operand [row t][k = n] here
 #pragma unroll
-    for (int r = 0; r < 4; r++) acc[r] *= exp2_fast(cum_s[trow + lq + r] * kLog2e);
-    // in-chunk part
+    for (int r = 0; r < 4; r++) acc[r] *= row_scale[r];
+    // in-chunk part: M [t][s] x X [s][p], s in the permuted order
 #pragma unroll
     for (int kk = 0; kk < kQ / 32; kk++) {
-      if (kk * 32 > trow + 15) break;
-      acc = mfma(lds8(&Ms[trow + lr][kk * 32 + lk]), lds8(&Xt[pb * 16 + lr][kk * 32 + lk]), acc);
+      if (2 * kk > tb) break;  // M is zero there
+      bf16x8 xf;
+      const uint2 lo = *reinterpret_cast<const uint2*>(&Xt[p][kk * 32 + lq]);
+      const uint2 hi = *reinterpret_cast<const uint2*>(&Xt[p][kk * 32 + 16 + lq]);
+      xf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+      acc = mfma(mf[kk], xf, acc);
     }
-    const int p = pb * 16 + lr;
 #pragma unroll
     for (int r = 0; r < 4; r++) {
-      const int t = trow + lq + r;
+      const int t = tb * 16 + lq + r;
       if (t < n_steps) {
         const int64_t idx = (row0 + t) * E + int64_t(h) * kP + p;
         float v = acc[r];
         if (HAS_D) v = fmaf(Dh, from_bf16(Xt[p][t]), v);
-        if (HAS_Z) v *= silu(from_bf16(z[idx]));
+        if (HAS_Z) v *= silu(zv[pb][r]);
         y[idx] = to_bf16(v);
       }
     }
@@ -319,7 +355,7 @@ __global__ __launch_bounds__(256) void ssd_fill_kernel(float* __restrict__ dst, 
 }
 
 template <int NK, bool SOFTPLUS>
-hipError_t run_ssd(const SsdArgs& a, int n_chunks, float* states, float* cum_last) {
+hipError_t run_ssd(const SsdArgs& a, int n_chunks, bf16_bits* states, float* cum_last) {
   const int H = int(a.H), N = int(a.N);
   const int64_t blocks = a.b * n_chunks * H;
   const bf16_bits* x = static_cast<const bf16_bits*>(a.x);
@@ -339,7 +375,7 @@ hipError_t run_ssd(const SsdArgs& a, int n_chunks, float* states, float* cum_las
   bf16_bits* y = static_cast<bf16_bits*>(a.y);
 #define SSM_SSD_SCAN(HZ, HD)                                                                                  \
   return launch_kind(kKindSsdScan, ssd_scan_kernel<NK, SOFTPLUS, HZ, HD>, blocks, kSsdThreads, a.stream, x, dl, \
-                     a.A, B, C, a.D, z, a.bias, (const float*)states, y, a.L, H, N, n_chunks)
+                     a.A, B, C, a.D, z, a.bias, (const bf16_bits*)states, y, a.L, H, N, n_chunks)
   if (a.z) {
     if (a.D) SSM_SSD_SCAN(true, true);
     SSM_SSD_SCAN(true, false);
@@ -350,7 +386,7 @@ hipError_t run_ssd(const SsdArgs& a, int n_chunks, float* states, float* cum_las
 }
 
 template <int NK>
-hipError_t ssd_sp(const SsdArgs& a, int n_chunks, float* states, float* cum_last) {
+hipError_t ssd_sp(const SsdArgs& a, int n_chunks, bf16_bits* states, float* cum_last) {
   return a.softplus ? run_ssd<NK, true>(a, n_chunks, states, cum_last) : run_ssd<NK, false>(a, n_chunks, states, cum_last);
 }
 
@@ -367,13 +403,15 @@ hipError_t launch_ssd(const SsdArgs& a) {
     return launch_kind(kKindSsdCarry, ssd_fill_kernel, (n + 255) / 256, 256, a.stream, a.last_state, a.h0, n);
   }
   const int n_chunks = int((a.L + kQ - 1) / kQ);
+  // workspace: chunk states [b][chunk][h][p][n] in bf16, then the chunks' decay exponents
   const size_t n_states = size_t(a.b) * size_t(n_chunks) * size_t(a.H) * size_t(a.N) * kP;
   const size_t n_cum = size_t(a.b) * size_t(n_chunks) * size_t(a.H);
+  const size_t state_bytes = (n_states * sizeof(bf16_bits) + 255) / 256 * 256;
   void* ws = nullptr;
-  hipError_t err = hipMallocAsync(&ws, (n_states + n_cum) * sizeof(float), a.stream);
+  hipError_t err = hipMallocAsync(&ws, state_bytes + n_cum * sizeof(float), a.stream);
   if (err != hipSuccess) return err;
-  float* states = static_cast<float*>(ws);
-  float* cum_last = states + n_states;
+  bf16_bits* states = static_cast<bf16_bits*>(ws);
+  float* cum_last = reinterpret_cast<float*>(static_cast<char*>(ws) + state_bytes);
   const int nk = int((a.N + 31) / 32);
   switch (nk) {
     case 1: err = ssd_sp<1>(a, n_chunks, states, cum_last); break;
