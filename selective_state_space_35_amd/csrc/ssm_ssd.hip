@@ -52,6 +52,12 @@ __device__ __forceinline__ bf16x8 lds8(const bf16_bits* p) { return *reinterpret
 __device__ __forceinline__ bf16_bits to_bf16(float v) { return __builtin_bit_cast(bf16_bits, static_cast<__bf16>(v)); }
 __device__ __forceinline__ float from_bf16(bf16_bits v) { return __uint_as_float(uint32_t(v) << 16); }
 
+// Column index of element k in row r of a transposed tile: 8-element (16-byte)
+// blocks are XOR-swizzled by (r / 8) mod 8, so the transposed writes of eight
+// rows r, r + 8, ... land in different LDS banks, while every 16-byte block
+// (all an MFMA fragment reads) stays contiguous.
+__device__ __forceinline__ int swz(int r, int k) { return (((k >> 3) ^ ((r >> 3) & 7)) << 3) | (k & 7); }
+
 // Steps and their running sums inside the chunk: d[s] (0 past the end) and
 // cum[s] = A_h * (d_0 + ... + d_s), computed by the first wave.
 template <bool SOFTPLUS>
@@ -119,8 +125,8 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_state_kernel(
     const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-      Bt[n8 + 2 * j][s] = bf16_bits(u[j] & 0xffff);
-      Bt[n8 + 2 * j + 1][s] = bf16_bits(u[j] >> 16);
+      Bt[n8 + 2 * j][swz(n8 + 2 * j, s)] = bf16_bits(u[j] & 0xffff);
+      Bt[n8 + 2 * j + 1][swz(n8 + 2 * j + 1, s)] = bf16_bits(u[j] >> 16);
     }
   }
   __syncthreads();
@@ -133,8 +139,8 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_state_kernel(
     const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-      Xw[p8 + 2 * j][s] = to_bf16(from_bf16(bf16_bits(u[j] & 0xffff)) * w);
-      Xw[p8 + 2 * j + 1][s] = to_bf16(from_bf16(bf16_bits(u[j] >> 16)) * w);
+      Xw[p8 + 2 * j][swz(p8 + 2 * j, s)] = to_bf16(from_bf16(bf16_bits(u[j] & 0xffff)) * w);
+      Xw[p8 + 2 * j + 1][swz(p8 + 2 * j + 1, s)] = to_bf16(from_bf16(bf16_bits(u[j] >> 16)) * w);
     }
   }
   __syncthreads();
@@ -144,13 +150,14 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_state_kernel(
   bf16_bits* out = states + ((bi * n_chunks + c) * H + h) * int64_t(kP) * N;  // [p][n]
   bf16x8 xf[kQ / 32];
 #pragma unroll
-  for (int kk = 0; kk < kQ / 32; kk++) xf[kk] = lds8(&Xw[wv * 16 + lr][kk * 32 + lk]);
+  for (int kk = 0; kk < kQ / 32; kk++) xf[kk] = lds8(&Xw[wv * 16 + lr][swz(wv * 16 + lr, kk * 32 + lk)]);
 #pragma unroll
   for (int nb = 0; nb < NP / 16; nb++) {
     if (nb * 16 >= N) break;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < kQ / 32; kk++) acc = mfma(xf[kk], lds8(&Bt[nb * 16 + lr][kk * 32 + lk]), acc);
+    for (int kk = 0; kk < kQ / 32; kk++)
+      acc = mfma(xf[kk], lds8(&Bt[nb * 16 + lr][swz(nb * 16 + lr, kk * 32 + lk)]), acc);
 #pragma unroll
     for (int r = 0; r < 4; r++) out[int64_t(wv * 16 + 4 * (l / 16) + r) * N + nb * 16 + lr] = to_bf16(acc[r]);
   }
