@@ -39,6 +39,7 @@ namespace {
 constexpr int kQ = 64;           // steps per chunk
 constexpr int kP = 64;           // channels per head
 constexpr int kSsdThreads = 256; // 4 waves
+static_assert(kSsdThreads == 4 * kQ, "a thread per (pair of steps, 8 channels) of a chunk");
 constexpr int kPad = 8;          // bf16 elements added to every LDS row (breaks bank aliasing)
 
 typedef __attribute__((ext_vector_type(4))) float f32x4;
@@ -58,19 +59,23 @@ __device__ __forceinline__ float from_bf16(bf16_bits v) { return __uint_as_float
 // (all an MFMA fragment reads) stays contiguous.
 __device__ __forceinline__ int swz(int r, int k) { return (((k >> 3) ^ ((r >> 3) & 7)) << 3) | (k & 7); }
 
-// Steps and their running sums inside the chunk: d[s] (0 past the end) and
-// cum[s] = A_h * (d_0 + ... + d_s), computed by the first wave.
+// Raw step of lane s of the first wave (delta + bias; 0 past the end of the
+// sequence), read early so its latency overlaps the other loads of the chunk.
+__device__ __forceinline__ float step_input(const bf16_bits* __restrict__ delta, const float* __restrict__ bias,
+                                            int64_t row0, int H, int h, int n_steps) {
+  const int s = threadIdx.x;
+  if (s >= kWave || s >= n_steps) return 0.f;
+  return from_bf16(delta[(row0 + s) * H + h]) + (bias ? bias[h] : 0.f);
+}
+
+// Steps and their running sums inside the chunk, by the first wave: d[s] (0 past
+// the end) and cum[s] = A_h * (d_0 + ... + d_s), written to LDS.
 template <bool SOFTPLUS>
-__device__ __forceinline__ void chunk_steps(const bf16_bits* __restrict__ delta, const float* __restrict__ bias,
-                                            float Ah, int64_t row0, int H, int h, int n_steps, float* d_s,
-                                            float* cum_s) {
+__device__ __forceinline__ void chunk_steps(float raw, float Ah, int n_steps, float* d_s, float* cum_s) {
+  static_assert(kQ == kWave, "one step per lane of the first wave");
   if (threadIdx.x < kWave) {
     const int s = threadIdx.x;
-    float d = 0.f;
-    if (s < n_steps) {
-      d = from_bf16(delta[(row0 + s) * H + h]) + (bias ? bias[h] : 0.f);
-      if (SOFTPLUS) d = softplus(d);
-    }
+    const float d = s < n_steps ? (SOFTPLUS ? softplus(raw) : raw) : 0.f;
     float c = d * Ah;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
@@ -82,22 +87,39 @@ __device__ __forceinline__ void chunk_steps(const bf16_bits* __restrict__ delta,
   }
 }
 
-// [rows x cols] bf16 tile of a row-major global matrix (row stride ld elements,
-// 16-byte aligned rows, cols a multiple of 8) into LDS with row stride lds_ld;
-// rows >= valid_rows and columns >= valid_cols are zero.
-__device__ __forceinline__ void stage_rows(const bf16_bits* __restrict__ src, int64_t ld, int rows, int valid_rows,
-                                           int cols, int valid_cols, bf16_bits* dst, int lds_ld) {
-  const int per_row = cols / 8;
-  for (int i = threadIdx.x; i < rows * per_row; i += kSsdThreads) {
-    const int r = i / per_row, c8 = (i % per_row) * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r < valid_rows && c8 < valid_cols) v = *reinterpret_cast<const uint4*>(src + r * ld + c8);
-    *reinterpret_cast<uint4*>(dst + r * lds_ld + c8) = v;
+__device__ __forceinline__ uint4 ld16(const bf16_bits* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  return uint32_t(to_bf16(lo)) | (uint32_t(to_bf16(hi)) << 16);
+}
+// the 8 bf16 of v, each times w, rounded back to bf16
+__device__ __forceinline__ uint4 scale8(uint4 v, float w) {
+  const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++)
+    o[j] = pack2(__uint_as_float(u[j] << 16) * w, __uint_as_float(u[j] & 0xffff0000u) * w);
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// Rows s and s + 1 (s even) of columns c8 .. c8 + 7 (c8 a multiple of 8), given
+// as two 16-byte vectors, stored transposed into T (row stride ld): T[c8 + e][s]
+// and T[c8 + e][s + 1] go out as one 32-bit word, in the swizzled column blocks
+// of swz (the same for all 8 rows, which share r / 8).
+__device__ __forceinline__ void store_pair_t(bf16_bits* T, int ld, int c8, int s, uint4 a, uint4 b) {
+  const uint32_t ua[4] = {a.x, a.y, a.z, a.w}, ub[4] = {b.x, b.y, b.z, b.w};
+  bf16_bits* col = T + swz(c8, s);
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    *reinterpret_cast<uint32_t*>(col + (c8 + 2 * j) * ld) = (ua[j] & 0xffffu) | (ub[j] << 16);
+    *reinterpret_cast<uint32_t*>(col + (c8 + 2 * j + 1) * ld) = (ua[j] >> 16) | (ub[j] & 0xffff0000u);
   }
 }
 
 // ---------------------------------------------------------------------------
 // chunk state, transposed: S_c[p, n] = sum_s (w o X)[s, p] B[s, n]  (bf16 out)
+// Every global read of the chunk is issued first (B and x as pairs of rows, so
+// the transposed LDS tiles are written one 32-bit word per two steps); the
+// result goes back through LDS and out in whole 16-byte row pieces.
 // ---------------------------------------------------------------------------
 template <int NK, bool SOFTPLUS>  // NK: the state size padded to a multiple of 32, in units of 32
 __global__ __launch_bounds__(kSsdThreads) void ssd_state_kernel(
@@ -105,9 +127,17 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_state_kernel(
     const bf16_bits* __restrict__ B, const float* __restrict__ bias, bf16_bits* __restrict__ states,
     float* __restrict__ cum_last, int64_t L, int H, int N, int n_chunks) {
   constexpr int NP = NK * 32;
+  constexpr int kBV = kQ / 2 * (NP / 8);  // (row pair, 16-byte column block) items of B
+  constexpr int nBV = (kBV + kSsdThreads - 1) / kSsdThreads;
+  constexpr int kTileB = NP * (kQ + kPad) + kP * (kQ + kPad);  // Bt then Xw, bf16 elements
+  constexpr int kOutB = kP * (NP + kPad);                      // the result [p][n], over them afterwards
+  static_assert(kOutB <= kTileB, "result tile fits over the operand tiles");
   __shared__ float d_s[kQ], cum_s[kQ];
-  __shared__ __attribute__((aligned(16))) bf16_bits Bt[NP][kQ + kPad];   // B transposed: [n][s]
-  __shared__ __attribute__((aligned(16))) bf16_bits Xw[kP][kQ + kPad];   // (w o X) transposed: [p][s]
+  __shared__ __attribute__((aligned(16))) bf16_bits pool[kTileB];
+  bf16_bits* Bt = pool;                         // B transposed: [n][s]
+  bf16_bits* Xw = pool + NP * (kQ + kPad);      // (w o X) transposed: [p][s]
+  bf16_bits* So = pool;                         // result [p][n]
+  constexpr int ldt = kQ + kPad, ldo = NP + kPad;
   const int h = blockIdx.x % H;
   const int rest = blockIdx.x / H;
   const int c = rest % n_chunks;
@@ -116,50 +146,60 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_state_kernel(
   const int n_steps = int(std::min<int64_t>(kQ, L - t0));
   const int64_t row0 = bi * L + t0;
   const int64_t E = int64_t(H) * kP;
-  chunk_steps<SOFTPLUS>(delta, bias, A[h], row0, H, h, n_steps, d_s, cum_s);
-  // B^T: 16-byte row reads, transposed writes
-  for (int i = threadIdx.x; i < kQ * (NP / 8); i += kSsdThreads) {
-    const int s = i / (NP / 8), n8 = (i % (NP / 8)) * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (s < n_steps && n8 < N) v = *reinterpret_cast<const uint4*>(B + (row0 + s) * N + n8);
-    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+  const uint4 zero = make_uint4(0, 0, 0, 0);
+  // this thread's x rows s0, s0 + 1 and channels p8 .. p8 + 7
+  const int s0 = 2 * (threadIdx.x >> 3), p8 = (threadIdx.x & 7) * 8;
+  const bf16_bits* xr = x + (row0 + s0) * E + int64_t(h) * kP + p8;
+  const uint4 x0 = s0 < n_steps ? ld16(xr) : zero;
+  const uint4 x1 = s0 + 1 < n_steps ? ld16(xr + E) : zero;
+  uint4 b0[nBV], b1[nBV];
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      Bt[n8 + 2 * j][swz(n8 + 2 * j, s)] = bf16_bits(u[j] & 0xffff);
-      Bt[n8 + 2 * j + 1][swz(n8 + 2 * j + 1, s)] = bf16_bits(u[j] >> 16);
-    }
+  for (int k = 0; k < nBV; k++) {
+    const int v = threadIdx.x + k * kSsdThreads;
+    const int sp = 2 * (v / (NP / 8)), n8 = (v % (NP / 8)) * 8;
+    const bool ok = v < kBV && n8 < N;
+    b0[k] = ok && sp < n_steps ? ld16(B + (row0 + sp) * N + n8) : zero;
+    b1[k] = ok && sp + 1 < n_steps ? ld16(B + (row0 + sp + 1) * N + n8) : zero;
+  }
+  const float raw = step_input(delta, bias, row0, H, h, n_steps);
+  chunk_steps<SOFTPLUS>(raw, A[h], n_steps, d_s, cum_s);
+#pragma unroll
+  for (int k = 0; k < nBV; k++) {
+    const int v = threadIdx.x + k * kSsdThreads;
+    if (v < kBV) store_pair_t(Bt, ldt, (v % (NP / 8)) * 8, 2 * (v / (NP / 8)), b0[k], b1[k]);
   }
   __syncthreads();
   const float last = cum_s[kQ - 1];
-  for (int i = threadIdx.x; i < kQ * (kP / 8); i += kSsdThreads) {
-    const int s = i / (kP / 8), p8 = (i % (kP / 8)) * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (s < n_steps) v = *reinterpret_cast<const uint4*>(x + (row0 + s) * E + int64_t(h) * kP + p8);
-    const float w = exp2_fast((last - cum_s[s]) * kLog2e) * d_s[s];
-    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      Xw[p8 + 2 * j][swz(p8 + 2 * j, s)] = to_bf16(from_bf16(bf16_bits(u[j] & 0xffff)) * w);
-      Xw[p8 + 2 * j + 1][swz(p8 + 2 * j + 1, s)] = to_bf16(from_bf16(bf16_bits(u[j] >> 16)) * w);
-    }
-  }
+  const float w0 = exp2_fast((last - cum_s[s0]) * kLog2e) * d_s[s0];
+  const float w1 = exp2_fast((last - cum_s[s0 + 1]) * kLog2e) * d_s[s0 + 1];
+  store_pair_t(Xw, ldt, p8, s0, scale8(x0, w0), scale8(x1, w1));
   __syncthreads();
   // wave w: rows p in [16 w, 16 w + 16), every 16-column block of n
   const int wv = threadIdx.x / kWave, l = threadIdx.x % kWave;
   const int lr = l % 16, lk = 8 * (l / 16);
-  bf16_bits* out = states + ((bi * n_chunks + c) * H + h) * int64_t(kP) * N;  // [p][n]
   bf16x8 xf[kQ / 32];
 #pragma unroll
-  for (int kk = 0; kk < kQ / 32; kk++) xf[kk] = lds8(&Xw[wv * 16 + lr][swz(wv * 16 + lr, kk * 32 + lk)]);
+  for (int kk = 0; kk < kQ / 32; kk++) xf[kk] = lds8(&Xw[(wv * 16 + lr) * ldt + swz(wv * 16 + lr, kk * 32 + lk)]);
+  f32x4 acc[NP / 16];
 #pragma unroll
   for (int nb = 0; nb < NP / 16; nb++) {
-    if (nb * 16 >= N) break;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (nb * 16 < N) {
 #pragma unroll
-    for (int kk = 0; kk < kQ / 32; kk++)
-      acc = mfma(xf[kk], lds8(&Bt[nb * 16 + lr][swz(nb * 16 + lr, kk * 32 + lk)]), acc);
+      for (int kk = 0; kk < kQ / 32; kk++)
+        acc[nb] = mfma(xf[kk], lds8(&Bt[(nb * 16 + lr) * ldt + swz(nb * 16 + lr, kk * 32 + lk)]), acc[nb]);
+    }
+  }
+  __syncthreads();  // every wave is done with Bt and Xw before the result goes over them
 #pragma unroll
-    for (int r = 0; r < 4; r++) out[int64_t(wv * 16 + 4 * (l / 16) + r) * N + nb * 16 + lr] = to_bf16(acc[r]);
+  for (int nb = 0; nb < NP / 16; nb++)
+#pragma unroll
+    for (int r = 0; r < 4; r++) So[(wv * 16 + 4 * (l / 16) + r) * ldo + nb * 16 + lr] = to_bf16(acc[nb][r]);
+  __syncthreads();
+  bf16_bits* out = states + ((bi * n_chunks + c) * H + h) * int64_t(kP) * N;  // [p][n]
+  for (int v = threadIdx.x; v < kP * (NP / 8); v += kSsdThreads) {
+    const int p = v / (NP / 8), n8 = (v % (NP / 8)) * 8;
+    if (n8 < N) *reinterpret_cast<uint4*>(out + int64_t(p) * N + n8) = *reinterpret_cast<const uint4*>(&So[p * ldo + n8]);
   }
   if (threadIdx.x == 0) cum_last[(bi * n_chunks + c) * H + h] = last;
 }
@@ -217,6 +257,11 @@ __global__ __launch_bounds__(256) void ssd_carry_kernel(bf16_bits* states, const
 // product directly, with the contraction index s in the order the transposed
 // tiles give it (s = 4 g + r and 16 + 4 g + r for lane group g); X is read in
 // the same order.
+// Every global read of the chunk (x, z, C, B, the incoming state, the steps) is
+// issued before anything else.  x, z and y are handled per thread as two rows
+// of 8 channels (16-byte accesses); the products' results go through an fp32
+// LDS tile laid over the C and B tiles, and D x and the gate are applied with
+// the thread's own x and z.
 // ---------------------------------------------------------------------------
 template <int NK, bool SOFTPLUS, bool HAS_Z, bool HAS_D>
 __global__ __launch_bounds__(kSsdThreads) void ssd_scan_kernel(
@@ -225,10 +270,22 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_scan_kernel(
     const bf16_bits* __restrict__ z, const float* __restrict__ bias, const bf16_bits* __restrict__ states,
     bf16_bits* __restrict__ y, int64_t L, int H, int N, int n_chunks) {
   constexpr int NP = NK * 32;
+  constexpr int ldr = NP + kPad;          // C, B and incoming-state tiles, bf16 elements per row
+  constexpr int ldt = kQ + kPad;          // X transposed
+  constexpr int ldy = kP + 4;             // fp32 result tile
+  constexpr int kCV = kQ * (NP / 8);      // 16-byte pieces of a C or B tile
+  constexpr int kSV = kP * (NP / 8);      // 16-byte pieces of the incoming state
+  constexpr int nCV = (kCV + kSsdThreads - 1) / kSsdThreads;
+  constexpr int nSV = (kSV + kSsdThreads - 1) / kSsdThreads;
+  constexpr int kCBbytes = 2 * kQ * ldr * 2;
+  constexpr int kYbytes = kQ * ldy * 4;
   __shared__ float d_s[kQ], cum_s[kQ];
-  __shared__ __attribute__((aligned(16))) bf16_bits Cs[kQ][NP + kPad];    // C rows [t][n]
-  __shared__ __attribute__((aligned(16))) bf16_bits Bs[kQ][NP + kPad];    // B rows [s][n]
-  __shared__ __attribute__((aligned(16))) bf16_bits Xt[kP][kQ + kPad];    // X transposed [p][s]
+  __shared__ __attribute__((aligned(16))) bf16_bits Xt[kP * ldt];   // X transposed [p][s]
+  __shared__ __attribute__((aligned(16))) bf16_bits Ss[kP * ldr];   // incoming state [p][n]
+  __shared__ __attribute__((aligned(16))) char pool[kCBbytes > kYbytes ? kCBbytes : kYbytes];
+  bf16_bits* Cs = reinterpret_cast<bf16_bits*>(pool);                // C rows [t][n]
+  bf16_bits* Bs = Cs + kQ * ldr;                                     // B rows [s][n]
+  float* Ys = reinterpret_cast<float*>(pool);                        // results [t][p], after C and B
   const int h = blockIdx.x % H;
   const int rest = blockIdx.x / H;
   const int c = rest % n_chunks;
@@ -237,56 +294,64 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_scan_kernel(
   const int n_steps = int(std::min<int64_t>(kQ, L - t0));
   const int64_t row0 = bi * L + t0;
   const int64_t E = int64_t(H) * kP;
+  const uint4 zero = make_uint4(0, 0, 0, 0);
+
+  // ---- global reads ----
+  const int s0 = 2 * (threadIdx.x >> 3), p8 = (threadIdx.x & 7) * 8;  // this thread's rows and channels
+  const int64_t xo = (row0 + s0) * E + int64_t(h) * kP + p8;
+  const uint4 x0 = s0 < n_steps ? ld16(x + xo) : zero;
+  const uint4 x1 = s0 + 1 < n_steps ? ld16(x + xo + E) : zero;
+  uint4 z0 = zero, z1 = zero;
+  if (HAS_Z) {
+    if (s0 < n_steps) z0 = ld16(z + xo);
+    if (s0 + 1 < n_steps) z1 = ld16(z + xo + E);
+  }
+  uint4 cv[nCV], bv[nCV];
+#pragma unroll
+  for (int k = 0; k < nCV; k++) {
+    const int v = threadIdx.x + k * kSsdThreads;
+    const int r = v / (NP / 8), n8 = (v % (NP / 8)) * 8;
+    const bool ok = v < kCV && r < n_steps && n8 < N;
+    cv[k] = ok ? ld16(C + (row0 + r) * N + n8) : zero;
+    bv[k] = ok ? ld16(B + (row0 + r) * N + n8) : zero;
+  }
+  const bf16_bits* Sin = states + ((bi * n_chunks + c) * H + h) * int64_t(kP) * N;
+  uint4 sv[nSV];
+#pragma unroll
+  for (int k = 0; k < nSV; k++) {
+    const int v = threadIdx.x + k * kSsdThreads;
+    const int p = v / (NP / 8), n8 = (v % (NP / 8)) * 8;
+    sv[k] = v < kSV && n8 < N ? ld16(Sin + int64_t(p) * N + n8) : zero;
+  }
+  const float raw = step_input(delta, bias, row0, H, h, n_steps);
+
+  // ---- LDS tiles ----
+  chunk_steps<SOFTPLUS>(raw, A[h], n_steps, d_s, cum_s);
+#pragma unroll
+  for (int k = 0; k < nCV; k++) {
+    const int v = threadIdx.x + k * kSsdThreads;
+    if (v < kCV) {
+      const int o = (v / (NP / 8)) * ldr + (v % (NP / 8)) * 8;
+      *reinterpret_cast<uint4*>(Cs + o) = cv[k];
+      *reinterpret_cast<uint4*>(Bs + o) = bv[k];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < nSV; k++) {
+    const int v = threadIdx.x + k * kSsdThreads;
+    if (v < kSV) *reinterpret_cast<uint4*>(Ss + (v / (NP / 8)) * ldr + (v % (NP / 8)) * 8) = sv[k];
+  }
+  store_pair_t(Xt, ldt, p8, s0, x0, x1);
+  __syncthreads();
+
   const int wv = threadIdx.x / kWave, l = threadIdx.x % kWave;
   const int lr = l % 16, lg = l / 16, lk = 8 * lg, lq = 4 * lg;
   const int tb = wv;                 // this wave's step block
   const int t_own = tb * 16 + lr;    // the step this lane carries through the mixing product
-  // Global reads this lane needs later are issued first, so their latency overlaps
-  // the staging and the mixing matrix: the gate of its outputs and the incoming
-  // state's fragments ([p][n] bf16).
-  float zv[kP / 16][4];
-  if (HAS_Z) {
-#pragma unroll
-    for (int pb = 0; pb < kP / 16; pb++)
-#pragma unroll
-      for (int r = 0; r < 4; r++) {
-        const int t = tb * 16 + lq + r;
-        zv[pb][r] = t < n_steps ? from_bf16(z[(row0 + t) * E + int64_t(h) * kP + pb * 16 + lr]) : 0.f;
-      }
-  }
-  const bf16_bits* Sin = states + ((bi * n_chunks + c) * H + h) * int64_t(kP) * N;
-  bf16x8 sfr[kP / 16][NK];
-#pragma unroll
-  for (int pb = 0; pb < kP / 16; pb++)
-#pragma unroll
-    for (int kk = 0; kk < NK; kk++) {
-      if (kk * 32 + lk < N) {
-        sfr[pb][kk] = *reinterpret_cast<const bf16x8*>(Sin + int64_t(pb * 16 + lr) * N + kk * 32 + lk);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; j++) sfr[pb][kk][j] = static_cast<__bf16>(0.f);
-      }
-    }
-  chunk_steps<SOFTPLUS>(delta, bias, A[h], row0, H, h, n_steps, d_s, cum_s);
-  stage_rows(C + row0 * N, N, kQ, n_steps, NP, N, &Cs[0][0], NP + kPad);
-  stage_rows(B + row0 * N, N, kQ, n_steps, NP, N, &Bs[0][0], NP + kPad);
-  for (int i = threadIdx.x; i < kQ * (kP / 8); i += kSsdThreads) {
-    const int s = i / (kP / 8), p8 = (i % (kP / 8)) * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (s < n_steps) v = *reinterpret_cast<const uint4*>(x + (row0 + s) * E + int64_t(h) * kP + p8);
-    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      Xt[p8 + 2 * j][s] = bf16_bits(u[j] & 0xffff);
-      Xt[p8 + 2 * j + 1][s] = bf16_bits(u[j] >> 16);
-    }
-  }
-  __syncthreads();
-
   const float cum_t = cum_s[t_own];
   bf16x8 cf[NK];                     // C rows of this wave's steps, as the operand [k = n][column t]
 #pragma unroll
-  for (int kk = 0; kk < NK; kk++) cf[kk] = lds8(&Cs[tb * 16 + lr][kk * 32 + lk]);
+  for (int kk = 0; kk < NK; kk++) cf[kk] = lds8(&Cs[t_own * ldr + kk * 32 + lk]);
 
   // mixing matrix, transposed tiles (rows s, column t): m[sb][r] = M[t_own][16 sb + 4 g + r]
   float m[kQ / 16][4];
@@ -297,7 +362,7 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_scan_kernel(
     if (sb <= tb) {  // blocks above the diagonal are zero
       f32x4 g = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < NK; kk++) g = mfma(lds8(&Bs[sb * 16 + lr][kk * 32 + lk]), cf[kk], g);
+      for (int kk = 0; kk < NK; kk++) g = mfma(lds8(&Bs[(sb * 16 + lr) * ldr + kk * 32 + lk]), cf[kk], g);
 #pragma unroll
       for (int r = 0; r < 4; r++) {
         const int s = sb * 16 + lq + r;
@@ -316,40 +381,66 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_scan_kernel(
       mf[kk][4 + r] = static_cast<__bf16>(m[2 * kk + 1][r]);
     }
   }
-  const float Dh = HAS_D ? D[h] : 0.f;
   float row_scale[4];  // exp(cum_t) of this lane's output rows
 #pragma unroll
   for (int r = 0; r < 4; r++) row_scale[r] = exp2_fast(cum_s[tb * 16 + lq + r] * kLog2e);
+  f32x4 acc[kP / 16];
 #pragma unroll
   for (int pb = 0; pb < kP / 16; pb++) {
     const int p = pb * 16 + lr;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
     // incoming-state part: [t][n] x [n][p]; rows scaled by exp(cum_t)
 #pragma unroll
-    for (int kk = 0; kk < NK; kk++)
-      acc = mfma(cf[kk], sfr[pb][kk], acc);  // the C fragment serves as the A operand [row t][k = n] here
+    for (int kk = 0; kk < NK; kk++)  // the C fragment serves as the A operand [row t][k = n] here
+      acc[pb] = mfma(cf[kk], lds8(&Ss[p * ldr + kk * 32 + lk]), acc[pb]);
 #pragma unroll
-    for (int r = 0; r < 4; r++) acc[r] *= row_scale[r];
+    for (int r = 0; r < 4; r++) acc[pb][r] *= row_scale[r];
     // in-chunk part: M [t][s] x X [s][p], s in the permuted order
 #pragma unroll
     for (int kk = 0; kk < kQ / 32; kk++) {
       if (2 * kk > tb) break;  // M is zero there
-      bf16x8 xf;
-      const uint2 lo = *reinterpret_cast<const uint2*>(&Xt[p][kk * 32 + lq]);
-      const uint2 hi = *reinterpret_cast<const uint2*>(&Xt[p][kk * 32 + 16 + lq]);
-      xf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-      acc = mfma(mf[kk], xf, acc);
+      const uint2 lo = *reinterpret_cast<const uint2*>(&Xt[p * ldt + swz(p, kk * 32 + lq)]);
+      const uint2 hi = *reinterpret_cast<const uint2*>(&Xt[p * ldt + swz(p, kk * 32 + 16 + lq)]);
+      acc[pb] = mfma(mf[kk], __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y)), acc[pb]);
     }
+  }
+  __syncthreads();  // every wave is done with C and B before the results go over them
+  // Volatile: hipcc (ROCm 7.2) pairs two of these 16 stores into one ds_write2_b32 with
+  // the first offset divided by 4 twice (816 bytes encoded as 51 dwords), so rows
+  // t = 3 mod 4 of the first 16 channels were never written.  Single stores avoid it.
+  volatile float* Yv = Ys;
 #pragma unroll
-    for (int r = 0; r < 4; r++) {
-      const int t = tb * 16 + lq + r;
-      if (t < n_steps) {
-        const int64_t idx = (row0 + t) * E + int64_t(h) * kP + p;
-        float v = acc[r];
-        if (HAS_D) v = fmaf(Dh, from_bf16(Xt[p][t]), v);
-        if (HAS_Z) v *= silu(zv[pb][r]);
-        y[idx] = to_bf16(v);
+  for (int pb = 0; pb < kP / 16; pb++)
+#pragma unroll
+    for (int r = 0; r < 4; r++) Yv[(tb * 16 + lq + r) * ldy + pb * 16 + lr] = acc[pb][r];
+  __syncthreads();
+
+  // ---- D x, gate, bf16 rows out ----
+  const float Dh = HAS_D ? D[h] : 0.f;
+#pragma unroll
+  for (int j = 0; j < 2; j++) {
+    const int s = s0 + j;
+    if (s < n_steps) {
+      const float4 a = *reinterpret_cast<const float4*>(&Ys[s * ldy + p8]);
+      const float4 b = *reinterpret_cast<const float4*>(&Ys[s * ldy + p8 + 4]);
+      float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      const uint4 xv = j ? x1 : x0, zv = j ? z1 : z0;
+      const uint32_t xu[4] = {xv.x, xv.y, xv.z, xv.w}, zu[4] = {zv.x, zv.y, zv.z, zv.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        float lo = v[2 * q], hi = v[2 * q + 1];
+        if (HAS_D) {
+          lo = fmaf(Dh, __uint_as_float(xu[q] << 16), lo);
+          hi = fmaf(Dh, __uint_as_float(xu[q] & 0xffff0000u), hi);
+        }
+        if (HAS_Z) {
+          lo *= silu(__uint_as_float(zu[q] << 16));
+          hi *= silu(__uint_as_float(zu[q] & 0xffff0000u));
+        }
+        o[q] = pack2(lo, hi);
       }
+      *reinterpret_cast<uint4*>(y + xo + int64_t(j) * E) = make_uint4(o[0], o[1], o[2], o[3]);
     }
   }
 }
