@@ -1,0 +1,100 @@
+"""Guard against a hipcc miscompile of paired LDS accesses (CPU only: compiles, runs nothing).
+
+hipcc's load/store optimizer (ROCm 7.2) merges two LDS accesses from one base
+register into a single ds_read2/ds_write2 whose offsets are in element units.
+In one of our kernels it emitted the first offset divided by the element size
+twice (816 bytes -> 51 dwords instead of 204), so a store silently went to the
+wrong address.  The kernel now avoids that pairing; this test recompiles every
+source with the machine IR printed before and after that pass and checks that
+each merged pair addresses exactly the two bytes offsets it replaced (directly,
+or from a new base register = old base + constant).
+"""
+import os
+import re
+import shutil
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "selective_state_space_35_amd", "csrc")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+SOURCES = ["ssm_kernels.hip", "ssm_conv.hip", "ssm_bwd.hip", "ssm_ssd.hip"]
+PASS = "si-load-store-opt"
+
+SINGLE = re.compile(r"DS_(?:WRITE|READ)_B(?:32|64)(?:_gfx9)? (.*?):: \((?:store|load) \(s(?:32|64)\) "
+                    r"(?:into|from) (%ir\.[\w.]+)")
+PAIR = re.compile(r"(DS_(?:WRITE|READ)2(ST64)?_B(32|64)(?:_gfx9)?) (.*?):: \((?:store|load) \(s\d+\) "
+                  r"(?:into|from) (%ir\.[\w.]+).*?\((?:store|load) \(s\d+\) (?:into|from) (%ir\.[\w.]+)")
+CONST = re.compile(r"\s*(%\d+):\w+ = (?:S_MOV_B32|V_MOV_B32_e32) (-?\d+)\b")
+ADD = re.compile(r"\s*(%\d+):vgpr_32 = (?:nuw |nsw )*V_ADD_U32_e64 (?:killed )?(%\d+):\w+, (?:killed )?(%\d+):\w+")
+
+
+def _mir(src, when):
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}", "--cuda-device-only", "-S",
+           "-o", os.devnull, os.path.join(CSRC, src), "-mllvm", f"-print-{when}={PASS}"]
+    r = subprocess.run(cmd, capture_output=True, text=True, cwd="/tmp")
+    assert r.returncode == 0, r.stderr[-2000:]
+    out = {}
+    for blk in re.split(r"# \*\*\* IR Dump (?:Before|After) ", r.stdout + r.stderr)[1:]:
+        m = re.search(r"# Machine code for function (\S+):", blk)
+        if m:
+            out[m.group(1).rstrip(":")] = blk
+    return out
+
+
+def _operands(text):
+    ops = [o.replace("killed ", "").strip() for o in text.split(",")]
+    return ops, [int(o) for o in ops if re.fullmatch(r"-?\d+", o)]
+
+
+def _check(src):
+    with ThreadPoolExecutor(2) as ex:
+        before, after = ex.map(lambda w: _mir(src, w), ("before", "after"))
+    merged, problems = 0, []
+    for fn, mir in after.items():
+        orig = {}  # memory operand -> (address register, byte offset)
+        for line in before.get(fn, "").splitlines():
+            m = SINGLE.search(line)
+            if m:
+                ops, nums = _operands(m.group(1))
+                orig[m.group(2)] = (ops[0].split(":")[0], nums[-2] % 65536)
+        consts = {m.group(1): int(m.group(2)) for m in map(CONST.match, mir.splitlines()) if m}
+        rebase = {}
+        for m in map(ADD.match, mir.splitlines()):
+            if m and m.group(3) in consts:
+                rebase[m.group(1)] = (m.group(2), consts[m.group(3)])
+            elif m and m.group(2) in consts:
+                rebase[m.group(1)] = (m.group(3), consts[m.group(2)])
+        for line in mir.splitlines():
+            m = PAIR.search(line)
+            if not m or m.group(5) not in orig or m.group(6) not in orig:
+                continue
+            merged += 1
+            elt = int(m.group(3)) // 8 * (64 if m.group(2) else 1)
+            ops, nums = _operands(m.group(4))
+            base, o0, o1 = ops[0].split(":")[0], nums[-3], nums[-2]
+            (b0, want0), (b1, want1) = orig[m.group(5)], orig[m.group(6)]
+            k = 0
+            if base != b0:
+                base, k = rebase.get(base, (base, 0))
+            if base != b0 or b0 != b1:
+                problems.append(f"{fn}: {m.group(1)} from an unresolved base register")
+                continue
+            got = sorted([(o0 * elt + k) % (1 << 32), (o1 * elt + k) % (1 << 32)])
+            if got != sorted([want0, want1]):
+                problems.append(f"{fn}: {m.group(1)} offsets ({o0}, {o1}) x {elt} + {k} for byte offsets "
+                                f"({want0}, {want1})")
+    return merged, problems
+
+
+@pytest.mark.skipif(not shutil.which(HIPCC) and not os.path.exists(HIPCC), reason="hipcc not installed")
+def test_merged_lds_accesses_keep_their_offsets():
+    with ThreadPoolExecutor(len(SOURCES)) as ex:
+        results = dict(zip(SOURCES, ex.map(_check, SOURCES)))
+    problems = [p for _, (_, ps) in results.items() for p in ps]
+    assert not problems, "\n".join(problems[:20])
+    # the kernels that stage through LDS do get merged accesses: the check is not vacuous
+    assert results["ssm_ssd.hip"][0] > 100 and results["ssm_bwd.hip"][0] > 10, {k: v[0] for k, v in results.items()}
