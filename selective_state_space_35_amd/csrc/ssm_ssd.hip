@@ -36,10 +36,14 @@
 namespace ssm {
 namespace {
 
-constexpr int kQ = 64;           // steps per chunk
-constexpr int kP = 64;           // channels per head
-constexpr int kSsdThreads = 256; // 4 waves
-static_assert(kSsdThreads == 4 * kQ, "a thread per (pair of steps, 8 channels) of a chunk");
+#ifndef SSM_SSD_CHUNK
+#define SSM_SSD_CHUNK 128
+#endif
+constexpr int kQ = SSM_SSD_CHUNK;   // steps per chunk (64 or 128)
+constexpr int kP = 64;              // channels per head
+constexpr int kSsdThreads = 4 * kQ; // a thread per (pair of steps, 8 channels) of a chunk: kQ / 16 waves
+constexpr int kJ = kQ / kWave;      // steps per lane of the first wave in the running sum
+static_assert(kQ % kWave == 0 && kQ >= 64 && kQ <= 128, "chunk of 64 or 128 steps");
 constexpr int kPad = 8;          // bf16 elements added to every LDS row (breaks bank aliasing)
 
 typedef __attribute__((ext_vector_type(4))) float f32x4;
@@ -59,31 +63,61 @@ __device__ __forceinline__ float from_bf16(bf16_bits v) { return __uint_as_float
 // (all an MFMA fragment reads) stays contiguous.
 __device__ __forceinline__ int swz(int r, int k) { return (((k >> 3) ^ ((r >> 3) & 7)) << 3) | (k & 7); }
 
-// Raw step of lane s of the first wave (delta + bias; 0 past the end of the
-// sequence), read early so its latency overlaps the other loads of the chunk.
-__device__ __forceinline__ float step_input(const bf16_bits* __restrict__ delta, const float* __restrict__ bias,
-                                            int64_t row0, int H, int h, int n_steps) {
-  const int s = threadIdx.x;
-  if (s >= kWave || s >= n_steps) return 0.f;
-  return from_bf16(delta[(row0 + s) * H + h]) + (bias ? bias[h] : 0.f);
+// Raw steps kJ l .. kJ l + kJ - 1 of lane l of the first wave (delta + bias; 0
+// past the end of the sequence), read early so their latency overlaps the other
+// loads of the chunk.
+struct StepRaw {
+  float v[kJ];
+};
+__device__ __forceinline__ StepRaw step_input(const bf16_bits* __restrict__ delta, const float* __restrict__ bias,
+                                              int64_t row0, int H, int h, int n_steps) {
+  StepRaw r;
+  const float bh = (threadIdx.x < kWave && bias) ? bias[h] : 0.f;
+#pragma unroll
+  for (int j = 0; j < kJ; j++) {
+    const int s = kJ * int(threadIdx.x) + j;
+    r.v[j] = (threadIdx.x < kWave && s < n_steps) ? from_bf16(delta[(row0 + s) * H + h]) + bh : 0.f;
+  }
+  return r;
 }
 
 // Steps and their running sums inside the chunk, by the first wave: d[s] (0 past
-// the end) and cum[s] = A_h * (d_0 + ... + d_s), written to LDS.
+// the end) and cum[s] = A_h * (d_0 + ... + d_s), written to LDS.  Lane l sums its
+// own kJ steps, then the lanes' totals are scanned across the wave.  With w_s,
+// also w[s] = exp(cum[e] - cum[s]) d[s], e the last step of the 16-step block of s.
 template <bool SOFTPLUS>
-__device__ __forceinline__ void chunk_steps(float raw, float Ah, int n_steps, float* d_s, float* cum_s) {
-  static_assert(kQ == kWave, "one step per lane of the first wave");
+__device__ __forceinline__ void chunk_steps(const StepRaw& raw, float Ah, int n_steps, float* d_s, float* cum_s,
+                                            float* w_s = nullptr) {
   if (threadIdx.x < kWave) {
-    const int s = threadIdx.x;
-    const float d = s < n_steps ? (SOFTPLUS ? softplus(raw) : raw) : 0.f;
-    float c = d * Ah;
+    const int l = threadIdx.x;
+    float d[kJ], c[kJ], run = 0.f;
+#pragma unroll
+    for (int j = 0; j < kJ; j++) {
+      const int s = kJ * l + j;
+      d[j] = s < n_steps ? (SOFTPLUS ? softplus(raw.v[j]) : raw.v[j]) : 0.f;
+      run += d[j] * Ah;
+      c[j] = run;
+    }
+    float tot = run;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
-      const float o = __shfl_up(c, off);
-      if (s >= off) c += o;
+      const float o = __shfl_up(tot, off);
+      if (l >= off) tot += o;
     }
-    d_s[s] = d;
-    cum_s[s] = c;
+    const float before = tot - run;  // the lanes below this one
+    float cum[kJ];
+#pragma unroll
+    for (int j = 0; j < kJ; j++) {
+      cum[j] = kJ == 1 ? tot : before + c[j];
+      d_s[kJ * l + j] = d[j];
+      cum_s[kJ * l + j] = cum[j];
+    }
+    if (w_s) {
+      constexpr int kLanesPerBlock = 16 / kJ;
+      const float cum_e = __shfl(cum[kJ - 1], (l & ~(kLanesPerBlock - 1)) | (kLanesPerBlock - 1));
+#pragma unroll
+      for (int j = 0; j < kJ; j++) w_s[kJ * l + j] = exp2_fast((cum_e - cum[j]) * kLog2e) * d[j];
+    }
   }
 }
 
@@ -161,7 +195,7 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_state_kernel(
     b0[k] = ok && sp < n_steps ? ld16(B + (row0 + sp) * N + n8) : zero;
     b1[k] = ok && sp + 1 < n_steps ? ld16(B + (row0 + sp + 1) * N + n8) : zero;
   }
-  const float raw = step_input(delta, bias, row0, H, h, n_steps);
+  const StepRaw raw = step_input(delta, bias, row0, H, h, n_steps);
   chunk_steps<SOFTPLUS>(raw, A[h], n_steps, d_s, cum_s);
 #pragma unroll
   for (int k = 0; k < nBV; k++) {
@@ -174,27 +208,33 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_state_kernel(
   const float w1 = exp2_fast((last - cum_s[s0 + 1]) * kLog2e) * d_s[s0 + 1];
   store_pair_t(Xw, ldt, p8, s0, scale8(x0, w0), scale8(x1, w1));
   __syncthreads();
-  // wave w: rows p in [16 w, 16 w + 16), every 16-column block of n
+  // wave w: rows p in [16 pb, 16 pb + 16) with pb = w mod 4, and the 16-column
+  // blocks of n congruent to w / 4 modulo the number of waves / 4
+  constexpr int kWaves = kSsdThreads / kWave, kNBW = (NP / 16) * 4 / kWaves;  // column blocks per wave
+  static_assert(kNBW * kWaves == (NP / 16) * 4, "the column blocks divide over the waves");
   const int wv = threadIdx.x / kWave, l = threadIdx.x % kWave;
   const int lr = l % 16, lk = 8 * (l / 16);
+  const int pb = wv % 4, nb0 = wv / 4;
   bf16x8 xf[kQ / 32];
 #pragma unroll
-  for (int kk = 0; kk < kQ / 32; kk++) xf[kk] = lds8(&Xw[(wv * 16 + lr) * ldt + swz(wv * 16 + lr, kk * 32 + lk)]);
-  f32x4 acc[NP / 16];
+  for (int kk = 0; kk < kQ / 32; kk++) xf[kk] = lds8(&Xw[(pb * 16 + lr) * ldt + swz(pb * 16 + lr, kk * 32 + lk)]);
+  f32x4 acc[kNBW];
 #pragma unroll
-  for (int nb = 0; nb < NP / 16; nb++) {
-    acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < kNBW; i++) {
+    const int nb = nb0 + i * (kWaves / 4);
+    acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (nb * 16 < N) {
 #pragma unroll
       for (int kk = 0; kk < kQ / 32; kk++)
-        acc[nb] = mfma(xf[kk], lds8(&Bt[(nb * 16 + lr) * ldt + swz(nb * 16 + lr, kk * 32 + lk)]), acc[nb]);
+        acc[i] = mfma(xf[kk], lds8(&Bt[(nb * 16 + lr) * ldt + swz(nb * 16 + lr, kk * 32 + lk)]), acc[i]);
     }
   }
   __syncthreads();  // every wave is done with Bt and Xw before the result goes over them
 #pragma unroll
-  for (int nb = 0; nb < NP / 16; nb++)
+  for (int i = 0; i < kNBW; i++)
 #pragma unroll
-    for (int r = 0; r < 4; r++) So[(wv * 16 + 4 * (l / 16) + r) * ldo + nb * 16 + lr] = to_bf16(acc[nb][r]);
+    for (int r = 0; r < 4; r++)
+      So[(pb * 16 + 4 * (l / 16) + r) * ldo + (nb0 + i * (kWaves / 4)) * 16 + lr] = to_bf16(acc[i][r]);
   __syncthreads();
   bf16_bits* out = states + ((bi * n_chunks + c) * H + h) * int64_t(kP) * N;  // [p][n]
   for (int v = threadIdx.x; v < kP * (NP / 8); v += kSsdThreads) {
@@ -264,28 +304,29 @@ __global__ __launch_bounds__(256) void ssd_carry_kernel(bf16_bits* states, const
 // the thread's own x and z.
 // ---------------------------------------------------------------------------
 template <int NK, bool SOFTPLUS, bool HAS_Z, bool HAS_D>
-__global__ __launch_bounds__(kSsdThreads) void ssd_scan_kernel(
+__global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(6))) void ssd_scan_kernel(
     const bf16_bits* __restrict__ x, const bf16_bits* __restrict__ delta, const float* __restrict__ A,
     const bf16_bits* __restrict__ B, const bf16_bits* __restrict__ C, const float* __restrict__ D,
     const bf16_bits* __restrict__ z, const float* __restrict__ bias, const bf16_bits* __restrict__ states,
     bf16_bits* __restrict__ y, int64_t L, int H, int N, int n_chunks) {
   constexpr int NP = NK * 32;
-  constexpr int ldr = NP + kPad;          // C, B and incoming-state tiles, bf16 elements per row
+  constexpr int ldr = NP + kPad;          // B and incoming-state tiles, bf16 elements per row
   constexpr int ldt = kQ + kPad;          // X transposed
   constexpr int ldy = kP + 4;             // fp32 result tile
-  constexpr int kCV = kQ * (NP / 8);      // 16-byte pieces of a C or B tile
+  constexpr int kBV = kQ * (NP / 8);      // 16-byte pieces of the B tile
   constexpr int kSV = kP * (NP / 8);      // 16-byte pieces of the incoming state
-  constexpr int nCV = (kCV + kSsdThreads - 1) / kSsdThreads;
+  constexpr int nBV = (kBV + kSsdThreads - 1) / kSsdThreads;
   constexpr int nSV = (kSV + kSsdThreads - 1) / kSsdThreads;
-  constexpr int kCBbytes = 2 * kQ * ldr * 2;
-  constexpr int kYbytes = kQ * ldy * 4;
-  __shared__ float d_s[kQ], cum_s[kQ];
-  __shared__ __attribute__((aligned(16))) bf16_bits Xt[kP * ldt];   // X transposed [p][s]
-  __shared__ __attribute__((aligned(16))) bf16_bits Ss[kP * ldr];   // incoming state [p][n]
-  __shared__ __attribute__((aligned(16))) char pool[kCBbytes > kYbytes ? kCBbytes : kYbytes];
-  bf16_bits* Cs = reinterpret_cast<bf16_bits*>(pool);                // C rows [t][n]
-  bf16_bits* Bs = Cs + kQ * ldr;                                     // B rows [s][n]
-  float* Ys = reinterpret_cast<float*>(pool);                        // results [t][p], after C and B
+  constexpr int kBbytes = kQ * ldr * 2, kXbytes = kP * ldt * 2, kSbytes = kP * ldr * 2;
+  constexpr int kTiles = kBbytes + kXbytes + kSbytes, kYbytes = kQ * ldy * 4;
+  __shared__ float d_s[kQ], cum_s[kQ], w_s[kQ];
+  // B rows [s][n], X transposed [p][s] and the incoming state [p][n]; once the
+  // products are done, the fp32 results [t][p] over all three
+  __shared__ __attribute__((aligned(16))) char pool[kTiles > kYbytes ? kTiles : kYbytes];
+  bf16_bits* Bs = reinterpret_cast<bf16_bits*>(pool);
+  bf16_bits* Xt = reinterpret_cast<bf16_bits*>(pool + kBbytes);
+  bf16_bits* Ss = reinterpret_cast<bf16_bits*>(pool + kBbytes + kXbytes);
+  float* Ys = reinterpret_cast<float*>(pool);
   const int h = blockIdx.x % H;
   const int rest = blockIdx.x / H;
   const int c = rest % n_chunks;
@@ -301,19 +342,22 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_scan_kernel(
   const int64_t xo = (row0 + s0) * E + int64_t(h) * kP + p8;
   const uint4 x0 = s0 < n_steps ? ld16(x + xo) : zero;
   const uint4 x1 = s0 + 1 < n_steps ? ld16(x + xo + E) : zero;
-  uint4 z0 = zero, z1 = zero;
-  if (HAS_Z) {
-    if (s0 < n_steps) z0 = ld16(z + xo);
-    if (s0 + 1 < n_steps) z1 = ld16(z + xo + E);
-  }
-  uint4 cv[nCV], bv[nCV];
+  uint4 bv[nBV];
 #pragma unroll
-  for (int k = 0; k < nCV; k++) {
+  for (int k = 0; k < nBV; k++) {
     const int v = threadIdx.x + k * kSsdThreads;
     const int r = v / (NP / 8), n8 = (v % (NP / 8)) * 8;
-    const bool ok = v < kCV && r < n_steps && n8 < N;
-    cv[k] = ok ? ld16(C + (row0 + r) * N + n8) : zero;
-    bv[k] = ok ? ld16(B + (row0 + r) * N + n8) : zero;
+    bv[k] = v < kBV && r < n_steps && n8 < N ? ld16(B + (row0 + r) * N + n8) : zero;
+  }
+  const int wv = threadIdx.x / kWave, l = threadIdx.x % kWave;
+  const int lr = l % 16, lg = l / 16, lk = 8 * lg, lq = 4 * lg;
+  const int tb = wv;                 // this wave's step block
+  const int t_own = tb * 16 + lr;    // the step this lane carries through the mixing product
+  bf16x8 cf[NK];  // C row of step t_own, n = 32 kk + lk .. + 7: the operand [k = n][column t], straight from memory
+#pragma unroll
+  for (int kk = 0; kk < NK; kk++) {
+    const uint4 v = t_own < n_steps && kk * 32 + lk < N ? ld16(C + (row0 + t_own) * N + kk * 32 + lk) : zero;
+    cf[kk] = __builtin_bit_cast(bf16x8, v);
   }
   const bf16_bits* Sin = states + ((bi * n_chunks + c) * H + h) * int64_t(kP) * N;
   uint4 sv[nSV];
@@ -323,18 +367,14 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_scan_kernel(
     const int p = v / (NP / 8), n8 = (v % (NP / 8)) * 8;
     sv[k] = v < kSV && n8 < N ? ld16(Sin + int64_t(p) * N + n8) : zero;
   }
-  const float raw = step_input(delta, bias, row0, H, h, n_steps);
+  const StepRaw raw = step_input(delta, bias, row0, H, h, n_steps);
 
   // ---- LDS tiles ----
-  chunk_steps<SOFTPLUS>(raw, A[h], n_steps, d_s, cum_s);
+  chunk_steps<SOFTPLUS>(raw, A[h], n_steps, d_s, cum_s, SOFTPLUS ? w_s : nullptr);
 #pragma unroll
-  for (int k = 0; k < nCV; k++) {
+  for (int k = 0; k < nBV; k++) {
     const int v = threadIdx.x + k * kSsdThreads;
-    if (v < kCV) {
-      const int o = (v / (NP / 8)) * ldr + (v % (NP / 8)) * 8;
-      *reinterpret_cast<uint4*>(Cs + o) = cv[k];
-      *reinterpret_cast<uint4*>(Bs + o) = bv[k];
-    }
+    if (v < kBV) *reinterpret_cast<uint4*>(Bs + (v / (NP / 8)) * ldr + (v % (NP / 8)) * 8) = bv[k];
   }
 #pragma unroll
   for (int k = 0; k < nSV; k++) {
@@ -344,42 +384,48 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_scan_kernel(
   store_pair_t(Xt, ldt, p8, s0, x0, x1);
   __syncthreads();
 
-  const int wv = threadIdx.x / kWave, l = threadIdx.x % kWave;
-  const int lr = l % 16, lg = l / 16, lk = 8 * lg, lq = 4 * lg;
-  const int tb = wv;                 // this wave's step block
-  const int t_own = tb * 16 + lr;    // the step this lane carries through the mixing product
   const float cum_t = cum_s[t_own];
-  bf16x8 cf[NK];                     // C rows of this wave's steps, as the operand [k = n][column t]
-#pragma unroll
-  for (int kk = 0; kk < NK; kk++) cf[kk] = lds8(&Cs[t_own * ldr + kk * 32 + lk]);
 
-  // mixing matrix, transposed tiles (rows s, column t): m[sb][r] = M[t_own][16 sb + 4 g + r]
-  float m[kQ / 16][4];
-#pragma unroll
-  for (int sb = 0; sb < kQ / 16; sb++) {
-#pragma unroll
-    for (int r = 0; r < 4; r++) m[sb][r] = 0.f;
-    if (sb <= tb) {  // blocks above the diagonal are zero
-      f32x4 g = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < NK; kk++) g = mfma(lds8(&Bs[(sb * 16 + lr) * ldr + kk * 32 + lk]), cf[kk], g);
-#pragma unroll
-      for (int r = 0; r < 4; r++) {
-        const int s = sb * 16 + lq + r;
-        m[sb][r] = (s <= t_own) ? g[r] * exp2_fast((cum_t - cum_s[s]) * kLog2e) * d_s[s] : 0.f;
-      }
-    }
-  }
-  // A operands of the in-chunk product: K block kk covers s in [32 kk, 32 kk + 32) in the order
-  // (4 g + r, 16 + 4 g + r), r = 0..3
+  // Mixing matrix, transposed tiles (rows s, column t): lane (g, t_own) computes
+  // M[t_own][16 sb + 4 g + r] and stores it straight into the A operand of the
+  // in-chunk product: K block kk covers s in [32 kk, 32 kk + 32) in the order
+  // (4 g + r, 16 + 4 g + r), r = 0..3.  Blocks above the diagonal are zero.
+  // With softplus steps (d >= 0, so cum moves one way along the chunk), a block
+  // below the diagonal takes exp(cum_t - cum_s) as exp(cum_t - cum_e) w_s / d_s,
+  // e the block's last step: both factors lie between 1 and the product, and
+  // one exponential per lane serves the block's four values.
   bf16x8 mf[kQ / 32];
 #pragma unroll
   for (int kk = 0; kk < kQ / 32; kk++) {
 #pragma unroll
-    for (int r = 0; r < 4; r++) {
-      mf[kk][r] = static_cast<__bf16>(m[2 * kk][r]);
-      mf[kk][4 + r] = static_cast<__bf16>(m[2 * kk + 1][r]);
+    for (int half = 0; half < 2; half++) {
+      const int sb = 2 * kk + half;
+      float mv[4] = {0.f, 0.f, 0.f, 0.f};
+      if (sb <= tb) {
+        f32x4 g = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k2 = 0; k2 < NK; k2++) g = mfma(lds8(&Bs[(sb * 16 + lr) * ldr + k2 * 32 + lk]), cf[k2], g);
+        if (SOFTPLUS && sb < tb) {
+          const float rf = exp2_fast((cum_t - cum_s[sb * 16 + 15]) * kLog2e);
+#pragma unroll
+          for (int r = 0; r < 4; r++) mv[r] = g[r] * rf * w_s[sb * 16 + lq + r];
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; r++) {
+            const int s = sb * 16 + lq + r;
+            mv[r] = (s <= t_own) ? g[r] * exp2_fast((cum_t - cum_s[s]) * kLog2e) * d_s[s] : 0.f;
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; r++) mf[kk][4 * half + r] = static_cast<__bf16>(mv[r]);
     }
+  }
+  // the gate, needed only at the end: read now, so its latency overlaps the products
+  uint4 z0 = zero, z1 = zero;
+  if (HAS_Z) {
+    if (s0 < n_steps) z0 = ld16(z + xo);
+    if (s0 + 1 < n_steps) z1 = ld16(z + xo + E);
   }
   float row_scale[4];  // exp(cum_t) of this lane's output rows
 #pragma unroll
@@ -404,7 +450,7 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_scan_kernel(
       acc[pb] = mfma(mf[kk], __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y)), acc[pb]);
     }
   }
-  __syncthreads();  // every wave is done with C and B before the results go over them
+  __syncthreads();  // every wave is done with the operand tiles before the results go over them
   // Volatile: hipcc (ROCm 7.2) pairs two of these 16 stores into one ds_write2_b32 with
   // the first offset divided by 4 twice (816 bytes encoded as 51 dwords), so rows
   // t = 3 mod 4 of the first 16 channels were never written.  Single stores avoid it.

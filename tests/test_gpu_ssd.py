@@ -6,7 +6,7 @@ head's channels; it is pinned against the dense structured mixing matrix in
 tests/test_oracle_pins.py.  The GPU path takes bf16 operands in its matrix
 products and accumulates in fp32; outputs are bf16, so the bf16 bound applies:
 |x - x_ref| <= 2e-2 * (1 + |x_ref|), elementwise on y and on the last state.
-Cases: state sizes 16..128, ragged lengths around the 64-step chunk, every flag,
+Cases: state sizes 16..128, ragged lengths around the 128-step chunk (and 64), every flag,
 an initial state, the empty sequence, determinism, agreement with ssm_scan_fwd
 on broadcast inputs, the mid-size workload in full and the long workload
 (b1 L65536 H80 P64 N64) on sampled heads.
@@ -88,7 +88,7 @@ def test_flags(gate, with_D, with_bias, softplus):
     check(x, f"ssd flags z={gate} D={with_D} bias={with_bias} sp={softplus}")
 
 
-@pytest.mark.parametrize("L", [1, 5, 63, 64, 65, 128, 200])
+@pytest.mark.parametrize("L", [1, 5, 63, 64, 65, 127, 128, 129, 200, 255, 256, 257, 400])
 def test_lengths(L):
     w = BASE.with_shape(L=L, H=2, N=64)
     say(f"ssd L={L}")
