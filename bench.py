@@ -93,7 +93,7 @@ def ssd_bytes(b, L, H, P, N, s, gate=True):
     return b * L * E * ((2 if gate else 1) + 1) * s + b * L * H * s + 2 * b * L * N * s + 2 * H * 4 + b * E * N * 4
 
 
-def ssd_flops(b, L, H, P, N, Q=64):
+def ssd_flops(b, L, H, P, N, Q=128):
     """Matrix-product flops of the chunked form: C B^T (causal half), L o (C B^T) X (causal half), C S_in, B^T (w o X)."""
     chunks = (L + Q - 1) // Q
     per = Q * Q * N + Q * Q * P + 2 * Q * N * P  # multiply-adds per (chunk, head), causal halves counted

@@ -44,6 +44,9 @@ constexpr int kP = 64;              // channels per head
 constexpr int kSsdThreads = 4 * kQ; // a thread per (pair of steps, 8 channels) of a chunk: kQ / 16 waves
 constexpr int kJ = kQ / kWave;      // steps per lane of the first wave in the running sum
 static_assert(kQ % kWave == 0 && kQ >= 64 && kQ <= 128, "chunk of 64 or 128 steps");
+#ifndef SSM_SSD_CARRY_U
+#define SSM_SSD_CARRY_U 16  // chunks whose loads the chain keeps in flight
+#endif
 constexpr int kPad = 8;          // bf16 elements added to every LDS row (breaks bank aliasing)
 
 typedef __attribute__((ext_vector_type(4))) float f32x4;
@@ -138,14 +141,15 @@ __device__ __forceinline__ uint4 scale8(uint4 v, float w) {
 // Rows s and s + 1 (s even) of columns c8 .. c8 + 7 (c8 a multiple of 8), given
 // as two 16-byte vectors, stored transposed into T (row stride ld): T[c8 + e][s]
 // and T[c8 + e][s + 1] go out as one 32-bit word, in the swizzled column blocks
-// of swz (the same for all 8 rows, which share r / 8).
+// of swz (the same for all 8 rows, which share r / 8).  The words are assembled
+// with byte permutes (low halves of a and b; high halves of a and b).
 __device__ __forceinline__ void store_pair_t(bf16_bits* T, int ld, int c8, int s, uint4 a, uint4 b) {
   const uint32_t ua[4] = {a.x, a.y, a.z, a.w}, ub[4] = {b.x, b.y, b.z, b.w};
   bf16_bits* col = T + swz(c8, s);
 #pragma unroll
   for (int j = 0; j < 4; j++) {
-    *reinterpret_cast<uint32_t*>(col + (c8 + 2 * j) * ld) = (ua[j] & 0xffffu) | (ub[j] << 16);
-    *reinterpret_cast<uint32_t*>(col + (c8 + 2 * j + 1) * ld) = (ua[j] >> 16) | (ub[j] & 0xffff0000u);
+    *reinterpret_cast<uint32_t*>(col + (c8 + 2 * j) * ld) = __builtin_amdgcn_perm(ub[j], ua[j], 0x05040100u);
+    *reinterpret_cast<uint32_t*>(col + (c8 + 2 * j + 1) * ld) = __builtin_amdgcn_perm(ub[j], ua[j], 0x07060302u);
   }
 }
 
@@ -339,9 +343,10 @@ __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(6))
 
   // ---- global reads ----
   const int s0 = 2 * (threadIdx.x >> 3), p8 = (threadIdx.x & 7) * 8;  // this thread's rows and channels
+  const bool ok0 = s0 < n_steps, ok1 = s0 + 1 < n_steps;
   const int64_t xo = (row0 + s0) * E + int64_t(h) * kP + p8;
-  const uint4 x0 = s0 < n_steps ? ld16(x + xo) : zero;
-  const uint4 x1 = s0 + 1 < n_steps ? ld16(x + xo + E) : zero;
+  const uint4 x0 = ok0 ? ld16(x + xo) : zero;
+  const uint4 x1 = ok1 ? ld16(x + xo + E) : zero;
   uint4 bv[nBV];
 #pragma unroll
   for (int k = 0; k < nBV; k++) {
@@ -424,8 +429,8 @@ __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(6))
   // the gate, needed only at the end: read now, so its latency overlaps the products
   uint4 z0 = zero, z1 = zero;
   if (HAS_Z) {
-    if (s0 < n_steps) z0 = ld16(z + xo);
-    if (s0 + 1 < n_steps) z1 = ld16(z + xo + E);
+    if (ok0) z0 = ld16(z + xo);
+    if (ok1) z1 = ld16(z + xo + E);
   }
   float row_scale[4];  // exp(cum_t) of this lane's output rows
 #pragma unroll
@@ -466,7 +471,7 @@ __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(6))
 #pragma unroll
   for (int j = 0; j < 2; j++) {
     const int s = s0 + j;
-    if (s < n_steps) {
+    if (j ? ok1 : ok0) {
       const float4 a = *reinterpret_cast<const float4*>(&Ys[s * ldy + p8]);
       const float4 b = *reinterpret_cast<const float4*>(&Ys[s * ldy + p8 + 4]);
       float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
@@ -511,7 +516,7 @@ hipError_t run_ssd(const SsdArgs& a, int n_chunks, bf16_bits* states, float* cum
                                a.A, B, a.bias, states, cum_last, a.L, H, N, n_chunks);
   if (err != hipSuccess) return err;
   const int64_t lanes = a.b * H * int64_t(N) * kP;
-  err = n_chunks > 33 ? launch_kind(kKindSsdCarry, ssd_carry_kernel<16>, (lanes + 255) / 256, 256, a.stream, states,
+  err = n_chunks > 33 ? launch_kind(kKindSsdCarry, ssd_carry_kernel<SSM_SSD_CARRY_U>, (lanes + 255) / 256, 256, a.stream, states,
                                     (const float*)cum_last, a.h0, a.last_state, a.b, H, N, n_chunks)
                       : launch_kind(kKindSsdCarry, ssd_carry_kernel<4>, (lanes + 255) / 256, 256, a.stream, states,
                                     (const float*)cum_last, a.h0, a.last_state, a.b, H, N, n_chunks);
