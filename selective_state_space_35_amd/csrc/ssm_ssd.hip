@@ -17,10 +17,14 @@
 //   S_out = exp(cum_last) S_in + B^T (w o X),            w_s = exp(cum_last - cum_s) d_s
 //
 // Kernels (bf16 I/O; matrix products take bf16 operands and accumulate in fp32;
-// chunk states are handed between kernels in bf16, laid out [p][n]):
-//   ssd_state_kernel  per (batch, chunk, head): (w o X)^T B -> chunk state [P, N]
-//   ssd_carry_kernel  per (batch, head, p, n): chain of chunk states (fp32 in registers) -> state entering each chunk
-//   ssd_scan_kernel   per (batch, chunk, head): Y as above, + D x, gate, store
+// states laid out [p][n]).  The chunks are grouped in segments of kSeg:
+//   ssd_state_kernel  per (batch, segment, head): walks the segment's chunks, (w o X)^T B
+//                     per chunk chained in fp32 registers -> each chunk's incoming state
+//                     from inside the segment (bf16) and the segment's own state (fp32)
+//   ssd_carry_kernel  per (batch, head, p, n): chain over segments (fp32) -> state entering
+//                     each segment, and the last state
+//   ssd_scan_kernel   per (batch, chunk, head): S_in = inside part + decayed segment state,
+//                     then Y as above, + D x, gate, store
 // MFMA: v_mfma_f32_16x16x32_bf16.  Lane l of a wave holds A-operand row l % 16,
 // k = 8 (l / 16) .. +7; B-operand column l % 16, same k; result rows
 // 4 (l / 16) .. +3 of column l % 16.
@@ -44,9 +48,7 @@ constexpr int kP = 64;              // channels per head
 constexpr int kSsdThreads = 4 * kQ; // a thread per (pair of steps, 8 channels) of a chunk: kQ / 16 waves
 constexpr int kJ = kQ / kWave;      // steps per lane of the first wave in the running sum
 static_assert(kQ % kWave == 0 && kQ >= 64 && kQ <= 128, "chunk of 64 or 128 steps");
-#ifndef SSM_SSD_CARRY_U
-#define SSM_SSD_CARRY_U 16  // chunks whose loads the chain keeps in flight
-#endif
+constexpr int kSeg = 8;             // chunks per segment of the chunk-state walk
 constexpr int kPad = 8;          // bf16 elements added to every LDS row (breaks bank aliasing)
 
 typedef __attribute__((ext_vector_type(4))) float f32x4;
@@ -125,6 +127,12 @@ __device__ __forceinline__ void chunk_steps(const StepRaw& raw, float Ah, int n_
 }
 
 __device__ __forceinline__ uint4 ld16(const bf16_bits* p) { return *reinterpret_cast<const uint4*>(p); }
+// 16 bytes at byte offset off of a buffer, or zeros when !ok (the offset is then
+// pushed past the descriptor's range, which the hardware answers with zeros)
+__device__ __forceinline__ uint4 ld16_or_zero(__amdgpu_buffer_rsrc_t r, bool ok, int off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, ok ? off : 0x7fffffff, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   return uint32_t(to_bf16(lo)) | (uint32_t(to_bf16(hi)) << 16);
 }
@@ -154,109 +162,163 @@ __device__ __forceinline__ void store_pair_t(bf16_bits* T, int ld, int c8, int s
 }
 
 // ---------------------------------------------------------------------------
-// chunk state, transposed: S_c[p, n] = sum_s (w o X)[s, p] B[s, n]  (bf16 out)
-// Every global read of the chunk is issued first (B and x as pairs of rows, so
-// the transposed LDS tiles are written one 32-bit word per two steps); the
-// result goes back through LDS and out in whole 16-byte row pieces.
+// chunk states along a segment of kSeg chunks, per (batch, segment, head).
+// Chunk c's own state, transposed, S_c[p, n] = sum_s (w o X)[s, p] B[s, n], comes
+// from the MFMA units in fp32 and is chained in registers along the segment:
+//   R_c = state entering chunk c from the segment's earlier chunks alone
+//       = exp(cum_last of chunk c-1) R_{c-1} + S_{c-1},   R = 0 at the segment start.
+// Written per chunk: R_c in bf16 [p][n] (not for the segment's first chunk, where
+// it is zero) and phi_c = A_h * (steps of the segment before chunk c); per
+// segment: R after its last chunk in fp32 [p][n] and the segment's A_h * (sum of
+// its steps).  Capped at 80 VGPRs so that three 8-wave workgroups share a CU: their
+// interleaving hides the reads better than a prefetch of the next chunk, whose
+// registers would leave room for two (measured 302 against 333 us at ssd_long).
 // ---------------------------------------------------------------------------
 template <int NK, bool SOFTPLUS>  // NK: the state size padded to a multiple of 32, in units of 32
-__global__ __launch_bounds__(kSsdThreads) void ssd_state_kernel(
+__global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(6))) void ssd_state_kernel(
     const bf16_bits* __restrict__ x, const bf16_bits* __restrict__ delta, const float* __restrict__ A,
-    const bf16_bits* __restrict__ B, const float* __restrict__ bias, bf16_bits* __restrict__ states,
-    float* __restrict__ cum_last, int64_t L, int H, int N, int n_chunks) {
+    const bf16_bits* __restrict__ B, const float* __restrict__ bias, bf16_bits* __restrict__ rin,
+    float* __restrict__ phi, float* __restrict__ seg_state, float* __restrict__ seg_decay, int64_t L, int H, int N,
+    int n_chunks, int n_segs) {
   constexpr int NP = NK * 32;
   constexpr int kBV = kQ / 2 * (NP / 8);  // (row pair, 16-byte column block) items of B
   constexpr int nBV = (kBV + kSsdThreads - 1) / kSsdThreads;
-  constexpr int kTileB = NP * (kQ + kPad) + kP * (kQ + kPad);  // Bt then Xw, bf16 elements
-  constexpr int kOutB = kP * (NP + kPad);                      // the result [p][n], over them afterwards
-  static_assert(kOutB <= kTileB, "result tile fits over the operand tiles");
-  __shared__ float d_s[kQ], cum_s[kQ];
-  __shared__ __attribute__((aligned(16))) bf16_bits pool[kTileB];
-  bf16_bits* Bt = pool;                         // B transposed: [n][s]
-  bf16_bits* Xw = pool + NP * (kQ + kPad);      // (w o X) transposed: [p][s]
-  bf16_bits* So = pool;                         // result [p][n]
   constexpr int ldt = kQ + kPad, ldo = NP + kPad;
+  constexpr int kWaves = kSsdThreads / kWave, kNBW = (NP / 16) * 4 / kWaves;  // 16-column blocks per wave
+  static_assert(kNBW * kWaves == (NP / 16) * 4, "the column blocks divide over the waves");
+  __shared__ float d_s[kQ], cum_s[kQ];
+  __shared__ __attribute__((aligned(16))) bf16_bits Bt[NP * ldt];   // B transposed: [n][s]
+  __shared__ __attribute__((aligned(16))) bf16_bits Xw[kP * ldt];   // (w o X) transposed: [p][s]
+  __shared__ __attribute__((aligned(16))) bf16_bits So[kP * ldo];   // R_c in bf16 [p][n], on its way out
   const int h = blockIdx.x % H;
   const int rest = blockIdx.x / H;
-  const int c = rest % n_chunks;
-  const int64_t bi = rest / n_chunks;
-  const int64_t t0 = int64_t(c) * kQ;
-  const int n_steps = int(std::min<int64_t>(kQ, L - t0));
-  const int64_t row0 = bi * L + t0;
+  const int g = rest % n_segs;
+  const int64_t bi = rest / n_segs;
+  const int c_begin = g * kSeg, c_end = std::min(c_begin + kSeg, n_chunks);
   const int64_t E = int64_t(H) * kP;
-  const uint4 zero = make_uint4(0, 0, 0, 0);
+  const float Ah = A[h];
   // this thread's x rows s0, s0 + 1 and channels p8 .. p8 + 7
   const int s0 = 2 * (threadIdx.x >> 3), p8 = (threadIdx.x & 7) * 8;
-  const bf16_bits* xr = x + (row0 + s0) * E + int64_t(h) * kP + p8;
-  const uint4 x0 = s0 < n_steps ? ld16(xr) : zero;
-  const uint4 x1 = s0 + 1 < n_steps ? ld16(xr + E) : zero;
-  uint4 b0[nBV], b1[nBV];
-#pragma unroll
-  for (int k = 0; k < nBV; k++) {
-    const int v = threadIdx.x + k * kSsdThreads;
-    const int sp = 2 * (v / (NP / 8)), n8 = (v % (NP / 8)) * 8;
-    const bool ok = v < kBV && n8 < N;
-    b0[k] = ok && sp < n_steps ? ld16(B + (row0 + sp) * N + n8) : zero;
-    b1[k] = ok && sp + 1 < n_steps ? ld16(B + (row0 + sp + 1) * N + n8) : zero;
-  }
-  const StepRaw raw = step_input(delta, bias, row0, H, h, n_steps);
-  chunk_steps<SOFTPLUS>(raw, A[h], n_steps, d_s, cum_s);
-#pragma unroll
-  for (int k = 0; k < nBV; k++) {
-    const int v = threadIdx.x + k * kSsdThreads;
-    if (v < kBV) store_pair_t(Bt, ldt, (v % (NP / 8)) * 8, 2 * (v / (NP / 8)), b0[k], b1[k]);
-  }
-  __syncthreads();
-  const float last = cum_s[kQ - 1];
-  const float w0 = exp2_fast((last - cum_s[s0]) * kLog2e) * d_s[s0];
-  const float w1 = exp2_fast((last - cum_s[s0 + 1]) * kLog2e) * d_s[s0 + 1];
-  store_pair_t(Xw, ldt, p8, s0, scale8(x0, w0), scale8(x1, w1));
-  __syncthreads();
   // wave w: rows p in [16 pb, 16 pb + 16) with pb = w mod 4, and the 16-column
   // blocks of n congruent to w / 4 modulo the number of waves / 4
-  constexpr int kWaves = kSsdThreads / kWave, kNBW = (NP / 16) * 4 / kWaves;  // column blocks per wave
-  static_assert(kNBW * kWaves == (NP / 16) * 4, "the column blocks divide over the waves");
   const int wv = threadIdx.x / kWave, l = threadIdx.x % kWave;
   const int lr = l % 16, lk = 8 * (l / 16);
   const int pb = wv % 4, nb0 = wv / 4;
-  bf16x8 xf[kQ / 32];
+
+  struct Reads {
+    uint4 x0, x1, b0[nBV], b1[nBV];
+    StepRaw raw;
+  };
+  // the chunk's reads through buffer descriptors based at its first row, so a
+  // guarded load needs neither a branch nor a select of addresses
+  auto read_chunk = [&](int c) {
+    Reads r;
+    const int64_t t0 = int64_t(c) * kQ;
+    const int n_steps = int(std::min<int64_t>(kQ, L - t0));
+    const int64_t row0 = bi * L + t0;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + row0 * E + int64_t(h) * kP);
+    const int xoff = (s0 * int(E) + p8) * 2;  // kQ rows of E bf16 stay far below 2 GiB
+    r.x0 = ld16_or_zero(rx, s0 < n_steps, xoff);
+    r.x1 = ld16_or_zero(rx, s0 + 1 < n_steps, xoff + int(E) * 2);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + row0 * N);
 #pragma unroll
-  for (int kk = 0; kk < kQ / 32; kk++) xf[kk] = lds8(&Xw[(pb * 16 + lr) * ldt + swz(pb * 16 + lr, kk * 32 + lk)]);
-  f32x4 acc[kNBW];
+    for (int k = 0; k < nBV; k++) {
+      const int v = threadIdx.x + k * kSsdThreads;
+      const int sp = 2 * (v / (NP / 8)), n8 = (v % (NP / 8)) * 8;
+      const bool ok = v < kBV && n8 < N;
+      r.b0[k] = ld16_or_zero(rb, ok && sp < n_steps, (sp * N + n8) * 2);
+      r.b1[k] = ld16_or_zero(rb, ok && sp + 1 < n_steps, ((sp + 1) * N + n8) * 2);
+    }
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(delta + row0 * H + h);
+    const float bh = bias ? bias[h] : 0.f;
+#pragma unroll
+    for (int j = 0; j < kJ; j++) {
+      const int st = kJ * int(threadIdx.x) + j;
+      const bool ok = threadIdx.x < kWave && st < n_steps;
+      const float dv = __uint_as_float(
+          uint32_t(__builtin_amdgcn_raw_buffer_load_b16(rd, ok ? st * H * 2 : 0x7fffffff, 0, 0)) << 16);
+      r.raw.v[j] = ok ? dv + bh : 0.f;
+    }
+    return r;
+  };
+
+  f32x4 R[kNBW];
+#pragma unroll
+  for (int i = 0; i < kNBW; i++) R[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float lphi = 0.f;  // A_h * (steps of the segment so far); uniform
+  for (int c = c_begin; c < c_end; c++) {
+    const Reads cur = read_chunk(c);
+    const int n_steps = int(std::min<int64_t>(kQ, L - int64_t(c) * kQ));
+    __syncthreads();  // the previous chunk is done with d_s, cum_s and the tiles
+    chunk_steps<SOFTPLUS>(cur.raw, Ah, n_steps, d_s, cum_s);
+#pragma unroll
+    for (int k = 0; k < nBV; k++) {
+      const int v = threadIdx.x + k * kSsdThreads;
+      if (v < kBV) store_pair_t(Bt, ldt, (v % (NP / 8)) * 8, 2 * (v / (NP / 8)), cur.b0[k], cur.b1[k]);
+    }
+    if (c > c_begin) {
+#pragma unroll
+      for (int i = 0; i < kNBW; i++)
+#pragma unroll
+        for (int r = 0; r < 4; r++)
+          So[(pb * 16 + 4 * (l / 16) + r) * ldo + (nb0 + i * (kWaves / 4)) * 16 + lr] = to_bf16(R[i][r]);
+    }
+    __syncthreads();
+    const float last = cum_s[kQ - 1];
+    const float w0 = exp2_fast((last - cum_s[s0]) * kLog2e) * d_s[s0];
+    const float w1 = exp2_fast((last - cum_s[s0 + 1]) * kLog2e) * d_s[s0 + 1];
+    store_pair_t(Xw, ldt, p8, s0, scale8(cur.x0, w0), scale8(cur.x1, w1));
+    if (c > c_begin) {  // R_c out in 16-byte row pieces
+      bf16_bits* out = rin + ((bi * n_chunks + c) * H + h) * int64_t(kP) * N;
+      for (int v = threadIdx.x; v < kP * (NP / 8); v += kSsdThreads) {
+        const int p = v / (NP / 8), n8 = (v % (NP / 8)) * 8;
+        if (n8 < N)
+          *reinterpret_cast<uint4*>(out + int64_t(p) * N + n8) = *reinterpret_cast<const uint4*>(&So[p * ldo + n8]);
+      }
+    }
+    if (threadIdx.x == 0) phi[(bi * n_chunks + c) * H + h] = lphi;
+    __syncthreads();
+    bf16x8 xf[kQ / 32];
+#pragma unroll
+    for (int kk = 0; kk < kQ / 32; kk++) xf[kk] = lds8(&Xw[(pb * 16 + lr) * ldt + swz(pb * 16 + lr, kk * 32 + lk)]);
+    const float decay = exp2_fast(last * kLog2e);
+#pragma unroll
+    for (int i = 0; i < kNBW; i++) {
+      const int nb = nb0 + i * (kWaves / 4);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      if (nb * 16 < N) {
+#pragma unroll
+        for (int kk = 0; kk < kQ / 32; kk++)
+          acc = mfma(xf[kk], lds8(&Bt[(nb * 16 + lr) * ldt + swz(nb * 16 + lr, kk * 32 + lk)]), acc);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; r++) R[i][r] = fmaf(decay, R[i][r], acc[r]);
+    }
+    lphi += last;
+  }
+  // the segment's aggregate: R after its last chunk (fp32 [p][n]) and its log-decay
+  float* so = seg_state + ((bi * n_segs + g) * H + h) * int64_t(kP) * N;
 #pragma unroll
   for (int i = 0; i < kNBW; i++) {
-    const int nb = nb0 + i * (kWaves / 4);
-    acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (nb * 16 < N) {
+    const int n = (nb0 + i * (kWaves / 4)) * 16 + lr;
+    if (n < N) {
 #pragma unroll
-      for (int kk = 0; kk < kQ / 32; kk++)
-        acc[i] = mfma(xf[kk], lds8(&Bt[(nb * 16 + lr) * ldt + swz(nb * 16 + lr, kk * 32 + lk)]), acc[i]);
+      for (int r = 0; r < 4; r++) so[int64_t(pb * 16 + 4 * (l / 16) + r) * N + n] = R[i][r];
     }
   }
-  __syncthreads();  // every wave is done with Bt and Xw before the result goes over them
-#pragma unroll
-  for (int i = 0; i < kNBW; i++)
-#pragma unroll
-    for (int r = 0; r < 4; r++)
-      So[(pb * 16 + 4 * (l / 16) + r) * ldo + (nb0 + i * (kWaves / 4)) * 16 + lr] = to_bf16(acc[i][r]);
-  __syncthreads();
-  bf16_bits* out = states + ((bi * n_chunks + c) * H + h) * int64_t(kP) * N;  // [p][n]
-  for (int v = threadIdx.x; v < kP * (NP / 8); v += kSsdThreads) {
-    const int p = v / (NP / 8), n8 = (v % (NP / 8)) * 8;
-    if (n8 < N) *reinterpret_cast<uint4*>(out + int64_t(p) * N + n8) = *reinterpret_cast<const uint4*>(&So[p * ldo + n8]);
-  }
-  if (threadIdx.x == 0) cum_last[(bi * n_chunks + c) * H + h] = last;
+  if (threadIdx.x == 0) seg_decay[(bi * n_segs + g) * H + h] = lphi;
 }
 
 // ---------------------------------------------------------------------------
-// carry: per (batch, head, p, n), state entering chunk c (bf16, in place of
-// S_c; the chain itself is kept in fp32); the state after the last chunk goes
-// to last_state [b, E, N] in fp32
+// carry over segments: per (batch, head, p, n), the state entering segment g,
+// S_g = exp(seg_decay[g - 1]) S_{g-1} + R_end[g - 1] from the incoming state,
+// in fp32, written in place of R_end[g]; the state after the last segment goes
+// to last_state [b, E, N]
 // ---------------------------------------------------------------------------
 template <int U>
-__global__ __launch_bounds__(256) void ssd_carry_kernel(bf16_bits* states, const float* __restrict__ cum_last,
+__global__ __launch_bounds__(256) void ssd_carry_kernel(float* seg_state, const float* __restrict__ seg_decay,
                                                         const float* __restrict__ h0, float* __restrict__ last_state,
-                                                        int64_t b, int H, int N, int n_chunks) {
+                                                        int64_t b, int H, int N, int n_segs) {
   const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t per_head = int64_t(N) * kP;
   if (gid >= b * H * per_head) return;
@@ -267,26 +329,26 @@ __global__ __launch_bounds__(256) void ssd_carry_kernel(bf16_bits* states, const
   const int64_t E = int64_t(H) * kP;
   const int64_t st = (bi * E + int64_t(h) * kP) * N + within;  // [b][e = h P + p][n]
   float S = h0 ? h0[st] : 0.f;
-  auto slot = [&](int c) { return ((bi * n_chunks + c) * H + h) * per_head + within; };
+  auto slot = [&](int g) { return ((bi * n_segs + g) * H + h) * per_head + within; };
   float Ss[U], Ls[U];
-  auto load = [&](int c0) {
+  auto load = [&](int g0) {
 #pragma unroll
     for (int k = 0; k < U; k++) {
-      const int cc = (c0 + k < n_chunks) ? c0 + k : n_chunks - 1;  // past the end: a valid slot, unused
-      Ss[k] = from_bf16(states[slot(cc)]);
-      Ls[k] = cum_last[(bi * n_chunks + cc) * H + h];
+      const int gg = (g0 + k < n_segs) ? g0 + k : n_segs - 1;  // past the end: a valid slot, unused
+      Ss[k] = seg_state[slot(gg)];
+      Ls[k] = seg_decay[(bi * n_segs + gg) * H + h];
     }
   };
   load(0);
-  for (int c0 = 0; c0 < n_chunks; c0 += U) {
+  for (int g0 = 0; g0 < n_segs; g0 += U) {
     float Sc[U], Lc[U];
 #pragma unroll
     for (int k = 0; k < U; k++) { Sc[k] = Ss[k]; Lc[k] = Ls[k]; }
-    if (c0 + U < n_chunks) load(c0 + U);
+    if (g0 + U < n_segs) load(g0 + U);
 #pragma unroll
     for (int k = 0; k < U; k++) {
-      if (c0 + k < n_chunks) {
-        states[slot(c0 + k)] = to_bf16(S);
+      if (g0 + k < n_segs) {
+        seg_state[slot(g0 + k)] = S;
         S = fmaf(exp2_fast(Lc[k] * kLog2e), S, Sc[k]);
       }
     }
@@ -311,8 +373,9 @@ template <int NK, bool SOFTPLUS, bool HAS_Z, bool HAS_D>
 __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(6))) void ssd_scan_kernel(
     const bf16_bits* __restrict__ x, const bf16_bits* __restrict__ delta, const float* __restrict__ A,
     const bf16_bits* __restrict__ B, const bf16_bits* __restrict__ C, const float* __restrict__ D,
-    const bf16_bits* __restrict__ z, const float* __restrict__ bias, const bf16_bits* __restrict__ states,
-    bf16_bits* __restrict__ y, int64_t L, int H, int N, int n_chunks) {
+    const bf16_bits* __restrict__ z, const float* __restrict__ bias, const bf16_bits* __restrict__ rin,
+    const float* __restrict__ phi, const float* __restrict__ seg_state, bf16_bits* __restrict__ y, int64_t L, int H,
+    int N, int n_chunks, int n_segs) {
   constexpr int NP = NK * 32;
   constexpr int ldr = NP + kPad;          // B and incoming-state tiles, bf16 elements per row
   constexpr int ldt = kQ + kPad;          // X transposed
@@ -364,14 +427,23 @@ __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(6))
     const uint4 v = t_own < n_steps && kk * 32 + lk < N ? ld16(C + (row0 + t_own) * N + kk * 32 + lk) : zero;
     cf[kk] = __builtin_bit_cast(bf16x8, v);
   }
-  const bf16_bits* Sin = states + ((bi * n_chunks + c) * H + h) * int64_t(kP) * N;
+  // incoming state S_in = R_c + exp(phi_c) S_g: the segment-local part (bf16, zero at
+  // the segment's first chunk) and the state entering the segment (fp32)
+  const bool seg_first = c % kSeg == 0;
+  const bf16_bits* Rin = rin + ((bi * n_chunks + c) * H + h) * int64_t(kP) * N;
+  const float* Sg = seg_state + ((bi * n_segs + c / kSeg) * H + h) * int64_t(kP) * N;
   uint4 sv[nSV];
+  float4 sg0[nSV], sg1[nSV];
 #pragma unroll
   for (int k = 0; k < nSV; k++) {
     const int v = threadIdx.x + k * kSsdThreads;
     const int p = v / (NP / 8), n8 = (v % (NP / 8)) * 8;
-    sv[k] = v < kSV && n8 < N ? ld16(Sin + int64_t(p) * N + n8) : zero;
+    const bool ok = v < kSV && n8 < N;
+    sv[k] = ok && !seg_first ? ld16(Rin + int64_t(p) * N + n8) : zero;
+    sg0[k] = ok ? *reinterpret_cast<const float4*>(Sg + int64_t(p) * N + n8) : make_float4(0.f, 0.f, 0.f, 0.f);
+    sg1[k] = ok ? *reinterpret_cast<const float4*>(Sg + int64_t(p) * N + n8 + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
+  const float ephi = exp2_fast(phi[(bi * n_chunks + c) * H + h] * kLog2e);
   const StepRaw raw = step_input(delta, bias, row0, H, h, n_steps);
 
   // ---- LDS tiles ----
@@ -384,7 +456,16 @@ __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(6))
 #pragma unroll
   for (int k = 0; k < nSV; k++) {
     const int v = threadIdx.x + k * kSsdThreads;
-    if (v < kSV) *reinterpret_cast<uint4*>(Ss + (v / (NP / 8)) * ldr + (v % (NP / 8)) * 8) = sv[k];
+    if (v < kSV) {
+      const uint32_t r[4] = {sv[k].x, sv[k].y, sv[k].z, sv[k].w};
+      const float sg[8] = {sg0[k].x, sg0[k].y, sg0[k].z, sg0[k].w, sg1[k].x, sg1[k].y, sg1[k].z, sg1[k].w};
+      uint32_t o[4];
+#pragma unroll
+      for (int q = 0; q < 4; q++)
+        o[q] = pack2(fmaf(ephi, sg[2 * q], __uint_as_float(r[q] << 16)),
+                     fmaf(ephi, sg[2 * q + 1], __uint_as_float(r[q] & 0xffff0000u)));
+      *reinterpret_cast<uint4*>(Ss + (v / (NP / 8)) * ldr + (v % (NP / 8)) * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
   }
   store_pair_t(Xt, ldt, p8, s0, x0, x1);
   __syncthreads();
@@ -503,28 +584,39 @@ __global__ __launch_bounds__(256) void ssd_fill_kernel(float* __restrict__ dst, 
   if (i < n) dst[i] = src ? src[i] : 0.f;
 }
 
+// Workspace of one call: the chunks' segment-local incoming states (bf16), the
+// chunks' phi, the segments' states (fp32) and their log-decays.
+struct SsdWork {
+  bf16_bits* rin;
+  float* phi;
+  float* seg_state;
+  float* seg_decay;
+};
+
 template <int NK, bool SOFTPLUS>
-hipError_t run_ssd(const SsdArgs& a, int n_chunks, bf16_bits* states, float* cum_last) {
+hipError_t run_ssd(const SsdArgs& a, int n_chunks, int n_segs, const SsdWork& w) {
   const int H = int(a.H), N = int(a.N);
-  const int64_t blocks = a.b * n_chunks * H;
   const bf16_bits* x = static_cast<const bf16_bits*>(a.x);
   const bf16_bits* dl = static_cast<const bf16_bits*>(a.delta);
   const bf16_bits* B = static_cast<const bf16_bits*>(a.B);
   const bf16_bits* C = static_cast<const bf16_bits*>(a.C);
   const bf16_bits* z = static_cast<const bf16_bits*>(a.z);
-  hipError_t err = launch_kind(kKindSsdState, ssd_state_kernel<NK, SOFTPLUS>, blocks, kSsdThreads, a.stream, x, dl,
-                               a.A, B, a.bias, states, cum_last, a.L, H, N, n_chunks);
+  hipError_t err = launch_kind(kKindSsdState, ssd_state_kernel<NK, SOFTPLUS>, a.b * n_segs * H, kSsdThreads, a.stream,
+                               x, dl, a.A, B, a.bias, w.rin, w.phi, w.seg_state, w.seg_decay, a.L, H, N, n_chunks,
+                               n_segs);
   if (err != hipSuccess) return err;
   const int64_t lanes = a.b * H * int64_t(N) * kP;
-  err = n_chunks > 33 ? launch_kind(kKindSsdCarry, ssd_carry_kernel<SSM_SSD_CARRY_U>, (lanes + 255) / 256, 256, a.stream, states,
-                                    (const float*)cum_last, a.h0, a.last_state, a.b, H, N, n_chunks)
-                      : launch_kind(kKindSsdCarry, ssd_carry_kernel<4>, (lanes + 255) / 256, 256, a.stream, states,
-                                    (const float*)cum_last, a.h0, a.last_state, a.b, H, N, n_chunks);
+  err = n_segs > 33 ? launch_kind(kKindSsdCarry, ssd_carry_kernel<16>, (lanes + 255) / 256, 256, a.stream, w.seg_state,
+                                  (const float*)w.seg_decay, a.h0, a.last_state, a.b, H, N, n_segs)
+                    : launch_kind(kKindSsdCarry, ssd_carry_kernel<4>, (lanes + 255) / 256, 256, a.stream, w.seg_state,
+                                  (const float*)w.seg_decay, a.h0, a.last_state, a.b, H, N, n_segs);
   if (err != hipSuccess) return err;
   bf16_bits* y = static_cast<bf16_bits*>(a.y);
+  const int64_t blocks = a.b * n_chunks * H;
 #define SSM_SSD_SCAN(HZ, HD)                                                                                  \
   return launch_kind(kKindSsdScan, ssd_scan_kernel<NK, SOFTPLUS, HZ, HD>, blocks, kSsdThreads, a.stream, x, dl, \
-                     a.A, B, C, a.D, z, a.bias, (const bf16_bits*)states, y, a.L, H, N, n_chunks)
+                     a.A, B, C, a.D, z, a.bias, (const bf16_bits*)w.rin, (const float*)w.phi,               \
+                     (const float*)w.seg_state, y, a.L, H, N, n_chunks, n_segs)
   if (a.z) {
     if (a.D) SSM_SSD_SCAN(true, true);
     SSM_SSD_SCAN(true, false);
@@ -535,8 +627,8 @@ hipError_t run_ssd(const SsdArgs& a, int n_chunks, bf16_bits* states, float* cum
 }
 
 template <int NK>
-hipError_t ssd_sp(const SsdArgs& a, int n_chunks, bf16_bits* states, float* cum_last) {
-  return a.softplus ? run_ssd<NK, true>(a, n_chunks, states, cum_last) : run_ssd<NK, false>(a, n_chunks, states, cum_last);
+hipError_t ssd_sp(const SsdArgs& a, int n_chunks, int n_segs, const SsdWork& w) {
+  return a.softplus ? run_ssd<NK, true>(a, n_chunks, n_segs, w) : run_ssd<NK, false>(a, n_chunks, n_segs, w);
 }
 
 }  // namespace
@@ -552,21 +644,26 @@ hipError_t launch_ssd(const SsdArgs& a) {
     return launch_kind(kKindSsdCarry, ssd_fill_kernel, (n + 255) / 256, 256, a.stream, a.last_state, a.h0, n);
   }
   const int n_chunks = int((a.L + kQ - 1) / kQ);
-  // workspace: chunk states [b][chunk][h][p][n] in bf16, then the chunks' decay exponents
-  const size_t n_states = size_t(a.b) * size_t(n_chunks) * size_t(a.H) * size_t(a.N) * kP;
-  const size_t n_cum = size_t(a.b) * size_t(n_chunks) * size_t(a.H);
-  const size_t state_bytes = (n_states * sizeof(bf16_bits) + 255) / 256 * 256;
+  const int n_segs = (n_chunks + kSeg - 1) / kSeg;
+  auto up = [](size_t bytes) { return (bytes + 255) / 256 * 256; };
+  const size_t per_state = size_t(a.N) * kP;
+  const size_t rin_bytes = up(size_t(a.b) * n_chunks * a.H * per_state * sizeof(bf16_bits));
+  const size_t phi_bytes = up(size_t(a.b) * n_chunks * a.H * sizeof(float));
+  const size_t seg_bytes = up(size_t(a.b) * n_segs * a.H * per_state * sizeof(float));
+  const size_t dec_bytes = up(size_t(a.b) * n_segs * a.H * sizeof(float));
   void* ws = nullptr;
-  hipError_t err = hipMallocAsync(&ws, state_bytes + n_cum * sizeof(float), a.stream);
+  hipError_t err = hipMallocAsync(&ws, rin_bytes + phi_bytes + seg_bytes + dec_bytes, a.stream);
   if (err != hipSuccess) return err;
-  bf16_bits* states = static_cast<bf16_bits*>(ws);
-  float* cum_last = reinterpret_cast<float*>(static_cast<char*>(ws) + state_bytes);
+  char* p = static_cast<char*>(ws);
+  const SsdWork w = {reinterpret_cast<bf16_bits*>(p), reinterpret_cast<float*>(p + rin_bytes),
+                     reinterpret_cast<float*>(p + rin_bytes + phi_bytes),
+                     reinterpret_cast<float*>(p + rin_bytes + phi_bytes + seg_bytes)};
   const int nk = int((a.N + 31) / 32);
   switch (nk) {
-    case 1: err = ssd_sp<1>(a, n_chunks, states, cum_last); break;
-    case 2: err = ssd_sp<2>(a, n_chunks, states, cum_last); break;
-    case 3: err = ssd_sp<3>(a, n_chunks, states, cum_last); break;
-    default: err = ssd_sp<4>(a, n_chunks, states, cum_last); break;
+    case 1: err = ssd_sp<1>(a, n_chunks, n_segs, w); break;
+    case 2: err = ssd_sp<2>(a, n_chunks, n_segs, w); break;
+    case 3: err = ssd_sp<3>(a, n_chunks, n_segs, w); break;
+    default: err = ssd_sp<4>(a, n_chunks, n_segs, w); break;
   }
   hipError_t ferr = hipFreeAsync(ws, a.stream);
   return err != hipSuccess ? err : ferr;

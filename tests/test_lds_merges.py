@@ -55,12 +55,12 @@ def _check(src):
         before, after = ex.map(lambda w: _mir(src, w), ("before", "after"))
     merged, problems = 0, []
     for fn, mir in after.items():
-        orig = {}  # memory operand -> (address register, byte offset)
+        orig = {}  # memory operand -> [(address register, byte offset)], one per access that uses it
         for line in before.get(fn, "").splitlines():
             m = SINGLE.search(line)
             if m:
                 ops, nums = _operands(m.group(1))
-                orig[m.group(2)] = (ops[0].split(":")[0], nums[-2] % 65536)
+                orig.setdefault(m.group(2), []).append((ops[0].split(":")[0], nums[-2] % 65536))
         consts = {m.group(1): int(m.group(2)) for m in map(CONST.match, mir.splitlines()) if m}
         rebase = {}
         for m in map(ADD.match, mir.splitlines()):
@@ -76,17 +76,23 @@ def _check(src):
             elt = int(m.group(3)) // 8 * (64 if m.group(2) else 1)
             ops, nums = _operands(m.group(4))
             base, o0, o1 = ops[0].split(":")[0], nums[-3], nums[-2]
-            (b0, want0), (b1, want1) = orig[m.group(5)], orig[m.group(6)]
-            k = 0
-            if base != b0:
-                base, k = rebase.get(base, (base, 0))
-            if base != b0 or b0 != b1:
-                problems.append(f"{fn}: {m.group(1)} from an unresolved base register")
-                continue
-            got = sorted([(o0 * elt + k) % (1 << 32), (o1 * elt + k) % (1 << 32)])
-            if got != sorted([want0, want1]):
-                problems.append(f"{fn}: {m.group(1)} offsets ({o0}, {o1}) x {elt} + {k} for byte offsets "
-                                f"({want0}, {want1})")
+            old_base, k = rebase.get(base, (base, 0))
+
+            def replaces(b0, w0, b1, w1):
+                if b0 != b1:
+                    return False
+                if b0 == base:  # same base register: offsets in element units
+                    return sorted([o0 * elt, o1 * elt]) == sorted([w0, w1])
+                if b0 == old_base:  # new base register = old base + k
+                    return sorted([(o0 * elt + k) % (1 << 32), (o1 * elt + k) % (1 << 32)]) == sorted([w0, w1])
+                return False
+
+            # an IR access can appear more than once (unrolled or duplicated code): the pair
+            # must replace two of the original accesses, from one base register
+            ok = any(replaces(b0, w0, b1, w1) for (b0, w0) in orig[m.group(5)] for (b1, w1) in orig[m.group(6)])
+            if not ok:
+                problems.append(f"{fn}: {m.group(1)} offsets ({o0}, {o1}) x {elt} (base {base}, rebased by {k}) "
+                                f"match no pair of the accesses it replaced: {orig[m.group(5)]}, {orig[m.group(6)]}")
     return merged, problems
 
 
