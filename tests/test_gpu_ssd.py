@@ -6,7 +6,8 @@ head's channels; it is pinned against the dense structured mixing matrix in
 tests/test_oracle_pins.py.  The GPU path takes bf16 operands in its matrix
 products and accumulates in fp32; outputs are bf16, so the bf16 bound applies:
 |x - x_ref| <= 2e-2 * (1 + |x_ref|), elementwise on y and on the last state.
-Cases: state sizes 16..128, ragged lengths around the 128-step chunk (and 64), every flag,
+Cases: state sizes 16..128, ragged lengths around the 128-step chunk (and 64) and the
+1024-step segment the chunk states are chained along, every flag,
 an initial state, the empty sequence, determinism, agreement with ssm_scan_fwd
 on broadcast inputs, the mid-size workload in full and the long workload
 (b1 L65536 H80 P64 N64) on sampled heads.
@@ -93,6 +94,15 @@ def test_lengths(L):
     w = BASE.with_shape(L=L, H=2, N=64)
     say(f"ssd L={L}")
     check(make(w, 10 + L, with_h0=True), f"ssd L={L}")
+
+
+@pytest.mark.parametrize("L,b,with_h0", [(1023, 1, True), (1024, 1, False), (1025, 2, True), (2049, 1, True),
+                                         (3 * 1024 + 130, 1, False)])
+def test_segment_edges(L, b, with_h0):
+    """Lengths around the 1024-step segments of 8 chunks that the chunk states are chained along."""
+    w = BASE.with_shape(L=L, b=b, H=1, N=32)
+    say(f"ssd segment edge L={L} b={b} h0={with_h0}")
+    check(make(w, 50 + L, with_h0=with_h0), f"ssd segment edge L={L}")
 
 
 def test_empty_sequence_and_no_heads():
