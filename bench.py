@@ -297,7 +297,48 @@ def main():
                            for k, v in prof.items() if v[1]},
                "note": "includes the workspace allocation and the forward chunk-state passes it reruns"}
         log(f"[bench] backward {bwd}")
-        del dy
+
+        # training form: the forward keeps the state every 64 steps, the backward starts its chunks from them
+        saved = torch.empty(ssm.saved_states_shape(w.b, w.L, w.E, w.N), dtype=torch.float32, device=dev)
+        ys = torch.empty_like(x["u"])
+
+        def fwd_save():
+            ssm.ssm_scan_fwd_save(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
+                                  x["softplus"], y=ys, saved_states=saved)
+
+        def bwd_saved():
+            return ssm.ssm_scan_bwd_saved(x["u"], x["delta"], x["A"], x["B"], x["C"], dy, saved, x["D"], x["z"],
+                                          x["delta_bias"], x["softplus"])
+
+        fwd_save()
+        g = bwd_saved()
+        del g
+        torch.cuda.synchronize()
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        f0.record(stream)
+        for _ in range(reps):
+            fwd_save()
+        f1.record(stream)
+        torch.cuda.synchronize()
+        ssm.ssm_profile_read()
+        ssm.ssm_profile_enable(True)
+        b0.record(stream)
+        for _ in range(reps):
+            g = bwd_saved()
+        b1.record(stream)
+        torch.cuda.synchronize()
+        ssm.ssm_profile_enable(False)
+        del g
+        prof = ssm.ssm_profile_read()
+        fs_ms, bs_ms = f0.elapsed_time(f1) / reps, b0.elapsed_time(b1) / reps
+        bwd["from_saved_states"] = {
+            "forward_with_save_ms": round(fs_ms, 4), "backward_ms": round(bs_ms, 4),
+            "saved_bytes": saved.numel() * 4,
+            "kernels": {k: {"avg_us": round(1e3 * v[0] / v[1], 2), "launches": v[1]} for k, v in prof.items() if v[1]},
+            "note": "ssm_scan_fwd_save keeps the state every 64 steps (1/64 of the states); ssm_scan_bwd_saved "
+                    "starts its 64-step chunks from them instead of rerunning the forward chunk-state passes"}
+        log(f"[bench] backward from saved states {bwd['from_saved_states']}")
+        del dy, saved, ys
 
     # the scan with a scalar transition per head, in chunks of MFMA matrix products
     ssd = None

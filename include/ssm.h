@@ -127,6 +127,35 @@ SSM_API int ssm_scan_fwd_from(const void* u, const void* delta, const float* A, 
                               int64_t b, int64_t L, int64_t E, int64_t N, int dtype, void* stream);
 
 /*
+ * Interval of the states saved by ssm_scan_fwd_save: the backward's chunk.
+ */
+#define SSM_SAVE_INTERVAL 64
+
+/*
+ * ssm_scan_fwd_from that also saves the state at every SSM_SAVE_INTERVAL-th
+ * step, for ssm_scan_bwd_saved.  The backward recomputes the states inside its
+ * 64-step chunks from the state entering each chunk; taking those boundary
+ * states from the forward spares it a pass over the sequence.  Only the
+ * boundaries are kept (1/64 of the [b, L, E, N] states), in line with keeping
+ * the expanded state on chip and recomputing intermediates in the backward
+ * ("Mamba: Linear-Time Sequence Modeling with Selective State Spaces",
+ * abhik.ai, "Compose the updates instead of waiting for every state").
+ *
+ * saved_states  [b, K, E, N] float (device), K = ceil(L / 64) - 1 (0 when
+ *               L <= 64; then it may be NULL): saved_states[bi, k, e, n] is
+ *               the state h[n] of (bi, e) after step 64 (k + 1) - 1, i.e. the
+ *               state entering step 64 (k + 1).  Written fully; must not
+ *               overlap any other argument.
+ * Everything else, and the results y and last_state, as ssm_scan_fwd_from.
+ * Errors: SSM_ERR_NULL when K > 0 and saved_states is NULL; SSM_ERR_ALIGN
+ * when it is not 4-byte aligned; otherwise as ssm_scan_fwd_from.
+ */
+SSM_API int ssm_scan_fwd_save(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                              const float* D, const void* z, const float* delta_bias, int softplus,
+                              const float* initial_state, void* y, float* last_state, float* saved_states,
+                              int64_t b, int64_t L, int64_t E, int64_t N, int dtype, void* stream);
+
+/*
  * One recurrent step for every (b, e) -- the SSM half of the decode step of
  * [AB] row 6 "Carry both buffers to the next token":
  *   d          = delta[b,e] + delta_bias[e], softplus(d) when softplus != 0
@@ -182,6 +211,23 @@ SSM_API int ssm_scan_bwd(const void* u, const void* delta, const float* A, const
                          void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz, float* d_delta_bias,
                          float* d_initial_state, int64_t b, int64_t L, int64_t E, int64_t N, int dtype,
                          void* stream);
+
+/*
+ * ssm_scan_bwd with the states entering its chunks taken from saved_states
+ * (the output of ssm_scan_fwd_save on the same inputs and initial_state:
+ * [b, K, E, N] float, K = ceil(L / 64) - 1, read only) instead of being
+ * recomputed.  Same outputs as ssm_scan_bwd up to rounding (the forward's
+ * states are the same recurrence evaluated over its own chunks); the
+ * workspace shrinks by the recomputed states.  Errors: SSM_ERR_NULL when
+ * K > 0 and saved_states is NULL; SSM_ERR_ALIGN when it is not 4-byte
+ * aligned; otherwise as ssm_scan_bwd.
+ */
+SSM_API int ssm_scan_bwd_saved(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                               const float* D, const void* z, const float* delta_bias, int softplus,
+                               const float* initial_state, const float* saved_states, const void* dy,
+                               const float* d_last_state, void* du, void* ddelta, float* dA, float* dB, float* dC,
+                               float* dD, void* dz, float* d_delta_bias, float* d_initial_state, int64_t b,
+                               int64_t L, int64_t E, int64_t N, int dtype, void* stream);
 
 /*
  * The scan with a scalar transition per head -- structured state-space

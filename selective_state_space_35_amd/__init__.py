@@ -85,10 +85,14 @@ def load_library():
     lib.ssm_scan_fwd.argtypes = [_vp] * 8 + [_int, _vp, _vp] + [_i64] * 4 + [_int, _vp]
     lib.ssm_scan_fwd_from.restype = _int
     lib.ssm_scan_fwd_from.argtypes = [_vp] * 8 + [_int, _vp, _vp, _vp] + [_i64] * 4 + [_int, _vp]
+    lib.ssm_scan_fwd_save.restype = _int
+    lib.ssm_scan_fwd_save.argtypes = [_vp] * 8 + [_int, _vp, _vp, _vp, _vp] + [_i64] * 4 + [_int, _vp]
     lib.ssm_state_update.restype = _int
     lib.ssm_state_update.argtypes = [_vp] * 9 + [_int, _vp] + [_i64] * 3 + [_int, _vp]
     lib.ssm_scan_bwd.restype = _int
     lib.ssm_scan_bwd.argtypes = [_vp] * 8 + [_int] + [_vp] * 12 + [_i64] * 4 + [_int, _vp]
+    lib.ssm_scan_bwd_saved.restype = _int
+    lib.ssm_scan_bwd_saved.argtypes = [_vp] * 8 + [_int] + [_vp] * 13 + [_i64] * 4 + [_int, _vp]
     lib.ssm_ssd_fwd.restype = _int
     lib.ssm_ssd_fwd.argtypes = [_vp] * 8 + [_int] + [_vp] * 3 + [_i64] * 5 + [_int, _vp]
     lib.ssm_conv_fwd.restype = _int
@@ -183,12 +187,22 @@ def _raise_on(fn, status):
         raise SSMError(fn, status, detail)
 
 
+SAVE_INTERVAL = 64  # SSM_SAVE_INTERVAL of include/ssm.h
+
+
+def saved_states_shape(b, L, E, N):
+    """Shape of the states ``ssm_scan_fwd_save`` keeps: one [E, N] slice per 64 steps but the last."""
+    return (b, max((L + SAVE_INTERVAL - 1) // SAVE_INTERVAL - 1, 0), E, N)
+
+
 def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=False, y=None,
-                 last_state=None, return_last_state=True, initial_state=None):
+                 last_state=None, return_last_state=True, initial_state=None, saved_states=None):
     """Selective scan forward on the GPU.  Returns ``(y, last_state)`` (last_state None if not requested).
 
     ``initial_state`` [b, E, N] float32 continues the recurrence from that state
-    (the C entry point ``ssm_scan_fwd_from``); None starts from zero.
+    (the C entry point ``ssm_scan_fwd_from``); None starts from zero.  A given
+    ``saved_states`` buffer (``saved_states_shape``, float32) receives the state
+    every 64 steps (the C entry point ``ssm_scan_fwd_save``).
     """
     import torch
 
@@ -223,6 +237,15 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=Fa
     _check(torch, "initial_state", initial_state, (b, E, N), torch.float32, device, optional=True)
     if initial_state is not None and last_state is not None and initial_state.data_ptr() == last_state.data_ptr():
         raise ValueError("initial_state must not be the last_state buffer")
+    if saved_states is not None:
+        _check(torch, "saved_states", saved_states, saved_states_shape(b, L, E, N), torch.float32, device)
+        with torch.cuda.device(device):
+            status = lib.ssm_scan_fwd_save(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                           _ptr(delta_bias), int(bool(softplus)), _ptr(initial_state), _ptr(y),
+                                           _ptr(last_state), _ptr(saved_states), b, L, E, N, code,
+                                           _stream_of(torch, device))
+        _raise_on("ssm_scan_fwd_save", status)
+        return y, last_state
     with torch.cuda.device(device):
         if initial_state is None:
             status = lib.ssm_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
@@ -243,13 +266,40 @@ def ssm_scan_fwd_from(u, delta, A, B, C, D=None, z=None, delta_bias=None, softpl
                         return_last_state=return_last_state, initial_state=initial_state)
 
 
+def ssm_scan_fwd_save(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=False, initial_state=None,
+                      y=None, last_state=None, saved_states=None):
+    """``ssm_scan_fwd_from`` that also keeps the state every 64 steps for ``ssm_scan_bwd_saved``.
+
+    Returns ``(y, last_state, saved_states)``; saved_states [b, ceil(L / 64) - 1, E, N] float32 holds
+    the state entering steps 64, 128, ...
+    """
+    import torch
+
+    b, L, E = u.shape
+    N = A.shape[1]
+    if saved_states is None:
+        saved_states = torch.empty(saved_states_shape(b, L, E, N), dtype=torch.float32, device=u.device)
+    y, last_state = ssm_scan_fwd(u, delta, A, B, C, D, z, delta_bias, softplus, y=y, last_state=last_state,
+                                 initial_state=initial_state, saved_states=saved_states)
+    return y, last_state, saved_states
+
+
+def ssm_scan_bwd_saved(u, delta, A, B, C, dy, saved_states, D=None, z=None, delta_bias=None, softplus=False,
+                       initial_state=None, d_last_state=None):
+    """``ssm_scan_bwd`` with the states entering its chunks from ``ssm_scan_fwd_save``."""
+    return ssm_scan_bwd(u, delta, A, B, C, dy, D, z, delta_bias, softplus, initial_state=initial_state,
+                        d_last_state=d_last_state, saved_states=saved_states)
+
+
 def ssm_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=False, initial_state=None,
-                 d_last_state=None):
+                 d_last_state=None, saved_states=None):
     """Gradients of sum(dy * y) + sum(d_last_state * last_state) for ``ssm_scan_fwd_from``'s arguments.
 
     Returns a dict: du, ddelta (and dz when z is given) [b, L, E] in the streamed dtype;
     dA [E, N], dB and dC [b, L, N], d_initial_state [b, E, N], dD and d_delta_bias [E]
-    (None when D / delta_bias are None), all float32.
+    (None when D / delta_bias are None), all float32.  ``saved_states`` from
+    ``ssm_scan_fwd_save`` on the same inputs replaces the recomputed chunk states
+    (the C entry point ``ssm_scan_bwd_saved``).
     """
     import torch
 
@@ -288,6 +338,17 @@ def ssm_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplu
         "d_delta_bias": torch.empty((E,), dtype=f32, device=device) if delta_bias is not None else None,
         "d_initial_state": torch.empty((b, E, N), dtype=f32, device=device),
     }
+    if saved_states is not None:
+        _check(torch, "saved_states", saved_states, saved_states_shape(b, L, E, N), f32, device)
+        with torch.cuda.device(device):
+            status = lib.ssm_scan_bwd_saved(
+                _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                int(bool(softplus)), _ptr(initial_state), _ptr(saved_states), _ptr(dy), _ptr(d_last_state),
+                _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]),
+                _ptr(g["dz"]), _ptr(g["d_delta_bias"]), _ptr(g["d_initial_state"]), b, L, E, N, code,
+                _stream_of(torch, device))
+        _raise_on("ssm_scan_bwd_saved", status)
+        return g
     with torch.cuda.device(device):
         status = lib.ssm_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
                                   int(bool(softplus)), _ptr(initial_state), _ptr(dy), _ptr(d_last_state), _ptr(g["du"]),

@@ -39,6 +39,22 @@ int check_sizes(int64_t b, int64_t L, int64_t E, int64_t N, int dtype) {
   return SSM_OK;
 }
 
+// states saved by ssm_scan_fwd_save: one [E, N] slice per kSaveEvery steps but the last
+int64_t saved_count(int64_t b, int64_t L, int64_t E, int64_t N) {
+  if (b <= 0 || L <= ssm::kSaveEvery || E <= 0 || N <= 0) return 0;
+  return b * ((L + ssm::kSaveEvery - 1) / ssm::kSaveEvery - 1) * E * N;
+}
+
+int scan_fwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C, const float* D,
+                  const void* z, const float* delta_bias, int softplus, const float* initial_state, void* y,
+                  float* last_state, float* saved, int64_t b, int64_t L, int64_t E, int64_t N, int dtype,
+                  void* stream);
+int scan_bwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C, const float* D,
+                  const void* z, const float* delta_bias, int softplus, const float* initial_state,
+                  const float* saved, const void* dy, const float* d_last_state, void* du, void* ddelta, float* dA,
+                  float* dB, float* dC, float* dD, void* dz, float* d_delta_bias, float* d_initial_state, int64_t b,
+                  int64_t L, int64_t E, int64_t N, int dtype, void* stream);
+
 }  // namespace
 
 extern "C" {
@@ -54,6 +70,30 @@ int ssm_scan_fwd_from(const void* u, const void* delta, const float* A, const vo
                       const float* D, const void* z, const float* delta_bias, int softplus,
                       const float* initial_state, void* y, float* last_state, int64_t b, int64_t L, int64_t E,
                       int64_t N, int dtype, void* stream) {
+  return scan_fwd_impl(u, delta, A, B, C, D, z, delta_bias, softplus, initial_state, y, last_state, nullptr, b, L, E, N,
+                       dtype, stream);
+}
+
+int ssm_scan_fwd_save(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                      const float* D, const void* z, const float* delta_bias, int softplus,
+                      const float* initial_state, void* y, float* last_state, float* saved_states, int64_t b,
+                      int64_t L, int64_t E, int64_t N, int dtype, void* stream) {
+  int st = check_sizes(b, L, E, N, dtype);
+  if (st != SSM_OK) return st;
+  if (saved_count(b, L, E, N) > 0 && !saved_states) return SSM_ERR_NULL;
+  if (saved_states && !aligned(saved_states, 4)) return SSM_ERR_ALIGN;
+  return scan_fwd_impl(u, delta, A, B, C, D, z, delta_bias, softplus, initial_state, y, last_state, saved_states, b, L,
+                       E, N, dtype, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int scan_fwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C, const float* D,
+                  const void* z, const float* delta_bias, int softplus, const float* initial_state, void* y,
+                  float* last_state, float* saved, int64_t b, int64_t L, int64_t E, int64_t N, int dtype,
+                  void* stream) {
   int st = check_sizes(b, L, E, N, dtype);
   if (st != SSM_OK) return st;
   if (b == 0 || E == 0) return SSM_OK;
@@ -73,10 +113,15 @@ int ssm_scan_fwd_from(const void* u, const void* delta, const float* A, const vo
   ssm::ScanArgs a;
   a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias;
   a.softplus = softplus ? 1 : 0; a.y = y; a.last_state = last_state; a.h0 = initial_state;
+  a.saved = saved_count(b, L, E, N) > 0 ? saved : nullptr;
   a.b = b; a.L = L; a.E = E; a.N = N; a.dtype = dtype;
   a.stream = static_cast<hipStream_t>(stream);
   return hip_status(ssm::launch_scan(a));
 }
+
+}  // namespace
+
+extern "C" {
 
 int ssm_state_update(float* state, const void* x, const void* delta, const float* A, const void* B, const void* C,
                      const float* D, const void* z, const float* delta_bias, int softplus, void* y, int64_t b,
@@ -109,6 +154,33 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
                  const float* d_last_state, void* du, void* ddelta, float* dA, float* dB, float* dC, float* dD,
                  void* dz, float* d_delta_bias, float* d_initial_state, int64_t b, int64_t L, int64_t E, int64_t N,
                  int dtype, void* stream) {
+  return scan_bwd_impl(u, delta, A, B, C, D, z, delta_bias, softplus, initial_state, nullptr, dy, d_last_state, du,
+                       ddelta, dA, dB, dC, dD, dz, d_delta_bias, d_initial_state, b, L, E, N, dtype, stream);
+}
+
+int ssm_scan_bwd_saved(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                       const float* D, const void* z, const float* delta_bias, int softplus,
+                       const float* initial_state, const float* saved_states, const void* dy,
+                       const float* d_last_state, void* du, void* ddelta, float* dA, float* dB, float* dC, float* dD,
+                       void* dz, float* d_delta_bias, float* d_initial_state, int64_t b, int64_t L, int64_t E,
+                       int64_t N, int dtype, void* stream) {
+  int st = check_sizes(b, L, E, N, dtype);
+  if (st != SSM_OK) return st;
+  if (saved_count(b, L, E, N) > 0 && !saved_states) return SSM_ERR_NULL;
+  if (saved_states && !aligned(saved_states, 4)) return SSM_ERR_ALIGN;
+  return scan_bwd_impl(u, delta, A, B, C, D, z, delta_bias, softplus, initial_state, saved_states, dy, d_last_state,
+                       du, ddelta, dA, dB, dC, dD, dz, d_delta_bias, d_initial_state, b, L, E, N, dtype, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int scan_bwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C, const float* D,
+                  const void* z, const float* delta_bias, int softplus, const float* initial_state,
+                  const float* saved, const void* dy, const float* d_last_state, void* du, void* ddelta, float* dA,
+                  float* dB, float* dC, float* dD, void* dz, float* d_delta_bias, float* d_initial_state, int64_t b,
+                  int64_t L, int64_t E, int64_t N, int dtype, void* stream) {
   int st = check_sizes(b, L, E, N, dtype);
   if (st != SSM_OK) return st;
   int64_t bl = 0, ble = 0;
@@ -135,10 +207,15 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
   a.softplus = softplus ? 1 : 0; a.h0 = initial_state; a.dy = dy; a.dlast = d_last_state;
   a.du = du; a.ddelta = ddelta; a.dA = dA; a.dB = dB; a.dC = dC; a.dD = D ? dD : nullptr; a.dz = z ? dz : nullptr;
   a.dbias = delta_bias ? d_delta_bias : nullptr; a.dh0 = d_initial_state;
+  a.saved = saved_count(b, L, E, N) > 0 ? saved : nullptr;
   a.b = b; a.L = L; a.E = E; a.N = N; a.dtype = dtype;
   a.stream = static_cast<hipStream_t>(stream);
   return hip_status(ssm::launch_scan_bwd(a));
 }
+
+}  // namespace
+
+extern "C" {
 
 int ssm_ssd_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C, const float* D,
                 const void* z, const float* delta_bias, int softplus, const float* initial_state, void* y,

@@ -211,7 +211,7 @@ __global__ __launch_bounds__(kBwdWaves * kWave) __attribute__((amdgpu_waves_per_
     const T* __restrict__ u, const T* __restrict__ delta, const float* __restrict__ A,
     const float* __restrict__ B16, const float* __restrict__ C16, const float* __restrict__ D,
     const T* __restrict__ z, const float* __restrict__ bias, const T* __restrict__ dy, const float* __restrict__ h0,
-    const float* __restrict__ fcarry, int fslots, const float* __restrict__ xin, T* __restrict__ du,
+    const float* __restrict__ fcarry, int fslots, int fchunks, const float* __restrict__ xin, T* __restrict__ du,
     T* __restrict__ ddelta, T* __restrict__ dz, float* __restrict__ dh0, float* __restrict__ dA_part,
     float* __restrict__ dDb_part, float* __restrict__ dbc_part, int64_t L, int64_t E, int N, int n_chunks,
     int e_blocks) {
@@ -291,7 +291,7 @@ __global__ __launch_bounds__(kBwdWaves * kWave) __attribute__((amdgpu_waves_per_
     if (c == 0)
       h[k] = (h0 && n < N) ? h0[(bi * E + ec) * N + n] : 0.f;
     else
-      h[k] = n < N ? fcarry[((bi * n_chunks + c - 1) * E + ec) * fslots + n] : 0.f;
+      h[k] = n < N ? fcarry[((bi * fchunks + c - 1) * E + ec) * fslots + n] : 0.f;
     X[k] = xin[((bi * n_chunks + c) * E + ec) * kS + n];
   }
   __syncthreads();
@@ -578,18 +578,19 @@ hipError_t fill(float* dst, const float* src, int64_t n, hipStream_t s) {
 
 template <typename T, bool SOFTPLUS, bool HAS_Z, bool HAS_D>
 hipError_t run_main(const BwdArgs& a, int n_chunks, int e_blocks, const float* B16, const float* C16,
-                    const float* fcarry, int fslots, const float* xin, float* dA_part, float* dDb_part,
+                    const float* fcarry, int fslots, int fchunks, const float* xin, float* dA_part, float* dDb_part,
                     float* dbc_part) {
   return launch_kind(kKindBwdMain, bwd_main_kernel<T, SOFTPLUS, HAS_Z, HAS_D>, a.b * n_chunks * e_blocks,
                      kBwdWaves * kWave, a.stream, static_cast<const T*>(a.u), static_cast<const T*>(a.delta), a.A, B16,
                      C16, a.D, static_cast<const T*>(a.z), a.bias, static_cast<const T*>(a.dy), a.h0, fcarry, fslots,
-                     xin, static_cast<T*>(a.du), static_cast<T*>(a.ddelta), static_cast<T*>(a.dz), a.dh0, dA_part,
-                     dDb_part, dbc_part, a.L, a.E, int(a.N), n_chunks, e_blocks);
+                     fchunks, xin, static_cast<T*>(a.du), static_cast<T*>(a.ddelta), static_cast<T*>(a.dz), a.dh0,
+                     dA_part, dDb_part, dbc_part, a.L, a.E, int(a.N), n_chunks, e_blocks);
 }
 
 template <typename T>
 hipError_t bwd_typed(const BwdArgs& a, int n_chunks, const float* B16, const float* C16, const float* fcarry,
-                     int fslots, float* xagg, float* xsum, float* dA_part, float* dDb_part, float* dbc_part) {
+                     int fslots, int fchunks, float* xagg, float* xsum, float* dA_part, float* dDb_part,
+                     float* dbc_part) {
   const int N = int(a.N);
   const int eb_agg = int((a.E + kWave - 1) / kWave);
   hipError_t err = hipSuccess;
@@ -616,8 +617,9 @@ hipError_t bwd_typed(const BwdArgs& a, int n_chunks, const float* B16, const flo
                                     (const float*)xsum, a.dlast, a.b, a.E, N, n_chunks);
   if (err != hipSuccess) return err;
   const int e_blocks = int((a.E + kChPerBlock - 1) / kChPerBlock);
-#define SSM_BWD_MAIN(SP, HZ, HD) \
-  return run_main<T, SP, HZ, HD>(a, n_chunks, e_blocks, B16, C16, fcarry, fslots, xagg, dA_part, dDb_part, dbc_part)
+#define SSM_BWD_MAIN(SP, HZ, HD)                                                                              \
+  return run_main<T, SP, HZ, HD>(a, n_chunks, e_blocks, B16, C16, fcarry, fslots, fchunks, xagg, dA_part, dDb_part, \
+                                 dbc_part)
   const bool hz = a.z != nullptr, hd = a.D != nullptr;
   if (a.softplus) {
     if (hz) { if (hd) SSM_BWD_MAIN(true, true, true); else SSM_BWD_MAIN(true, true, false); }
@@ -649,14 +651,19 @@ hipError_t launch_scan_bwd(const BwdArgs& a) {
   }
   const int n_chunks = int((L + kBwdChunk - 1) / kBwdChunk);
   const int e_blocks = int((E + kChPerBlock - 1) / kChPerBlock);
-  const int fslots = chunk_state_slots(N);
+  // states entering the chunks: the forward's saved states ([b, chunk - 1, E, N]) when
+  // given (the chunk is the save interval), else recomputed here
+  static_assert(kBwdChunk == kSaveEvery, "the saved states are the chunk boundaries");
+  const bool saved = a.saved != nullptr;
+  const int fslots = saved ? int(N) : chunk_state_slots(N);
+  const int fchunks = saved ? n_chunks - 1 : n_chunks;  // chunk slots per batch row
   // workspace (floats): [widened rows | B16 | C16 | forward carries | forward sums | reverse carries |
   //                      reverse sums | dB/dC partials | dA partials | dD/dbias partials]
   const size_t nb = size_t(b), nL = size_t(L), nE = size_t(E), nc = size_t(n_chunks);
-  const size_t n_rows = a.dtype == 0 ? 0 : 2 * nb * nL * size_t(N);
+  const size_t n_rows = a.dtype == 0 || saved ? 0 : 2 * nb * nL * size_t(N);
   const size_t n_row16 = nb * nL * kS;
-  const size_t n_fc = n_chunks > 1 ? nb * nc * nE * size_t(fslots) : 0;
-  const size_t n_fs = n_chunks > 1 ? nb * nc * nE : 0;
+  const size_t n_fc = n_chunks > 1 && !saved ? nb * nc * nE * size_t(fslots) : 0;
+  const size_t n_fs = n_chunks > 1 && !saved ? nb * nc * nE : 0;
   const size_t n_xa = nb * nc * nE * kS;
   const size_t n_xs = nb * nc * nE;
   const size_t n_bc = nb * nL * size_t(e_blocks) * kRed;
@@ -676,7 +683,7 @@ hipError_t launch_scan_bwd(const BwdArgs& a) {
   float* rows = f + offs[0];
   float* B16 = f + offs[1];
   float* C16 = f + offs[2];
-  float* fcarry = f + offs[3];
+  const float* fcarry = saved ? a.saved : f + offs[3];
   float* fsum = f + offs[4];
   float* xagg = f + offs[5];
   float* xsum = f + offs[6];
@@ -691,7 +698,7 @@ hipError_t launch_scan_bwd(const BwdArgs& a) {
                      : launch_kind(kKindBwdRows, bwd_rows_kernel<bf16_bits>, (nr16 + 255) / 256, 256, a.stream,
                                    static_cast<const bf16_bits*>(a.B), static_cast<const bf16_bits*>(a.C), B16, C16,
                                    b * L, int(N));
-  if (err == hipSuccess && n_chunks > 1) {
+  if (err == hipSuccess && n_chunks > 1 && !saved) {
     ScanArgs s{};
     s.u = a.u; s.delta = a.delta; s.A = a.A; s.B = a.B; s.C = a.C; s.D = a.D; s.z = a.z; s.bias = a.bias;
     s.softplus = a.softplus; s.y = nullptr; s.last_state = nullptr; s.h0 = a.h0;
@@ -700,12 +707,13 @@ hipError_t launch_scan_bwd(const BwdArgs& a) {
     pl.chunk_len = kBwdChunk;
     pl.n_chunks = n_chunks;
     pl.e_blocks = int((E + kWave - 1) / kWave);
-    err = launch_chunk_states(s, pl, rows, fcarry, fsum);
+    err = launch_chunk_states(s, pl, rows, f + offs[3], fsum);
   }
   if (err == hipSuccess)
-    err = a.dtype == 0 ? bwd_typed<float>(a, n_chunks, B16, C16, fcarry, fslots, xagg, xsum, dA_part, dDb_part, dbc)
-                       : bwd_typed<bf16_bits>(a, n_chunks, B16, C16, fcarry, fslots, xagg, xsum, dA_part, dDb_part,
-                                              dbc);
+    err = a.dtype == 0 ? bwd_typed<float>(a, n_chunks, B16, C16, fcarry, fslots, fchunks, xagg, xsum, dA_part,
+                                          dDb_part, dbc)
+                       : bwd_typed<bf16_bits>(a, n_chunks, B16, C16, fcarry, fslots, fchunks, xagg, xsum, dA_part,
+                                              dDb_part, dbc);
   if (err == hipSuccess) {
     const int64_t n = b * L * kRed;
     err = launch_kind(kKindBwdReduce, bwd_reduce_bc_kernel, (n + 255) / 256, 256, a.stream, (const float*)dbc, a.dB,

@@ -20,10 +20,12 @@ struct ScanArgs {
   void* y;
   float* last_state;   // nullable
   const float* h0;     // nullable: incoming state [b, E, N] (zero when null)
+  float* saved;        // nullable: the state after every kSaveEvery-th step, [b, K, E, N], K = ceil(L / kSaveEvery) - 1
   int64_t b, L, E, N;
   int dtype;           // 0 = f32, 1 = bf16
   hipStream_t stream;
 };
+constexpr int64_t kSaveEvery = 64;  // interval of the saved states (the backward's chunk)
 
 struct UpdateArgs {
   float* state;
@@ -103,6 +105,7 @@ struct BwdArgs {
   void* dz;            // required when z is given
   float* dbias;        // nullable
   float* dh0;          // nullable
+  const float* saved;  // nullable: the forward's states every kSaveEvery steps (ScanArgs::saved)
   int64_t b, L, E, N;
   int dtype;
   hipStream_t stream;

@@ -245,14 +245,15 @@ __global__ __launch_bounds__(256) void scan_carry_kernel(const float* __restrict
 // ---------------------------------------------------------------------------
 // FULL: every lane of every block is a real channel (E % 64 == 0), so the
 // per-step store needs no exec-mask branch.
-template <typename T, int NS, bool EXACT, bool SOFTPLUS, bool HAS_Z, bool FULL>
+template <typename T, int NS, bool EXACT, bool SOFTPLUS, bool HAS_Z, bool FULL, bool SAVE>
 __global__ __launch_bounds__(kWave) SSM_SCAN_OCCUPANCY void scan_main_kernel(
     const T* __restrict__ u, const T* __restrict__ delta, const float* __restrict__ A,
     const float* __restrict__ B, const float* __restrict__ C, const float* __restrict__ D,
     const T* __restrict__ z, const float* __restrict__ bias, T* __restrict__ y,
-    float* __restrict__ last_state, const float* __restrict__ carry, const float* __restrict__ h0, int64_t L,
-    int64_t E, int N, int64_t chunk_len, int n_chunks, int e_blocks) {
+    float* __restrict__ last_state, const float* __restrict__ carry, const float* __restrict__ h0,
+    float* __restrict__ saved, int64_t L, int64_t E, int N, int64_t chunk_len, int n_chunks, int e_blocks) {
   const BlockPos p = block_pos(n_chunks, e_blocks, E, L, chunk_len);
+  const int64_t n_saved = (L + kSaveEvery - 1) / kSaveEvery - 1;
   float A2[NS];
 #pragma unroll
   for (int n = 0; n < NS; n++) A2[n] = (EXACT || n < N) ? A[p.ec * N + n] * kLog2e : 0.f;
@@ -308,6 +309,14 @@ __global__ __launch_bounds__(kWave) SSM_SCAN_OCCUPANCY void scan_main_kernel(
     if (HAS_Z) out *= silu(zz);
     if (FULL || p.active) buf_store(ry, voff, soff, out, (T*)nullptr);
     soff += row_bytes;
+    // the state after every kSaveEvery-th step of the sequence, for the backward (a uniform
+    // test; a variant of its own, so that the kernel without it compiles as before)
+    if (SAVE && (p.t0 + ks) % kSaveEvery == 0 && (p.t0 + ks) < L && p.active) {
+      float* dst = saved + ((p.bi * n_saved + (p.t0 + ks) / kSaveEvery - 1) * E + p.e) * N;
+#pragma unroll
+      for (int n = 0; n < NS; n++)
+        if (EXACT || n < N) dst[n] = h[n];
+    }
   };
   const int n_groups = n_steps / kGroup;
   float cu[kGroup], cd[kGroup], cz[kGroup];
@@ -511,9 +520,14 @@ hipError_t run_scan(const ScanArgs& a, const ScanPlan& pl, const ScanBufs& w) {
   const int N = int(a.N);
   hipError_t err = run_carries<T, NS, EXACT, SOFTPLUS>(a, pl, w);
   if (err != hipSuccess) return err;
-  return launch_kind(kKindMain, scan_main_kernel<T, NS, EXACT, SOFTPLUS, HAS_Z, FULL>, a.b * pl.n_chunks * pl.e_blocks, kWave,
-                a.stream, u, dl, a.A, w.B, w.C, a.D, z, a.bias, y, a.last_state, (const float*)w.carry, a.h0, a.L,
-                a.E, N, pl.chunk_len, pl.n_chunks, pl.e_blocks);
+  const int64_t blocks = a.b * pl.n_chunks * pl.e_blocks;
+  if (a.saved)  // the saving variant exists for the general channel count only
+    return launch_kind(kKindMain, scan_main_kernel<T, NS, EXACT, SOFTPLUS, HAS_Z, false, true>, blocks, kWave, a.stream,
+                       u, dl, a.A, w.B, w.C, a.D, z, a.bias, y, a.last_state, (const float*)w.carry, a.h0, a.saved, a.L,
+                       a.E, N, pl.chunk_len, pl.n_chunks, pl.e_blocks);
+  return launch_kind(kKindMain, scan_main_kernel<T, NS, EXACT, SOFTPLUS, HAS_Z, FULL, false>, blocks, kWave, a.stream,
+                     u, dl, a.A, w.B, w.C, a.D, z, a.bias, y, a.last_state, (const float*)w.carry, a.h0,
+                     (float*)nullptr, a.L, a.E, N, pl.chunk_len, pl.n_chunks, pl.e_blocks);
 }
 
 template <typename T, int NS, bool EXACT, bool FULL>

@@ -187,6 +187,44 @@ def test_bwd_validation(lib):
                dB=None, dC=None) == OK
 
 
+def fwd_save(lib, saved=FAKE, u=FAKE, b=1, L=200, E=64, N=16, dtype=0):
+    return lib.ssm_scan_fwd_save(u, FAKE, FAKE, FAKE, FAKE, None, None, None, 1, None, FAKE, None, saved, b, L, E, N,
+                                 dtype, None)
+
+
+def bwd_saved(lib, saved=FAKE, **kw):
+    args = dict(u=FAKE, b=1, L=200, E=64, N=16, dtype=0, dy=FAKE)
+    args.update(kw)
+    a = args
+    return lib.ssm_scan_bwd_saved(a["u"], FAKE, FAKE, FAKE, FAKE, None, None, None, 1, None, saved, a["dy"], None, FAKE,
+                                  FAKE, FAKE, FAKE, FAKE, None, None, None, None, a["b"], a["L"], a["E"], a["N"],
+                                  a["dtype"], None)
+
+
+def test_saved_state_entry_points_validation(lib):
+    # the saved states are required as soon as the sequence is longer than one interval of 64
+    assert fwd_save(lib, saved=None, L=65) == ERR_NULL
+    assert bwd_saved(lib, saved=None, L=65) == ERR_NULL
+    assert fwd_save(lib, saved=FAKE + 2) == ERR_ALIGN
+    assert bwd_saved(lib, saved=FAKE + 2) == ERR_ALIGN
+    # otherwise the checks of ssm_scan_fwd_from / ssm_scan_bwd apply
+    assert fwd_save(lib, dtype=3) == ERR_DTYPE
+    assert fwd_save(lib, N=0) == ERR_N
+    assert fwd_save(lib, u=None) == ERR_NULL
+    assert fwd_save(lib, b=-1) == ERR_DIM
+    assert bwd_saved(lib, dtype=3) == ERR_DTYPE
+    assert bwd_saved(lib, u=None) == ERR_NULL
+    assert bwd_saved(lib, dy=None) == ERR_NULL
+    assert bwd_saved(lib, E=1 << 26) == ERR_DIM
+    # nothing to do: no saved states are needed, pointers are not looked at
+    assert fwd_save(lib, saved=None, b=0, u=None) == OK
+    assert fwd_save(lib, saved=None, E=0, u=None) == OK
+    assert ssm.saved_states_shape(3, 64, 5, 4) == (3, 0, 5, 4)
+    assert ssm.saved_states_shape(3, 65, 5, 4) == (3, 1, 5, 4)
+    assert ssm.saved_states_shape(2, 65536, 5120, 16) == (2, 1023, 5120, 16)
+    assert ssm.saved_states_shape(1, 0, 5, 4) == (1, 0, 5, 4)
+
+
 def ssd(lib, x=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, bias=None, h0=None, y=FAKE, last=None,
         b=1, L=8, H=2, P=64, N=16, dtype=1):
     return lib.ssm_ssd_fwd(x, delta, A, B, C, D, z, bias, 1, h0, y, last, b, L, H, P, N, dtype, None)
