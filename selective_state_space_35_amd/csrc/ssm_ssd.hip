@@ -62,11 +62,27 @@ __device__ __forceinline__ bf16x8 lds8(const bf16_bits* p) { return *reinterpret
 __device__ __forceinline__ bf16_bits to_bf16(float v) { return __builtin_bit_cast(bf16_bits, static_cast<__bf16>(v)); }
 __device__ __forceinline__ float from_bf16(bf16_bits v) { return __uint_as_float(uint32_t(v) << 16); }
 
-// Column index of element k in row r of a transposed tile: 8-element (16-byte)
-// blocks are XOR-swizzled by (r / 8) mod 8, so the transposed writes of eight
-// rows r, r + 8, ... land in different LDS banks, while every 16-byte block
-// (all an MFMA fragment reads) stays contiguous.
-__device__ __forceinline__ int swz(int r, int k) { return (((k >> 3) ^ ((r >> 3) & 7)) << 3) | (k & 7); }
+// Four consecutive rows of one column of a row-major bf16 tile, by the
+// transposing LDS read of gfx950 (ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane m names 8 bytes and lane i receives element i % 4 of the bytes
+// named by lanes i / 4 + 4 j, j = 0..3 (measured on the device).  With lane m of
+// the group pointing at T[r0 + m / 4][c0 + 4 (m % 4)], lane i receives
+// T[r0 + j][c0 + i], j = 0..3: half of an MFMA operand fragment (column c0 + i,
+// four consecutive k) of a tile stored [k][column].  r0 may differ between the
+// four lane groups.  Rows of 144 bytes (or any stride that puts the 16 rows read
+// at once on distinct multiples of 4 banks) keep the read at two passes.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_col4(const bf16_bits* T, int ld, int r0, int c0) {
+  const int m = threadIdx.x % 16;
+  const bf16_bits* p = T + (r0 + m / 4) * ld + c0 + 4 * (m % 4);
+  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p);
+  return __builtin_bit_cast(uint2, v);
+}
+// an MFMA operand fragment of a [k][column] tile: column c0 + lane % 16, k = r0 .. r0 + 3 and r1 .. r1 + 3
+__device__ __forceinline__ bf16x8 lds_frag(const bf16_bits* T, int ld, int r0, int r1, int c0) {
+  const uint2 a = lds_col4(T, ld, r0, c0), b = lds_col4(T, ld, r1, c0);
+  return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
+}
 
 // Raw steps kJ l .. kJ l + kJ - 1 of lane l of the first wave (delta + bias; 0
 // past the end of the sequence), read early so their latency overlaps the other
@@ -146,21 +162,6 @@ __device__ __forceinline__ uint4 scale8(uint4 v, float w) {
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-// Rows s and s + 1 (s even) of columns c8 .. c8 + 7 (c8 a multiple of 8), given
-// as two 16-byte vectors, stored transposed into T (row stride ld): T[c8 + e][s]
-// and T[c8 + e][s + 1] go out as one 32-bit word, in the swizzled column blocks
-// of swz (the same for all 8 rows, which share r / 8).  The words are assembled
-// with byte permutes (low halves of a and b; high halves of a and b).
-__device__ __forceinline__ void store_pair_t(bf16_bits* T, int ld, int c8, int s, uint4 a, uint4 b) {
-  const uint32_t ua[4] = {a.x, a.y, a.z, a.w}, ub[4] = {b.x, b.y, b.z, b.w};
-  bf16_bits* col = T + swz(c8, s);
-#pragma unroll
-  for (int j = 0; j < 4; j++) {
-    *reinterpret_cast<uint32_t*>(col + (c8 + 2 * j) * ld) = __builtin_amdgcn_perm(ub[j], ua[j], 0x05040100u);
-    *reinterpret_cast<uint32_t*>(col + (c8 + 2 * j + 1) * ld) = __builtin_amdgcn_perm(ub[j], ua[j], 0x07060302u);
-  }
-}
-
 // ---------------------------------------------------------------------------
 // chunk states along a segment of kSeg chunks, per (batch, segment, head).
 // Chunk c's own state, transposed, S_c[p, n] = sum_s (w o X)[s, p] B[s, n], comes
@@ -170,7 +171,9 @@ __device__ __forceinline__ void store_pair_t(bf16_bits* T, int ld, int c8, int s
 // Written per chunk: R_c in bf16 [p][n] (not for the segment's first chunk, where
 // it is zero) and phi_c = A_h * (steps of the segment before chunk c); per
 // segment: R after its last chunk in fp32 [p][n] and the segment's A_h * (sum of
-// its steps).  Capped at 80 VGPRs so that three 8-wave workgroups share a CU: their
+// its steps).  B and the weighted X are staged row-major ([s][n], [s][p], 16-byte
+// row writes) and the MFMA operands are read down their columns with the
+// transposing LDS read.  Capped at 80 VGPRs so that three 8-wave workgroups share a CU: their
 // interleaving hides the reads better than a prefetch of the next chunk, whose
 // registers would leave room for two (measured 302 against 333 us at ssd_long).
 // ---------------------------------------------------------------------------
@@ -183,12 +186,12 @@ __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(6))
   constexpr int NP = NK * 32;
   constexpr int kBV = kQ / 2 * (NP / 8);  // (row pair, 16-byte column block) items of B
   constexpr int nBV = (kBV + kSsdThreads - 1) / kSsdThreads;
-  constexpr int ldt = kQ + kPad, ldo = NP + kPad;
+  constexpr int ldb = NP + kPad, ldx = kP + kPad, ldo = NP + kPad;
   constexpr int kWaves = kSsdThreads / kWave, kNBW = (NP / 16) * 4 / kWaves;  // 16-column blocks per wave
   static_assert(kNBW * kWaves == (NP / 16) * 4, "the column blocks divide over the waves");
   __shared__ float d_s[kQ], cum_s[kQ];
-  __shared__ __attribute__((aligned(16))) bf16_bits Bt[NP * ldt];   // B transposed: [n][s]
-  __shared__ __attribute__((aligned(16))) bf16_bits Xw[kP * ldt];   // (w o X) transposed: [p][s]
+  __shared__ __attribute__((aligned(16))) bf16_bits Bs[kQ * ldb];   // B rows [s][n]
+  __shared__ __attribute__((aligned(16))) bf16_bits Xw[kQ * ldx];   // (w o X) rows [s][p]
   __shared__ __attribute__((aligned(16))) bf16_bits So[kP * ldo];   // R_c in bf16 [p][n], on its way out
   const int h = blockIdx.x % H;
   const int rest = blockIdx.x / H;
@@ -254,7 +257,11 @@ __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(6))
 #pragma unroll
     for (int k = 0; k < nBV; k++) {
       const int v = threadIdx.x + k * kSsdThreads;
-      if (v < kBV) store_pair_t(Bt, ldt, (v % (NP / 8)) * 8, 2 * (v / (NP / 8)), cur.b0[k], cur.b1[k]);
+      if (v < kBV) {
+        bf16_bits* row = Bs + 2 * (v / (NP / 8)) * ldb + (v % (NP / 8)) * 8;
+        *reinterpret_cast<uint4*>(row) = cur.b0[k];
+        *reinterpret_cast<uint4*>(row + ldb) = cur.b1[k];
+      }
     }
     if (c > c_begin) {
 #pragma unroll
@@ -267,7 +274,8 @@ __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(6))
     const float last = cum_s[kQ - 1];
     const float w0 = exp2_fast((last - cum_s[s0]) * kLog2e) * d_s[s0];
     const float w1 = exp2_fast((last - cum_s[s0 + 1]) * kLog2e) * d_s[s0 + 1];
-    store_pair_t(Xw, ldt, p8, s0, scale8(cur.x0, w0), scale8(cur.x1, w1));
+    *reinterpret_cast<uint4*>(Xw + s0 * ldx + p8) = scale8(cur.x0, w0);
+    *reinterpret_cast<uint4*>(Xw + (s0 + 1) * ldx + p8) = scale8(cur.x1, w1);
     if (c > c_begin) {  // R_c out in 16-byte row pieces
       bf16_bits* out = rin + ((bi * n_chunks + c) * H + h) * int64_t(kP) * N;
       for (int v = threadIdx.x; v < kP * (NP / 8); v += kSsdThreads) {
@@ -280,7 +288,8 @@ __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(6))
     __syncthreads();
     bf16x8 xf[kQ / 32];
 #pragma unroll
-    for (int kk = 0; kk < kQ / 32; kk++) xf[kk] = lds8(&Xw[(pb * 16 + lr) * ldt + swz(pb * 16 + lr, kk * 32 + lk)]);
+    for (int kk = 0; kk < kQ / 32; kk++)  // A operand: rows p, k = s (read down the columns of [s][p])
+      xf[kk] = lds_frag(Xw, ldx, kk * 32 + lk, kk * 32 + lk + 4, pb * 16);
     const float decay = exp2_fast(last * kLog2e);
 #pragma unroll
     for (int i = 0; i < kNBW; i++) {
@@ -289,7 +298,7 @@ __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(6))
       if (nb * 16 < N) {
 #pragma unroll
         for (int kk = 0; kk < kQ / 32; kk++)
-          acc = mfma(xf[kk], lds8(&Bt[(nb * 16 + lr) * ldt + swz(nb * 16 + lr, kk * 32 + lk)]), acc);
+          acc = mfma(xf[kk], lds_frag(Bs, ldb, kk * 32 + lk, kk * 32 + lk + 4, nb * 16), acc);
       }
 #pragma unroll
       for (int r = 0; r < 4; r++) R[i][r] = fmaf(decay, R[i][r], acc[r]);
@@ -361,8 +370,8 @@ __global__ __launch_bounds__(256) void ssd_carry_kernel(float* seg_state, const 
 // matrix is built transposed (rows s, columns t) so that each lane ends with
 // its own step t in registers: those values are the A operand of the next
 // product directly, with the contraction index s in the order the transposed
-// tiles give it (s = 4 g + r and 16 + 4 g + r for lane group g); X is read in
-// the same order.
+// tiles give it (s = 4 g + r and 16 + 4 g + r for lane group g); X, staged
+// row-major, is read in the same order down its columns (transposing LDS read).
 // Every global read of the chunk (x, z, C, B, the incoming state, the steps) is
 // issued before anything else.  x, z and y are handled per thread as two rows
 // of 8 channels (16-byte accesses); the products' results go through an fp32
@@ -378,20 +387,20 @@ __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(6))
     int N, int n_chunks, int n_segs) {
   constexpr int NP = NK * 32;
   constexpr int ldr = NP + kPad;          // B and incoming-state tiles, bf16 elements per row
-  constexpr int ldt = kQ + kPad;          // X transposed
+  constexpr int ldx = kP + kPad;          // X rows [s][p]
   constexpr int ldy = kP + 4;             // fp32 result tile
   constexpr int kBV = kQ * (NP / 8);      // 16-byte pieces of the B tile
   constexpr int kSV = kP * (NP / 8);      // 16-byte pieces of the incoming state
   constexpr int nBV = (kBV + kSsdThreads - 1) / kSsdThreads;
   constexpr int nSV = (kSV + kSsdThreads - 1) / kSsdThreads;
-  constexpr int kBbytes = kQ * ldr * 2, kXbytes = kP * ldt * 2, kSbytes = kP * ldr * 2;
+  constexpr int kBbytes = kQ * ldr * 2, kXbytes = kQ * ldx * 2, kSbytes = kP * ldr * 2;
   constexpr int kTiles = kBbytes + kXbytes + kSbytes, kYbytes = kQ * ldy * 4;
   __shared__ float d_s[kQ], cum_s[kQ], w_s[kQ];
-  // B rows [s][n], X transposed [p][s] and the incoming state [p][n]; once the
+  // B rows [s][n], X rows [s][p] and the incoming state [p][n]; once the
   // products are done, the fp32 results [t][p] over all three
   __shared__ __attribute__((aligned(16))) char pool[kTiles > kYbytes ? kTiles : kYbytes];
   bf16_bits* Bs = reinterpret_cast<bf16_bits*>(pool);
-  bf16_bits* Xt = reinterpret_cast<bf16_bits*>(pool + kBbytes);
+  bf16_bits* Xs = reinterpret_cast<bf16_bits*>(pool + kBbytes);
   bf16_bits* Ss = reinterpret_cast<bf16_bits*>(pool + kBbytes + kXbytes);
   float* Ys = reinterpret_cast<float*>(pool);
   const int h = blockIdx.x % H;
@@ -467,7 +476,8 @@ __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(6))
       *reinterpret_cast<uint4*>(Ss + (v / (NP / 8)) * ldr + (v % (NP / 8)) * 8) = make_uint4(o[0], o[1], o[2], o[3]);
     }
   }
-  store_pair_t(Xt, ldt, p8, s0, x0, x1);
+  *reinterpret_cast<uint4*>(Xs + s0 * ldx + p8) = x0;
+  *reinterpret_cast<uint4*>(Xs + (s0 + 1) * ldx + p8) = x1;
   __syncthreads();
 
   const float cum_t = cum_s[t_own];
@@ -531,9 +541,8 @@ __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(6))
 #pragma unroll
     for (int kk = 0; kk < kQ / 32; kk++) {
       if (2 * kk > tb) break;  // M is zero there
-      const uint2 lo = *reinterpret_cast<const uint2*>(&Xt[p * ldt + swz(p, kk * 32 + lq)]);
-      const uint2 hi = *reinterpret_cast<const uint2*>(&Xt[p * ldt + swz(p, kk * 32 + 16 + lq)]);
-      acc[pb] = mfma(mf[kk], __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y)), acc[pb]);
+      // B operand: column p, k = s in the permuted order, read down the columns of [s][p]
+      acc[pb] = mfma(mf[kk], lds_frag(Xs, ldx, kk * 32 + lq, kk * 32 + 16 + lq, pb * 16), acc[pb]);
     }
   }
   __syncthreads();  // every wave is done with the operand tiles before the results go over them
