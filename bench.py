@@ -260,6 +260,64 @@ def main():
                   "bytes_per_call": ub,
                   "note": "the 84 MB fp32 state fits in the 256 MB Infinity Cache, so carried-state traffic "
                           "can be served from it; GB/s is algorithmic bytes over kernel time"}
+
+        # one generation step of the block's kernels per token: the convolution token step, then the state
+        # update on its output; eager launches against the same T tokens captured once in a HIP graph
+        def token_step(bt, T=32):
+            g2 = torch.Generator(device=dev).manual_seed(args.seed + 5)
+            v_tok = torch.randn((T, bt, wd.E), generator=g2, device=dev).to(torch.bfloat16)
+            dl = torch.randn((T, bt, wd.E), generator=g2, device=dev).to(torch.bfloat16)
+            Bt = torch.randn((T, bt, wd.N), generator=g2, device=dev).to(torch.bfloat16)
+            Ct = torch.randn((T, bt, wd.N), generator=g2, device=dev).to(torch.bfloat16)
+            zt = torch.randn((T, bt, wd.E), generator=g2, device=dev).to(torch.bfloat16)
+            q = torch.randn((wd.E, 4), generator=g2, device=dev) * 0.5
+            cb = torch.randn((wd.E,), generator=g2, device=dev) * 0.1
+            cst = torch.zeros((bt, wd.E, 4), dtype=torch.bfloat16, device=dev)
+            sst = torch.zeros((bt, wd.E, wd.N), dtype=torch.float32, device=dev)
+            xs = torch.empty((T, bt, wd.E), dtype=torch.bfloat16, device=dev)
+            ys = torch.empty((T, bt, wd.E), dtype=torch.bfloat16, device=dev)
+
+            def tokens():
+                for k in range(T):
+                    ssm.ssm_conv_update(cst, v_tok[k], q, cb, x=xs[k])
+                    ssm.ssm_state_update(sst, xs[k], dl[k], xd["A"], Bt[k], Ct[k], xd["D"], zt[k],
+                                         xd["delta_bias"], xd["softplus"], y=ys[k])
+
+            tokens()
+            torch.cuda.synchronize()
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0.record(stream)
+            for _ in range(reps):
+                tokens()
+            t1.record(stream)
+            torch.cuda.synchronize()
+            eager_us = 1e3 * t0.elapsed_time(t1) / (reps * T)
+            side = torch.cuda.Stream()
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                tokens()
+            stream.wait_stream(side)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                tokens()
+            torch.cuda.synchronize()
+            t0.record(stream)
+            for _ in range(reps):
+                graph.replay()
+            t1.record(stream)
+            torch.cuda.synchronize()
+            graph_us = 1e3 * t0.elapsed_time(t1) / (reps * T)
+            del graph
+            return {"eager_us_per_token": round(eager_us, 2), "graph_us_per_token": round(graph_us, 2)}
+
+        update["token_step"] = {
+            "workload": f"per token: ssm_conv_update (K4) then ssm_state_update, E{wd.E} N{wd.N} bf16, 32 tokens",
+            "b256": token_step(wd.b), "b1": token_step(1),
+            "note": "both entry points launch on the caller's stream with no workspace and no memset, so the "
+                    "token loop can be captured in a HIP graph (torch.cuda.CUDAGraph) and replayed; at b1 the "
+                    "step is launch-bound"}
+        log(f"[bench] token step {update['token_step']}")
         del xd, st, yd
 
     # backward of the scan on the same workload (gradients of every input, states recomputed)
