@@ -610,11 +610,13 @@ hipError_t update_typed(const UpdateArgs& a) {
 ScanPlan plan_scan(int64_t b, int64_t L, int64_t E, int elem_bytes) {
   ScanPlan pl;
   pl.e_blocks = int((E + kWave - 1) / kWave);
-  // Enough waves that every SIMD of the 256 CUs sees several rounds of them
-  // (register use allows 4 resident per SIMD); measured best on the long
-  // sequence.  The sequence is cut only when batch x channel blocks alone
-  // cannot provide them.
-  int64_t target = 16384;
+  // Enough waves that every SIMD of the 256 CUs sees several rounds of them:
+  // register use allows 4 resident per SIMD, 4096 on the chip, and 20480 is
+  // five whole rounds (a target just past a multiple of 4096 leaves a last
+  // round almost empty; 16384 gave 205 chunks x 80 blocks = 16400 waves on
+  // the long sequence, 1.3% slower).  The sequence is cut only when batch x
+  // channel blocks alone cannot provide them.
+  int64_t target = 20480;
   if (const char* s = std::getenv("SSM_SCAN_TARGET_WAVES")) {
     const long v = std::strtol(s, nullptr, 10);
     if (v > 0) target = v;

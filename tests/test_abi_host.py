@@ -286,6 +286,9 @@ def test_scan_plan_query(lib, monkeypatch):
         assert cl >= 1 and nc >= 1
         assert (nc - 1) * cl < L <= nc * cl, (b, L, E, cl, nc)  # chunks tile the sequence exactly
         assert cl * E * (4 if dt == "f32" else 2) < 2 ** 31  # 32-bit buffer offsets inside a chunk
+    # the long sequence: 256 chunks x 80 channel blocks = 20480 waves, five whole
+    # rounds of the 4096 waves (256 CUs x 4 SIMDs x 4) the chip holds at once
+    assert ssm.ssm_scan_plan(1, 65536, 5120, 16, "bf16") == (256, 256)
     # the tuning variables are honoured
     monkeypatch.setenv("SSM_SCAN_TARGET_WAVES", "100000")
     monkeypatch.setenv("SSM_SCAN_MIN_CHUNK", "8")
