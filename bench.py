@@ -23,6 +23,12 @@ Prints ONE JSON line on stdout:
   roofline_hbm the same kernel's algorithmic bytes over its duration vs 8 TB/s
   cpu_baseline the fp64 oracle on a bounded channel sample of the same inputs
                (channels are independent chains), timed on the host cores
+  configs      the tiny (b1 L64 E16 N4 fp32), block (b32 L512 E512 N16 fp32) and
+               mid (b8 L2048 E1536 N16 bf16) scans and the long scan's one-GPU
+               share under 8-way channel sharding (E640), each call timed on its
+               own: median and min, elem/s, algorithmic GB/s against 8 TB/s and
+               against a measured 1 GiB copy, ALU-issue fraction; the oracle's
+               rate on 1 and on all host threads, and parity of the timed outputs
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -130,6 +136,111 @@ def load_traffic(kernel, workload):
     return doc.get("hbm_bytes_per_launch"), doc.get("note", "")
 
 
+def copy_bandwidth(torch, dev, stream, nbytes=1 << 30, reps=10):
+    """GB/s of a plain device-to-device copy (bytes read + bytes written over its time)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    del src
+    return 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9, dst
+
+
+def scan_configs(ssm, workloads, torch, dev, stream, seed, cpu=True):
+    """Each scan configuration timed call by call, with the oracle beside it.
+
+    The block and mid configurations are small enough to stay in the 256 MB
+    Infinity Cache between calls, so a 1 GiB buffer is written before every
+    timed call (outside its event pair).  The tiny one is launch-bound.  The
+    long workload's share at E = 640 is what one GPU of 8 runs when the
+    channels are split over them.  With ``cpu``, the fp64 oracle runs on the
+    same inputs, on 1 thread and on the host's threads, and checks the
+    timed outputs elementwise.
+    """
+    import numpy as np
+
+    copy_gbps, flush = copy_bandwidth(torch, dev, stream)
+    out = {"copy_GBps": round(copy_gbps, 1),
+           "copy_note": "1 GiB device-to-device copy: bytes read + written over its time",
+           "timing": "event pair around each call on the launch stream; median and min over the calls"}
+    if cpu:
+        import oracle
+
+        threads = oracle.default_threads()
+    for wc, reps, flushed, t1 in ((workloads.TINY, 200, False, True), (workloads.BLOCK, 100, True, True),
+                                  (workloads.MID, 100, True, True), (workloads.LONG_E640, 20, False, False)):
+        xc = workloads.make_scan_inputs(wc, seed=seed, device=dev, backend="torch" if wc.L * wc.E > 1 << 24 else "numpy")
+        yc = torch.empty_like(xc["u"])
+        lc = torch.empty((wc.b, wc.E, wc.N), dtype=torch.float32, device=dev)
+
+        def call():
+            ssm.ssm_scan_fwd(xc["u"], xc["delta"], xc["A"], xc["B"], xc["C"], xc["D"], xc["z"],
+                             xc["delta_bias"], xc["softplus"], y=yc, last_state=lc)
+
+        for _ in range(5):
+            call()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for k in range(reps):
+            if flushed:
+                flush.fill_(k & 0x7F)
+            ev[k][0].record(stream)
+            call()
+            ev[k][1].record(stream)
+        torch.cuda.synchronize()
+        us = sorted(1e3 * a.elapsed_time(b) for a, b in ev)
+        med, mn = us[len(us) // 2], us[0]
+        s = 2 if wc.dtype == "bf16" else 4
+        nb = scan_bytes(wc.b, wc.L, wc.E, wc.N, s, gate=wc.z is not None)
+        sl = scan_slots(wc.b, wc.L, wc.E, wc.N, softplus=wc.softplus, gate=wc.z is not None,
+                        has_d=wc.D is not None, has_bias=wc.delta_bias is not None, bf16=(wc.dtype == "bf16"))
+        el = wc.b * wc.L * wc.E
+        gbps = nb / (med * 1e-6) / 1e9
+        rec = {"workload": wc.description, "calls": reps, "cache_flushed": flushed,
+               "us_median": round(med, 2), "us_min": round(mn, 2), "elem_per_s": el / (med * 1e-6),
+               "algorithmic_bytes": nb, "GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+               "copy_frac": round(gbps / copy_gbps, 4),
+               "alu_frac": round(sl / (med * 1e-6) / VALU_SLOT_PEAK, 4),
+               "plan": dict(zip(("chunk_len", "n_chunks"), ssm.ssm_scan_plan(wc.b, wc.L, wc.E, wc.N, wc.dtype)))}
+        if cpu:
+            a64 = [oracle.to_f64(xc[k]) for k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")]
+            rates = {}
+            for th in ((1, threads) if t1 else (threads,)):
+                c0 = time.perf_counter()
+                y_ref, last_ref = oracle.scan(*a64, softplus=xc["softplus"], threads=th)
+                rates[f"threads_{th}"] = el / (time.perf_counter() - c0)
+            rec["cpu_oracle_elem_per_s"] = rates
+            err = lambda g, r: float(np.max(np.abs(g - r) / (1 + np.abs(r)))) if r.size else 0.0
+            bound = 2e-2 if wc.dtype == "bf16" else 1e-4
+            rec["parity"] = {"y": err(oracle.to_f64(yc), y_ref), "last_state": err(oracle.to_f64(lc), last_ref),
+                             "bound": bound}
+        out[wc.name] = rec
+        del xc, yc, lc
+    del flush
+    if cpu:  # the decode workload on the host: a sample of its token steps (the GPU side is state_update)
+        wd = workloads.DECODE.with_shape(steps=8)
+        xd = workloads.make_decode_inputs(wd, seed=seed, device=dev, backend="torch")
+        xd = {k: (v.cpu() if torch.is_tensor(v) else v) for k, v in xd.items()}
+        rates = {}
+        for th in (1, threads):
+            st = oracle.to_f64(xd["state0"])
+            c0 = time.perf_counter()
+            for k in range(wd.steps):
+                st, _ = oracle.state_update(st, xd["x"][k], xd["delta"][k], xd["A"], xd["B"][k], xd["C"][k], xd["D"],
+                                            xd["z"][k], xd["delta_bias"], xd["softplus"], threads=th)
+            rates[f"threads_{th}"] = round(1e6 * (time.perf_counter() - c0) / wd.steps, 1)
+        out["decode"] = {"workload": workloads.DECODE.description, "cpu_oracle_us_per_call": rates,
+                         "sample": f"the first {wd.steps} of {workloads.DECODE.steps} token steps"}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -142,6 +253,7 @@ def main():
     ap.add_argument("--no-conv", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-ssd", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-configuration scan timings")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -516,6 +628,14 @@ def main():
                   "bound": 2e-2, "channels_checked": nch}
         log(f"[bench] cpu baseline {cpu['value']:.3e} elem/s on {threads} threads; parity {parity}")
 
+    # the other scan configurations, and the long workload's one-GPU share under channel
+    # sharding: every call timed on its own (event pair on the launch stream), median and min
+    configs = None
+    if not args.no_configs:
+        configs = scan_configs(ssm, workloads, torch, dev, stream, args.seed,
+                               cpu=not args.no_cpu_baseline)
+        log(f"[bench] configs {configs}")
+
     out = {
         "metric": "selective-scan B·L·E elems/s and achieved HBM GB/s (% of MI355X peak)",
         "value": value,
@@ -550,6 +670,7 @@ def main():
         "ssd": ssd,
         "cpu_baseline": cpu,
         "parity": parity,
+        "configs": configs,
     }
     print(json.dumps(out), flush=True)
 

@@ -107,6 +107,12 @@ LONG = ScanWorkload(
     B=("normal", 0.0, 0.25), C=("normal", 0.0, 0.25), D=N01,
     description="long-sequence scan: b1 L65536 E5120 N16 bf16 I/O, fp32 state, 5% reset steps",
 )
+# one GPU's share of the long scan when its channels are split over 8 GPUs (channels
+# are independent chains, so the share is the same kernel at E = 5120 / 8)
+LONG_E640 = LONG.with_shape(
+    name="long_e640", E=640,
+    description="one GPU's share of the long scan split 8 ways over channels: b1 L65536 E640 N16 bf16 I/O",
+)
 DECODE = DecodeWorkload(
     "decode", b=256, E=5120, N=16, steps=128, dtype="bf16",
     description="generation state update: b256 E5120 N16, 128 successive single-token updates",
