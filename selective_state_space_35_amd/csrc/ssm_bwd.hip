@@ -18,9 +18,10 @@
 //      of kBwdChunk steps give the state entering every chunk;
 //   2. bwd_chunk_agg_kernel: per chunk, the state gradient reached from zero
 //      walking the chunk backwards (the reverse-time aggregate);
-//   3. bwd_carry_kernel: the chain of those aggregates from the last chunk to
-//      the first, started from dlast: the gradient entering every chunk from
-//      its end (the decay of a chunk is exp(A * sum of its steps), as forward);
+//   3. chain_kernel (ssm_chain.h), in reverse: the chain of those aggregates
+//      from the last chunk to the first, started from dlast: the gradient
+//      entering every chunk from its end (the decay of a chunk is
+//      exp(A * sum of its steps), as forward);
 //   4. bwd_main_kernel: per chunk, states recomputed from the chunk's incoming
 //      state (checkpoints every kSub steps, then each sub-block's states in
 //      registers), the reverse walk, every gradient;
@@ -36,6 +37,7 @@
 
 #include <algorithm>
 
+#include "ssm_chain.h"
 #include "ssm_device.h"
 #include "ssm_internal.h"
 #include "ssm_profile.h"
@@ -119,51 +121,6 @@ __global__ __launch_bounds__(kWave) void bwd_chunk_agg_kernel(
     for (int n = 0; n < kS; n++) dst[n] = X[n];
     xsum[(bi * n_chunks + c) * E + e] = float(dsum);
   }
-}
-
-// ---------------------------------------------------------------------------
-// 3. reverse carry: per (b, e, n), X = dlast; for c = last .. 1:
-//    slot c <- X (gradient entering chunk c from its end);
-//    X <- exp(A * sum_c d) * X + aggregate_c;   finally slot 0 <- X.
-// ---------------------------------------------------------------------------
-template <int U>
-__global__ __launch_bounds__(256) void bwd_carry_kernel(const float* __restrict__ A, float* xagg,
-                                                        const float* __restrict__ xsum,
-                                                        const float* __restrict__ dlast, int64_t b, int64_t E, int N,
-                                                        int n_chunks) {
-  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (gid >= b * E * kS) return;
-  const int n = int(gid % kS);
-  const int64_t ch = gid / kS;
-  const int64_t e = ch % E, bi = ch / E;
-  const float a2 = n < N ? A[e * N + n] * kLog2e : 0.f;
-  const int64_t first = bi * n_chunks * E + e;  // slot of chunk 0; chunk c is at first + c * E
-  float X = (dlast && n < N) ? dlast[ch * N + n] : 0.f;
-  // chunks n_chunks-1 .. 1, U at a time; the aggregates of the next U are in flight meanwhile
-  float Rs[U], Ss[U];
-  auto load = [&](int c0) {  // c0: the highest chunk of the group
-#pragma unroll
-    for (int k = 0; k < U; k++) {
-      const int c = (c0 - k >= 1) ? c0 - k : 1;  // below chunk 1: a valid slot, unused
-      Rs[k] = xagg[(first + int64_t(c) * E) * kS + n];
-      Ss[k] = xsum[first + int64_t(c) * E];
-    }
-  };
-  if (n_chunks > 1) load(n_chunks - 1);
-  for (int c0 = n_chunks - 1; c0 >= 1; c0 -= U) {
-    float Rc[U], Sc[U];
-#pragma unroll
-    for (int k = 0; k < U; k++) { Rc[k] = Rs[k]; Sc[k] = Ss[k]; }
-    if (c0 - U >= 1) load(c0 - U);
-#pragma unroll
-    for (int k = 0; k < U; k++) {
-      if (c0 - k >= 1) {
-        xagg[(first + int64_t(c0 - k) * E) * kS + n] = X;
-        X = fmaf(exp2_fast(a2 * Sc[k]), X, Rc[k]);
-      }
-    }
-  }
-  xagg[first * kS + n] = X;
 }
 
 // Sum over the 16 channels of a wave (lane = 4 * channel + quarter) of four
@@ -610,11 +567,10 @@ hipError_t bwd_typed(const BwdArgs& a, int n_chunks, const float* B16, const flo
 #undef SSM_BWD_AGG
     if (err != hipSuccess) return err;
   }
-  const int64_t lanes = a.b * a.E * kS;
-  err = n_chunks > 33 ? launch_kind(kKindBwdCarry, bwd_carry_kernel<32>, (lanes + 255) / 256, 256, a.stream, a.A,
-                                    xagg, (const float*)xsum, a.dlast, a.b, a.E, N, n_chunks)
-                      : launch_kind(kKindBwdCarry, bwd_carry_kernel<8>, (lanes + 255) / 256, 256, a.stream, a.A, xagg,
-                                    (const float*)xsum, a.dlast, a.b, a.E, N, n_chunks);
+  // slot c <- the gradient entering chunk c from its end, for c = last .. 1 (reverse, exclusive),
+  // then slot 0 <- the gradient reaching the start of the sequence
+  const ChainArgs chain{xagg, xsum, a.A, a.dlast, nullptr, a.b, a.E, kS, N, n_chunks, n_chunks - 1};
+  err = launch_chain<true, true, true>(kKindBwdCarry, chain, a.stream);
   if (err != hipSuccess) return err;
   const int e_blocks = int((a.E + kChPerBlock - 1) / kChPerBlock);
 #define SSM_BWD_MAIN(SP, HZ, HD)                                                                              \

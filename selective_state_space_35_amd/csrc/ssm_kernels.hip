@@ -30,8 +30,8 @@
 //   1. scan_chunk_agg_kernel: per chunk, the state reached from zero and the
 //      sum of the steps d (the product of the retentions over the chunk is
 //      exp(A_n * sum d), so its "a" half needs no per-state work);
-//   2. scan_carry_kernel: a sequential combine over the chunk aggregates,
-//      giving every chunk its incoming state;
+//   2. chain_kernel (ssm_chain.h): the chain of the chunk aggregates, giving
+//      every chunk its incoming state;
 //   3. scan_main_kernel: every chunk rescans from its incoming state and
 //      writes y (and the last chunk writes last_state).
 // Only y and last_state are written to HBM besides the small per-chunk
@@ -44,6 +44,7 @@
 #include <cstdlib>
 #include <type_traits>
 
+#include "ssm_chain.h"
 #include "ssm_device.h"
 #include "ssm_internal.h"
 #include "ssm_profile.h"
@@ -192,51 +193,6 @@ __global__ __launch_bounds__(kWave) SSM_SCAN_OCCUPANCY void scan_chunk_agg_kerne
 #pragma unroll
     for (int n = 0; n < NS; n++) dst[n] = h[n];
     chunk_sum[(p.bi * n_chunks + p.c) * E + p.e] = float(dsum);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// 2. carries: state at the end of chunk c = exp(A_n * sum_c d) * (state at the
-//    end of chunk c-1) + aggregate_c, written over aggregate_c.
-// ---------------------------------------------------------------------------
-template <int NS, int U>
-__global__ __launch_bounds__(256) void scan_carry_kernel(const float* __restrict__ A, float* carry,
-                                                         const float* __restrict__ chunk_sum,
-                                                         const float* __restrict__ h0, int64_t b, int64_t E, int N,
-                                                         int n_chunks) {
-  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (gid >= b * E * NS) return;
-  const int n = int(gid % NS);
-  const int64_t ch = gid / NS;
-  const int64_t e = ch % E, bi = ch / E;
-  const float a2 = n < N ? A[e * N + n] * kLog2e : 0.f;
-  const int64_t first = bi * n_chunks * E + e;  // slot of chunk 0; chunk c is at first + c * E
-  const int n_comb = n_chunks - 1;              // chunks whose end state is needed
-  // The combines are a dependent chain, but their inputs are not: the
-  // aggregates of the next U chunks are loaded while the current U combine.
-  float Hs[U], Ss[U];
-  auto load = [&](int c0) {
-#pragma unroll
-    for (int k = 0; k < U; k++) {
-      const int c = (c0 + k < n_comb) ? c0 + k : n_comb - 1;  // past the end: a valid slot, unused
-      Hs[k] = carry[(first + int64_t(c) * E) * NS + n];
-      Ss[k] = chunk_sum[first + int64_t(c) * E];
-    }
-  };
-  float h = (h0 && n < N) ? h0[ch * N + n] : 0.f;  // incoming state of chunk 0
-  load(0);
-  for (int c0 = 0; c0 < n_comb; c0 += U) {
-    float Hc[U], Sc[U];
-#pragma unroll
-    for (int k = 0; k < U; k++) { Hc[k] = Hs[k]; Sc[k] = Ss[k]; }
-    if (c0 + U < n_comb) load(c0 + U);
-#pragma unroll
-    for (int k = 0; k < U; k++) {
-      if (c0 + k < n_comb) {
-        h = fmaf(exp2_fast(a2 * Sc[k]), h, Hc[k]);
-        carry[(first + int64_t(c0 + k) * E) * NS + n] = h;
-      }
-    }
   }
 }
 
@@ -502,13 +458,9 @@ hipError_t run_carries(const ScanArgs& a, const ScanPlan& pl, const ScanBufs& w)
                                a.stream, static_cast<const T*>(a.u), static_cast<const T*>(a.delta), a.A, w.B, a.bias,
                                w.carry, w.csum, a.L, a.E, N, pl.chunk_len, pl.n_chunks, agg, pl.e_blocks);
   if (err != hipSuccess) return err;
-  const int64_t lanes = a.b * a.E * NS;
-  // prefetch depth: 32 chunks for long chains, 8 when there are few chunks
-  return pl.n_chunks > 33
-             ? launch_kind(kKindCarry, scan_carry_kernel<NS, 32>, (lanes + 255) / 256, 256, a.stream, a.A, w.carry,
-                           (const float*)w.csum, a.h0, a.b, a.E, N, pl.n_chunks)
-             : launch_kind(kKindCarry, scan_carry_kernel<NS, 8>, (lanes + 255) / 256, 256, a.stream, a.A, w.carry,
-                           (const float*)w.csum, a.h0, a.b, a.E, N, pl.n_chunks);
+  // the state at the end of chunk c (forward, inclusive), from the incoming state of the sequence
+  const ChainArgs c{w.carry, w.csum, a.A, a.h0, nullptr, a.b, a.E, NS, N, pl.n_chunks, pl.n_chunks - 1};
+  return launch_chain<false, false, false>(kKindCarry, c, a.stream);
 }
 
 template <typename T, int NS, bool EXACT, bool SOFTPLUS, bool HAS_Z, bool FULL>

@@ -21,8 +21,8 @@
 //   ssd_state_kernel  per (batch, segment, head): walks the segment's chunks, (w o X)^T B
 //                     per chunk chained in fp32 registers -> each chunk's incoming state
 //                     from inside the segment (bf16) and the segment's own state (fp32)
-//   ssd_carry_kernel  per (batch, head, p, n): chain over segments (fp32) -> state entering
-//                     each segment, and the last state
+//   chain_kernel      per (batch, head, p, n): chain over segments (fp32, ssm_chain.h) ->
+//                     state entering each segment, and the last state
 //   ssd_scan_kernel   per (batch, chunk, head): S_in = inside part + decayed segment state,
 //                     then Y as above, + D x, gate, store
 // MFMA: v_mfma_f32_16x16x32_bf16.  Lane l of a wave holds A-operand row l % 16,
@@ -33,6 +33,7 @@
 
 #include <algorithm>
 
+#include "ssm_chain.h"
 #include "ssm_device.h"
 #include "ssm_internal.h"
 #include "ssm_profile.h"
@@ -328,52 +329,6 @@ __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(6))
   if (threadIdx.x == 0) seg_decay[(bi * n_segs + g) * H + h] = lphi;
 }
 
-// ---------------------------------------------------------------------------
-// carry over segments: per (batch, head, p, n), the state entering segment g,
-// S_g = exp(seg_decay[g - 1]) S_{g-1} + R_end[g - 1] from the incoming state,
-// in fp32, written in place of R_end[g]; the state after the last segment goes
-// to last_state [b, E, N]
-// ---------------------------------------------------------------------------
-template <int U>
-__global__ __launch_bounds__(256) void ssd_carry_kernel(float* seg_state, const float* __restrict__ seg_decay,
-                                                        const float* __restrict__ h0, float* __restrict__ last_state,
-                                                        int64_t b, int H, int N, int n_segs) {
-  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t per_head = int64_t(N) * kP;
-  if (gid >= b * H * per_head) return;
-  const int64_t within = gid % per_head;  // p * N + n
-  const int64_t bh = gid / per_head;
-  const int h = int(bh % H);
-  const int64_t bi = bh / H;
-  const int64_t E = int64_t(H) * kP;
-  const int64_t st = (bi * E + int64_t(h) * kP) * N + within;  // [b][e = h P + p][n]
-  float S = h0 ? h0[st] : 0.f;
-  auto slot = [&](int g) { return ((bi * n_segs + g) * H + h) * per_head + within; };
-  float Ss[U], Ls[U];
-  auto load = [&](int g0) {
-#pragma unroll
-    for (int k = 0; k < U; k++) {
-      const int gg = (g0 + k < n_segs) ? g0 + k : n_segs - 1;  // past the end: a valid slot, unused
-      Ss[k] = seg_state[slot(gg)];
-      Ls[k] = seg_decay[(bi * n_segs + gg) * H + h];
-    }
-  };
-  load(0);
-  for (int g0 = 0; g0 < n_segs; g0 += U) {
-    float Sc[U], Lc[U];
-#pragma unroll
-    for (int k = 0; k < U; k++) { Sc[k] = Ss[k]; Lc[k] = Ls[k]; }
-    if (g0 + U < n_segs) load(g0 + U);
-#pragma unroll
-    for (int k = 0; k < U; k++) {
-      if (g0 + k < n_segs) {
-        seg_state[slot(g0 + k)] = S;
-        S = fmaf(exp2_fast(Lc[k] * kLog2e), S, Sc[k]);
-      }
-    }
-  }
-  if (last_state) last_state[st] = S;
-}
 
 // ---------------------------------------------------------------------------
 // outputs of a chunk.  Wave w owns steps t in [16 w, 16 w + 16).  The mixing
@@ -624,11 +579,12 @@ hipError_t run_ssd(const SsdArgs& a, int n_chunks, int n_segs, const SsdWork& w)
                                x, dl, a.A, B, a.bias, w.rin, w.phi, w.seg_state, w.seg_decay, a.L, H, N, n_chunks,
                                n_segs);
   if (err != hipSuccess) return err;
-  const int64_t lanes = a.b * H * int64_t(N) * kP;
-  err = n_segs > 33 ? launch_kind(kKindSsdCarry, ssd_carry_kernel<16>, (lanes + 255) / 256, 256, a.stream, w.seg_state,
-                                  (const float*)w.seg_decay, a.h0, a.last_state, a.b, H, N, n_segs)
-                    : launch_kind(kKindSsdCarry, ssd_carry_kernel<4>, (lanes + 255) / 256, 256, a.stream, w.seg_state,
-                                  (const float*)w.seg_decay, a.h0, a.last_state, a.b, H, N, n_segs);
+  // the state entering every segment (forward, exclusive) from the incoming state, the state
+  // after the last one to last_state; per (batch, head, p, n), a segment's decay is exp(seg_decay)
+  const int per_head = N * kP;
+  const ChainArgs chain{w.seg_state, w.seg_decay, nullptr, a.h0, a.last_state, a.b, H, per_head, per_head, n_segs,
+                        n_segs};
+  err = launch_chain<false, true, false>(kKindSsdCarry, chain, a.stream);
   if (err != hipSuccess) return err;
   bf16_bits* y = static_cast<bf16_bits*>(a.y);
   const int64_t blocks = a.b * n_chunks * H;

@@ -1,0 +1,127 @@
+"""GPU parity of the chunk chain cut into stretches (chain_kernel with G > 1).
+
+The chain that joins the chunks of a cut sequence runs one thread per state
+coordinate when there are many of them; with few (a long sequence over few
+channels) each chain is cut into G = 2, 4 or 8 stretches that are reduced,
+combined through LDS and walked again.  The stretch count follows from the
+sizes, and the environment variable SSM_CHAIN_STRETCHES forces it, so every
+stretched variant runs here on inputs the oracle checks in full:
+
+* the forward scan cut into 188 chunks of 8 steps, G = 1, 2, 4, 8, with and
+  without an initial state (the forward chain, value leaving each chunk);
+* the backward (reverse chain, value entering each chunk from its end, then the
+  start of the sequence) with the forward chunk states it recomputes, G = 2, 4, 8;
+* the scalar-per-head scan over 6 segments with G = 8, so that stretches are
+  empty (value entering each segment, and the last state);
+* the long workload's one-GPU share under 8-way channel sharding (b1 L65536 E640
+  N16 bf16) with the stretch count chosen by the sizes, all channels.
+
+Bounds as in the other parity tests: tol * (1 + |ref|) elementwise, tol = 1e-4
+for fp32 I/O and 2e-2 for bf16 I/O.
+"""
+import pytest
+
+import oracle
+import workloads
+from tests.gpu_common import say, to_device
+from tests.parity import TOL, max_normalised_error
+from tests.test_gpu_bwd import NAMES, ORACLE_NAME
+
+pytestmark = pytest.mark.gpu
+
+N01 = ("normal", 0.0, 1.0)
+FWD = workloads.ScanWorkload("chain_fwd", b=2, L=1500, E=70, N=16, dtype="f32", u=N01, delta=("normal", -1.0, 0.7),
+                             z=N01, B=N01, C=N01, D=N01, delta_bias=("normal", 0.0, 0.3), softplus=True)
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("with_h0", [False, True])
+def test_forward_chain_stretches(G, with_h0, monkeypatch):
+    import torch
+
+    import selective_state_space_35_amd as ssm
+
+    monkeypatch.setenv("SSM_SCAN_MIN_CHUNK", "8")
+    monkeypatch.setenv("SSM_SCAN_TARGET_WAVES", "100000")
+    monkeypatch.setenv("SSM_CHAIN_STRETCHES", str(G))
+    w = FWD
+    x = to_device(workloads.make_scan_inputs(w, seed=G))
+    h0 = torch.randn((w.b, w.E, w.N), generator=torch.Generator().manual_seed(G)).cuda() if with_h0 else None
+    plan = ssm.ssm_scan_plan(w.b, w.L, w.E, w.N, w.dtype)
+    assert plan == (8, 188)
+    say(f"chain forward G={G} h0={with_h0} plan={plan}")
+    y, last = ssm.ssm_scan_fwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
+                               x["softplus"], initial_state=h0)
+    torch.cuda.synchronize()
+    y_ref, last_ref = oracle.scan(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
+                                  x["softplus"], h0=h0)
+    ey = max_normalised_error(oracle.to_f64(y), y_ref)
+    el = max_normalised_error(oracle.to_f64(last), last_ref)
+    print(f"[parity] chain forward G={G} h0={with_h0}: y {ey:.2e} last {el:.2e}", flush=True)
+    assert ey <= TOL["f32"] and el <= TOL["f32"]
+
+
+@pytest.mark.parametrize("G", [2, 4, 8])
+def test_backward_chain_stretches(G, monkeypatch):
+    import torch
+
+    import selective_state_space_35_amd as ssm
+
+    monkeypatch.setenv("SSM_CHAIN_STRETCHES", str(G))
+    w = FWD
+    x = to_device(workloads.make_scan_inputs(w, seed=10 + G))
+    gen = torch.Generator().manual_seed(G)
+    dy = torch.randn(x["u"].shape, generator=gen).cuda()
+    h0 = torch.randn((w.b, w.E, w.N), generator=gen).cuda()
+    dlast = torch.randn((w.b, w.E, w.N), generator=gen).cuda()
+    say(f"chain backward G={G}: b{w.b} L{w.L} E{w.E} N{w.N}")
+    g = ssm.ssm_scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], dy, x["D"], x["z"], x["delta_bias"],
+                         x["softplus"], initial_state=h0, d_last_state=dlast)
+    torch.cuda.synchronize()
+    r = oracle.scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"], x["softplus"],
+                        h0=h0, dy=dy, dlast=dlast)
+    worst = {n: max_normalised_error(oracle.to_f64(g[n]), r[ORACLE_NAME.get(n, n)]) for n in NAMES}
+    print(f"[parity] chain backward G={G}: " + ", ".join(f"{k} {v:.2e}" for k, v in worst.items()), flush=True)
+    for name, err in worst.items():
+        assert err <= TOL["f32"], f"{name}: {err:.3e}"
+
+
+def test_segment_chain_with_empty_stretches(monkeypatch):
+    import torch
+
+    import selective_state_space_35_amd as ssm
+
+    monkeypatch.setenv("SSM_CHAIN_STRETCHES", "8")
+    w = workloads.SsdWorkload("chain_ssd", b=1, L=5 * 1024 + 37, H=2, N=32, with_bias=True)
+    x = to_device(workloads.make_ssd_inputs(w, seed=3))
+    h0 = torch.randn((w.b, w.E, w.N), generator=torch.Generator().manual_seed(3)).cuda()
+    say(f"chain segments G=8: b{w.b} L{w.L} H{w.H} N{w.N} (6 segments)")
+    y, last = ssm.ssm_ssd_fwd(x["x"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
+                              x["softplus"], initial_state=h0)
+    torch.cuda.synchronize()
+    y_ref, last_ref = oracle.ssd(x["x"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
+                                 x["softplus"], h0=h0)
+    ey = max_normalised_error(oracle.to_f64(y), y_ref)
+    el = max_normalised_error(oracle.to_f64(last), last_ref)
+    print(f"[parity] chain segments G=8: y {ey:.2e} last {el:.2e}", flush=True)
+    assert ey <= TOL["bf16"] and el <= TOL["bf16"]
+
+
+def test_channel_share_of_the_long_workload():
+    """b1 L65536 E640 N16 bf16: 10240 state coordinates over 1024 chunks, stretched by the sizes."""
+    import torch
+
+    import selective_state_space_35_amd as ssm
+
+    w = workloads.LONG_E640
+    x = workloads.make_scan_inputs(w, seed=0, device="cuda", backend="torch")
+    say(f"chain long channel share {w.description} plan={ssm.ssm_scan_plan(w.b, w.L, w.E, w.N, w.dtype)}")
+    y, last = ssm.ssm_scan_fwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
+                               x["softplus"])
+    torch.cuda.synchronize()
+    y_ref, last_ref = oracle.scan(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
+                                  x["softplus"])
+    ey = max_normalised_error(oracle.to_f64(y), y_ref)
+    el = max_normalised_error(oracle.to_f64(last), last_ref)
+    print(f"[parity] long channel share: y {ey:.2e} last {el:.2e}", flush=True)
+    assert ey <= TOL["bf16"] and el <= TOL["bf16"]
