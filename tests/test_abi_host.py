@@ -289,6 +289,10 @@ def test_scan_plan_query(lib, monkeypatch):
     # the long sequence: 256 chunks x 80 channel blocks = 20480 waves, five whole
     # rounds of the 4096 waves (256 CUs x 4 SIMDs x 4) the chip holds at once
     assert ssm.ssm_scan_plan(1, 65536, 5120, 16, "bf16") == (256, 256)
+    # 64-step chunks fill the chip for the mid workload (6144 waves); the block workload
+    # (2048 waves at 64 steps) is cut into 32-step chunks instead
+    assert ssm.ssm_scan_plan(8, 2048, 1536, 16, "bf16") == (64, 32)
+    assert ssm.ssm_scan_plan(32, 512, 512, 16, "f32") == (32, 16)
     # the tuning variables are honoured
     monkeypatch.setenv("SSM_SCAN_TARGET_WAVES", "100000")
     monkeypatch.setenv("SSM_SCAN_MIN_CHUNK", "8")
