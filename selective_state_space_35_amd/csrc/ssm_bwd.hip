@@ -144,18 +144,6 @@ __device__ __forceinline__ void sum_channels(float v0, float v1, float v2, float
   }
 }
 
-// value of quad lane j, for every lane of the quad (DPP quad_perm [j, j, j, j]);
-// j is a constant once the calling loop is unrolled, so the switch folds away
-__device__ __forceinline__ float quad_bcast(float v, int j) {
-  const int b = __float_as_int(v);
-  switch (j) {
-    case 0: return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x00, 0xF, 0xF, false));
-    case 1: return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x55, 0xF, 0xF, false));
-    case 2: return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0xAA, 0xF, 0xF, false));
-    default: return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0xFF, 0xF, 0xF, false));
-  }
-}
-
 // Streams of one chunk staged in LDS: [stream][step][channel of the block].
 // Slots u, delta and z receive du, ddelta and dz once their inputs are dead.
 enum { kSu = 0, kSd = 1, kSy = 2, kSz = 3 };

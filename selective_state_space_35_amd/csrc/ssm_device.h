@@ -44,6 +44,17 @@ __device__ __forceinline__ float quad_xor1(float v) {  // value of lane ^ 1 with
 __device__ __forceinline__ float quad_xor2(float v) {  // value of lane ^ 2 within the quad
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
 }
+// value of quad lane j, for every lane of the quad (DPP quad_perm [j, j, j, j]);
+// j is a constant once the calling loop is unrolled, so the switch folds away
+__device__ __forceinline__ float quad_bcast(float v, int j) {
+  const int b = __float_as_int(v);
+  switch (j) {
+    case 0: return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x00, 0xF, 0xF, false));
+    case 1: return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x55, 0xF, 0xF, false));
+    case 2: return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0xAA, 0xF, 0xF, false));
+    default: return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0xFF, 0xF, 0xF, false));
+  }
+}
 
 // Raw buffer resource over a tensor region (CDNA buffer descriptor: 48-bit
 // base, no stride, 2 GiB range, dword3 as used for gfx9-family buffer ops).

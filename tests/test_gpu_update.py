@@ -3,8 +3,9 @@
 Covers the generation workload (b256 E5120 N16, 128 successive updates,
 state carried in HBM) at full size with oracle-checked batch rows, reduced
 sizes with ragged channel counts, every state size 1..16, the vector and
-the unaligned (scalar) memory paths, both dtypes, flags, and the identity
-"L token updates == one scan over L".
+the unaligned (scalar) memory paths, the path that stages x, step, z and y
+through LDS (bit for bit against the per-lane one), both dtypes, flags, and
+the identity "L token updates == one scan over L".
 """
 import numpy as np
 import pytest
@@ -102,6 +103,39 @@ def test_unaligned_state_uses_scalar_path():
     st = buf[1:].view(w.b, w.E, w.N)
     assert st.data_ptr() % 16 != 0
     run_steps(x, w.steps, kind="f32", what="update unaligned", state=st)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("gate", [True, False])
+@pytest.mark.parametrize("b,N", [(3, 16), (6, 12)])
+def test_staged_inputs_and_outputs(dtype, gate, b, N):
+    """E a multiple of 64 with aligned rows: x, step, z and y move through LDS in 16-byte pieces.
+
+    Checked against the oracle over several steps (batch not a multiple of the 4 rows a
+    workgroup covers; N = 12 takes the padded state layout), and bit for bit against the
+    per-lane path, which an output whose base is not 16-byte aligned forces."""
+    import torch
+
+    import selective_state_space_35_amd as ssm
+
+    say(f"update staged {dtype} gate={gate} b{b} N{N}")
+    w = workloads.DECODE.with_shape(b=b, E=192, N=N, steps=5, dtype=dtype, z=workloads.N01 if gate else None)
+    x = make(w, seed=b + N)
+    run_steps(x, w.steps, kind=dtype, what=f"update staged {dtype} gate={gate} b{b} N{N}")
+    st_a = torch.randn((w.b, w.E, w.N), generator=torch.Generator().manual_seed(b)).cuda()
+    st_b = st_a.clone()
+    io = x["x"].dtype
+    y_a = torch.empty((w.b, w.E), dtype=io, device="cuda")
+    y_buf = torch.empty(w.b * w.E + 1, dtype=io, device="cuda")
+    y_b = y_buf[1:].view(w.b, w.E)
+    assert y_a.data_ptr() % 16 == 0 and y_b.data_ptr() % 16 != 0
+    for k in range(w.steps):
+        for st, y in ((st_a, y_a), (st_b, y_b)):
+            ssm.ssm_state_update(st, x["x"][k], x["delta"][k], x["A"], x["B"][k], x["C"][k], x["D"],
+                                 None if x["z"] is None else x["z"][k], x["delta_bias"], x["softplus"], y=y)
+        torch.cuda.synchronize()
+        assert torch.equal(y_a, y_b), f"step {k}: staged and per-lane outputs differ"
+    assert torch.equal(st_a, st_b), "staged and per-lane states differ"
 
 
 def test_token_steps_equal_scan():
