@@ -341,8 +341,9 @@ __global__ __launch_bounds__(256) void fill_state_kernel(float* __restrict__ p, 
 // are not repeated in every lane.  STAGE (that layout, E a multiple of 64,
 // 16-byte aligned rows): the workgroup's 64 channels x 4 rows of x, step and
 // z come in through LDS as 16-byte pieces and y goes out the same way,
-// instead of 2- or 4-byte accesses per lane (the decode workload: 37.4 ->
-// 34.2 us per call with events around each call).
+// instead of 2- or 4-byte accesses per lane; with VEC the 4 rows of B and C
+// come in the same way (the decode workload: 37.4 -> 32.7 us per call with
+// events around each call).
 constexpr int kRows = SSM_UPDATE_ROWS;
 
 template <typename T, int NS, bool VEC, bool SOFTPLUS, bool HAS_Z, bool STAGE>
@@ -358,6 +359,7 @@ __global__ __launch_bounds__(256) void state_update_kernel(
   constexpr int kPieces = 64 / kEpp;         // pieces per 64-channel row
   __shared__ __attribute__((aligned(16))) T xs[3][4][64];  // x, step, z of the workgroup (STAGE)
   __shared__ __attribute__((aligned(16))) T ys[4][64];     // y of the workgroup (STAGE)
+  __shared__ __attribute__((aligned(16))) T bcs[2][4][NS];  // B and C rows of the 4 batch rows (STAGE and VEC)
   const int rb = blockIdx.x / row_blocks;  // group of kRows batch rows: uniform per workgroup
   const int r = (blockIdx.x - rb * row_blocks) * 256 + threadIdx.x;
   const int e_raw = r / LPC;
@@ -389,6 +391,17 @@ __global__ __launch_bounds__(256) void state_update_kernel(
       *reinterpret_cast<uint4*>(&xs[arr][row][piece * kEpp]) =
           *reinterpret_cast<const uint4*>(src + int64_t(bi) * E + e0 + piece * kEpp);
     }
+    if constexpr (VEC) {  // B and C rows (NS elements each) by the threads of the workgroup's last two waves
+      constexpr int kBcPieces = NS / kEpp;
+      const int t = int(threadIdx.x) - 128;
+      if (t >= 0 && t < 2 * 4 * kBcPieces) {
+        const int arr = t / (4 * kBcPieces), row = (t / kBcPieces) % 4, piece = t % kBcPieces;
+        const int bi_raw = rb * kRows + row;
+        const int bi = bi_raw < b ? bi_raw : b - 1;
+        *reinterpret_cast<uint4*>(&bcs[arr][row][piece * kEpp]) =
+            *reinterpret_cast<const uint4*>((arr ? C : B) + int64_t(bi) * NS + piece * kEpp);
+      }
+    }
     __syncthreads();
   }
 
@@ -405,7 +418,13 @@ __global__ __launch_bounds__(256) void state_update_kernel(
     if constexpr (VEC) {  // N == NS, state / B / C rows aligned for vector access
       const float4 sv = *reinterpret_cast<const float4*>(state + cc[j] * NS + n0);
       s[j][0] = sv.x; s[j][1] = sv.y; s[j][2] = sv.z; s[j][3] = sv.w;
-      if constexpr (std::is_same<T, float>::value) {
+      if constexpr (STAGE) {
+#pragma unroll
+        for (int kk = 0; kk < 4; kk++) {
+          bn[j][kk] = load_elem(&bcs[0][j][n0 + kk]);
+          cn[j][kk] = load_elem(&bcs[1][j][n0 + kk]);
+        }
+      } else if constexpr (std::is_same<T, float>::value) {
         const float4 b4 = *reinterpret_cast<const float4*>(B + int64_t(bi) * NS + n0);
         const float4 c4 = *reinterpret_cast<const float4*>(C + int64_t(bi) * NS + n0);
         bn[j][0] = b4.x; bn[j][1] = b4.y; bn[j][2] = b4.z; bn[j][3] = b4.w;
@@ -619,7 +638,8 @@ hipError_t update_flags(const UpdateArgs& a) {
   if constexpr (NS == 16 && kRows == 4) {
     // x, step, z and y move through LDS in 16-byte pieces: whole 64-channel blocks, aligned rows
     auto al16 = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
-    if (a.E % 64 == 0 && al16(a.x) && al16(a.delta) && al16(a.y) && (!a.z || al16(a.z)))
+    if (a.E % 64 == 0 && al16(a.x) && al16(a.delta) && al16(a.y) && (!a.z || al16(a.z)) &&
+        (!VEC || (al16(a.B) && al16(a.C))))
       return update_launch<T, NS, VEC, true>(a);
   }
   return update_launch<T, NS, VEC, false>(a);

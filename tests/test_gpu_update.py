@@ -123,19 +123,29 @@ def test_staged_inputs_and_outputs(dtype, gate, b, N):
     x = make(w, seed=b + N)
     run_steps(x, w.steps, kind=dtype, what=f"update staged {dtype} gate={gate} b{b} N{N}")
     st_a = torch.randn((w.b, w.E, w.N), generator=torch.Generator().manual_seed(b)).cuda()
-    st_b = st_a.clone()
+    st_b, st_c = st_a.clone(), st_a.clone()
     io = x["x"].dtype
-    y_a = torch.empty((w.b, w.E), dtype=io, device="cuda")
+    y_a, y_c = (torch.empty((w.b, w.E), dtype=io, device="cuda") for _ in range(2))
     y_buf = torch.empty(w.b * w.E + 1, dtype=io, device="cuda")
     y_b = y_buf[1:].view(w.b, w.E)
     assert y_a.data_ptr() % 16 == 0 and y_b.data_ptr() % 16 != 0
+    # B and C at a base 8 bytes (bf16) or 4 bytes (fp32) past 16-byte alignment: their rows are
+    # then read per lane (bf16: 8-byte vector loads; fp32: the scalar-state path)
+    off = 4 if dtype == "bf16" else 1
+    bc_buf = torch.empty(2, w.b * w.N + off, dtype=io, device="cuda")
+    B_c, C_c = bc_buf[0, off:].view(w.b, w.N), bc_buf[1, off:].view(w.b, w.N)
+    assert B_c.data_ptr() % 16 != 0
     for k in range(w.steps):
-        for st, y in ((st_a, y_a), (st_b, y_b)):
-            ssm.ssm_state_update(st, x["x"][k], x["delta"][k], x["A"], x["B"][k], x["C"][k], x["D"],
+        B_c.copy_(x["B"][k])
+        C_c.copy_(x["C"][k])
+        for st, y, Bk, Ck in ((st_a, y_a, x["B"][k], x["C"][k]), (st_b, y_b, x["B"][k], x["C"][k]),
+                              (st_c, y_c, B_c, C_c)):
+            ssm.ssm_state_update(st, x["x"][k], x["delta"][k], x["A"], Bk, Ck, x["D"],
                                  None if x["z"] is None else x["z"][k], x["delta_bias"], x["softplus"], y=y)
         torch.cuda.synchronize()
         assert torch.equal(y_a, y_b), f"step {k}: staged and per-lane outputs differ"
-    assert torch.equal(st_a, st_b), "staged and per-lane states differ"
+        assert torch.equal(y_a, y_c), f"step {k}: staged and per-lane B / C outputs differ"
+    assert torch.equal(st_a, st_b) and torch.equal(st_a, st_c), "staged and per-lane states differ"
 
 
 def test_token_steps_equal_scan():
