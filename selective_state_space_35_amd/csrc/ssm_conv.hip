@@ -268,8 +268,19 @@ __global__ __launch_bounds__(256) void conv_state_copy_kernel(const T* __restric
   if (i < n) store_elem(dst + i, src ? load_elem(src + i) : 0.f);
 }
 
-// One token for every (b, e): shift the K-sample state left, append v, x = silu(cb + q . state).
+// Bytes of a channel's K-sample state slice and of its K weights, when each
+// can move as one aligned vector access (a power of two, at most 16 bytes).
 template <typename T, int K>
+struct ConvSlice {
+  static constexpr int kStateBytes = K * int(sizeof(T)), kWeightBytes = K * 4;
+  static constexpr bool pow2(int n) { return n > 0 && n <= 16 && (n & (n - 1)) == 0; }
+  static constexpr bool kVec = pow2(kStateBytes) && pow2(kWeightBytes);
+};
+
+// One token for every (b, e): shift the K-sample state left, append v, x = silu(cb + q . state).
+// VEC: the state slice and the weights of a channel each move as one vector access
+// (K = 4 in bf16: 8 and 16 bytes) instead of K element accesses.
+template <typename T, int K, bool VEC>
 __global__ __launch_bounds__(256) void conv_update_kernel(T* __restrict__ state, const T* __restrict__ v,
                                                           const float* __restrict__ q, const float* __restrict__ cb,
                                                           T* __restrict__ x, int E, int row_blocks) {
@@ -278,16 +289,42 @@ __global__ __launch_bounds__(256) void conv_update_kernel(T* __restrict__ state,
   if (e >= E) return;
   const int64_t cc = int64_t(bi) * E + e;
   T* st = state + cc * K;
-  float s[K];
+  constexpr bool kV = ConvSlice<T, K>::kVec;  // the slice sizes are alignments only when they are powers of two
+  struct alignas(kV ? ConvSlice<T, K>::kStateBytes : int(sizeof(T))) SV { T v[K]; };
+  struct alignas(kV ? ConvSlice<T, K>::kWeightBytes : 4) QV { float v[K]; };
+  static_assert(!VEC || kV, "vector access needs power-of-two slices");
+  float s[K], w[K];
+  if constexpr (VEC) {
+    const SV sv = *reinterpret_cast<const SV*>(st);
+    const QV qv = *reinterpret_cast<const QV*>(q + int64_t(e) * K);
 #pragma unroll
-  for (int k = 0; k < K; k++) s[k] = load_elem(st + k);
+    for (int k = 0; k < K; k++) {
+      s[k] = load_elem(&sv.v[k]);
+      w[k] = qv.v[k];
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < K; k++) {
+      s[k] = load_elem(st + k);
+      w[k] = q[int64_t(e) * K + k];
+    }
+  }
   const float vt = load_elem(v + cc);
   float acc = cb ? cb[e] : 0.f;
+  float sh[K];
 #pragma unroll
   for (int k = 0; k < K; k++) {
-    const float sk = (k + 1 < K) ? s[k + 1] : vt;  // shifted state: oldest dropped, newest appended
-    acc = fmaf(q[int64_t(e) * K + k], sk, acc);
-    store_elem(st + k, sk);
+    sh[k] = (k + 1 < K) ? s[k + 1] : vt;  // shifted state: oldest dropped, newest appended
+    acc = fmaf(w[k], sh[k], acc);
+  }
+  if constexpr (VEC) {
+    SV out;
+#pragma unroll
+    for (int k = 0; k < K; k++) store_elem(&out.v[k], sh[k]);
+    *reinterpret_cast<SV*>(st) = out;
+  } else {
+#pragma unroll
+    for (int k = 0; k < K; k++) store_elem(st + k, sh[k]);
   }
   store_elem(x + cc, silu(acc));
 }
@@ -313,7 +350,15 @@ hipError_t conv_fwd_k(const ConvArgs& a) {
 template <typename T, int K>
 hipError_t conv_update_k(const ConvArgs& a) {
   const int row_blocks = int((a.E + 255) / 256);
-  return launch_kind(kKindConvUpdate, conv_update_kernel<T, K>, a.b * row_blocks, 256, a.stream,
+  if constexpr (ConvSlice<T, K>::kVec) {
+    const bool vec = reinterpret_cast<uintptr_t>(a.state_out) % ConvSlice<T, K>::kStateBytes == 0 &&
+                     reinterpret_cast<uintptr_t>(a.q) % ConvSlice<T, K>::kWeightBytes == 0;
+    if (vec)
+      return launch_kind(kKindConvUpdate, conv_update_kernel<T, K, true>, a.b * row_blocks, 256, a.stream,
+                         static_cast<T*>(a.state_out), static_cast<const T*>(a.v), a.q, a.cb, static_cast<T*>(a.x),
+                         int(a.E), row_blocks);
+  }
+  return launch_kind(kKindConvUpdate, conv_update_kernel<T, K, false>, a.b * row_blocks, 256, a.stream,
                      static_cast<T*>(a.state_out), static_cast<const T*>(a.v), a.q, a.cb, static_cast<T*>(a.x),
                      int(a.E), row_blocks);
 }

@@ -210,3 +210,29 @@ def test_unaligned_channel_offsets():
     ref, st_ref = gpu_conv(x)
     torch.cuda.synchronize()
     assert torch.equal(out, ref) and torch.equal(st, st_ref)
+
+
+@pytest.mark.parametrize("K", [2, 4])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_token_update_vector_and_element_paths_agree(K, dtype):
+    """A state slice of a power-of-two size moves as one vector access when aligned; a state
+    view offset by one element takes the per-element path.  Both give the same bits."""
+    import torch
+
+    import selective_state_space_35_amd as ssm
+
+    w = BASE.with_shape(L=6, E=130, K=K, dtype=dtype, state_in=True)
+    x = make(w, seed=K + 40)
+    say(f"conv token vector vs element K={K} {dtype}")
+    st_a = x["state_in"].clone()
+    buf = torch.empty(st_a.numel() + 1, dtype=st_a.dtype, device="cuda")
+    st_b = buf[1:].view(st_a.shape)
+    st_b.copy_(st_a)
+    assert st_a.data_ptr() % 16 == 0 and st_b.data_ptr() % (K * st_a.element_size()) != 0
+    for t in range(w.L):
+        v_t = x["v"][:, t].contiguous()
+        ya = ssm.ssm_conv_update(st_a, v_t, x["weight"], x["conv_bias"])
+        yb = ssm.ssm_conv_update(st_b, v_t, x["weight"], x["conv_bias"])
+        torch.cuda.synchronize()
+        assert torch.equal(ya, yb), f"token {t}: outputs differ"
+    assert torch.equal(st_a, st_b)
