@@ -35,6 +35,7 @@ Convolution: v, x [b, L, E]; weight [E, K] float32 (1 <= K <= 8); conv_bias
 [E] float32; convolution state [b, E, K] in the streamed dtype, oldest sample
 first.  Streamed tensors are all float32 or all bfloat16.
 """
+import contextlib
 import ctypes
 import os
 
@@ -149,7 +150,7 @@ def ssm_profile_read():
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()  # an int: ctypes passes it as the void* argument
 
 
 def _dtype_code(torch, dt):
@@ -165,6 +166,11 @@ def _check(torch, name, t, shape, dtype, device, optional=False):
         if optional:
             return
         raise ValueError(f"{name} is required")
+    try:  # the common case in one pass; anything off falls through to the checks that name it
+        if t.dtype is dtype and t.shape == shape and t.get_device() == device.index and t.is_contiguous():
+            return
+    except (AttributeError, TypeError):
+        pass
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device != device:
@@ -178,7 +184,21 @@ def _check(torch, name, t, shape, dtype, device, optional=False):
 
 
 def _stream_of(torch, device):
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    """The current PyTorch stream of ``device`` as a raw handle."""
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return raw(device.index)
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+_NULL_CTX = contextlib.nullcontext()
+
+
+def _on(torch, device):
+    """A context with ``device`` current: a no-op when it already is (switching costs microseconds)."""
+    get = getattr(torch._C, "_cuda_getDevice", None)
+    current = get() if get is not None else torch.cuda.current_device()
+    return _NULL_CTX if current == device.index else torch.cuda.device(device)
 
 
 def _raise_on(fn, status):
@@ -239,14 +259,14 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=Fa
         raise ValueError("initial_state must not be the last_state buffer")
     if saved_states is not None:
         _check(torch, "saved_states", saved_states, saved_states_shape(b, L, E, N), torch.float32, device)
-        with torch.cuda.device(device):
+        with _on(torch, device):
             status = lib.ssm_scan_fwd_save(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                                            _ptr(delta_bias), int(bool(softplus)), _ptr(initial_state), _ptr(y),
                                            _ptr(last_state), _ptr(saved_states), b, L, E, N, code,
                                            _stream_of(torch, device))
         _raise_on("ssm_scan_fwd_save", status)
         return y, last_state
-    with torch.cuda.device(device):
+    with _on(torch, device):
         if initial_state is None:
             status = lib.ssm_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                                       _ptr(delta_bias), int(bool(softplus)), _ptr(y), _ptr(last_state),
@@ -340,7 +360,7 @@ def ssm_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplu
     }
     if saved_states is not None:
         _check(torch, "saved_states", saved_states, saved_states_shape(b, L, E, N), f32, device)
-        with torch.cuda.device(device):
+        with _on(torch, device):
             status = lib.ssm_scan_bwd_saved(
                 _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
                 int(bool(softplus)), _ptr(initial_state), _ptr(saved_states), _ptr(dy), _ptr(d_last_state),
@@ -349,7 +369,7 @@ def ssm_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplu
                 _stream_of(torch, device))
         _raise_on("ssm_scan_bwd_saved", status)
         return g
-    with torch.cuda.device(device):
+    with _on(torch, device):
         status = lib.ssm_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
                                   int(bool(softplus)), _ptr(initial_state), _ptr(dy), _ptr(d_last_state), _ptr(g["du"]),
                                   _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]),
@@ -398,7 +418,7 @@ def ssm_ssd_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=Fal
         last_state = torch.empty((b, E, N), dtype=f32, device=device)
     elif last_state is not None:
         _check(torch, "last_state", last_state, (b, E, N), f32, device)
-    with torch.cuda.device(device):
+    with _on(torch, device):
         status = lib.ssm_ssd_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
                                  int(bool(softplus)), _ptr(initial_state), _ptr(y), _ptr(last_state), b, L, H, P, N,
                                  code, _stream_of(torch, device))
@@ -434,7 +454,7 @@ def ssm_state_update(state, x, delta, A, B, C, D=None, z=None, delta_bias=None, 
         y = torch.empty((b, E), dtype=io, device=device)
     else:
         _check(torch, "y", y, (b, E), io, device)
-    with torch.cuda.device(device):
+    with _on(torch, device):
         status = lib.ssm_state_update(_ptr(state), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
                                       _ptr(z), _ptr(delta_bias), int(bool(softplus)), _ptr(y), b, E, N, code,
                                       _stream_of(torch, device))
@@ -476,7 +496,7 @@ def ssm_conv_fwd(v, weight, conv_bias=None, state_in=None, x=None, state_out=Non
         _check(torch, "state_out", state_out, (b, E, K), io, device)
     if state_in is not None and state_out is not None and state_in.data_ptr() == state_out.data_ptr():
         raise ValueError("state_in must not be the state_out buffer")
-    with torch.cuda.device(device):
+    with _on(torch, device):
         status = lib.ssm_conv_fwd(_ptr(v), _ptr(weight), _ptr(conv_bias), _ptr(state_in), _ptr(x), _ptr(state_out),
                                   b, L, E, K, code, _stream_of(torch, device))
     _raise_on("ssm_conv_fwd", status)
@@ -504,7 +524,7 @@ def ssm_conv_update(conv_state, v, weight, conv_bias=None, x=None):
         x = torch.empty((b, E), dtype=io, device=device)
     else:
         _check(torch, "x", x, (b, E), io, device)
-    with torch.cuda.device(device):
+    with _on(torch, device):
         status = lib.ssm_conv_update(_ptr(conv_state), _ptr(v), _ptr(weight), _ptr(conv_bias), _ptr(x), b, E, K, code,
                                      _stream_of(torch, device))
     _raise_on("ssm_conv_update", status)
