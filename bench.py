@@ -136,6 +136,18 @@ def load_traffic(kernel, workload):
     return doc.get("hbm_bytes_per_launch"), doc.get("note", "")
 
 
+def cpu_model():
+    """The host CPU's model name (first processor in /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def copy_bandwidth(torch, dev, stream, nbytes=1 << 30, reps=10):
     """GB/s of a plain device-to-device copy (bytes read + bytes written over its time)."""
     src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -618,7 +630,7 @@ def main():
         y_ref, last_ref = oracle.scan(*a, softplus=x["softplus"], threads=threads)
         cpu_s = time.perf_counter() - c0
         cpu = {"value": w.b * w.L * nch / cpu_s, "unit": "elem/s", "cores": threads, "kind": "oracle",
-               "seconds": round(cpu_s, 2),
+               "cpu_model": cpu_model(), "seconds": round(cpu_s, 2),
                "sample": f"{nch} of {w.E} channels (independent chains), full L={w.L}, b={w.b}; "
                          "fp64 sequential oracle, same inputs"}
         yg = oracle.to_f64(y.index_select(2, ch))
