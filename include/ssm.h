@@ -248,10 +248,14 @@ SSM_API int ssm_scan_bwd_saved(const void* u, const void* delta, const float* A,
  *   B, C            [b, L, N]    bf16   (16-byte aligned)
  *   initial_state, last_state [b, H*P, N] float (nullable)
  *   P == 64; N a multiple of 16 in 16..128 (else SSM_ERR_DIM / SSM_ERR_UNSUPPORTED_N);
+ *   H * P at most 8,323,520 channels, H <= 130,055 (a chunk's rows are addressed with 32-bit
+ *   offsets; larger returns SSM_ERR_DIM);
  *   dtype must be SSM_BF16 (the matrix products take bf16 operands and
  *   accumulate in fp32; SSM_F32 returns SSM_ERR_DTYPE).
- * Takes a workspace of b * ceil(L/64) * H * (64 * N + 1) floats from the
- * stream-ordered allocator on `stream`.
+ * Takes a workspace from the stream-ordered allocator on `stream`: with
+ * C = ceil(L/128) chunks and S = ceil(C/8) segments, b * C * H * 64 * N bf16
+ * values (each chunk's state from inside its segment), b * C * H floats, and
+ * b * S * H * (64 * N + 1) floats (the segment states and their decays).
  */
 SSM_API int ssm_ssd_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
                         const float* D, const void* z, const float* delta_bias, int softplus,

@@ -223,6 +223,7 @@ int ssm_ssd_fwd(const void* x, const void* delta, const float* A, const void* B,
   if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_DTYPE;
   if (dtype != SSM_BF16) return SSM_ERR_DTYPE;  // the matrix products take bf16 operands
   if (b < 0 || L < 0 || H < 0 || P != ssm::ssd_head_dim()) return SSM_ERR_DIM;
+  if (H > ssm::ssd_max_channels() / P) return SSM_ERR_DIM;
   if (N < 16 || N > 128 || N % 16 != 0) return SSM_ERR_UNSUPPORTED_N;
   int64_t E = 0, t = 0;
   if (!mul_ok(H, P, &E) || !mul_ok(b, L, &t) || !mul_ok(t, E, &t) || !mul_ok(t, 4, &t)) return SSM_ERR_DIM;

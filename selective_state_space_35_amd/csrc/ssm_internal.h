@@ -132,6 +132,7 @@ struct SsdArgs {
 };
 int64_t ssd_chunk_steps();  // steps per chunk
 int64_t ssd_head_dim();     // channels per head (P)
+int64_t ssd_max_channels(); // largest H * P the chunk kernels address with 32-bit offsets
 hipError_t launch_ssd(const SsdArgs& a);
 
 // Both return hipSuccess or the first HIP error met while enqueueing.

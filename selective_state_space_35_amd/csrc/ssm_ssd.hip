@@ -610,6 +610,9 @@ hipError_t ssd_sp(const SsdArgs& a, int n_chunks, int n_segs, const SsdWork& w) 
 
 int64_t ssd_chunk_steps() { return kQ; }
 int64_t ssd_head_dim() { return kP; }
+// The chunk-state kernel reads x through a buffer descriptor based at the chunk's first row,
+// with 32-bit byte offsets up to (kQ + 1) rows of H * kP bf16 channels.
+int64_t ssd_max_channels() { return (int64_t(INT32_MAX) / 2 - kP) / (kQ + 1); }
 
 hipError_t launch_ssd(const SsdArgs& a) {
   if (a.b == 0 || a.H == 0) return hipSuccess;

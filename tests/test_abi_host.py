@@ -244,6 +244,9 @@ def test_ssd_validation(lib):
     assert ssd(lib, delta=FAKE + 1) == ERR_ALIGN
     assert ssd(lib, last=FAKE + 2) == ERR_ALIGN
     assert ssd(lib, b=0, x=None, delta=None, A=None, B=None, C=None, y=None) == OK
+    # a chunk's 129 rows of H * 64 bf16 channels must stay within 32-bit byte offsets
+    assert ssd(lib, H=130056, L=1) == ERR_DIM
+    assert ssd(lib, H=130055, L=1, x=None) == ERR_NULL  # the size is accepted; the null x is not
 
 
 def test_binding_refuses_cpu_tensors():
