@@ -1,11 +1,21 @@
 /*
  * ssm.h -- C ABI of the MI355X (gfx950) selective-scan library (libssm.so).
  *
- * Two operations of the Mamba-1 (S6) selective state-space layer, forward
- * only, on one GPU:
+ * The Mamba-1 (S6) selective state-space operation and the steps around it,
+ * on one GPU:
  *
- *   ssm_scan_fwd      the selective scan over a whole sequence
- *   ssm_state_update  one recurrent step of the same recurrence (generation)
+ *   ssm_scan_fwd, ssm_scan_fwd_from   the selective scan over a whole sequence
+ *                                     (from zero, or from a given state)
+ *   ssm_state_update                  one recurrent step of the same recurrence (generation)
+ *   ssm_scan_bwd                      the gradients of the scan
+ *   ssm_scan_fwd_save, ssm_scan_bwd_saved
+ *                                     the training form: the forward keeps the state
+ *                                     every SSM_SAVE_INTERVAL steps for the backward
+ *   ssm_ssd_fwd                       the scan with a scalar transition per head
+ *   ssm_conv_fwd, ssm_conv_update     the causal depthwise convolution + SiLU before
+ *                                     the scan, and its token step
+ *   ssm_scan_plan, ssm_profile_*, ssm_status_string, ssm_last_hip_error, ssm_version
+ *                                     host-side queries
  *
  * Pages that define the operations (title, site):
  *   [KK] "mamba, from scratch" (khushi keswani)
@@ -22,9 +32,11 @@
  * Streams.  `stream` is a hipStream_t passed as void* (NULL = the default
  * stream).  Work is enqueued on it and the call returns without waiting;
  * errors raised while the kernels run surface at the caller's next
- * synchronisation.  The scan takes a temporary workspace from the
- * stream-ordered allocator (hipMallocAsync / hipFreeAsync on `stream`), so
- * concurrent calls on different streams do not share memory.
+ * synchronisation.  The scans (forward, backward, per head) take a temporary
+ * workspace from the stream-ordered allocator (hipMallocAsync / hipFreeAsync
+ * on `stream`), so concurrent calls on different streams do not share memory.
+ * ssm_state_update and ssm_conv_update take none and issue no memset: a
+ * caller can capture them in a HIP graph.
  *
  * Data types.  `dtype` (ssm_dtype) is the element type of the streamed
  * tensors u/x, delta, B, C, z and y: SSM_F32 (float) or SSM_BF16 (bfloat16,
@@ -32,8 +44,9 @@
  * Arithmetic is float32 throughout; bf16 outputs are rounded to nearest-even.
  *
  * Sizes.  b (batch), L (sequence length), E (expanded channels) and
- * N (state size per channel).  Supported: 1 <= N <= 16; b, L, E >= 0.
- * b == 0 or E == 0 is a no-op.  L == 0 writes a zero last_state.
+ * N (state size per channel).  Supported: 1 <= N <= 16 (ssm_ssd_fwd: N a
+ * multiple of 16 up to 128); b, L, E >= 0.  b == 0 or E == 0 is a no-op.
+ * L == 0 writes a zero last_state (or the incoming state, where one is given).
  *
  * Alignment.  Every array must be aligned to its element size; float arrays
  * to 4 bytes, bf16 arrays to 2 bytes.  (Tensors from a PyTorch allocator
@@ -71,7 +84,7 @@ typedef enum {
   SSM_ERR_NULL = -1,          /* a required pointer is NULL */
   SSM_ERR_DIM = -2,           /* a negative size, or a size product that overflows */
   SSM_ERR_DTYPE = -3,         /* dtype is not an ssm_dtype value */
-  SSM_ERR_UNSUPPORTED_N = -4, /* N outside 1..16 */
+  SSM_ERR_UNSUPPORTED_N = -4, /* N outside the supported range (1..16; ssm_ssd_fwd: 16..128 in steps of 16) */
   SSM_ERR_ALIGN = -5,         /* an array is not aligned to its element size */
   SSM_ERR_HIP = -6            /* HIP launch / allocation failure */
 } ssm_status;
