@@ -81,6 +81,60 @@ def test_state_update_sweep(seed):
     assert max_normalised_error(oracle.to_f64(st), ref) <= TOL[w.dtype]
 
 
+@pytest.mark.parametrize("seed", range(10))
+def test_state_update_staged_sweep(seed):
+    """E a multiple of 64 and N of 9..16: x, step, z, y (and for N = 16, B and C) move through LDS."""
+    import torch
+
+    import selective_state_space_35_amd as ssm
+
+    rng = np.random.default_rng(2500 + seed)
+    w = workloads.DECODE.with_shape(b=int(rng.integers(1, 20)), E=64 * int(rng.integers(1, 11)),
+                                    N=int(rng.choice([16, 16, int(rng.integers(9, 17))])), steps=3,
+                                    dtype=str(rng.choice(["f32", "bf16"])), z=N01 if rng.integers(2) else None,
+                                    D=N01 if rng.integers(2) else None,
+                                    delta_bias=("normal", 0.0, 0.3) if rng.integers(2) else None)
+    x = to_device(workloads.make_decode_inputs(w, seed=seed))
+    st = torch.randn((w.b, w.E, w.N), generator=torch.Generator().manual_seed(seed)).cuda()
+    ref = oracle.to_f64(st)
+    say(f"sweep staged update seed={seed}: b{w.b} E{w.E} N{w.N} {w.dtype} z={w.z is not None} D={w.D is not None}")
+    for k in range(w.steps):
+        y = ssm.ssm_state_update(st, x["x"][k], x["delta"][k], x["A"], x["B"][k], x["C"][k], x["D"],
+                                 None if x["z"] is None else x["z"][k], x["delta_bias"], x["softplus"])
+        ref, y_ref = oracle.state_update(ref, x["x"][k], x["delta"][k], x["A"], x["B"][k], x["C"][k], x["D"],
+                                         None if x["z"] is None else x["z"][k], x["delta_bias"], x["softplus"])
+        torch.cuda.synchronize()
+        assert max_normalised_error(oracle.to_f64(y), y_ref) <= TOL[w.dtype]
+    assert max_normalised_error(oracle.to_f64(st), ref) <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_chain_stretches_sweep(seed, monkeypatch):
+    """Few channels over many short chunks: the chunk chain cuts itself into stretches."""
+    import torch
+
+    import selective_state_space_35_amd as ssm
+
+    rng = np.random.default_rng(2700 + seed)
+    w = workloads.ScanWorkload(
+        f"csweep{seed}", b=int(rng.integers(1, 3)), L=int(rng.integers(600, 3000)), E=int(rng.integers(1, 200)),
+        N=int(rng.integers(1, 17)), dtype=str(rng.choice(["f32", "bf16"])), u=N01, delta=("normal", -1.0, 0.8),
+        z=N01 if rng.integers(2) else None, B=N01, C=N01, D=N01, delta_bias=None, softplus=True)
+    monkeypatch.setenv("SSM_SCAN_MIN_CHUNK", str(int(rng.choice([8, 16]))))
+    monkeypatch.setenv("SSM_SCAN_TARGET_WAVES", "100000")
+    x = to_device(workloads.make_scan_inputs(w, seed=seed))
+    h0 = torch.randn((w.b, w.E, w.N), generator=torch.Generator().manual_seed(seed)).cuda()
+    say(f"sweep chain seed={seed}: b{w.b} L{w.L} E{w.E} N{w.N} {w.dtype} "
+        f"plan={ssm.ssm_scan_plan(w.b, w.L, w.E, w.N, w.dtype)}")
+    y, last = ssm.ssm_scan_fwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
+                               x["softplus"], initial_state=h0)
+    torch.cuda.synchronize()
+    y_ref, last_ref = oracle.scan(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
+                                  x["softplus"], h0=h0)
+    assert max_normalised_error(oracle.to_f64(y), y_ref) <= TOL[w.dtype]
+    assert max_normalised_error(oracle.to_f64(last), last_ref) <= TOL[w.dtype]
+
+
 @pytest.mark.parametrize("seed", range(12))
 def test_backward_sweep(seed):
     import torch
