@@ -324,9 +324,9 @@ __global__ __launch_bounds__(256) void fill_state_kernel(float* __restrict__ p, 
 // ---------------------------------------------------------------------------
 // LPC = NS / 4 lanes share one channel, each holding 4 consecutive states, so
 // a wave reads and writes the fp32 state as one contiguous 1 KiB block per
-// instruction.  Workgroups are laid out per batch row (row_blocks of them per
-// row), so the row index is a per-workgroup scalar and the lane's channel is
-// plain 32-bit arithmetic.  The partial readouts of the LPC lanes are summed
+// instruction.  Workgroups are laid out per group of kRows batch rows
+// (row_blocks of them per group), so the rows are per-workgroup scalars and
+// the lane's channel is plain 32-bit arithmetic.  The partial readouts of the LPC lanes are summed
 // with DPP quad permutes (no LDS traffic).
 
 #ifndef SSM_UPDATE_ROWS
