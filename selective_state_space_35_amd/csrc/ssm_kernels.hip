@@ -666,22 +666,22 @@ hipError_t update_typed(const UpdateArgs& a) {
 ScanPlan plan_scan(int64_t b, int64_t L, int64_t E, int elem_bytes) {
   ScanPlan pl;
   pl.e_blocks = int((E + kWave - 1) / kWave);
-  // Enough waves that every SIMD of the 256 CUs sees several rounds of them:
-  // register use allows 4 resident per SIMD, 4096 on the chip, and 20480 is
-  // five whole rounds (a target just past a multiple of 4096 leaves a last
-  // round almost empty; 16384 gave 205 chunks x 80 blocks = 16400 waves on
-  // the long sequence, 1.3% slower).  The sequence is cut only when batch x
-  // channel blocks alone cannot provide them.
+  // Enough waves that every SIMD of the 256 CUs sees several rounds of them
+  // (the two passes hold 6 and 7 waves per SIMD).  20480 measured best on the
+  // long sequence among targets of 12288 to 30720: 256 chunks of 256 steps,
+  // 1.871 ms against 1.896 for 16384 and 1.93 for 22528 (means of repeated
+  // runs).  The sequence is cut only when batch x channel blocks alone cannot
+  // provide them.
   int64_t target = 20480;
   if (const char* s = std::getenv("SSM_SCAN_TARGET_WAVES")) {
     const long v = std::strtol(s, nullptr, 10);
     if (v > 0) target = v;
   }
   const int64_t base = b * pl.e_blocks;
-  // Chunks of at least 64 steps, or of 32 when 64-step chunks cannot give the
-  // chip one round of resident waves (4096) and the sequence has 256 steps or
-  // more (shorter ones are launch-bound): b32 L512 E512 takes 96 us in 16
-  // chunks of 32 steps against 114 us in 8 of 64.
+  // Chunks of at least 64 steps, or of 32 when 64-step chunks give fewer than
+  // 4096 waves (4 per SIMD) and the sequence has 256 steps or more (shorter
+  // ones are launch-bound): b32 L512 E512 takes 96 us in 16 chunks of 32 steps
+  // against 114 us in 8 of 64.
   int64_t min_chunk = (L >= 256 && base * ((L + 63) / 64) < 4096) ? 32 : 64;
   if (const char* s = std::getenv("SSM_SCAN_MIN_CHUNK")) {
     const long v = std::strtol(s, nullptr, 10);

@@ -289,8 +289,8 @@ def test_scan_plan_query(lib, monkeypatch):
         assert cl >= 1 and nc >= 1
         assert (nc - 1) * cl < L <= nc * cl, (b, L, E, cl, nc)  # chunks tile the sequence exactly
         assert cl * E * (4 if dt == "f32" else 2) < 2 ** 31  # 32-bit buffer offsets inside a chunk
-    # the long sequence: 256 chunks x 80 channel blocks = 20480 waves, five whole
-    # rounds of the 4096 waves (256 CUs x 4 SIMDs x 4) the chip holds at once
+    # the long sequence: 256 chunks x 80 channel blocks = 20480 waves, the target
+    # that measured best
     assert ssm.ssm_scan_plan(1, 65536, 5120, 16, "bf16") == (256, 256)
     # 64-step chunks fill the chip for the mid workload (6144 waves); the block workload
     # (2048 waves at 64 steps) is cut into 32-step chunks instead
