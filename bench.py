@@ -253,6 +253,305 @@ def scan_configs(ssm, workloads, torch, dev, stream, seed, cpu=True):
     return out
 
 
+def measure_decode(ssm, torch, workloads, dev, stream, seed):
+    """128 successive state updates of the decode workload, and the token step (eager and from a HIP graph)."""
+    wd = workloads.DECODE
+    xd = workloads.make_decode_inputs(wd, seed=seed, device=dev, backend="torch")
+    st = xd["state0"].clone()
+    yd = torch.empty(wd.b, wd.E, dtype=torch.bfloat16, device=dev)
+
+    def decode_pass():
+        for k in range(wd.steps):
+            ssm.ssm_state_update(st, xd["x"][k], xd["delta"][k], xd["A"], xd["B"][k], xd["C"][k], xd["D"],
+                                 xd["z"][k], xd["delta_bias"], xd["softplus"], y=yd)
+
+    decode_pass()
+    torch.cuda.synchronize()
+    reps = 5
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ssm.ssm_profile_enable(True)
+    e0.record(stream)
+    for _ in range(reps):
+        st.zero_()
+        decode_pass()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ssm.ssm_profile_enable(False)
+    upd = ssm.ssm_profile_read()["state_update"]
+    per_call_us = 1e3 * upd[0] / upd[1]
+    ub = update_bytes(wd.b, wd.E, wd.N, 2)
+    update = {"workload": wd.description, "us_per_call": round(per_call_us, 3),
+              "calls": upd[1], "wall_ms_per_128": round(e0.elapsed_time(e1) / reps, 4),
+              "GBps": round(ub / (per_call_us * 1e-6) / 1e9, 1),
+              "bytes_per_call": ub,
+              "note": "the 84 MB fp32 state fits in the 256 MB Infinity Cache, so carried-state traffic "
+                      "can be served from it; GB/s is algorithmic bytes over kernel time"}
+
+    # one generation step of the block's kernels per token: the convolution token step, then the state
+    # update on its output; eager launches against the same T tokens captured once in a HIP graph
+    def token_step(bt, T=32):
+        g2 = torch.Generator(device=dev).manual_seed(seed + 5)
+        v_tok = torch.randn((T, bt, wd.E), generator=g2, device=dev).to(torch.bfloat16)
+        dl = torch.randn((T, bt, wd.E), generator=g2, device=dev).to(torch.bfloat16)
+        Bt = torch.randn((T, bt, wd.N), generator=g2, device=dev).to(torch.bfloat16)
+        Ct = torch.randn((T, bt, wd.N), generator=g2, device=dev).to(torch.bfloat16)
+        zt = torch.randn((T, bt, wd.E), generator=g2, device=dev).to(torch.bfloat16)
+        q = torch.randn((wd.E, 4), generator=g2, device=dev) * 0.5
+        cb = torch.randn((wd.E,), generator=g2, device=dev) * 0.1
+        cst = torch.zeros((bt, wd.E, 4), dtype=torch.bfloat16, device=dev)
+        sst = torch.zeros((bt, wd.E, wd.N), dtype=torch.float32, device=dev)
+        xs = torch.empty((T, bt, wd.E), dtype=torch.bfloat16, device=dev)
+        ys = torch.empty((T, bt, wd.E), dtype=torch.bfloat16, device=dev)
+
+        def tokens():
+            for k in range(T):
+                ssm.ssm_conv_update(cst, v_tok[k], q, cb, x=xs[k])
+                ssm.ssm_state_update(sst, xs[k], dl[k], xd["A"], Bt[k], Ct[k], xd["D"], zt[k],
+                                     xd["delta_bias"], xd["softplus"], y=ys[k])
+
+        tokens()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(reps):
+            tokens()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        eager_us = 1e3 * t0.elapsed_time(t1) / (reps * T)
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            tokens()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            tokens()
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        graph_us = 1e3 * t0.elapsed_time(t1) / (reps * T)
+        del graph
+        return {"eager_us_per_token": round(eager_us, 2), "graph_us_per_token": round(graph_us, 2)}
+
+    update["token_step"] = {
+        "workload": f"per token: ssm_conv_update (K4) then ssm_state_update, E{wd.E} N{wd.N} bf16, 32 tokens",
+        "b256": token_step(wd.b), "b1": token_step(1),
+        "note": "both entry points launch on the caller's stream with no workspace and no memset, so the "
+                "token loop can be captured in a HIP graph (torch.cuda.CUDAGraph) and replayed; at b1 the "
+                "step is launch-bound"}
+    log(f"[bench] token step {update['token_step']}")
+    del xd, st, yd
+    return update
+
+
+def measure_backward(ssm, torch, dev, stream, x, w, steps, seed):
+    """ssm_scan_bwd on the long workload, and the training form (forward with saved states, backward from them)."""
+    s = 2 if w.dtype == "bf16" else 4
+    elems = w.b * w.L * w.E
+    gen = torch.Generator(device=dev).manual_seed(seed + 11)
+    dy = torch.randn(x["u"].shape, generator=gen, device=dev).to(x["u"].dtype)
+
+    def bwd_step():
+        return ssm.ssm_scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], dy, x["D"], x["z"],
+                                x["delta_bias"], x["softplus"])
+
+    for _ in range(2):
+        g = bwd_step()
+    del g
+    torch.cuda.synchronize()
+    ssm.ssm_profile_read()
+    ssm.ssm_profile_enable(True)
+    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = max(3, steps // 5)
+    b0.record(stream)
+    for _ in range(reps):
+        g = bwd_step()
+    b1.record(stream)
+    torch.cuda.synchronize()
+    ssm.ssm_profile_enable(False)
+    del g
+    prof = ssm.ssm_profile_read()
+    bwd_ms = b0.elapsed_time(b1) / reps
+    bb = bwd_bytes(w.b, w.L, w.E, w.N, s, gate=w.z is not None)
+    bwd = {"workload": "backward of the long-sequence scan (same inputs, dy ~ N(0,1) bf16)",
+           "ms_per_call": round(bwd_ms, 4), "elem_per_s": elems / (bwd_ms * 1e-3),
+           "algorithmic_bytes": bb, "GBps": round(bb / (bwd_ms * 1e-3) / 1e9, 1),
+           "kernels": {k: {"avg_us": round(1e3 * v[0] / v[1], 2), "launches": v[1]}
+                       for k, v in prof.items() if v[1]},
+           "note": "includes the workspace allocation and the forward chunk-state passes it reruns"}
+    log(f"[bench] backward {bwd}")
+
+    # training form: the forward keeps the state every 64 steps, the backward starts its chunks from them
+    saved = torch.empty(ssm.saved_states_shape(w.b, w.L, w.E, w.N), dtype=torch.float32, device=dev)
+    ys = torch.empty_like(x["u"])
+
+    def fwd_save():
+        ssm.ssm_scan_fwd_save(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
+                              x["softplus"], y=ys, saved_states=saved)
+
+    def bwd_saved():
+        return ssm.ssm_scan_bwd_saved(x["u"], x["delta"], x["A"], x["B"], x["C"], dy, saved, x["D"], x["z"],
+                                      x["delta_bias"], x["softplus"])
+
+    fwd_save()
+    g = bwd_saved()
+    del g
+    torch.cuda.synchronize()
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    f0.record(stream)
+    for _ in range(reps):
+        fwd_save()
+    f1.record(stream)
+    torch.cuda.synchronize()
+    ssm.ssm_profile_read()
+    ssm.ssm_profile_enable(True)
+    b0.record(stream)
+    for _ in range(reps):
+        g = bwd_saved()
+    b1.record(stream)
+    torch.cuda.synchronize()
+    ssm.ssm_profile_enable(False)
+    del g
+    prof = ssm.ssm_profile_read()
+    fs_ms, bs_ms = f0.elapsed_time(f1) / reps, b0.elapsed_time(b1) / reps
+    bwd["from_saved_states"] = {
+        "forward_with_save_ms": round(fs_ms, 4), "backward_ms": round(bs_ms, 4),
+        "saved_bytes": saved.numel() * 4,
+        "kernels": {k: {"avg_us": round(1e3 * v[0] / v[1], 2), "launches": v[1]} for k, v in prof.items() if v[1]},
+        "note": "ssm_scan_fwd_save keeps the state every 64 steps (1/64 of the states); ssm_scan_bwd_saved "
+                "starts its 64-step chunks from them instead of rerunning the forward chunk-state passes"}
+    log(f"[bench] backward from saved states {bwd['from_saved_states']}")
+    del dy, saved, ys
+    return bwd
+
+
+def measure_ssd(ssm, torch, workloads, dev, stream, seed):
+    """ssm_ssd_fwd on the scalar-per-head workload, with its per-kernel split."""
+    ws = workloads.SSD_LONG
+    xs = workloads.make_ssd_inputs(ws, seed=seed, device=dev, backend="torch")
+    ys = torch.empty_like(xs["x"])
+    ls = torch.empty((ws.b, ws.E, ws.N), dtype=torch.float32, device=dev)
+
+    def ssd_step():
+        ssm.ssm_ssd_fwd(xs["x"], xs["delta"], xs["A"], xs["B"], xs["C"], xs["D"], xs["z"], xs["delta_bias"],
+                        xs["softplus"], y=ys, last_state=ls)
+
+    for _ in range(3):
+        ssd_step()
+    torch.cuda.synchronize()
+    ssm.ssm_profile_read()
+    ssm.ssm_profile_enable(True)
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record(stream)
+    for _ in range(20):
+        ssd_step()
+    s1.record(stream)
+    torch.cuda.synchronize()
+    ssm.ssm_profile_enable(False)
+    prof = ssm.ssm_profile_read()
+    ssd_ms = s0.elapsed_time(s1) / 20
+    sb = ssd_bytes(ws.b, ws.L, ws.H, ws.P, ws.N, 2, gate=ws.gate)
+    sf = ssd_flops(ws.b, ws.L, ws.H, ws.P, ws.N)
+    ssd = {"workload": ws.description, "ms_per_call": round(ssd_ms, 4),
+           "elem_per_s": ws.b * ws.L * ws.E / (ssd_ms * 1e-3), "algorithmic_bytes": sb,
+           "GBps": round(sb / (ssd_ms * 1e-3) / 1e9, 1), "matrix_TFLOPs": round(sf / (ssd_ms * 1e-3) / 1e12, 2),
+           "kernels": {k: {"avg_us": round(1e3 * v[0] / v[1], 2), "launches": v[1]}
+                       for k, v in prof.items() if v[1]}}
+    log(f"[bench] ssd {ssd}")
+    del xs, ys, ls
+    return ssd
+
+
+def measure_conv(ssm, torch, workloads, dev, seed):
+    """ssm_conv_fwd on the long workload and ssm_conv_update on the decode workload."""
+    wc = workloads.CONV_LONG
+    xc = workloads.make_conv_inputs(wc, seed=seed, device=dev, backend="torch")
+    xo = torch.empty_like(xc["v"])
+    so = torch.empty((wc.b, wc.E, wc.K), dtype=xc["v"].dtype, device=dev)
+    for _ in range(3):
+        ssm.ssm_conv_fwd(xc["v"], xc["weight"], xc["conv_bias"], None, x=xo, state_out=so)
+    torch.cuda.synchronize()
+    ssm.ssm_profile_enable(True)
+    for _ in range(20):
+        ssm.ssm_conv_fwd(xc["v"], xc["weight"], xc["conv_bias"], None, x=xo, state_out=so)
+    torch.cuda.synchronize()
+    ssm.ssm_profile_enable(False)
+    cf = ssm.ssm_profile_read()["conv"]
+    cf_us = 1e3 * cf[0] / cf[1]
+    cb_ = conv_bytes(wc.b, wc.L, wc.E, wc.K, 2)
+    del xc, xo, so
+    wu = workloads.CONV_DECODE
+    xu = workloads.make_conv_inputs(wu, seed=seed, device=dev, backend="torch")
+    cst = xu["state_in"].clone()
+    v_t = xu["v"][:, 0].contiguous()
+    xt = torch.empty_like(v_t)
+    for _ in range(3):
+        ssm.ssm_conv_update(cst, v_t, xu["weight"], xu["conv_bias"], x=xt)
+    torch.cuda.synchronize()
+    ssm.ssm_profile_enable(True)
+    for _ in range(128):
+        ssm.ssm_conv_update(cst, v_t, xu["weight"], xu["conv_bias"], x=xt)
+    torch.cuda.synchronize()
+    ssm.ssm_profile_enable(False)
+    cu = ssm.ssm_profile_read()["conv_update"]
+    cu_us = 1e3 * cu[0] / cu[1]
+    ub_ = conv_update_bytes(wu.b, wu.E, wu.K, 2)
+    conv = {"sequence": {"workload": wc.description, "us_per_call": round(cf_us, 2), "calls": cf[1],
+                         "bytes_per_call": cb_, "GBps": round(cb_ / (cf_us * 1e-6) / 1e9, 1),
+                         "frac": round(cb_ / (cf_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)},
+            "token": {"workload": wu.description, "us_per_call": round(cu_us, 3), "calls": cu[1],
+                      "bytes_per_call": ub_, "GBps": round(ub_ / (cu_us * 1e-6) / 1e9, 1)}}
+    log(f"[bench] conv {conv}")
+    del xu, cst, v_t, xt
+    return conv
+
+
+def measure_cpu_baseline(torch, dev, x, w, y, last, cpu_seconds):
+    """The fp64 oracle on a bounded channel sample of the long workload's inputs, timed on the host
+    cores, and the parity of the GPU outputs on those channels."""
+    import numpy as np
+
+    import oracle
+
+    threads = oracle.default_threads()
+    rng = np.random.default_rng(1)
+
+    def sample(nch):
+        ch = torch.from_numpy(np.sort(rng.choice(w.E, size=nch, replace=False))).to(dev)
+        sel = lambda t: None if t is None else t.index_select(2, ch)
+        args_ = (sel(x["u"]), sel(x["delta"]), x["A"].index_select(0, ch), x["B"], x["C"],
+                 None if x["D"] is None else x["D"].index_select(0, ch), sel(x["z"]),
+                 None if x["delta_bias"] is None else x["delta_bias"].index_select(0, ch))
+        return ch, [oracle.to_f64(a) for a in args_]
+
+    # calibrate on a small sample, then size the measured sample to about --cpu-seconds
+    ch, a = sample(threads)
+    c0 = time.perf_counter()
+    oracle.scan(*a, softplus=x["softplus"], threads=threads)
+    rate = threads * w.L / (time.perf_counter() - c0)  # channel-steps per second
+    nch = int(max(threads, min(w.E, cpu_seconds * rate / w.L)))
+    nch = max(threads, (nch // threads) * threads)
+    ch, a = sample(nch)
+    c0 = time.perf_counter()
+    y_ref, last_ref = oracle.scan(*a, softplus=x["softplus"], threads=threads)
+    cpu_s = time.perf_counter() - c0
+    cpu = {"value": w.b * w.L * nch / cpu_s, "unit": "elem/s", "cores": threads, "kind": "oracle",
+           "cpu_model": cpu_model(), "seconds": round(cpu_s, 2),
+           "sample": f"{nch} of {w.E} channels (independent chains), full L={w.L}, b={w.b}; "
+                     "fp64 sequential oracle, same inputs"}
+    yg = oracle.to_f64(y.index_select(2, ch))
+    lg = oracle.to_f64(last.index_select(1, ch))
+    err = lambda g, r: float(np.max(np.abs(g - r) / (1 + np.abs(r))))
+    parity = {"y_max_normalised_error": err(yg, y_ref), "last_state_max_normalised_error": err(lg, last_ref),
+              "bound": 2e-2, "channels_checked": nch}
+    log(f"[bench] cpu baseline {cpu['value']:.3e} elem/s on {threads} threads; parity {parity}")
+    return cpu, parity
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -277,7 +576,6 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import selective_state_space_35_amd as ssm
@@ -351,294 +649,20 @@ def main():
                    "second (aggregate) pass over all but the last chunk; its slots are not algorithmic"}
 
     # state update (generation): 128 successive single-token updates, state carried in HBM
-    update = None
-    if not args.no_decode:
-        wd = workloads.DECODE
-        xd = workloads.make_decode_inputs(wd, seed=args.seed, device=dev, backend="torch")
-        st = xd["state0"].clone()
-        yd = torch.empty(wd.b, wd.E, dtype=torch.bfloat16, device=dev)
-
-        def decode_pass():
-            for k in range(wd.steps):
-                ssm.ssm_state_update(st, xd["x"][k], xd["delta"][k], xd["A"], xd["B"][k], xd["C"][k], xd["D"],
-                                     xd["z"][k], xd["delta_bias"], xd["softplus"], y=yd)
-
-        decode_pass()
-        torch.cuda.synchronize()
-        reps = 5
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ssm.ssm_profile_enable(True)
-        e0.record(stream)
-        for _ in range(reps):
-            st.zero_()
-            decode_pass()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ssm.ssm_profile_enable(False)
-        upd = ssm.ssm_profile_read()["state_update"]
-        per_call_us = 1e3 * upd[0] / upd[1]
-        ub = update_bytes(wd.b, wd.E, wd.N, 2)
-        update = {"workload": wd.description, "us_per_call": round(per_call_us, 3),
-                  "calls": upd[1], "wall_ms_per_128": round(e0.elapsed_time(e1) / reps, 4),
-                  "GBps": round(ub / (per_call_us * 1e-6) / 1e9, 1),
-                  "bytes_per_call": ub,
-                  "note": "the 84 MB fp32 state fits in the 256 MB Infinity Cache, so carried-state traffic "
-                          "can be served from it; GB/s is algorithmic bytes over kernel time"}
-
-        # one generation step of the block's kernels per token: the convolution token step, then the state
-        # update on its output; eager launches against the same T tokens captured once in a HIP graph
-        def token_step(bt, T=32):
-            g2 = torch.Generator(device=dev).manual_seed(args.seed + 5)
-            v_tok = torch.randn((T, bt, wd.E), generator=g2, device=dev).to(torch.bfloat16)
-            dl = torch.randn((T, bt, wd.E), generator=g2, device=dev).to(torch.bfloat16)
-            Bt = torch.randn((T, bt, wd.N), generator=g2, device=dev).to(torch.bfloat16)
-            Ct = torch.randn((T, bt, wd.N), generator=g2, device=dev).to(torch.bfloat16)
-            zt = torch.randn((T, bt, wd.E), generator=g2, device=dev).to(torch.bfloat16)
-            q = torch.randn((wd.E, 4), generator=g2, device=dev) * 0.5
-            cb = torch.randn((wd.E,), generator=g2, device=dev) * 0.1
-            cst = torch.zeros((bt, wd.E, 4), dtype=torch.bfloat16, device=dev)
-            sst = torch.zeros((bt, wd.E, wd.N), dtype=torch.float32, device=dev)
-            xs = torch.empty((T, bt, wd.E), dtype=torch.bfloat16, device=dev)
-            ys = torch.empty((T, bt, wd.E), dtype=torch.bfloat16, device=dev)
-
-            def tokens():
-                for k in range(T):
-                    ssm.ssm_conv_update(cst, v_tok[k], q, cb, x=xs[k])
-                    ssm.ssm_state_update(sst, xs[k], dl[k], xd["A"], Bt[k], Ct[k], xd["D"], zt[k],
-                                         xd["delta_bias"], xd["softplus"], y=ys[k])
-
-            tokens()
-            torch.cuda.synchronize()
-            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            t0.record(stream)
-            for _ in range(reps):
-                tokens()
-            t1.record(stream)
-            torch.cuda.synchronize()
-            eager_us = 1e3 * t0.elapsed_time(t1) / (reps * T)
-            side = torch.cuda.Stream()
-            side.wait_stream(stream)
-            with torch.cuda.stream(side):
-                tokens()
-            stream.wait_stream(side)
-            torch.cuda.synchronize()
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph):
-                tokens()
-            torch.cuda.synchronize()
-            t0.record(stream)
-            for _ in range(reps):
-                graph.replay()
-            t1.record(stream)
-            torch.cuda.synchronize()
-            graph_us = 1e3 * t0.elapsed_time(t1) / (reps * T)
-            del graph
-            return {"eager_us_per_token": round(eager_us, 2), "graph_us_per_token": round(graph_us, 2)}
-
-        update["token_step"] = {
-            "workload": f"per token: ssm_conv_update (K4) then ssm_state_update, E{wd.E} N{wd.N} bf16, 32 tokens",
-            "b256": token_step(wd.b), "b1": token_step(1),
-            "note": "both entry points launch on the caller's stream with no workspace and no memset, so the "
-                    "token loop can be captured in a HIP graph (torch.cuda.CUDAGraph) and replayed; at b1 the "
-                    "step is launch-bound"}
-        log(f"[bench] token step {update['token_step']}")
-        del xd, st, yd
+    update = None if args.no_decode else measure_decode(ssm, torch, workloads, dev, stream, args.seed)
 
     # backward of the scan on the same workload (gradients of every input, states recomputed)
-    bwd = None
-    if not args.no_bwd:
-        gen = torch.Generator(device=dev).manual_seed(args.seed + 11)
-        dy = torch.randn(x["u"].shape, generator=gen, device=dev).to(x["u"].dtype)
-
-        def bwd_step():
-            return ssm.ssm_scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], dy, x["D"], x["z"],
-                                    x["delta_bias"], x["softplus"])
-
-        for _ in range(2):
-            g = bwd_step()
-        del g
-        torch.cuda.synchronize()
-        ssm.ssm_profile_read()
-        ssm.ssm_profile_enable(True)
-        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = max(3, args.steps // 5)
-        b0.record(stream)
-        for _ in range(reps):
-            g = bwd_step()
-        b1.record(stream)
-        torch.cuda.synchronize()
-        ssm.ssm_profile_enable(False)
-        del g
-        prof = ssm.ssm_profile_read()
-        bwd_ms = b0.elapsed_time(b1) / reps
-        bb = bwd_bytes(w.b, w.L, w.E, w.N, s, gate=w.z is not None)
-        bwd = {"workload": "backward of the long-sequence scan (same inputs, dy ~ N(0,1) bf16)",
-               "ms_per_call": round(bwd_ms, 4), "elem_per_s": elems / (bwd_ms * 1e-3),
-               "algorithmic_bytes": bb, "GBps": round(bb / (bwd_ms * 1e-3) / 1e9, 1),
-               "kernels": {k: {"avg_us": round(1e3 * v[0] / v[1], 2), "launches": v[1]}
-                           for k, v in prof.items() if v[1]},
-               "note": "includes the workspace allocation and the forward chunk-state passes it reruns"}
-        log(f"[bench] backward {bwd}")
-
-        # training form: the forward keeps the state every 64 steps, the backward starts its chunks from them
-        saved = torch.empty(ssm.saved_states_shape(w.b, w.L, w.E, w.N), dtype=torch.float32, device=dev)
-        ys = torch.empty_like(x["u"])
-
-        def fwd_save():
-            ssm.ssm_scan_fwd_save(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
-                                  x["softplus"], y=ys, saved_states=saved)
-
-        def bwd_saved():
-            return ssm.ssm_scan_bwd_saved(x["u"], x["delta"], x["A"], x["B"], x["C"], dy, saved, x["D"], x["z"],
-                                          x["delta_bias"], x["softplus"])
-
-        fwd_save()
-        g = bwd_saved()
-        del g
-        torch.cuda.synchronize()
-        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        f0.record(stream)
-        for _ in range(reps):
-            fwd_save()
-        f1.record(stream)
-        torch.cuda.synchronize()
-        ssm.ssm_profile_read()
-        ssm.ssm_profile_enable(True)
-        b0.record(stream)
-        for _ in range(reps):
-            g = bwd_saved()
-        b1.record(stream)
-        torch.cuda.synchronize()
-        ssm.ssm_profile_enable(False)
-        del g
-        prof = ssm.ssm_profile_read()
-        fs_ms, bs_ms = f0.elapsed_time(f1) / reps, b0.elapsed_time(b1) / reps
-        bwd["from_saved_states"] = {
-            "forward_with_save_ms": round(fs_ms, 4), "backward_ms": round(bs_ms, 4),
-            "saved_bytes": saved.numel() * 4,
-            "kernels": {k: {"avg_us": round(1e3 * v[0] / v[1], 2), "launches": v[1]} for k, v in prof.items() if v[1]},
-            "note": "ssm_scan_fwd_save keeps the state every 64 steps (1/64 of the states); ssm_scan_bwd_saved "
-                    "starts its 64-step chunks from them instead of rerunning the forward chunk-state passes"}
-        log(f"[bench] backward from saved states {bwd['from_saved_states']}")
-        del dy, saved, ys
+    bwd = None if args.no_bwd else measure_backward(ssm, torch, dev, stream, x, w, args.steps, args.seed)
 
     # the scan with a scalar transition per head, in chunks of MFMA matrix products
-    ssd = None
-    if not args.no_ssd:
-        ws = workloads.SSD_LONG
-        xs = workloads.make_ssd_inputs(ws, seed=args.seed, device=dev, backend="torch")
-        ys = torch.empty_like(xs["x"])
-        ls = torch.empty((ws.b, ws.E, ws.N), dtype=torch.float32, device=dev)
-
-        def ssd_step():
-            ssm.ssm_ssd_fwd(xs["x"], xs["delta"], xs["A"], xs["B"], xs["C"], xs["D"], xs["z"], xs["delta_bias"],
-                            xs["softplus"], y=ys, last_state=ls)
-
-        for _ in range(3):
-            ssd_step()
-        torch.cuda.synchronize()
-        ssm.ssm_profile_read()
-        ssm.ssm_profile_enable(True)
-        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s0.record(stream)
-        for _ in range(20):
-            ssd_step()
-        s1.record(stream)
-        torch.cuda.synchronize()
-        ssm.ssm_profile_enable(False)
-        prof = ssm.ssm_profile_read()
-        ssd_ms = s0.elapsed_time(s1) / 20
-        sb = ssd_bytes(ws.b, ws.L, ws.H, ws.P, ws.N, 2, gate=ws.gate)
-        sf = ssd_flops(ws.b, ws.L, ws.H, ws.P, ws.N)
-        ssd = {"workload": ws.description, "ms_per_call": round(ssd_ms, 4),
-               "elem_per_s": ws.b * ws.L * ws.E / (ssd_ms * 1e-3), "algorithmic_bytes": sb,
-               "GBps": round(sb / (ssd_ms * 1e-3) / 1e9, 1), "matrix_TFLOPs": round(sf / (ssd_ms * 1e-3) / 1e12, 2),
-               "kernels": {k: {"avg_us": round(1e3 * v[0] / v[1], 2), "launches": v[1]}
-                           for k, v in prof.items() if v[1]}}
-        log(f"[bench] ssd {ssd}")
-        del xs, ys, ls
+    ssd = None if args.no_ssd else measure_ssd(ssm, torch, workloads, dev, stream, args.seed)
 
     # causal convolution in front of the scan (long workload) and its generation-time token step
-    conv = None
-    if not args.no_conv:
-        wc = workloads.CONV_LONG
-        xc = workloads.make_conv_inputs(wc, seed=args.seed, device=dev, backend="torch")
-        xo = torch.empty_like(xc["v"])
-        so = torch.empty((wc.b, wc.E, wc.K), dtype=xc["v"].dtype, device=dev)
-        for _ in range(3):
-            ssm.ssm_conv_fwd(xc["v"], xc["weight"], xc["conv_bias"], None, x=xo, state_out=so)
-        torch.cuda.synchronize()
-        ssm.ssm_profile_enable(True)
-        for _ in range(20):
-            ssm.ssm_conv_fwd(xc["v"], xc["weight"], xc["conv_bias"], None, x=xo, state_out=so)
-        torch.cuda.synchronize()
-        ssm.ssm_profile_enable(False)
-        cf = ssm.ssm_profile_read()["conv"]
-        cf_us = 1e3 * cf[0] / cf[1]
-        cb_ = conv_bytes(wc.b, wc.L, wc.E, wc.K, 2)
-        del xc, xo, so
-        wu = workloads.CONV_DECODE
-        xu = workloads.make_conv_inputs(wu, seed=args.seed, device=dev, backend="torch")
-        cst = xu["state_in"].clone()
-        v_t = xu["v"][:, 0].contiguous()
-        xt = torch.empty_like(v_t)
-        for _ in range(3):
-            ssm.ssm_conv_update(cst, v_t, xu["weight"], xu["conv_bias"], x=xt)
-        torch.cuda.synchronize()
-        ssm.ssm_profile_enable(True)
-        for _ in range(128):
-            ssm.ssm_conv_update(cst, v_t, xu["weight"], xu["conv_bias"], x=xt)
-        torch.cuda.synchronize()
-        ssm.ssm_profile_enable(False)
-        cu = ssm.ssm_profile_read()["conv_update"]
-        cu_us = 1e3 * cu[0] / cu[1]
-        ub_ = conv_update_bytes(wu.b, wu.E, wu.K, 2)
-        conv = {"sequence": {"workload": wc.description, "us_per_call": round(cf_us, 2), "calls": cf[1],
-                             "bytes_per_call": cb_, "GBps": round(cb_ / (cf_us * 1e-6) / 1e9, 1),
-                             "frac": round(cb_ / (cf_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)},
-                "token": {"workload": wu.description, "us_per_call": round(cu_us, 3), "calls": cu[1],
-                          "bytes_per_call": ub_, "GBps": round(ub_ / (cu_us * 1e-6) / 1e9, 1)}}
-        log(f"[bench] conv {conv}")
-        del xu, cst, v_t, xt
+    conv = None if args.no_conv else measure_conv(ssm, torch, workloads, dev, args.seed)
 
     # CPU baseline: the oracle on a bounded channel sample of the same inputs
-    cpu = None
-    parity = None
-    if not args.no_cpu_baseline:
-        import oracle
-
-        threads = oracle.default_threads()
-        rng = np.random.default_rng(1)
-
-        def sample(nch):
-            ch = torch.from_numpy(np.sort(rng.choice(w.E, size=nch, replace=False))).to(dev)
-            sel = lambda t: None if t is None else t.index_select(2, ch)
-            args_ = (sel(x["u"]), sel(x["delta"]), x["A"].index_select(0, ch), x["B"], x["C"],
-                     None if x["D"] is None else x["D"].index_select(0, ch), sel(x["z"]),
-                     None if x["delta_bias"] is None else x["delta_bias"].index_select(0, ch))
-            return ch, [oracle.to_f64(a) for a in args_]
-
-        # calibrate on a small sample, then size the measured sample to about --cpu-seconds
-        ch, a = sample(threads)
-        c0 = time.perf_counter()
-        oracle.scan(*a, softplus=x["softplus"], threads=threads)
-        rate = threads * w.L / (time.perf_counter() - c0)  # channel-steps per second
-        nch = int(max(threads, min(w.E, args.cpu_seconds * rate / w.L)))
-        nch = max(threads, (nch // threads) * threads)
-        ch, a = sample(nch)
-        c0 = time.perf_counter()
-        y_ref, last_ref = oracle.scan(*a, softplus=x["softplus"], threads=threads)
-        cpu_s = time.perf_counter() - c0
-        cpu = {"value": w.b * w.L * nch / cpu_s, "unit": "elem/s", "cores": threads, "kind": "oracle",
-               "cpu_model": cpu_model(), "seconds": round(cpu_s, 2),
-               "sample": f"{nch} of {w.E} channels (independent chains), full L={w.L}, b={w.b}; "
-                         "fp64 sequential oracle, same inputs"}
-        yg = oracle.to_f64(y.index_select(2, ch))
-        lg = oracle.to_f64(last.index_select(1, ch))
-        err = lambda g, r: float(np.max(np.abs(g - r) / (1 + np.abs(r))))
-        parity = {"y_max_normalised_error": err(yg, y_ref), "last_state_max_normalised_error": err(lg, last_ref),
-                  "bound": 2e-2, "channels_checked": nch}
-        log(f"[bench] cpu baseline {cpu['value']:.3e} elem/s on {threads} threads; parity {parity}")
+    cpu, parity = (None, None) if args.no_cpu_baseline else measure_cpu_baseline(
+        torch, dev, x, w, y, last, args.cpu_seconds)
 
     # the other scan configurations, and the long workload's one-GPU share under channel
     # sharding: every call timed on its own (event pair on the launch stream), median and min
