@@ -151,8 +151,10 @@ enum { kSu = 0, kSd = 1, kSy = 2, kSz = 3 };
 // ---------------------------------------------------------------------------
 // 4. main backward pass over one chunk of one 64-channel block
 // ---------------------------------------------------------------------------
+// Occupancy: three workgroups per CU with bf16 streams; with fp32 streams the
+// staged chunk doubles and LDS holds two.
 template <typename T, bool SOFTPLUS, bool HAS_Z, bool HAS_D>
-__global__ __launch_bounds__(kBwdWaves * kWave) __attribute__((amdgpu_waves_per_eu(3))) void bwd_main_kernel(
+__global__ __launch_bounds__(kBwdWaves * kWave) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 3 : 2))) void bwd_main_kernel(
     const T* __restrict__ u, const T* __restrict__ delta, const float* __restrict__ A,
     const float* __restrict__ B16, const float* __restrict__ C16, const float* __restrict__ D,
     const T* __restrict__ z, const float* __restrict__ bias, const T* __restrict__ dy, const float* __restrict__ h0,

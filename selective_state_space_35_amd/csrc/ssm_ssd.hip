@@ -187,9 +187,11 @@ __device__ __forceinline__ uint4 scale8(uint4 v, float w) {
 // transposing LDS read.  Capped at 80 VGPRs so that three 8-wave workgroups share a CU: their
 // interleaving hides the reads better than a prefetch of the next chunk, whose
 // registers would leave room for two (measured 302 against 333 us at ssd_long).
+// Above 64 states the tiles take more than a third of the LDS and two workgroups
+// share a CU.
 // ---------------------------------------------------------------------------
 template <int NK, bool SOFTPLUS>  // NK: the state size padded to a multiple of 32, in units of 32
-__global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(6))) void ssd_state_kernel(
+__global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(NK <= 2 ? 6 : 4))) void ssd_state_kernel(
     const bf16_bits* __restrict__ x, const bf16_bits* __restrict__ delta, const float* __restrict__ A,
     const bf16_bits* __restrict__ B, const float* __restrict__ bias, bf16_bits* __restrict__ rin,
     float* __restrict__ phi, float* __restrict__ seg_state, float* __restrict__ seg_decay, int64_t L, int H, int N,
@@ -341,10 +343,11 @@ __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(6))
 // issued before anything else.  x, z and y are handled per thread as two rows
 // of 8 channels (16-byte accesses); the products' results go through an fp32
 // LDS tile laid over the C and B tiles, and D x and the gate are applied with
-// the thread's own x and z.
+// the thread's own x and z.  Three workgroups share a CU up to 64 states (46 KB
+// of LDS each), two above.
 // ---------------------------------------------------------------------------
 template <int NK, bool SOFTPLUS, bool HAS_Z, bool HAS_D>
-__global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(6))) void ssd_scan_kernel(
+__global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(NK <= 2 ? 6 : 4))) void ssd_scan_kernel(
     const bf16_bits* __restrict__ x, const bf16_bits* __restrict__ delta, const float* __restrict__ A,
     const bf16_bits* __restrict__ B, const bf16_bits* __restrict__ C, const float* __restrict__ D,
     const bf16_bits* __restrict__ z, const float* __restrict__ bias, const bf16_bits* __restrict__ rin,
