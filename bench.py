@@ -552,6 +552,42 @@ def measure_cpu_baseline(torch, dev, x, w, y, last, cpu_seconds):
     return cpu, parity
 
 
+ALU_KINDS = {0: "v_fma_f32", 1: "v_exp_f32", 2: "4 v_fma_f32 + 1 v_exp_f32", 3: "2 v_fma_f32 + 1 v_exp_f32",
+             4: "v_mul_f32 with a DPP quad-broadcast operand", 5: "v_add_f32"}
+
+
+def alu_calibration(iters=20000, reps=3):
+    """Issue rates of the instruction kinds the scan kernels are made of, on this GPU, from the
+    calibration kernels of libssm_calib.so (built with the library's flags).  Each kind runs on
+    256 CUs x waves_per_simd x 4 waves; rates are lane-operations per second and the implied cycles
+    per wave64 instruction at the 2.4 GHz peak engine clock."""
+    import ctypes
+
+    from selective_state_space_35_amd import build as lib_build
+
+    lib = ctypes.CDLL(lib_build.CALIB_LIB)
+    lib.ssm_calib_alu.restype = ctypes.c_int
+    d = ctypes.c_double
+    lib.ssm_calib_alu.argtypes = [ctypes.c_int] * 4 + [ctypes.POINTER(d)] * 3
+    out = {"clock_GHz_assumed": 2.4, "simds": 1024, "flags": " ".join(lib_build.COMMON[:8]), "kinds": []}
+    for kind, wps in [(0, 1), (0, 2), (0, 4), (0, 8), (1, 8), (2, 8), (3, 8), (4, 8), (5, 8), (2, 4), (1, 4)]:
+        ms, valu, trans = d(), d(), d()
+        rc = lib.ssm_calib_alu(kind, 256 * wps, iters, reps, ctypes.byref(ms), ctypes.byref(valu), ctypes.byref(trans))
+        if rc != 0:
+            raise RuntimeError(f"ssm_calib_alu({kind}) returned {rc}")
+        sec = ms.value * 1e-3
+        cyc = 2.4e9 * sec * 1024  # SIMD-cycles at the peak clock
+        insts = (valu.value + trans.value) / 64
+        rec = {"kind": kind, "what": ALU_KINDS[kind], "waves_per_simd": wps, "ms": round(ms.value, 3),
+               "valu_lane_ops_per_s": valu.value / sec, "trans_lane_ops_per_s": trans.value / sec,
+               "cycles_per_wave_inst": round(cyc / insts, 3)}
+        if valu.value and trans.value:  # mixed: cycles per (one exp + its FMAs) group per wave
+            rec["cycles_per_group"] = round(cyc / (trans.value / 64), 3)
+        out["kinds"].append(rec)
+        log(f"[alu] {rec}")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -565,6 +601,8 @@ def main():
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-ssd", action="store_true")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-configuration scan timings")
+    ap.add_argument("--alu-calibration", action="store_true",
+                    help="only time the issue-rate calibration kernels (libssm_calib.so) and print their rates")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -586,6 +624,10 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.alu_calibration:
+        print(json.dumps(alu_calibration()), flush=True)
+        return
 
     if args.copy_calibration:
         nbytes = 1 << 30
@@ -631,7 +673,9 @@ def main():
     algo = scan_bytes(w.b, w.L, w.E, w.N, s, gate=w.z is not None)
     path_gbps = algo / (ms_per_step * 1e-3) / 1e9
     kernels = {k: {"avg_us": round(1e3 * v[0] / v[1], 2), "launches": v[1]} for k, v in per_kernel.items() if v[1]}
-    main_ms, main_n = per_kernel["scan_main"]
+    # the dominant kernel of the call: the single-pass scan, or the main pass of the chunked form
+    main_name = max((k for k in per_kernel if per_kernel[k][1]), key=lambda k: per_kernel[k][0])
+    main_ms, main_n = per_kernel[main_name]
     main_avg_s = main_ms / max(main_n, 1) * 1e-3
     achieved = algo / main_avg_s / 1e9
     traffic, traffic_note = load_traffic("scan_main", w.name)

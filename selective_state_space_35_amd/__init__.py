@@ -132,7 +132,7 @@ def ssm_scan_plan(b, L, E, N, dtype="bf16"):
     return cl.value, nc.value
 
 
-PROFILE_KINDS = 16
+PROFILE_KINDS = 17
 
 
 def ssm_profile_enable(on=True):

@@ -16,7 +16,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libssm.so")
-SOURCES = ["ssm_kernels.hip", "ssm_conv.hip", "ssm_bwd.hip", "ssm_ssd.hip", "ssm_api.hip", "ssm_profile.hip"]
+CALIB_SRC = os.path.join(PKG, "calib", "ssm_calib.hip")
+CALIB_LIB = os.path.join(PKG, "libssm_calib.so")
+SOURCES = ["ssm_kernels.hip", "ssm_fused.hip", "ssm_conv.hip", "ssm_bwd.hip", "ssm_ssd.hip", "ssm_api.hip", "ssm_profile.hip"]
 ARCH = os.environ.get("SSM_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -58,5 +60,14 @@ def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
     return out
 
 
+def build_calib(verbose: bool = False, out: str = CALIB_LIB) -> str:
+    """Compile libssm_calib.so: the issue-rate calibration kernels (benchmark support), same flags."""
+    tmp = out + ".tmp"
+    _run([HIPCC, *COMMON, "-shared", CALIB_SRC, "-o", tmp], verbose)
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose="-q" not in sys.argv))
+    print(build_calib(verbose="-q" not in sys.argv))

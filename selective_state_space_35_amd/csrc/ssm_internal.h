@@ -135,6 +135,34 @@ int64_t ssd_head_dim();     // channels per head (P)
 int64_t ssd_max_channels(); // largest H * P the chunk kernels address with 32-bit offsets
 hipError_t launch_ssd(const SsdArgs& a);
 
+// The single-pass scan (ssm_fused.hip): a workgroup walks the whole sequence for a
+// slice of channels, in blocks of W chunks of 8 steps joined through LDS.
+constexpr int kFusedMaxWaves = 16;
+struct FusedPlan {
+  int lpc;         // lanes per channel (4 states each): 1, 2 or 4
+  int cg;          // channels per workgroup (of one batch row)
+  int W;           // chunks per block
+  int BT;          // steps per block (W * 8)
+  int groups_row;  // workgroups per batch row
+  int n_wg;        // workgroups
+  int lanes;       // compute lanes: W * lpc * cg
+  int n_cmp;       // compute waves (the first ones); the lanes of chunk 0 chain the block's chunks
+  int n_prod;      // producer waves after them: global <-> LDS tiles
+  int n_threads;   // 64 * (n_cmp + n_prod)
+  int nblk;        // blocks over the sequence
+  int ux, ub;      // bytes one producer lane moves per access: rows of u, delta, z, y / rows of B, C
+  int xR, xM;      // u, delta, z, y tiles: rows per producer pass, passes per block
+  int bR, bM;      // B, C tiles: rows per producer pass, passes per block
+  int xrows, brows;  // rows of an LDS tile (xR * xM, bR * bM >= BT: the last pass may run past BT)
+  int o_x[3], o_bc[3], o_agg, o_hin, o_y[2], o_junk;  // LDS byte offsets (tiles triple / double buffered)
+  int lds_bytes;
+};
+// Plans the single-pass scan for this call; false when it does not apply (too
+// few channels to fill the chip, rows that are not whole 4-byte words, or
+// tiles that do not fit in LDS).
+bool plan_fused(const ScanArgs& a, int n_cu, FusedPlan* p);
+hipError_t launch_fused(const ScanArgs& a, const FusedPlan& p);
+
 // Both return hipSuccess or the first HIP error met while enqueueing.
 hipError_t launch_scan(const ScanArgs& a);
 hipError_t launch_state_update(const UpdateArgs& a);

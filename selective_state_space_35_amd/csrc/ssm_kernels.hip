@@ -712,6 +712,14 @@ hipError_t launch_scan(const ScanArgs& a) {
     return launch_kind(kKindFill, fill_state_kernel, (n + 255) / 256, 256, a.stream, a.last_state, a.h0, n);
   }
   const ScanPlan pl = plan_scan(a.b, a.L, a.E, a.dtype == 0 ? 4 : 2);
+  if (pl.n_chunks > 1) {  // the sequence has to be cut: the single-pass form, when it fills the chip
+    int dev = 0, n_cu = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err == hipSuccess) err = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err != hipSuccess) return err;
+    FusedPlan fp;
+    if (plan_fused(a, n_cu, &fp)) return launch_fused(a, fp);
+  }
   // workspace: [chunk aggregates | chunk step sums | widened B rows | widened C rows]
   const size_t slots = pl.n_chunks > 1 ? size_t(a.b) * size_t(pl.n_chunks) * size_t(a.E) : 0;
   const size_t n_agg = slots * size_t(scan_states(a.N));

@@ -23,7 +23,8 @@ enum : int {
   kKindSsdState = 13,   // scalar-per-head scan: chunk states (matrix products)
   kKindSsdCarry = 14,   // scalar-per-head scan: chain of chunk states
   kKindSsdScan = 15,    // scalar-per-head scan: chunk outputs (matrix products)
-  kNumKinds = 16
+  kKindFused = 16,      // single-pass scan: chunks of a block joined through LDS
+  kNumKinds = 17
 };
 
 // When profiling is on, creates and records the start event on `s` and returns true.

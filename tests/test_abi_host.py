@@ -310,5 +310,6 @@ def test_scan_plan_query(lib, monkeypatch):
 def test_profile_read_with_nothing_recorded(lib):
     out = ssm.ssm_profile_read()
     assert set(out) == {"widen_rows", "chunk_aggregate", "chunk_carry", "scan_main", "fill_state", "state_update",
-                        "conv", "conv_update", "bwd_rows", "bwd_aggregate", "bwd_carry", "bwd_main", "bwd_reduce", "ssd_state", "ssd_carry", "ssd_scan"}
+                        "conv", "conv_update", "bwd_rows", "bwd_aggregate", "bwd_carry", "bwd_main", "bwd_reduce", "ssd_state", "ssd_carry", "ssd_scan",
+                        "scan_fused"}
     assert all(v == (0.0, 0) for v in out.values())
