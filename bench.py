@@ -220,7 +220,8 @@ def scan_configs(ssm, workloads, torch, dev, stream, seed, cpu=True):
                "algorithmic_bytes": nb, "GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
                "copy_frac": round(gbps / copy_gbps, 4),
                "alu_frac": round(sl / (med * 1e-6) / VALU_SLOT_PEAK, 4),
-               "plan": dict(zip(("chunk_len", "n_chunks"), ssm.ssm_scan_plan(wc.b, wc.L, wc.E, wc.N, wc.dtype)))}
+               "plan": dict(zip(("path", "chunk_len", "n_chunks"),
+                                ssm.ssm_scan_plan(wc.b, wc.L, wc.E, wc.N, wc.dtype)))}
         if cpu:
             a64 = [oracle.to_f64(xc[k]) for k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")]
             rates = {}
@@ -644,7 +645,7 @@ def main():
     x = workloads.make_scan_inputs(w, seed=args.seed, device=dev, backend="torch")
     y = torch.empty_like(x["u"])
     last = torch.empty(w.b, w.E, w.N, dtype=torch.float32, device=dev)
-    chunk_len, n_chunks = ssm.ssm_scan_plan(w.b, w.L, w.E, w.N, w.dtype)
+    scan_path, chunk_len, n_chunks = ssm.ssm_scan_plan(w.b, w.L, w.E, w.N, w.dtype)
 
     def step():
         ssm.ssm_scan_fwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
@@ -732,7 +733,8 @@ def main():
         "config": {"workload": "long-sequence selective scan b1 L65536 E5120 N16, bf16 I/O, fp32 state, "
                                "softplus step, silu gate, D skip",
                    "b": w.b, "L": w.L, "E": w.E, "N": w.N, "io_dtype": w.dtype,
-                   "chunk_len": chunk_len, "n_chunks": n_chunks, "parallelism": "single GPU"},
+                   "scan_form": scan_path, "chunk_len": chunk_len, "n_chunks": n_chunks,
+                   "parallelism": "single GPU"},
         "hbm_GBps": path_gbps,
         "hbm_frac": path_gbps / HBM_PEAK_GBPS,
         "algorithmic_bytes_per_step": algo,

@@ -11,6 +11,7 @@
  *   ssm_scan_fwd_save, ssm_scan_bwd_saved
  *                                     the training form: the forward keeps the state
  *                                     every SSM_SAVE_INTERVAL steps for the backward
+ *   ssm_scan_fwd_tuned                the forward with its form and split chosen by the caller
  *   ssm_ssd_fwd                       the scan with a scalar transition per head
  *   ssm_conv_fwd, ssm_conv_update     the causal depthwise convolution + SiLU before
  *                                     the scan, and its token step
@@ -32,9 +33,11 @@
  * Streams.  `stream` is a hipStream_t passed as void* (NULL = the default
  * stream).  Work is enqueued on it and the call returns without waiting;
  * errors raised while the kernels run surface at the caller's next
- * synchronisation.  The scans (forward, backward, per head) take a temporary
- * workspace from the stream-ordered allocator (hipMallocAsync / hipFreeAsync
- * on `stream`), so concurrent calls on different streams do not share memory.
+ * synchronisation.  A forward scan in the single-pass form, or in one chunk,
+ * takes no workspace.  A forward scan cut into chunks (chunked form), the
+ * backward and the per-head scan take a temporary workspace from the
+ * stream-ordered allocator (hipMallocAsync / hipFreeAsync on `stream`), so
+ * concurrent calls on different streams do not share memory.
  * ssm_state_update and ssm_conv_update take none and issue no memset: a
  * caller can capture them in a HIP graph.
  *
@@ -86,7 +89,8 @@ typedef enum {
   SSM_ERR_DTYPE = -3,         /* dtype is not an ssm_dtype value */
   SSM_ERR_UNSUPPORTED_N = -4, /* N outside the supported range (1..16; ssm_ssd_fwd: 16..128 in steps of 16) */
   SSM_ERR_ALIGN = -5,         /* an array is not aligned to its element size */
-  SSM_ERR_HIP = -6            /* HIP launch / allocation failure */
+  SSM_ERR_HIP = -6,           /* HIP launch / allocation failure */
+  SSM_ERR_PLAN = -7           /* an ssm_scan_tuning value is invalid or does not apply to the call */
 } ssm_status;
 
 /*
@@ -167,6 +171,58 @@ SSM_API int ssm_scan_fwd_save(const void* u, const void* delta, const float* A, 
                               const float* D, const void* z, const float* delta_bias, int softplus,
                               const float* initial_state, void* y, float* last_state, float* saved_states,
                               int64_t b, int64_t L, int64_t E, int64_t N, int dtype, void* stream);
+
+/*
+ * Forms of the forward scan (ssm_scan_tuning.path, ssm_scan_plan).
+ *   SSM_PATH_CHUNKED      the sequence is cut into chunks when batch x channels
+ *                         alone cannot fill the GPU: a pass computes each
+ *                         chunk's map from zero, a chain composes the maps
+ *                         ([KK] "the scan"), a main pass rescans every chunk
+ *                         from its incoming state; one chunk is a single pass.
+ *   SSM_PATH_SINGLE_PASS  a workgroup walks the whole sequence for a slice of
+ *                         channels; chunks of 8 steps are run from zero, their
+ *                         maps chained through LDS and replayed from registers,
+ *                         so every input is read once and every retention
+ *                         exponential is evaluated once.
+ * SSM_PATH_AUTO takes the single pass where the sequence has to be cut and the
+ * chain of chunk maps per workgroup block stays short, else the chunked form.
+ */
+typedef enum {
+  SSM_PATH_AUTO = 0,
+  SSM_PATH_CHUNKED = 1,
+  SSM_PATH_SINGLE_PASS = 2
+} ssm_scan_path;
+
+/*
+ * Plan choices of a forward scan.  Zero fields leave the choice to the sizes.
+ *   path          an ssm_scan_path value
+ *   min_chunk     chunked form: shortest chunk, in steps (> 0 to set it)
+ *   target_waves  chunked form: the waves the cut aims for; the sequence is cut
+ *                 while b * ceil(E / 64) * 2 is below it (> 0 to set it)
+ * The choices change the order of the floating-point operations, not the
+ * definition computed.
+ */
+typedef struct {
+  int32_t path;
+  int32_t min_chunk;
+  int32_t target_waves;
+} ssm_scan_tuning;
+
+/*
+ * ssm_scan_fwd_save with explicit plan choices.  tuning may be NULL (every
+ * choice from the sizes, as ssm_scan_fwd_save); saved_states may be NULL (not
+ * saved, as ssm_scan_fwd_from); initial_state may be NULL (zero).
+ * Errors: SSM_ERR_PLAN when a tuning field is out of range or path is
+ * SSM_PATH_SINGLE_PASS and the single pass does not apply (its tiles need the
+ * rows of u, delta, z, y, B and C to be whole 8-byte units and 8-byte aligned
+ * tensors, and enough channels per compute unit); otherwise as
+ * ssm_scan_fwd_save.
+ */
+SSM_API int ssm_scan_fwd_tuned(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                               const float* D, const void* z, const float* delta_bias, int softplus,
+                               const float* initial_state, void* y, float* last_state, float* saved_states,
+                               const ssm_scan_tuning* tuning, int64_t b, int64_t L, int64_t E, int64_t N, int dtype,
+                               void* stream);
 
 /*
  * One recurrent step for every (b, e) -- the SSM half of the decode step of
@@ -306,27 +362,29 @@ SSM_API int ssm_conv_update(void* conv_state, const void* v, const float* q, con
                             int64_t b, int64_t E, int64_t K, int dtype, void* stream);
 
 /*
- * How ssm_scan_fwd will split a scan of this size along the sequence: it
- * writes the chunk length (steps) and the number of chunks.  One chunk means
- * a single pass; more chunks mean a chunk-aggregate pass, a carry pass over
- * the chunk boundaries and a main pass (the affine composition of
- * [KK] "the scan").  The split depends only on (b, L, E, dtype) and on the
- * tuning variables SSM_SCAN_TARGET_WAVES / SSM_SCAN_MIN_CHUNK if set.
- * Host-only: enqueues nothing.  Same argument checks as ssm_scan_fwd.
+ * How a forward scan of this size runs (tuning NULL: as ssm_scan_fwd): *path
+ * receives SSM_PATH_CHUNKED or SSM_PATH_SINGLE_PASS, *chunk_len and *n_chunks
+ * the chunks (single pass: chunks of 8 steps; chunked form: one chunk means a
+ * single pass over each channel, more chunks the aggregate, carry and main
+ * passes).  The plan assumes 256-byte aligned tensors (as allocators return
+ * them) and the current device's CU count (256, MI355X, when no device is
+ * visible).  Host-only: enqueues nothing.  Same argument checks as
+ * ssm_scan_fwd_tuned.
  */
-SSM_API int ssm_scan_plan(int64_t b, int64_t L, int64_t E, int64_t N, int dtype,
-                          int64_t* chunk_len, int64_t* n_chunks);
+SSM_API int ssm_scan_plan(int64_t b, int64_t L, int64_t E, int64_t N, int dtype, const ssm_scan_tuning* tuning,
+                          int* path, int64_t* chunk_len, int64_t* n_chunks);
 
 /*
  * Kernel timing for benchmarks.  While enabled (on != 0), every kernel the
  * library enqueues is bracketed by two HIP events recorded on the caller's
  * stream.  ssm_profile_read() waits for those events, writes per-kind totals
  * (milliseconds) and launch counts for kinds 0 .. n_kinds-1 and clears the
- * record.  Kinds: 0 widen_rows (bf16 B/C rows to f32), 1 chunk_aggregate,
- * 2 chunk_carry, 3 scan_main, 4 fill_state, 5 state_update, 6 conv,
- * 7 conv_update, 8 bwd_rows, 9 bwd_aggregate, 10 bwd_carry, 11 bwd_main,
- * 12 bwd_reduce, 13 ssd_state, 14 ssd_carry, 15 ssd_scan; names from
- * ssm_profile_kind_name().  Off by default; the events add a few
+ * record.  Kinds: 0 chunk_aggregate, 1 chunk_carry, 2 scan_main,
+ * 3 fill_state, 4 state_update, 5 conv, 6 conv_update, 7 bwd_rows,
+ * 8 bwd_aggregate, 9 bwd_carry, 10 bwd_main, 11 bwd_reduce, 12 ssd_state,
+ * 13 ssd_carry, 14 ssd_scan, 15 scan_fused (the single-pass forward),
+ * 16 widen_rows (float copies of the bf16 B / C rows of a cut forward); names
+ * from ssm_profile_kind_name().  Off by default; the events add a few
  * microseconds per launch.  Process-wide, thread-safe.
  */
 SSM_API int ssm_profile_enable(int on);

@@ -10,8 +10,13 @@ library is missing or the tensors are not on a GPU, the call raises.
 Functions (same names as the C entry points):
 
 * ``ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
-  softplus=False, y=None, last_state=None, return_last_state=True)``
-  -> ``(y, last_state)``
+  softplus=False, y=None, last_state=None, return_last_state=True,
+  initial_state=None, saved_states=None, tuning=None)`` -> ``(y, last_state)``;
+  ``tuning`` (a dict with keys ``path`` in "auto" / "chunked" /
+  "single_pass", ``min_chunk``, ``target_waves``) selects the C entry point
+  ``ssm_scan_fwd_tuned``
+* ``ssm_scan_plan(b, L, E, N, dtype="bf16", tuning=None)`` ->
+  ``(path, chunk_len, n_chunks)``: how the forward runs at that size
 * ``ssm_state_update(state, x, delta, A, B, C, D=None, z=None,
   delta_bias=None, softplus=False, y=None)`` -> ``y`` (``state`` is updated
   in place)
@@ -41,7 +46,7 @@ import os
 
 __all__ = [
     "ssm_scan_fwd", "ssm_scan_fwd_from", "ssm_scan_bwd", "ssm_ssd_fwd", "ssm_state_update", "ssm_conv_fwd", "ssm_conv_update", "ssm_scan_plan", "ssm_profile_enable", "ssm_profile_read",
-    "ssm_status_string", "library_path", "SSMError",
+    "ssm_status_string", "library_path", "SSMError", "ScanTuning", "SCAN_PATHS",
     "SSM_F32", "SSM_BF16", "load_library",
 ]
 
@@ -55,6 +60,28 @@ SSM_BF16 = 1
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
 _int = ctypes.c_int
+
+
+# ssm_scan_path values
+SCAN_PATHS = {"auto": 0, "chunked": 1, "single_pass": 2}
+_PATH_NAMES = {v: k for k, v in SCAN_PATHS.items()}
+
+
+class ScanTuning(ctypes.Structure):
+    """``ssm_scan_tuning``: path (ssm_scan_path), min_chunk, target_waves; zero fields mean the library's choice."""
+    _fields_ = [("path", ctypes.c_int32), ("min_chunk", ctypes.c_int32), ("target_waves", ctypes.c_int32)]
+
+
+def _tuning(tuning):
+    """A ScanTuning from None, a ScanTuning or a dict {path, min_chunk, target_waves}."""
+    if tuning is None or isinstance(tuning, ScanTuning):
+        return tuning
+    unknown = set(tuning) - {"path", "min_chunk", "target_waves"}
+    if unknown:
+        raise ValueError(f"unknown tuning keys {sorted(unknown)}")
+    path = tuning.get("path", "auto")
+    return ScanTuning(SCAN_PATHS[path] if isinstance(path, str) else int(path), int(tuning.get("min_chunk", 0)),
+                      int(tuning.get("target_waves", 0)))
 
 
 class SSMError(RuntimeError):
@@ -88,6 +115,9 @@ def load_library():
     lib.ssm_scan_fwd_from.argtypes = [_vp] * 8 + [_int, _vp, _vp, _vp] + [_i64] * 4 + [_int, _vp]
     lib.ssm_scan_fwd_save.restype = _int
     lib.ssm_scan_fwd_save.argtypes = [_vp] * 8 + [_int, _vp, _vp, _vp, _vp] + [_i64] * 4 + [_int, _vp]
+    lib.ssm_scan_fwd_tuned.restype = _int
+    lib.ssm_scan_fwd_tuned.argtypes = ([_vp] * 8 + [_int, _vp, _vp, _vp, _vp, ctypes.POINTER(ScanTuning)] +
+                                       [_i64] * 4 + [_int, _vp])
     lib.ssm_state_update.restype = _int
     lib.ssm_state_update.argtypes = [_vp] * 9 + [_int, _vp] + [_i64] * 3 + [_int, _vp]
     lib.ssm_scan_bwd.restype = _int
@@ -113,7 +143,8 @@ def load_library():
     lib.ssm_profile_kind_name.restype = ctypes.c_char_p
     lib.ssm_profile_kind_name.argtypes = [_int]
     lib.ssm_scan_plan.restype = _int
-    lib.ssm_scan_plan.argtypes = [_i64, _i64, _i64, _i64, _int, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]
+    lib.ssm_scan_plan.argtypes = [_i64, _i64, _i64, _i64, _int, ctypes.POINTER(ScanTuning), ctypes.POINTER(_int),
+                                  ctypes.POINTER(_i64), ctypes.POINTER(_i64)]
     _lib = lib
     return lib
 
@@ -122,14 +153,19 @@ def ssm_status_string(status: int) -> str:
     return load_library().ssm_status_string(int(status)).decode()
 
 
-def ssm_scan_plan(b, L, E, N, dtype="bf16"):
-    """(chunk_len, n_chunks) that ssm_scan_fwd uses for this size (host-only query)."""
+def ssm_scan_plan(b, L, E, N, dtype="bf16", tuning=None):
+    """(path, chunk_len, n_chunks) of a forward scan of this size (host-only query).
+
+    path is "chunked" or "single_pass"; see ssm_scan_plan in include/ssm.h.
+    """
     code = {"f32": SSM_F32, "bf16": SSM_BF16}.get(dtype, dtype)
-    cl, nc = _i64(0), _i64(0)
-    status = load_library().ssm_scan_plan(int(b), int(L), int(E), int(N), int(code), ctypes.byref(cl),
-                                          ctypes.byref(nc))
+    t = _tuning(tuning)
+    path, cl, nc = _int(0), _i64(0), _i64(0)
+    status = load_library().ssm_scan_plan(int(b), int(L), int(E), int(N), int(code),
+                                          ctypes.byref(t) if t is not None else None, ctypes.byref(path),
+                                          ctypes.byref(cl), ctypes.byref(nc))
     _raise_on("ssm_scan_plan", status)
-    return cl.value, nc.value
+    return _PATH_NAMES[path.value], cl.value, nc.value
 
 
 PROFILE_KINDS = 17
@@ -216,13 +252,14 @@ def saved_states_shape(b, L, E, N):
 
 
 def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=False, y=None,
-                 last_state=None, return_last_state=True, initial_state=None, saved_states=None):
+                 last_state=None, return_last_state=True, initial_state=None, saved_states=None, tuning=None):
     """Selective scan forward on the GPU.  Returns ``(y, last_state)`` (last_state None if not requested).
 
     ``initial_state`` [b, E, N] float32 continues the recurrence from that state
     (the C entry point ``ssm_scan_fwd_from``); None starts from zero.  A given
     ``saved_states`` buffer (``saved_states_shape``, float32) receives the state
-    every 64 steps (the C entry point ``ssm_scan_fwd_save``).
+    every 64 steps (the C entry point ``ssm_scan_fwd_save``).  ``tuning`` (dict
+    or ScanTuning) fixes the form and split (the C entry point ``ssm_scan_fwd_tuned``).
     """
     import torch
 
@@ -259,6 +296,16 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=Fa
         raise ValueError("initial_state must not be the last_state buffer")
     if saved_states is not None:
         _check(torch, "saved_states", saved_states, saved_states_shape(b, L, E, N), torch.float32, device)
+    t = _tuning(tuning)
+    if t is not None:
+        with _on(torch, device):
+            status = lib.ssm_scan_fwd_tuned(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                            _ptr(delta_bias), int(bool(softplus)), _ptr(initial_state), _ptr(y),
+                                            _ptr(last_state), _ptr(saved_states), ctypes.byref(t), b, L, E, N, code,
+                                            _stream_of(torch, device))
+        _raise_on("ssm_scan_fwd_tuned", status)
+        return y, last_state
+    if saved_states is not None:
         with _on(torch, device):
             status = lib.ssm_scan_fwd_save(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                                            _ptr(delta_bias), int(bool(softplus)), _ptr(initial_state), _ptr(y),
@@ -287,7 +334,7 @@ def ssm_scan_fwd_from(u, delta, A, B, C, D=None, z=None, delta_bias=None, softpl
 
 
 def ssm_scan_fwd_save(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=False, initial_state=None,
-                      y=None, last_state=None, saved_states=None):
+                      y=None, last_state=None, saved_states=None, tuning=None):
     """``ssm_scan_fwd_from`` that also keeps the state every 64 steps for ``ssm_scan_bwd_saved``.
 
     Returns ``(y, last_state, saved_states)``; saved_states [b, ceil(L / 64) - 1, E, N] float32 holds
@@ -300,7 +347,7 @@ def ssm_scan_fwd_save(u, delta, A, B, C, D=None, z=None, delta_bias=None, softpl
     if saved_states is None:
         saved_states = torch.empty(saved_states_shape(b, L, E, N), dtype=torch.float32, device=u.device)
     y, last_state = ssm_scan_fwd(u, delta, A, B, C, D, z, delta_bias, softplus, y=y, last_state=last_state,
-                                 initial_state=initial_state, saved_states=saved_states)
+                                 initial_state=initial_state, saved_states=saved_states, tuning=tuning)
     return y, last_state, saved_states
 
 

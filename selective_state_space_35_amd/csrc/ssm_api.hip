@@ -47,8 +47,8 @@ int64_t saved_count(int64_t b, int64_t L, int64_t E, int64_t N) {
 
 int scan_fwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C, const float* D,
                   const void* z, const float* delta_bias, int softplus, const float* initial_state, void* y,
-                  float* last_state, float* saved, int64_t b, int64_t L, int64_t E, int64_t N, int dtype,
-                  void* stream);
+                  float* last_state, float* saved, const ssm_scan_tuning* tuning, int64_t b, int64_t L, int64_t E,
+                  int64_t N, int dtype, void* stream);
 int scan_bwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C, const float* D,
                   const void* z, const float* delta_bias, int softplus, const float* initial_state,
                   const float* saved, const void* dy, const float* d_last_state, void* du, void* ddelta, float* dA,
@@ -70,8 +70,8 @@ int ssm_scan_fwd_from(const void* u, const void* delta, const float* A, const vo
                       const float* D, const void* z, const float* delta_bias, int softplus,
                       const float* initial_state, void* y, float* last_state, int64_t b, int64_t L, int64_t E,
                       int64_t N, int dtype, void* stream) {
-  return scan_fwd_impl(u, delta, A, B, C, D, z, delta_bias, softplus, initial_state, y, last_state, nullptr, b, L, E, N,
-                       dtype, stream);
+  return scan_fwd_impl(u, delta, A, B, C, D, z, delta_bias, softplus, initial_state, y, last_state, nullptr, nullptr, b,
+                       L, E, N, dtype, stream);
 }
 
 int ssm_scan_fwd_save(const void* u, const void* delta, const float* A, const void* B, const void* C,
@@ -82,19 +82,47 @@ int ssm_scan_fwd_save(const void* u, const void* delta, const float* A, const vo
   if (st != SSM_OK) return st;
   if (saved_count(b, L, E, N) > 0 && !saved_states) return SSM_ERR_NULL;
   if (saved_states && !aligned(saved_states, 4)) return SSM_ERR_ALIGN;
-  return scan_fwd_impl(u, delta, A, B, C, D, z, delta_bias, softplus, initial_state, y, last_state, saved_states, b, L,
-                       E, N, dtype, stream);
+  return scan_fwd_impl(u, delta, A, B, C, D, z, delta_bias, softplus, initial_state, y, last_state, saved_states,
+                       nullptr, b, L, E, N, dtype, stream);
+}
+
+int ssm_scan_fwd_tuned(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                       const float* D, const void* z, const float* delta_bias, int softplus,
+                       const float* initial_state, void* y, float* last_state, float* saved_states,
+                       const ssm_scan_tuning* tuning, int64_t b, int64_t L, int64_t E, int64_t N, int dtype,
+                       void* stream) {
+  int st = check_sizes(b, L, E, N, dtype);
+  if (st != SSM_OK) return st;
+  if (saved_states && !aligned(saved_states, 4)) return SSM_ERR_ALIGN;
+  return scan_fwd_impl(u, delta, A, B, C, D, z, delta_bias, softplus, initial_state, y, last_state, saved_states,
+                       tuning, b, L, E, N, dtype, stream);
 }
 
 }  // extern "C"
 
 namespace {
 
+// The library's form of ssm_scan_tuning (NULL: every choice from the sizes).
+int to_tuning(const ssm_scan_tuning* t, ssm::ScanTuning* out) {
+  *out = ssm::ScanTuning{};
+  if (!t) return SSM_OK;
+  if (t->path != SSM_PATH_AUTO && t->path != SSM_PATH_CHUNKED && t->path != SSM_PATH_SINGLE_PASS) return SSM_ERR_PLAN;
+  if (t->min_chunk < 0 || t->target_waves < 0) return SSM_ERR_PLAN;
+  out->path = t->path == SSM_PATH_CHUNKED ? ssm::kPathChunked
+              : t->path == SSM_PATH_SINGLE_PASS ? ssm::kPathSinglePass : ssm::kPathAuto;
+  out->min_chunk = t->min_chunk;
+  out->target_waves = t->target_waves;
+  return SSM_OK;
+}
+
 int scan_fwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C, const float* D,
                   const void* z, const float* delta_bias, int softplus, const float* initial_state, void* y,
-                  float* last_state, float* saved, int64_t b, int64_t L, int64_t E, int64_t N, int dtype,
-                  void* stream) {
+                  float* last_state, float* saved, const ssm_scan_tuning* tuning, int64_t b, int64_t L, int64_t E,
+                  int64_t N, int dtype, void* stream) {
   int st = check_sizes(b, L, E, N, dtype);
+  if (st != SSM_OK) return st;
+  ssm::ScanTuning tune;
+  st = to_tuning(tuning, &tune);
   if (st != SSM_OK) return st;
   if (b == 0 || E == 0) return SSM_OK;
   if (L > 0 && (!u || !delta || !A || !B || !C || !y)) return SSM_ERR_NULL;
@@ -105,8 +133,8 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A, const void* 
   const void* fl[] = {A, D, delta_bias, last_state, initial_state};
   for (const void* p : fl)
     if (p && !aligned(p, 4)) return SSM_ERR_ALIGN;
-  // with L > 0 the chunk count is bounded by L / 64 and the grid by b * E / 64 * chunks
-  const ssm::ScanPlan pl = ssm::plan_scan(b, L, E, int(es));
+  // the grid of the chunked form is b * ceil(E / 64) * chunks workgroups
+  const ssm::ScanPlan pl = ssm::plan_scan(b, L, E, int(es), tune);
   int64_t grid = 0;
   if (pl.chunk_len <= 0 || !mul_ok(b * pl.e_blocks, pl.n_chunks, &grid) || grid > INT32_MAX) return SSM_ERR_DIM;
 
@@ -116,6 +144,14 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A, const void* 
   a.saved = saved_count(b, L, E, N) > 0 ? saved : nullptr;
   a.b = b; a.L = L; a.E = E; a.N = N; a.dtype = dtype;
   a.stream = static_cast<hipStream_t>(stream);
+  a.tune = tune;
+  if (tune.path == ssm::kPathSinglePass && L > 0) {  // asked for explicitly: it has to apply
+    int n_cu = 0;
+    hipError_t err = ssm::device_cu_count(&n_cu);
+    if (err != hipSuccess) return hip_status(err);
+    ssm::FusedPlan fp;
+    if (ssm::choose_path(a, pl, n_cu, &fp) != ssm::kPathSinglePass) return SSM_ERR_PLAN;
+  }
   return hip_status(ssm::launch_scan(a));
 }
 
@@ -249,14 +285,38 @@ int ssm_ssd_fwd(const void* x, const void* delta, const float* A, const void* B,
   return hip_status(ssm::launch_ssd(a));
 }
 
-int ssm_scan_plan(int64_t b, int64_t L, int64_t E, int64_t N, int dtype, int64_t* chunk_len, int64_t* n_chunks) {
+int ssm_scan_plan(int64_t b, int64_t L, int64_t E, int64_t N, int dtype, const ssm_scan_tuning* tuning, int* path,
+                  int64_t* chunk_len, int64_t* n_chunks) {
   int st = check_sizes(b, L, E, N, dtype);
   if (st != SSM_OK) return st;
-  if (!chunk_len || !n_chunks) return SSM_ERR_NULL;
-  const ssm::ScanPlan pl = ssm::plan_scan(b, L, E, dtype == SSM_F32 ? 4 : 2);
+  if (!path || !chunk_len || !n_chunks) return SSM_ERR_NULL;
+  ssm::ScanTuning tune;
+  st = to_tuning(tuning, &tune);
+  if (st != SSM_OK) return st;
+  const ssm::ScanPlan pl = ssm::plan_scan(b, L, E, dtype == SSM_F32 ? 4 : 2, tune);
   if (pl.chunk_len <= 0) return SSM_ERR_DIM;
-  *chunk_len = pl.chunk_len;
-  *n_chunks = pl.n_chunks;
+  // the single-pass plan depends on the device's CU count (256 on MI355X, taken when no device is visible)
+  int n_cu = 0;
+  if (ssm::device_cu_count(&n_cu) != hipSuccess || n_cu <= 0) {
+    (void)hipGetLastError();
+    n_cu = 256;
+  }
+  ssm::ScanArgs a{};
+  a.b = b; a.L = L; a.E = E; a.N = N; a.dtype = dtype; a.tune = tune;
+  // the single pass reads 8-byte units: it is planned for 256-byte aligned tensors, as an allocator returns them
+  a.u = a.delta = a.B = a.C = a.y = reinterpret_cast<void*>(uintptr_t(256));
+  ssm::FusedPlan fp;
+  const int form = L > 0 ? ssm::choose_path(a, pl, n_cu, &fp) : ssm::kPathChunked;
+  if (form < 0) return SSM_ERR_PLAN;
+  if (form == ssm::kPathSinglePass) {
+    *path = SSM_PATH_SINGLE_PASS;
+    *chunk_len = 8;
+    *n_chunks = (L + 7) / 8;
+  } else {
+    *path = SSM_PATH_CHUNKED;
+    *chunk_len = pl.chunk_len;
+    *n_chunks = pl.n_chunks;
+  }
   return SSM_OK;
 }
 
@@ -312,7 +372,9 @@ const char* ssm_status_string(int status) {
     case SSM_ERR_NULL: return "a required pointer is NULL";
     case SSM_ERR_DIM: return "invalid or overflowing size";
     case SSM_ERR_DTYPE: return "unknown dtype";
-    case SSM_ERR_UNSUPPORTED_N: return "state size N must be in 1..16";
+    case SSM_ERR_UNSUPPORTED_N:
+      return "state size N outside the entry point's range (1..16; ssm_ssd_fwd: 16..128 in steps of 16)";
+    case SSM_ERR_PLAN: return "the requested scan form or tuning does not apply to this call";
     case SSM_ERR_ALIGN: return "array not aligned to its element size";
     case SSM_ERR_HIP: return "HIP launch or allocation failed";
     default: return "unknown status";

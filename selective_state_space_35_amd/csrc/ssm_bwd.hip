@@ -603,10 +603,9 @@ hipError_t launch_scan_bwd(const BwdArgs& a) {
   const bool saved = a.saved != nullptr;
   const int fslots = saved ? int(N) : chunk_state_slots(N);
   const int fchunks = saved ? n_chunks - 1 : n_chunks;  // chunk slots per batch row
-  // workspace (floats): [widened rows | B16 | C16 | forward carries | forward sums | reverse carries |
+  // workspace (floats): [B16 | C16 | forward carries | forward sums | reverse carries |
   //                      reverse sums | dB/dC partials | dA partials | dD/dbias partials]
   const size_t nb = size_t(b), nL = size_t(L), nE = size_t(E), nc = size_t(n_chunks);
-  const size_t n_rows = a.dtype == 0 || saved ? 0 : 2 * nb * nL * size_t(N);
   const size_t n_row16 = nb * nL * kS;
   const size_t n_fc = n_chunks > 1 && !saved ? nb * nc * nE * size_t(fslots) : 0;
   const size_t n_fs = n_chunks > 1 && !saved ? nb * nc * nE : 0;
@@ -616,9 +615,9 @@ hipError_t launch_scan_bwd(const BwdArgs& a) {
   const size_t n_da = nb * nc * nE * kS;
   const size_t n_dd = nb * nc * nE * 2;
   // every segment starts on a 256-byte boundary (the main kernel reads rows as float4)
-  const size_t sizes[10] = {n_rows, n_row16, n_row16, n_fc, n_fs, n_xa, n_xs, n_bc, n_da, n_dd};
-  size_t offs[10], total = 0;
-  for (int i = 0; i < 10; i++) {
+  const size_t sizes[9] = {n_row16, n_row16, n_fc, n_fs, n_xa, n_xs, n_bc, n_da, n_dd};
+  size_t offs[9], total = 0;
+  for (int i = 0; i < 9; i++) {
     offs[i] = total;
     total += (sizes[i] + 63) / 64 * 64;
   }
@@ -626,16 +625,15 @@ hipError_t launch_scan_bwd(const BwdArgs& a) {
   hipError_t err = hipMallocAsync(&ws, total * sizeof(float), a.stream);
   if (err != hipSuccess) return err;
   float* f = static_cast<float*>(ws);
-  float* rows = f + offs[0];
-  float* B16 = f + offs[1];
-  float* C16 = f + offs[2];
-  const float* fcarry = saved ? a.saved : f + offs[3];
-  float* fsum = f + offs[4];
-  float* xagg = f + offs[5];
-  float* xsum = f + offs[6];
-  float* dbc = f + offs[7];
-  float* dA_part = f + offs[8];
-  float* dDb_part = f + offs[9];
+  float* B16 = f + offs[0];
+  float* C16 = f + offs[1];
+  const float* fcarry = saved ? a.saved : f + offs[2];
+  float* fsum = f + offs[3];
+  float* xagg = f + offs[4];
+  float* xsum = f + offs[5];
+  float* dbc = f + offs[6];
+  float* dA_part = f + offs[7];
+  float* dDb_part = f + offs[8];
 
   const int64_t nr16 = b * L * kS;
   err = a.dtype == 0 ? launch_kind(kKindBwdRows, bwd_rows_kernel<float>, (nr16 + 255) / 256, 256, a.stream,
@@ -653,7 +651,7 @@ hipError_t launch_scan_bwd(const BwdArgs& a) {
     pl.chunk_len = kBwdChunk;
     pl.n_chunks = n_chunks;
     pl.e_blocks = int((E + kWave - 1) / kWave);
-    err = launch_chunk_states(s, pl, rows, f + offs[3], fsum);
+    err = launch_chunk_states(s, pl, f + offs[2], fsum);
   }
   if (err == hipSuccess)
     err = a.dtype == 0 ? bwd_typed<float>(a, n_chunks, B16, C16, fcarry, fslots, fchunks, xagg, xsum, dA_part,

@@ -27,7 +27,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <cstdlib>
 #include <type_traits>
 
 #include "ssm_device.h"
@@ -130,13 +129,8 @@ __global__ __launch_bounds__(64 * G > 256 ? 64 * G : 256) void chain_kernel(Chai
 // Stretches per chain: 1 with at least 65536 positions (1024 waves: enough
 // loads in flight to stream the aggregates at full bandwidth), else doubled
 // up to 8 while the threads stay below that count and every stretch keeps at
-// least 32 chunks.  The environment variable SSM_CHAIN_STRETCHES (1, 2, 4 or
-// 8) overrides it.
+// least 32 chunks.
 inline int chain_stretches(int64_t positions, int K) {
-  if (const char* e = std::getenv("SSM_CHAIN_STRETCHES")) {
-    const long v = std::strtol(e, nullptr, 10);
-    if (v == 1 || v == 2 || v == 4 || v == 8) return int(v);
-  }
   constexpr int64_t kEnough = int64_t(1) << 16;
   int G = 1;
   while (G < 8 && positions * G < kEnough && K / (2 * G) >= 32) G *= 2;

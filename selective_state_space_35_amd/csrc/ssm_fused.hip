@@ -425,7 +425,7 @@ hipError_t fused_typed(const ScanArgs& a, const FusedPlan& p) {
 
 }  // namespace
 
-bool plan_fused(const ScanArgs& a, int n_cu, FusedPlan* out) {
+bool plan_fused(const ScanArgs& a, int n_cu, int max_w, FusedPlan* out) {
   FusedPlan p{};
   const int64_t b = a.b, L = a.L, E = a.E, N = a.N;
   const int es = a.dtype == 0 ? 4 : 2;
@@ -451,10 +451,20 @@ bool plan_fused(const ScanArgs& a, int n_cu, FusedPlan* out) {
   if (b * p.groups_row > INT32_MAX) return false;
   p.n_wg = int(b * p.groups_row);
   const int lpg = p.lpc * p.cg;
+  // one producer pass moves plane units: xR rows of the group's channels, bR rows of B / C
+  const int plane = 64 * kProd;
+  const int xdu = p.cg * es / 8, bdu = int(N) * es / 8;
+  p.xR = plane / xdu;
+  p.bR = plane / bdu;
+  if (p.xR < 1 || p.bR < 1) return false;
+  // chunks per block: as many as the compute waves hold, within the producers' registers
+  // (6 passes of [u | delta | z], 3 of B / C per block) and the sequence
   int64_t W = (64 * (kFusedMaxWaves - kProd)) / lpg;
-  W = std::min<int64_t>(W, 16);  // the chunk-0 lanes chain W maps per block
+  W = std::min<int64_t>(W, kFusedMaxChunks);
+  W = std::min<int64_t>(W, 6 * p.xR / kT);
+  W = std::min<int64_t>(W, 3 * p.bR / kT);
   W = std::min<int64_t>(W, (L + kT - 1) / kT);
-  if (W < 1) return false;
+  if (W < 1 || W > max_w) return false;  // the chunk-0 lanes chain W maps per block
   p.W = int(W);
   p.BT = p.W * kT;
   p.lanes = p.W * lpg;
@@ -465,11 +475,6 @@ bool plan_fused(const ScanArgs& a, int n_cu, FusedPlan* out) {
   const int64_t nblk = (L + p.BT - 1) / p.BT;
   if (nblk > INT32_MAX) return false;
   p.nblk = int(nblk);
-  const int plane = 64 * kProd;
-  const int xdu = p.cg * es / 8, bdu = int(N) * es / 8;
-  p.xR = plane / xdu;
-  p.bR = plane / bdu;
-  if (p.xR < 1 || p.bR < 1) return false;
   p.xM = (p.BT + p.xR - 1) / p.xR;
   p.bM = (p.BT + p.bR - 1) / p.bR;
   if (p.xM > 6 || p.bM > 3) return false;  // the producers' registers

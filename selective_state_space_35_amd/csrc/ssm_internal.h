@@ -7,6 +7,18 @@
 
 namespace ssm {
 
+// Forms of the forward scan.
+constexpr int kPathAuto = 0;        // chosen from the sizes
+constexpr int kPathChunked = 1;     // one pass per chunk of the sequence (with aggregate + carry passes when cut)
+constexpr int kPathSinglePass = 2;  // the single-pass form (ssm_fused.hip)
+
+// Explicit plan choices of a forward scan; zero fields leave the choice to the sizes.
+struct ScanTuning {
+  int path = kPathAuto;
+  int min_chunk = 0;     // chunked form: shortest chunk (steps)
+  int target_waves = 0;  // chunked form: waves the cut aims for
+};
+
 struct ScanArgs {
   const void* u;
   const void* delta;
@@ -24,6 +36,7 @@ struct ScanArgs {
   int64_t b, L, E, N;
   int dtype;           // 0 = f32, 1 = bf16
   hipStream_t stream;
+  ScanTuning tune;
 };
 constexpr int64_t kSaveEvery = 64;  // interval of the saved states (the backward's chunk)
 
@@ -71,16 +84,15 @@ struct ScanPlan {
 
 // elem_bytes: size of the streamed element type (4 for f32, 2 for bf16).
 // chunk_len == 0 means the row size is too large to address (rejected).
-ScanPlan plan_scan(int64_t b, int64_t L, int64_t E, int elem_bytes);
+ScanPlan plan_scan(int64_t b, int64_t L, int64_t E, int elem_bytes, const ScanTuning& tune = ScanTuning{});
 
 // State slots per channel in the chunk-state buffers (N, or 16 when N is not 4, 8 or 16).
 int chunk_state_slots(int64_t N);
 // Incoming state of every chunk of the scan described by `a` cut as `pl` says:
 // afterwards carry[(b * n_chunks + c) * E + e][slots] holds the state at the end
-// of chunk c (c < n_chunks - 1) and csum the sum of steps of chunk c.  `rows`
-// (2 * b * L * N floats) is scratch for widened bf16 rows.  y / last_state are
-// not touched.
-hipError_t launch_chunk_states(const ScanArgs& a, const ScanPlan& pl, float* rows, float* carry, float* csum);
+// of chunk c (c < n_chunks - 1) and csum the sum of steps of chunk c.  y /
+// last_state are not touched.
+hipError_t launch_chunk_states(const ScanArgs& a, const ScanPlan& pl, float* carry, float* csum);
 
 // Backward of the scan (gradients of every input).
 struct BwdArgs {
@@ -157,14 +169,30 @@ struct FusedPlan {
   int o_x[3], o_bc[3], o_agg, o_hin, o_y[2], o_junk;  // LDS byte offsets (tiles triple / double buffered)
   int lds_bytes;
 };
-// Plans the single-pass scan for this call; false when it does not apply (too
-// few channels to fill the chip, rows that are not whole 4-byte words, or
-// tiles that do not fit in LDS).
-bool plan_fused(const ScanArgs& a, int n_cu, FusedPlan* p);
+// Most chunks per block the single-pass form takes (the chain of their maps is serial).
+constexpr int kFusedMaxChunks = 16;
+// Most chunks per block it takes when the form is chosen from the sizes: at 4
+// chunks (b8 L2048 E1536 bf16) it ran 18% faster than the chunked form, at 11
+// (b1 L65536 E5120 bf16, 20 channels per CU) 17% slower.
+constexpr int kFusedChainMax = 8;
+// Plans the single-pass scan for this call with at most max_w chunks per block;
+// false when it does not apply (too few channels to fill the chip, rows that
+// are not whole 8-byte units, or tiles that do not fit in LDS).
+bool plan_fused(const ScanArgs& a, int n_cu, int max_w, FusedPlan* p);
 hipError_t launch_fused(const ScanArgs& a, const FusedPlan& p);
 
-// Both return hipSuccess or the first HIP error met while enqueueing.
-hipError_t launch_scan(const ScanArgs& a);
+// The form a forward scan takes: kPathChunked or kPathSinglePass (then *fp is
+// its plan), or -1 when a.tune asks for the single pass and it does not apply.
+int choose_path(const ScanArgs& a, const ScanPlan& pl, int n_cu, FusedPlan* fp);
+// Compute units of the current device.
+hipError_t device_cu_count(int* n_cu);
+// Bytes of workspace the chunked form of this scan needs (0 for one chunk).
+size_t chunked_workspace_bytes(const ScanArgs& a, const ScanPlan& pl);
+
+// Both return hipSuccess or the first HIP error met while enqueueing.  A cut
+// chunked scan takes its workspace from `workspace` when given (at least
+// chunked_workspace_bytes), else from the stream-ordered pool.
+hipError_t launch_scan(const ScanArgs& a, void* workspace = nullptr, size_t workspace_bytes = 0);
 hipError_t launch_state_update(const UpdateArgs& a);
 
 }  // namespace ssm

@@ -41,7 +41,6 @@
 #include <stdint.h>
 
 #include <algorithm>
-#include <cstdlib>
 #include <type_traits>
 
 #include "ssm_chain.h"
@@ -52,18 +51,74 @@
 namespace ssm {
 namespace {
 
-// Row of NS coefficients of B or C at one (batch, step), always float32 (bf16
-// rows are widened once by widen_rows_kernel).  The row address is
-// wave-uniform, so these are scalar loads into SGPRs.  EXACT means N == NS;
-// otherwise entries n >= N read as zero, which keeps padded states at zero.
+// Row of NS coefficients of B or C at one (batch, step).  The row address is
+// wave-uniform, so a row is fetched with scalar loads into SGPRs one step
+// ahead (RowBuf) and unpacked to floats when the step uses it (unpack_row).
+// EXACT means N == NS; otherwise entries n >= N read as zero, which keeps
+// padded states at zero.
+//
+// A bf16 row is fetched as the 32-bit words that cover it and split on the
+// scalar ALU.  `odd` says that the row starts in the upper half of a word (odd
+// N, or a tensor that starts 2 bytes into a word); the caller tracks it from
+// the element index (a pointer turned into an integer here would keep the
+// loads off the scalar unit).  Every word read lies inside the aligned words
+// that hold the row's own values.
+template <typename T, int NS>
+struct RowBuf;
+template <int NS>
+struct RowBuf<float, NS> {
+  float v[NS];
+};
+template <int NS>
+struct RowBuf<bf16_bits, NS> {
+  uint32_t w[NS / 2 + 1];
+  int odd;
+};
+
 template <int NS, bool EXACT>
-__device__ __forceinline__ void load_row(const float* __restrict__ row, int N, float (&out)[NS]) {
+__device__ __forceinline__ void fetch_row(const float* __restrict__ row, int /*odd*/, int N, RowBuf<float, NS>& r) {
 #pragma unroll
-  for (int n = 0; n < NS; n++) out[n] = (EXACT || n < N) ? row[n] : 0.f;
+  for (int n = 0; n < NS; n++) r.v[n] = (EXACT || n < N) ? row[n] : 0.f;
 }
 
-// bf16 -> f32 copy of the B and C rows (b*L*N values each), so the per-step
-// scalar loads of the scan kernels need no unpacking on the scalar ALU.
+template <int NS, bool EXACT>
+__device__ __forceinline__ void fetch_row(const bf16_bits* __restrict__ row, int odd, int N,
+                                          RowBuf<bf16_bits, NS>& r) {
+  const uint32_t* __restrict__ w = reinterpret_cast<const uint32_t*>(row - odd);
+  r.odd = odd;
+#pragma unroll
+  for (int k = 0; k < NS / 2; k++) r.w[k] = (EXACT || 2 * k < N + odd) ? w[k] : 0u;  // word k holds a value
+  r.w[NS / 2] = (NS < N + odd) ? w[NS / 2] : 0u;
+}
+
+template <int NS, bool EXACT>
+__device__ __forceinline__ void unpack_row(const RowBuf<float, NS>& r, int /*N*/, float (&out)[NS]) {
+#pragma unroll
+  for (int n = 0; n < NS; n++) out[n] = r.v[n];
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+
+template <int NS, bool EXACT>
+__device__ __forceinline__ void unpack_row(const RowBuf<bf16_bits, NS>& r, int N, float (&out)[NS]) {
+  if (r.odd == 0) {  // value 2k is the low half of word k, value 2k + 1 its high half
+#pragma unroll
+    for (int k = 0; k < NS / 2; k++) {
+      out[2 * k] = (EXACT || 2 * k < N) ? bf16_lo(r.w[k]) : 0.f;
+      out[2 * k + 1] = (EXACT || 2 * k + 1 < N) ? bf16_hi(r.w[k]) : 0.f;
+    }
+  } else {  // value 2k is the high half of word k, value 2k + 1 the low half of word k + 1
+#pragma unroll
+    for (int k = 0; k < NS / 2; k++) {
+      out[2 * k] = (EXACT || 2 * k < N) ? bf16_hi(r.w[k]) : 0.f;
+      out[2 * k + 1] = (EXACT || 2 * k + 1 < N) ? bf16_lo(r.w[k + 1]) : 0.f;
+    }
+  }
+}
+
+// bf16 -> f32 copy of the B and C rows (b*L*N values each), for a scan cut
+// into chunks.
 __global__ __launch_bounds__(256) void widen_rows_kernel(const bf16_bits* __restrict__ B,
                                                          const bf16_bits* __restrict__ C, float* __restrict__ Bf,
                                                          float* __restrict__ Cf, int64_t n) {
@@ -120,12 +175,12 @@ __device__ __forceinline__ BlockPos block_pos(int n_chunks, int e_blocks, int64_
 // ---------------------------------------------------------------------------
 // 1. chunk aggregates: state reached from zero over the chunk, and sum of d
 // ---------------------------------------------------------------------------
-template <typename T, int NS, bool EXACT, bool SOFTPLUS>
+template <typename T, typename R, int NS, bool EXACT, bool SOFTPLUS>
 __global__ __launch_bounds__(kWave) SSM_SCAN_OCCUPANCY void scan_chunk_agg_kernel(
     const T* __restrict__ u, const T* __restrict__ delta, const float* __restrict__ A,
-    const float* __restrict__ B, const float* __restrict__ bias, float* __restrict__ carry,
+    const R* __restrict__ B, const float* __restrict__ bias, float* __restrict__ carry,
     float* __restrict__ chunk_sum, int64_t L, int64_t E, int N, int64_t chunk_len, int n_chunks,
-    int agg_chunks, int e_blocks) {
+    int agg_chunks, int e_blocks, int rows_odd) {
   // grid covers chunks 0 .. agg_chunks-1 (the last chunk's aggregate is never needed)
   const BlockPos p = block_pos(agg_chunks, e_blocks, E, L, chunk_len);
   float A2[NS];
@@ -141,9 +196,10 @@ __global__ __launch_bounds__(kWave) SSM_SCAN_OCCUPANCY void scan_chunk_agg_kerne
   const __amdgpu_buffer_rsrc_t rd = make_rsrc(delta + p.row0);
   const int voff = p.lane_ld * int(sizeof(T));
   const int row_bytes = int(E * int64_t(sizeof(T)));  // the plan keeps chunk_len * row_bytes < 2^31
-  const float* brow = B + (p.bi * L + p.t0) * int64_t(N);
-  float bn[NS];
-  load_row<NS, EXACT>(brow, N, bn);
+  const R* brow = B + (p.bi * L + p.t0) * int64_t(N);
+  int bodd = int(((p.bi * L + p.t0) * int64_t(N) + rows_odd) & 1);  // the row starts in a word's upper half
+  RowBuf<R, NS> bn;
+  fetch_row<NS, EXACT>(brow, bodd, N, bn);
 
   int ks = 0;  // step index inside the chunk
   const int n_steps = int(p.t1 - p.t0);
@@ -151,10 +207,12 @@ __global__ __launch_bounds__(kWave) SSM_SCAN_OCCUPANCY void scan_chunk_agg_kerne
     d += bv;
     if (SOFTPLUS) d = softplus(d);
     float bcur[NS];
-#pragma unroll
-    for (int n = 0; n < NS; n++) bcur[n] = bn[n];
-    if (++ks < n_steps) brow += N;     // the last step re-reads its own row: never past the end of B
-    load_row<NS, EXACT>(brow, N, bn);  // next step's row, fetched while this step computes
+    unpack_row<NS, EXACT>(bn, N, bcur);
+    if (++ks < n_steps) {  // the last step re-reads its own row: never past the end of B
+      brow += N;
+      bodd ^= N & 1;
+    }
+    fetch_row<NS, EXACT>(brow, bodd, N, bn);  // next step's row, fetched while this step computes
     const float dx = d * x;
 #pragma unroll
     for (int n = 0; n < NS; n++) h[n] = fmaf(exp2_fast(d * A2[n]), h[n], dx * bcur[n]);
@@ -201,13 +259,14 @@ __global__ __launch_bounds__(kWave) SSM_SCAN_OCCUPANCY void scan_chunk_agg_kerne
 // ---------------------------------------------------------------------------
 // FULL: every lane of every block is a real channel (E % 64 == 0), so the
 // per-step store needs no exec-mask branch.
-template <typename T, int NS, bool EXACT, bool SOFTPLUS, bool HAS_Z, bool FULL, bool SAVE>
+template <typename T, typename R, int NS, bool EXACT, bool SOFTPLUS, bool HAS_Z, bool FULL, bool SAVE>
 __global__ __launch_bounds__(kWave) SSM_SCAN_OCCUPANCY void scan_main_kernel(
     const T* __restrict__ u, const T* __restrict__ delta, const float* __restrict__ A,
-    const float* __restrict__ B, const float* __restrict__ C, const float* __restrict__ D,
+    const R* __restrict__ B, const R* __restrict__ C, const float* __restrict__ D,
     const T* __restrict__ z, const float* __restrict__ bias, T* __restrict__ y,
     float* __restrict__ last_state, const float* __restrict__ carry, const float* __restrict__ h0,
-    float* __restrict__ saved, int64_t L, int64_t E, int N, int64_t chunk_len, int n_chunks, int e_blocks) {
+    float* __restrict__ saved, int64_t L, int64_t E, int N, int64_t chunk_len, int n_chunks, int e_blocks,
+    int rows_odd) {
   const BlockPos p = block_pos(n_chunks, e_blocks, E, L, chunk_len);
   const int64_t n_saved = (L + kSaveEvery - 1) / kSaveEvery - 1;
   float A2[NS];
@@ -232,11 +291,13 @@ __global__ __launch_bounds__(kWave) SSM_SCAN_OCCUPANCY void scan_main_kernel(
   const __amdgpu_buffer_rsrc_t ry = make_rsrc(y + p.row0);
   const int voff = p.lane_ld * int(sizeof(T));
   const int row_bytes = int(E * int64_t(sizeof(T)));  // the plan keeps chunk_len * row_bytes < 2^31
-  const float* brow = B + (p.bi * L + p.t0) * int64_t(N);
-  const float* crow = C + (p.bi * L + p.t0) * int64_t(N);
-  float bn[NS], cn[NS];
-  load_row<NS, EXACT>(brow, N, bn);
-  load_row<NS, EXACT>(crow, N, cn);
+  const R* brow = B + (p.bi * L + p.t0) * int64_t(N);
+  const R* crow = C + (p.bi * L + p.t0) * int64_t(N);
+  const int rodd = int(((p.bi * L + p.t0) * int64_t(N)) & 1);  // rows starting in a word's upper half
+  int bodd = rodd ^ (rows_odd & 1), codd = rodd ^ (rows_odd >> 1);
+  RowBuf<R, NS> bn, cn;
+  fetch_row<NS, EXACT>(brow, bodd, N, bn);
+  fetch_row<NS, EXACT>(crow, codd, N, cn);
   int soff = 0;  // byte offset of the current step's row inside the chunk
   int ks = 0;    // step index inside the chunk
   const int n_steps = int(p.t1 - p.t0);
@@ -245,14 +306,16 @@ __global__ __launch_bounds__(kWave) SSM_SCAN_OCCUPANCY void scan_main_kernel(
     d += bv;
     if (SOFTPLUS) d = softplus(d);
     float bcur[NS], ccur[NS];
-#pragma unroll
-    for (int n = 0; n < NS; n++) { bcur[n] = bn[n]; ccur[n] = cn[n]; }
+    unpack_row<NS, EXACT>(bn, N, bcur);
+    unpack_row<NS, EXACT>(cn, N, ccur);
     if (++ks < n_steps) {  // the last step re-reads its own rows: never past the end of B / C
       brow += N;
       crow += N;
+      bodd ^= N & 1;
+      codd ^= N & 1;
     }
-    load_row<NS, EXACT>(brow, N, bn);  // next step's rows are fetched while this step computes
-    load_row<NS, EXACT>(crow, N, cn);
+    fetch_row<NS, EXACT>(brow, bodd, N, bn);  // next step's rows are fetched while this step computes
+    fetch_row<NS, EXACT>(crow, codd, N, cn);
     const float dx = d * x;
     float acc0 = 0.f, acc1 = 0.f;  // two chains halve the dependent-FMA depth of the readout
 #pragma unroll
@@ -530,79 +593,88 @@ __global__ __launch_bounds__(256) void state_update_kernel(
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-// Scan launch resources: float rows of B and C (the caller's arrays for fp32
-// I/O, widened copies for bf16) and the per-chunk workspace.
+// 1 when a bf16 tensor starts 2 bytes into a 32-bit word.
+int bf16_rows_odd(const void* p) { return int((reinterpret_cast<uintptr_t>(p) >> 1) & 1); }
+
+// Rows of B and C as the kernels read them (the caller's arrays, or float
+// copies of bf16 ones) and the per-chunk workspace of a cut scan.
 struct ScanBufs {
-  const float* B;
-  const float* C;
+  const void* B;
+  const void* C;
+  int rows_odd;  // bf16 rows: bit 0 / bit 1 set when B / C starts 2 bytes into a 32-bit word
   float* carry;  // [b][n_chunks][E][NS] chunk aggregates, then incoming states
   float* csum;   // [b][n_chunks][E] sum of steps per chunk
 };
 
 // Chunk aggregates, then the carry chain: afterwards carry slot c holds the
 // state at the end of chunk c (the incoming state of chunk c + 1).
-template <typename T, int NS, bool EXACT, bool SOFTPLUS>
+template <typename T, typename R, int NS, bool EXACT, bool SOFTPLUS>
 hipError_t run_carries(const ScanArgs& a, const ScanPlan& pl, const ScanBufs& w) {
   if (pl.n_chunks <= 1) return hipSuccess;
   const int N = int(a.N);
   const int agg = pl.n_chunks - 1;
-  hipError_t err = launch_kind(kKindAgg, scan_chunk_agg_kernel<T, NS, EXACT, SOFTPLUS>, a.b * agg * pl.e_blocks, kWave,
-                               a.stream, static_cast<const T*>(a.u), static_cast<const T*>(a.delta), a.A, w.B, a.bias,
-                               w.carry, w.csum, a.L, a.E, N, pl.chunk_len, pl.n_chunks, agg, pl.e_blocks);
+  hipError_t err = launch_kind(kKindAgg, scan_chunk_agg_kernel<T, R, NS, EXACT, SOFTPLUS>, a.b * agg * pl.e_blocks,
+                               kWave, a.stream, static_cast<const T*>(a.u), static_cast<const T*>(a.delta), a.A,
+                               static_cast<const R*>(w.B), a.bias, w.carry, w.csum, a.L, a.E, N, pl.chunk_len,
+                               pl.n_chunks, agg, pl.e_blocks, w.rows_odd & 1);
   if (err != hipSuccess) return err;
   // the state at the end of chunk c (forward, inclusive), from the incoming state of the sequence
   const ChainArgs c{w.carry, w.csum, a.A, a.h0, nullptr, a.b, a.E, NS, N, pl.n_chunks, pl.n_chunks - 1};
   return launch_chain<false, false, false>(kKindCarry, c, a.stream);
 }
 
-template <typename T, int NS, bool EXACT, bool SOFTPLUS, bool HAS_Z, bool FULL>
+template <typename T, typename R, int NS, bool EXACT, bool SOFTPLUS, bool HAS_Z, bool FULL>
 hipError_t run_scan(const ScanArgs& a, const ScanPlan& pl, const ScanBufs& w) {
   const T* u = static_cast<const T*>(a.u);
   const T* dl = static_cast<const T*>(a.delta);
   const T* z = static_cast<const T*>(a.z);
+  const R* B = static_cast<const R*>(w.B);
+  const R* C = static_cast<const R*>(w.C);
   T* y = static_cast<T*>(a.y);
   const int N = int(a.N);
-  hipError_t err = run_carries<T, NS, EXACT, SOFTPLUS>(a, pl, w);
+  hipError_t err = run_carries<T, R, NS, EXACT, SOFTPLUS>(a, pl, w);
   if (err != hipSuccess) return err;
   const int64_t blocks = a.b * pl.n_chunks * pl.e_blocks;
   if (a.saved)  // the saving variant exists for the general channel count only
-    return launch_kind(kKindMain, scan_main_kernel<T, NS, EXACT, SOFTPLUS, HAS_Z, false, true>, blocks, kWave, a.stream,
-                       u, dl, a.A, w.B, w.C, a.D, z, a.bias, y, a.last_state, (const float*)w.carry, a.h0, a.saved, a.L,
-                       a.E, N, pl.chunk_len, pl.n_chunks, pl.e_blocks);
-  return launch_kind(kKindMain, scan_main_kernel<T, NS, EXACT, SOFTPLUS, HAS_Z, FULL, false>, blocks, kWave, a.stream,
-                     u, dl, a.A, w.B, w.C, a.D, z, a.bias, y, a.last_state, (const float*)w.carry, a.h0,
-                     (float*)nullptr, a.L, a.E, N, pl.chunk_len, pl.n_chunks, pl.e_blocks);
+    return launch_kind(kKindMain, scan_main_kernel<T, R, NS, EXACT, SOFTPLUS, HAS_Z, false, true>, blocks, kWave, a.stream,
+                       u, dl, a.A, B, C, a.D, z, a.bias, y, a.last_state, (const float*)w.carry, a.h0, a.saved, a.L,
+                       a.E, N, pl.chunk_len, pl.n_chunks, pl.e_blocks, w.rows_odd);
+  return launch_kind(kKindMain, scan_main_kernel<T, R, NS, EXACT, SOFTPLUS, HAS_Z, FULL, false>, blocks, kWave, a.stream,
+                     u, dl, a.A, B, C, a.D, z, a.bias, y, a.last_state, (const float*)w.carry, a.h0,
+                     (float*)nullptr, a.L, a.E, N, pl.chunk_len, pl.n_chunks, pl.e_blocks, w.rows_odd);
 }
 
-template <typename T, int NS, bool EXACT, bool FULL>
+template <typename T, typename R, int NS, bool EXACT, bool FULL>
 hipError_t scan_flags(const ScanArgs& a, const ScanPlan& pl, const ScanBufs& w) {
   const bool z = a.z != nullptr;
   if (a.softplus) {
-    return z ? run_scan<T, NS, EXACT, true, true, FULL>(a, pl, w) : run_scan<T, NS, EXACT, true, false, FULL>(a, pl, w);
+    return z ? run_scan<T, R, NS, EXACT, true, true, FULL>(a, pl, w)
+             : run_scan<T, R, NS, EXACT, true, false, FULL>(a, pl, w);
   }
-  return z ? run_scan<T, NS, EXACT, false, true, FULL>(a, pl, w) : run_scan<T, NS, EXACT, false, false, FULL>(a, pl, w);
+  return z ? run_scan<T, R, NS, EXACT, false, true, FULL>(a, pl, w)
+           : run_scan<T, R, NS, EXACT, false, false, FULL>(a, pl, w);
 }
 
-template <typename T, int NS, bool EXACT>
+template <typename T, typename R, int NS, bool EXACT>
 hipError_t scan_full(const ScanArgs& a, const ScanPlan& pl, const ScanBufs& w) {
-  return (a.E % kWave == 0) ? scan_flags<T, NS, EXACT, true>(a, pl, w) : scan_flags<T, NS, EXACT, false>(a, pl, w);
+  return (a.E % kWave == 0) ? scan_flags<T, R, NS, EXACT, true>(a, pl, w) : scan_flags<T, R, NS, EXACT, false>(a, pl, w);
 }
 
 // state slots per channel in the workspace: N for the exact-size kernels, 16 for the padded one
 int scan_states(int64_t N) { return (N == 4 || N == 8 || N == 16) ? int(N) : 16; }
 
-template <typename T>
+template <typename T, typename R>
 hipError_t scan_typed(const ScanArgs& a, const ScanPlan& pl, const ScanBufs& w) {
-  if (a.N == 16) return scan_full<T, 16, true>(a, pl, w);
-  if (a.N == 8) return scan_full<T, 8, true>(a, pl, w);
-  if (a.N == 4) return scan_full<T, 4, true>(a, pl, w);
-  return scan_full<T, 16, false>(a, pl, w);
+  if (a.N == 16) return scan_full<T, R, 16, true>(a, pl, w);
+  if (a.N == 8) return scan_full<T, R, 8, true>(a, pl, w);
+  if (a.N == 4) return scan_full<T, R, 4, true>(a, pl, w);
+  return scan_full<T, R, 16, false>(a, pl, w);
 }
 
 template <typename T>
 hipError_t carries_typed(const ScanArgs& a, const ScanPlan& pl, const ScanBufs& w) {
 #define SSM_CARRIES(NS, EX) \
-  return a.softplus ? run_carries<T, NS, EX, true>(a, pl, w) : run_carries<T, NS, EX, false>(a, pl, w)
+  return a.softplus ? run_carries<T, T, NS, EX, true>(a, pl, w) : run_carries<T, T, NS, EX, false>(a, pl, w)
   if (a.N == 16) { SSM_CARRIES(16, true); }
   if (a.N == 8) { SSM_CARRIES(8, true); }
   if (a.N == 4) { SSM_CARRIES(4, true); }
@@ -663,7 +735,7 @@ hipError_t update_typed(const UpdateArgs& a) {
 
 }  // namespace
 
-ScanPlan plan_scan(int64_t b, int64_t L, int64_t E, int elem_bytes) {
+ScanPlan plan_scan(int64_t b, int64_t L, int64_t E, int elem_bytes, const ScanTuning& tune) {
   ScanPlan pl;
   pl.e_blocks = int((E + kWave - 1) / kWave);
   // Enough waves that every SIMD of the 256 CUs sees several rounds of them
@@ -672,21 +744,14 @@ ScanPlan plan_scan(int64_t b, int64_t L, int64_t E, int elem_bytes) {
   // 1.871 ms against 1.896 for 16384 and 1.93 for 22528 (means of repeated
   // runs).  The sequence is cut only when batch x channel blocks alone cannot
   // provide them.
-  int64_t target = 20480;
-  if (const char* s = std::getenv("SSM_SCAN_TARGET_WAVES")) {
-    const long v = std::strtol(s, nullptr, 10);
-    if (v > 0) target = v;
-  }
+  const int64_t target = tune.target_waves > 0 ? tune.target_waves : 20480;
   const int64_t base = b * pl.e_blocks;
   // Chunks of at least 64 steps, or of 32 when 64-step chunks give fewer than
   // 4096 waves (4 per SIMD) and the sequence has 256 steps or more (shorter
   // ones are launch-bound): b32 L512 E512 takes 96 us in 16 chunks of 32 steps
   // against 114 us in 8 of 64.
   int64_t min_chunk = (L >= 256 && base * ((L + 63) / 64) < 4096) ? 32 : 64;
-  if (const char* s = std::getenv("SSM_SCAN_MIN_CHUNK")) {
-    const long v = std::strtol(s, nullptr, 10);
-    if (v > 0) min_chunk = v;
-  }
+  if (tune.min_chunk > 0) min_chunk = tune.min_chunk;
   pl.chunk_len = std::max<int64_t>(L, 1);
   pl.n_chunks = 1;
   if (base > 0 && base * 2 < target && L > min_chunk) {
@@ -704,50 +769,97 @@ ScanPlan plan_scan(int64_t b, int64_t L, int64_t E, int elem_bytes) {
   return pl;
 }
 
-hipError_t launch_scan(const ScanArgs& a) {
+// Workspace of a cut scan, in floats: [chunk aggregates | chunk step sums | float
+// rows of B | of C].  A cut bf16 scan reads float copies of its B / C rows: the
+// rows are taken once per step by every wave of a chunk, and unpacking bf16 on
+// the scalar ALU made the long b1 L65536 E5120 scan 4-8% slower.  One chunk
+// reads the bf16 rows directly and takes no workspace.
+struct WsLayout {
+  size_t carry, csum, rows, total;  // offsets and size in floats
+};
+WsLayout ws_layout(const ScanArgs& a, const ScanPlan& pl) {
+  WsLayout l{0, 0, 0, 0};
+  if (pl.n_chunks <= 1) return l;
+  const size_t slots = size_t(a.b) * size_t(pl.n_chunks) * size_t(a.E);
+  l.csum = slots * size_t(scan_states(a.N));
+  l.rows = l.csum + slots;
+  const size_t n_rows = a.dtype == 0 ? 0 : size_t(a.b) * size_t(a.L) * size_t(a.N);
+  l.total = l.rows + 2 * n_rows;
+  return l;
+}
+
+size_t chunked_workspace_bytes(const ScanArgs& a, const ScanPlan& pl) { return ws_layout(a, pl).total * sizeof(float); }
+
+int choose_path(const ScanArgs& a, const ScanPlan& pl, int n_cu, FusedPlan* fp) {
+  if (a.tune.path == kPathChunked) return kPathChunked;
+  if (a.tune.path == kPathSinglePass) return plan_fused(a, n_cu, kFusedMaxChunks, fp) ? kPathSinglePass : -1;
+  // by default the single pass runs where the sequence has to be cut and its
+  // chain of chunk maps per block stays short
+  if (pl.n_chunks > 1 && plan_fused(a, n_cu, kFusedChainMax, fp)) return kPathSinglePass;
+  return kPathChunked;
+}
+
+hipError_t device_cu_count(int* n_cu) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err == hipSuccess) err = hipDeviceGetAttribute(n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  return err;
+}
+
+hipError_t launch_scan(const ScanArgs& a, void* workspace, size_t workspace_bytes) {
   if (a.b == 0 || a.E == 0) return hipSuccess;
   if (a.L == 0) {  // no step: the last state is the incoming one
     if (!a.last_state) return hipSuccess;
     const int64_t n = a.b * a.E * a.N;
     return launch_kind(kKindFill, fill_state_kernel, (n + 255) / 256, 256, a.stream, a.last_state, a.h0, n);
   }
-  const ScanPlan pl = plan_scan(a.b, a.L, a.E, a.dtype == 0 ? 4 : 2);
-  if (pl.n_chunks > 1) {  // the sequence has to be cut: the single-pass form, when it fills the chip
-    int dev = 0, n_cu = 0;
-    hipError_t err = hipGetDevice(&dev);
-    if (err == hipSuccess) err = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
-    if (err != hipSuccess) return err;
-    FusedPlan fp;
-    if (plan_fused(a, n_cu, &fp)) return launch_fused(a, fp);
-  }
-  // workspace: [chunk aggregates | chunk step sums | widened B rows | widened C rows]
-  const size_t slots = pl.n_chunks > 1 ? size_t(a.b) * size_t(pl.n_chunks) * size_t(a.E) : 0;
-  const size_t n_agg = slots * size_t(scan_states(a.N));
-  const size_t n_rows = a.dtype == 0 ? 0 : size_t(a.b) * size_t(a.L) * size_t(a.N);
-  const size_t n_floats = n_agg + slots + 2 * n_rows;
+  const ScanPlan pl = plan_scan(a.b, a.L, a.E, a.dtype == 0 ? 4 : 2, a.tune);
+  int n_cu = 0;
+  hipError_t err = device_cu_count(&n_cu);
+  if (err != hipSuccess) return err;
+  FusedPlan fp;
+  const int path = choose_path(a, pl, n_cu, &fp);
+  if (path < 0) return hipErrorInvalidConfiguration;  // the caller checked this before
+  if (path == kPathSinglePass) return launch_fused(a, fp);
+  // workspace, taken from the caller or from the stream's pool
+  const WsLayout lay = ws_layout(a, pl);
+  const size_t need = lay.total * sizeof(float);
   void* ws = nullptr;
-  if (n_floats > 0) {
-    hipError_t err = hipMallocAsync(&ws, n_floats * sizeof(float), a.stream);
-    if (err != hipSuccess) return err;
+  bool own = false;
+  if (need > 0) {
+    if (workspace) {
+      if (workspace_bytes < need) return hipErrorInvalidValue;
+      ws = workspace;
+    } else {
+      err = hipMallocAsync(&ws, need, a.stream);
+      if (err != hipSuccess) return err;
+      own = true;
+    }
   }
-  float* f = static_cast<float*>(ws);
+  float* const f = static_cast<float*>(ws);
   ScanBufs w;
-  w.carry = slots ? f : nullptr;
-  w.csum = slots ? f + n_agg : nullptr;
-  hipError_t err = hipSuccess;
+  w.carry = need ? f + lay.carry : nullptr;
+  w.csum = need ? f + lay.csum : nullptr;
+  w.B = a.B;
+  w.C = a.C;
+  w.rows_odd = 0;
   if (a.dtype == 0) {
-    w.B = static_cast<const float*>(a.B);
-    w.C = static_cast<const float*>(a.C);
-  } else {
-    float* Bf = f + n_agg + slots;
-    float* Cf = Bf + n_rows;
+    err = scan_typed<float, float>(a, pl, w);
+  } else if (need) {  // cut: float copies of the rows
+    const size_t n_rows = size_t(a.b) * size_t(a.L) * size_t(a.N);
+    float* const Bf = f + lay.rows;
+    float* const Cf = Bf + n_rows;
     err = launch_kind(kKindWiden, widen_rows_kernel, int64_t((n_rows + 255) / 256), 256, a.stream,
-                 static_cast<const bf16_bits*>(a.B), static_cast<const bf16_bits*>(a.C), Bf, Cf, int64_t(n_rows));
+                      static_cast<const bf16_bits*>(a.B), static_cast<const bf16_bits*>(a.C), Bf, Cf,
+                      int64_t(n_rows));
     w.B = Bf;
     w.C = Cf;
+    if (err == hipSuccess) err = scan_typed<bf16_bits, float>(a, pl, w);
+  } else {
+    w.rows_odd = bf16_rows_odd(a.B) | (bf16_rows_odd(a.C) << 1);
+    err = scan_typed<bf16_bits, bf16_bits>(a, pl, w);
   }
-  if (err == hipSuccess) err = a.dtype == 0 ? scan_typed<float>(a, pl, w) : scan_typed<bf16_bits>(a, pl, w);
-  if (ws) {
+  if (own) {
     hipError_t ferr = hipFreeAsync(ws, a.stream);
     if (err == hipSuccess) err = ferr;
   }
@@ -756,23 +868,15 @@ hipError_t launch_scan(const ScanArgs& a) {
 
 int chunk_state_slots(int64_t N) { return scan_states(N); }
 
-hipError_t launch_chunk_states(const ScanArgs& a, const ScanPlan& pl, float* rows, float* carry, float* csum) {
+hipError_t launch_chunk_states(const ScanArgs& a, const ScanPlan& pl, float* carry, float* csum) {
   if (a.b == 0 || a.E == 0 || pl.n_chunks <= 1) return hipSuccess;
   ScanBufs w;
   w.carry = carry;
   w.csum = csum;
-  w.C = nullptr;
-  if (a.dtype == 0) {
-    w.B = static_cast<const float*>(a.B);
-    return carries_typed<float>(a, pl, w);
-  }
-  const int64_t n_rows = a.b * a.L * a.N;
-  hipError_t err = launch_kind(kKindWiden, widen_rows_kernel, (n_rows + 255) / 256, 256, a.stream,
-                               static_cast<const bf16_bits*>(a.B), static_cast<const bf16_bits*>(a.C), rows,
-                               rows + n_rows, n_rows);
-  if (err != hipSuccess) return err;
-  w.B = rows;
-  return carries_typed<bf16_bits>(a, pl, w);
+  w.B = a.B;
+  w.C = a.C;
+  w.rows_odd = a.dtype == 0 ? 0 : bf16_rows_odd(a.B);
+  return a.dtype == 0 ? carries_typed<float>(a, pl, w) : carries_typed<bf16_bits>(a, pl, w);
 }
 
 hipError_t launch_state_update(const UpdateArgs& a) {

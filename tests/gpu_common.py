@@ -17,13 +17,13 @@ def to_device(inputs, device="cuda"):
     return {k: (v.to(device) if hasattr(v, "to") else v) for k, v in inputs.items()}
 
 
-def gpu_scan(x, return_last_state=True):
+def gpu_scan(x, return_last_state=True, tuning=None):
     import torch
 
     import selective_state_space_35_amd as ssm
 
     y, last = ssm.ssm_scan_fwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
-                               x["softplus"], return_last_state=return_last_state)
+                               x["softplus"], return_last_state=return_last_state, tuning=tuning)
     torch.cuda.synchronize()
     return y, last
 
@@ -61,10 +61,10 @@ def pick(t, channels=None, batches=None, ch_axis=2):
     return oracle.to_f64(t)
 
 
-def check_scan(x, kind, what, channels=None, batches=None, y=None, last=None):
+def check_scan(x, kind, what, channels=None, batches=None, y=None, last=None, tuning=None):
     """Run GPU (unless outputs given) and oracle; assert the elementwise bound on y and last_state."""
     if y is None:
-        y, last = gpu_scan(x)
+        y, last = gpu_scan(x, tuning=tuning)
     y_ref, last_ref = oracle_scan(x, channels, batches)
     ey = max_normalised_error(pick(y, channels, batches), y_ref)
     el = max_normalised_error(pick(last, channels, batches, ch_axis=1), last_ref)

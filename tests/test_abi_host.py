@@ -277,31 +277,41 @@ def test_binding_raises_when_library_missing(monkeypatch):
         ssm.load_library()
 
 
-def test_scan_plan_query(lib, monkeypatch):
-    monkeypatch.delenv("SSM_SCAN_TARGET_WAVES", raising=False)
-    monkeypatch.delenv("SSM_SCAN_MIN_CHUNK", raising=False)
+def test_scan_plan_query(lib):
     # a tiny problem is one chunk; big batch x channel counts need no split
-    assert ssm.ssm_scan_plan(1, 64, 16, 4, "f32") == (64, 1)
-    assert ssm.ssm_scan_plan(256, 4096, 8192, 16, "bf16")[1] == 1
+    assert ssm.ssm_scan_plan(1, 64, 16, 4, "f32") == ("chunked", 64, 1)
+    assert ssm.ssm_scan_plan(256, 4096, 8192, 16, "bf16")[2] == 1
+    chunked = {"path": "chunked"}
     for (b, L, E, N, dt) in [(32, 512, 512, 16, "f32"), (8, 2048, 1536, 16, "bf16"), (1, 65536, 5120, 16, "bf16"),
                              (3, 1003, 70, 5, "bf16"), (1, 1 << 20, 64, 16, "f32")]:
-        cl, nc = ssm.ssm_scan_plan(b, L, E, N, dt)
-        assert cl >= 1 and nc >= 1
+        path, cl, nc = ssm.ssm_scan_plan(b, L, E, N, dt, tuning=chunked)
+        assert path == "chunked" and cl >= 1 and nc >= 1
         assert (nc - 1) * cl < L <= nc * cl, (b, L, E, cl, nc)  # chunks tile the sequence exactly
         assert cl * E * (4 if dt == "f32" else 2) < 2 ** 31  # 32-bit buffer offsets inside a chunk
-    # the long sequence: 256 chunks x 80 channel blocks = 20480 waves, the target
-    # that measured best
-    assert ssm.ssm_scan_plan(1, 65536, 5120, 16, "bf16") == (256, 256)
-    # 64-step chunks fill the chip for the mid workload (6144 waves); the block workload
-    # (2048 waves at 64 steps) is cut into 32-step chunks instead
-    assert ssm.ssm_scan_plan(8, 2048, 1536, 16, "bf16") == (64, 32)
-    assert ssm.ssm_scan_plan(32, 512, 512, 16, "f32") == (32, 16)
-    # the tuning variables are honoured
-    monkeypatch.setenv("SSM_SCAN_TARGET_WAVES", "100000")
-    monkeypatch.setenv("SSM_SCAN_MIN_CHUNK", "8")
-    assert ssm.ssm_scan_plan(3, 1003, 70, 16, "bf16") == (8, 126)
-    monkeypatch.setenv("SSM_SCAN_MIN_CHUNK", "1000")
-    assert ssm.ssm_scan_plan(3, 1003, 70, 16, "bf16") == (1000, 2)
+    # the long sequence: 256 chunks x 80 channel blocks = 20480 waves, the target that
+    # measured best; its single pass would chain 11 chunk maps per block, so the chunked
+    # form runs
+    assert ssm.ssm_scan_plan(1, 65536, 5120, 16, "bf16") == ("chunked", 256, 256)
+    # the chunked form of the mid workload takes 64-step chunks (6144 waves); the block
+    # workload (2048 waves at 64 steps) 32-step chunks
+    assert ssm.ssm_scan_plan(8, 2048, 1536, 16, "bf16", tuning=chunked) == ("chunked", 64, 32)
+    assert ssm.ssm_scan_plan(32, 512, 512, 16, "f32", tuning=chunked) == ("chunked", 32, 16)
+    # by default both run the single pass (4 and 3 chunk maps per block), in 8-step chunks
+    assert ssm.ssm_scan_plan(8, 2048, 1536, 16, "bf16") == ("single_pass", 8, 256)
+    assert ssm.ssm_scan_plan(32, 512, 512, 16, "f32") == ("single_pass", 8, 64)
+    # the tuning fields are honoured
+    forced = {"path": "chunked", "target_waves": 100000, "min_chunk": 8}
+    assert ssm.ssm_scan_plan(3, 1003, 70, 16, "bf16", tuning=forced) == ("chunked", 8, 126)
+    assert ssm.ssm_scan_plan(3, 1003, 70, 16, "bf16", tuning=dict(forced, min_chunk=1000)) == ("chunked", 1000, 2)
+    assert ssm.ssm_scan_plan(1, 65536, 5120, 16, "bf16", tuning={"path": "single_pass"}) == ("single_pass", 8, 8192)
+    # a single pass that cannot run (too few channels per CU; rows that are not whole
+    # 8-byte units) or an out-of-range field is refused
+    for bad in [dict(b=1, L=4096, E=64, N=16, dtype="f32", tuning={"path": "single_pass"}),
+                dict(b=8, L=4096, E=1538, N=16, dtype="bf16", tuning={"path": "single_pass"}),
+                dict(b=8, L=4096, E=1536, N=16, dtype="bf16", tuning={"path": 7}),
+                dict(b=8, L=4096, E=1536, N=16, dtype="bf16", tuning={"min_chunk": -1})]:
+        with pytest.raises(ssm.SSMError, match="SSM_ERR_PLAN|-7|tuning"):
+            ssm.ssm_scan_plan(**bad)
     # a row too wide for 32-bit offsets is rejected
     with pytest.raises(ssm.SSMError):
         ssm.ssm_scan_plan(1, 4, 1 << 31, 16, "f32")

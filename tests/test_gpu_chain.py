@@ -3,16 +3,19 @@
 The chain that joins the chunks of a cut sequence runs one thread per state
 coordinate when there are many of them; with few (a long sequence over few
 channels) each chain is cut into G = 2, 4 or 8 stretches that are reduced,
-combined through LDS and walked again.  The stretch count follows from the
-sizes, and the environment variable SSM_CHAIN_STRETCHES forces it, so every
-stretched variant runs here on inputs the oracle checks in full:
+combined through LDS and walked again.  G follows from the sizes: with fewer
+than 65536 / G state coordinates it doubles while every stretch keeps 32 chunks
+or more (K >= 64 chunks: G = 2, K >= 128: G = 4, K >= 256: G = 8).  The cases
+below pick their lengths so that every stretched variant runs on inputs the
+oracle checks in full:
 
-* the forward scan cut into 188 chunks of 8 steps, G = 1, 2, 4, 8, with and
-  without an initial state (the forward chain, value leaving each chunk);
-* the backward (reverse chain, value entering each chunk from its end, then the
-  start of the sequence) with the forward chunk states it recomputes, G = 2, 4, 8;
-* the scalar-per-head scan over 6 segments with G = 8, so that stretches are
-  empty (value entering each segment, and the last state);
+* the forward scan (chunked form, 8-step chunks) with 50, 100, 188 and 263
+  chunks over 2 x 70 channels x 16 states (G = 1, 2, 4, 8), with and without an
+  initial state (the forward chain, value leaving each chunk);
+* the backward (reverse chain over its 64-step chunks, value entering each chunk
+  from its end, then the start of the sequence) with the forward chunk states it
+  recomputes, at 94, 188 and 266 chunks (G = 2, 4, 8);
+* the scalar-per-head scan over 65 segments of 1024 steps (G = 2);
 * the long workload's one-GPU share under 8-way channel sharding (b1 L65536 E640
   N16 bf16) with the stretch count chosen by the sizes, all channels.
 
@@ -32,26 +35,24 @@ pytestmark = pytest.mark.gpu
 N01 = ("normal", 0.0, 1.0)
 FWD = workloads.ScanWorkload("chain_fwd", b=2, L=1500, E=70, N=16, dtype="f32", u=N01, delta=("normal", -1.0, 0.7),
                              z=N01, B=N01, C=N01, D=N01, delta_bias=("normal", 0.0, 0.3), softplus=True)
+EIGHT_STEP_CHUNKS = {"path": "chunked", "min_chunk": 8, "target_waves": 100000}
 
 
-@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("G,L", [(1, 400), (2, 800), (4, 1500), (8, 2100)])
 @pytest.mark.parametrize("with_h0", [False, True])
-def test_forward_chain_stretches(G, with_h0, monkeypatch):
+def test_forward_chain_stretches(G, L, with_h0):
     import torch
 
     import selective_state_space_35_amd as ssm
 
-    monkeypatch.setenv("SSM_SCAN_MIN_CHUNK", "8")
-    monkeypatch.setenv("SSM_SCAN_TARGET_WAVES", "100000")
-    monkeypatch.setenv("SSM_CHAIN_STRETCHES", str(G))
-    w = FWD
+    w = FWD.with_shape(L=L)
     x = to_device(workloads.make_scan_inputs(w, seed=G))
     h0 = torch.randn((w.b, w.E, w.N), generator=torch.Generator().manual_seed(G)).cuda() if with_h0 else None
-    plan = ssm.ssm_scan_plan(w.b, w.L, w.E, w.N, w.dtype)
-    assert plan == (8, 188)
+    plan = ssm.ssm_scan_plan(w.b, w.L, w.E, w.N, w.dtype, tuning=EIGHT_STEP_CHUNKS)
+    assert plan == ("chunked", 8, (L + 7) // 8)
     say(f"chain forward G={G} h0={with_h0} plan={plan}")
     y, last = ssm.ssm_scan_fwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
-                               x["softplus"], initial_state=h0)
+                               x["softplus"], initial_state=h0, tuning=EIGHT_STEP_CHUNKS)
     torch.cuda.synchronize()
     y_ref, last_ref = oracle.scan(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
                                   x["softplus"], h0=h0)
@@ -61,14 +62,13 @@ def test_forward_chain_stretches(G, with_h0, monkeypatch):
     assert ey <= TOL["f32"] and el <= TOL["f32"]
 
 
-@pytest.mark.parametrize("G", [2, 4, 8])
-def test_backward_chain_stretches(G, monkeypatch):
+@pytest.mark.parametrize("G,L", [(2, 6000), (4, 12000), (8, 17000)])
+def test_backward_chain_stretches(G, L):
     import torch
 
     import selective_state_space_35_amd as ssm
 
-    monkeypatch.setenv("SSM_CHAIN_STRETCHES", str(G))
-    w = FWD
+    w = FWD.with_shape(L=L)
     x = to_device(workloads.make_scan_inputs(w, seed=10 + G))
     gen = torch.Generator().manual_seed(G)
     dy = torch.randn(x["u"].shape, generator=gen).cuda()
@@ -86,16 +86,15 @@ def test_backward_chain_stretches(G, monkeypatch):
         assert err <= TOL["f32"], f"{name}: {err:.3e}"
 
 
-def test_segment_chain_with_empty_stretches(monkeypatch):
+def test_segment_chain_stretched():
     import torch
 
     import selective_state_space_35_amd as ssm
 
-    monkeypatch.setenv("SSM_CHAIN_STRETCHES", "8")
-    w = workloads.SsdWorkload("chain_ssd", b=1, L=5 * 1024 + 37, H=2, N=32, with_bias=True)
+    w = workloads.SsdWorkload("chain_ssd", b=1, L=64 * 1024 + 37, H=2, N=32, with_bias=True)
     x = to_device(workloads.make_ssd_inputs(w, seed=3))
     h0 = torch.randn((w.b, w.E, w.N), generator=torch.Generator().manual_seed(3)).cuda()
-    say(f"chain segments G=8: b{w.b} L{w.L} H{w.H} N{w.N} (6 segments)")
+    say(f"chain segments G=2: b{w.b} L{w.L} H{w.H} N{w.N} (65 segments)")
     y, last = ssm.ssm_ssd_fwd(x["x"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
                               x["softplus"], initial_state=h0)
     torch.cuda.synchronize()
@@ -103,7 +102,7 @@ def test_segment_chain_with_empty_stretches(monkeypatch):
                                  x["softplus"], h0=h0)
     ey = max_normalised_error(oracle.to_f64(y), y_ref)
     el = max_normalised_error(oracle.to_f64(last), last_ref)
-    print(f"[parity] chain segments G=8: y {ey:.2e} last {el:.2e}", flush=True)
+    print(f"[parity] chain segments G=2: y {ey:.2e} last {el:.2e}", flush=True)
     assert ey <= TOL["bf16"] and el <= TOL["bf16"]
 
 

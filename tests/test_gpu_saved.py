@@ -32,13 +32,13 @@ BASE = workloads.ScanWorkload("saved_small", b=2, L=300, E=70, N=16, dtype="f32"
                               D=workloads.N01, delta_bias=("normal", 0.0, 0.3), softplus=True)
 
 
-def fwd_save(x):
+def fwd_save(x, tuning=None):
     import torch
 
     import selective_state_space_35_amd as ssm
 
     y, last, saved = ssm.ssm_scan_fwd_save(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"],
-                                           x["delta_bias"], x["softplus"], initial_state=x["h0"])
+                                           x["delta_bias"], x["softplus"], initial_state=x["h0"], tuning=tuning)
     torch.cuda.synchronize()
     return y, last, saved
 
@@ -68,27 +68,26 @@ def check_grads(got, ref, kind, what):
         assert err <= TOL[kind], f"{what}: {name} error {err:.3e} > {TOL[kind]}"
 
 
-def force_chunks(monkeypatch, min_chunk):
-    if min_chunk:
-        monkeypatch.setenv("SSM_SCAN_MIN_CHUNK", str(min_chunk))
-        monkeypatch.setenv("SSM_SCAN_TARGET_WAVES", "100000")
+def force_chunks(min_chunk):
+    """The chunked form cut into chunks of min_chunk steps or more (None: the plan the sizes give)."""
+    return {"path": "chunked", "min_chunk": min_chunk, "target_waves": 100000} if min_chunk else None
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("min_chunk", [None, 40, 200])
-def test_saved_states_are_the_prefix_states(dtype, min_chunk, monkeypatch):
+def test_saved_states_are_the_prefix_states(dtype, min_chunk):
     import torch
 
     import selective_state_space_35_amd as ssm
 
-    force_chunks(monkeypatch, min_chunk)
+    tune = force_chunks(min_chunk)
     w = BASE.with_shape(dtype=dtype)
     x = make(w, seed=3, with_h0=True)
-    say(f"saved states {dtype} min_chunk={min_chunk} plan={ssm.ssm_scan_plan(w.b, w.L, w.E, w.N, w.dtype)}")
-    y, last, saved = fwd_save(x)
+    say(f"saved states {dtype} min_chunk={min_chunk} plan={ssm.ssm_scan_plan(w.b, w.L, w.E, w.N, w.dtype, tune)}")
+    y, last, saved = fwd_save(x, tune)
     assert saved.shape == ssm.saved_states_shape(w.b, w.L, w.E, w.N) == (w.b, 4, w.E, w.N)
-    y0, last0 = ssm.ssm_scan_fwd_from(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
-                                      x["softplus"], initial_state=x["h0"])
+    y0, last0 = ssm.ssm_scan_fwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
+                                 x["softplus"], initial_state=x["h0"], tuning=tune)
     torch.cuda.synchronize()
     assert torch.equal(y, y0) and torch.equal(last, last0)
     worst = 0.0
@@ -103,12 +102,12 @@ def test_saved_states_are_the_prefix_states(dtype, min_chunk, monkeypatch):
 
 @pytest.mark.parametrize("dtype,with_h0,with_dlast,min_chunk", [
     ("f32", True, True, None), ("f32", False, False, 40), ("bf16", True, False, 200), ("bf16", False, True, 40)])
-def test_backward_from_saved_states(dtype, with_h0, with_dlast, min_chunk, monkeypatch):
-    force_chunks(monkeypatch, min_chunk)
+def test_backward_from_saved_states(dtype, with_h0, with_dlast, min_chunk):
+    tune = force_chunks(min_chunk)
     w = BASE.with_shape(dtype=dtype)
     x = make(w, seed=5, with_h0=with_h0, with_dlast=with_dlast)
     say(f"bwd from saved states {dtype} h0={with_h0} dlast={with_dlast} min_chunk={min_chunk}")
-    _, _, saved = fwd_save(x)
+    _, _, saved = fwd_save(x, tune)
     check_grads(bwd_saved(x, saved), oracle_bwd(x), dtype, f"bwd saved {dtype} h0={with_h0} min_chunk={min_chunk}")
 
 

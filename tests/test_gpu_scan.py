@@ -43,14 +43,13 @@ def test_reduced_workloads(name, w):
 
 @pytest.mark.parametrize("min_chunk", [8, 24, 64, 1000])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_forced_chunk_splits(min_chunk, dtype, monkeypatch):
+def test_forced_chunk_splits(min_chunk, dtype):
     """Carries across chunk boundaries: many chunks, ragged last chunk, chunk longer than L."""
-    monkeypatch.setenv("SSM_SCAN_MIN_CHUNK", str(min_chunk))
-    monkeypatch.setenv("SSM_SCAN_TARGET_WAVES", "100000")
+    tune = {"path": "chunked", "min_chunk": min_chunk, "target_waves": 100000}
     base = workloads.MID if dtype == "bf16" else workloads.BLOCK
     w = base.with_shape(b=3, L=1003, E=70)
     say(f"forced chunks min_chunk={min_chunk} {dtype}")
-    check_scan(make(w, seed=2), dtype, f"chunks>={min_chunk} {dtype}")
+    check_scan(make(w, seed=2), dtype, f"chunks>={min_chunk} {dtype}", tuning=tune)
 
 
 @pytest.mark.parametrize("N", list(range(1, 17)))
@@ -60,6 +59,27 @@ def test_every_state_size(N):
     check_scan(make(w, seed=3), "bf16", f"N={N} bf16")
     wf = workloads.BLOCK.with_shape(b=1, L=200, E=65, N=N)
     check_scan(make(wf, seed=4), "f32", f"N={N} f32")
+
+
+@pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 8, 9, 15, 16])
+@pytest.mark.parametrize("shift", [0, 1])
+def test_bf16_rows_read_directly(N, shift):
+    """A scan in one chunk reads bf16 B / C rows as 32-bit words split on the scalar unit: rows that start in
+    the upper half of a word (odd N, or a tensor starting 2 bytes into a word) take the other half first."""
+    import torch
+
+    w = workloads.MID.with_shape(b=3, L=150, E=72, N=N)
+    x = make(w, seed=50 + N)
+    if shift:
+        for k in ("B", "C"):
+            t = x[k]
+            buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+            v = buf[1:].view(t.shape)
+            v.copy_(t)
+            x[k] = v
+        assert x["B"].data_ptr() % 4 == 2 and x["C"].data_ptr() % 4 == 2
+    say(f"bf16 rows direct N={N} shift={shift}")
+    check_scan(x, "bf16", f"bf16 rows N={N} shift={shift}", tuning={"path": "chunked", "target_waves": 1})
 
 
 @pytest.mark.parametrize("softplus", [False, True])
@@ -106,19 +126,19 @@ def test_degenerate_sizes():
         check_scan(make(w, seed=6), "bf16", f"{shape}")
 
 
-def test_zero_step_keeps_state_bitwise(monkeypatch):
+def test_zero_step_keeps_state_bitwise():
     """A vanishing step keeps the state exactly (retention 1, write 0)."""
     import torch
 
-    monkeypatch.setenv("SSM_SCAN_TARGET_WAVES", "1")  # one chunk: both runs share their arithmetic order
+    one_chunk = {"path": "chunked", "target_waves": 1}  # both runs share their arithmetic order
     for softplus, fill in [(False, 0.0), (True, -200.0)]:
         say(f"zero step softplus={softplus}")
         w = workloads.MID.with_shape(b=2, L=200, E=100, softplus=softplus, delta=("normal", 0.2, 0.05))
         x = make(w, seed=7)
         x["delta"][:, 100:] = fill
-        y, last = gpu_scan(x)
+        y, last = gpu_scan(x, tuning=one_chunk)
         half = {k: (v[:, :100].contiguous() if k in ("u", "delta", "z", "B", "C") else v) for k, v in x.items()}
-        _, last_half = gpu_scan(half)
+        _, last_half = gpu_scan(half, tuning=one_chunk)
         assert torch.equal(last, last_half)
 
 
@@ -257,25 +277,23 @@ def max_err(t, ref):
 
 
 @pytest.mark.parametrize("min_chunk", [None, 16])
-def test_continuation_equals_whole_sequence(min_chunk, monkeypatch):
+def test_continuation_equals_whole_sequence(min_chunk):
     """scan(L1 + L2) == scan(L2, initial_state = last_state of scan(L1)), split inside a chunk."""
     import torch
 
     import selective_state_space_35_amd as ssm
 
-    if min_chunk:
-        monkeypatch.setenv("SSM_SCAN_MIN_CHUNK", str(min_chunk))
-        monkeypatch.setenv("SSM_SCAN_TARGET_WAVES", "100000")
+    tune = {"path": "chunked", "min_chunk": min_chunk, "target_waves": 100000} if min_chunk else None
     say(f"continuation min_chunk={min_chunk}")
     w = workloads.MID.with_shape(b=2, L=1500, E=96)
     x = make(w, seed=13)
-    y_all, last_all = gpu_scan(x)
+    y_all, last_all = gpu_scan(x, tuning=tune)
     L1 = 611
     part = lambda sl: {k: (v[:, sl].contiguous() if k in ("u", "delta", "z", "B", "C") else v) for k, v in x.items()}
     p1, p2 = part(slice(0, L1)), part(slice(L1, None))
-    y1, last1 = gpu_scan(p1)
+    y1, last1 = gpu_scan(p1, tuning=tune)
     y2, last2 = ssm.ssm_scan_fwd(p2["u"], p2["delta"], p2["A"], p2["B"], p2["C"], p2["D"], p2["z"], p2["delta_bias"],
-                                 p2["softplus"], initial_state=last1)
+                                 p2["softplus"], initial_state=last1, tuning=tune)
     torch.cuda.synchronize()
     y_cat = torch.cat([y1, y2], dim=1)
     y_ref, last_ref = oracle.scan(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"], True)

@@ -2,11 +2,11 @@
 
 Each case draws its sizes, dtype and flags from a fixed seed (printed before the
 GPU call), so a failure names a reproducible configuration.  The forward scan
-cases also force the sequence to be cut into small chunks (SSM_SCAN_MIN_CHUNK,
-SSM_SCAN_TARGET_WAVES), so the chunk aggregate / carry path runs on small inputs.
+cases also force the chunked form with the sequence cut into small chunks (the
+tuning argument of ssm_scan_fwd_tuned), so the chunk aggregate / carry path runs
+on small inputs.
 Bounds as in the other parity tests: 1e-4 (fp32) / 2e-2 (bf16) times (1 + |ref|).
 """
-import os
 
 import numpy as np
 import pytest
@@ -35,21 +35,20 @@ def scan_case(seed):
 
 
 @pytest.mark.parametrize("seed", range(24))
-def test_scan_forward_sweep(seed, monkeypatch):
+def test_scan_forward_sweep(seed):
     import torch
 
     import selective_state_space_35_amd as ssm
 
     w, with_h0, min_chunk = scan_case(seed)
-    monkeypatch.setenv("SSM_SCAN_MIN_CHUNK", str(min_chunk))
-    monkeypatch.setenv("SSM_SCAN_TARGET_WAVES", "100000")
+    tune = {"path": "chunked", "min_chunk": min_chunk, "target_waves": 100000}
     x = to_device(workloads.make_scan_inputs(w, seed=seed))
     h0 = torch.randn((w.b, w.E, w.N), generator=torch.Generator().manual_seed(seed)).cuda() if with_h0 else None
     say(f"sweep scan seed={seed}: b{w.b} L{w.L} E{w.E} N{w.N} {w.dtype} z={w.z is not None} D={w.D is not None} "
         f"bias={w.delta_bias is not None} softplus={w.softplus} h0={with_h0} min_chunk={min_chunk} "
-        f"plan={ssm.ssm_scan_plan(w.b, w.L, w.E, w.N, w.dtype)}")
+        f"plan={ssm.ssm_scan_plan(w.b, w.L, w.E, w.N, w.dtype, tuning=tune)}")
     y, last = ssm.ssm_scan_fwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
-                               x["softplus"], initial_state=h0)
+                               x["softplus"], initial_state=h0, tuning=tune)
     torch.cuda.synchronize()
     y_ref, last_ref = oracle.scan(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
                                   x["softplus"], h0=h0)
@@ -109,7 +108,7 @@ def test_state_update_staged_sweep(seed):
 
 
 @pytest.mark.parametrize("seed", range(8))
-def test_chain_stretches_sweep(seed, monkeypatch):
+def test_chain_stretches_sweep(seed):
     """Few channels over many short chunks: the chunk chain cuts itself into stretches."""
     import torch
 
@@ -120,14 +119,13 @@ def test_chain_stretches_sweep(seed, monkeypatch):
         f"csweep{seed}", b=int(rng.integers(1, 3)), L=int(rng.integers(600, 3000)), E=int(rng.integers(1, 200)),
         N=int(rng.integers(1, 17)), dtype=str(rng.choice(["f32", "bf16"])), u=N01, delta=("normal", -1.0, 0.8),
         z=N01 if rng.integers(2) else None, B=N01, C=N01, D=N01, delta_bias=None, softplus=True)
-    monkeypatch.setenv("SSM_SCAN_MIN_CHUNK", str(int(rng.choice([8, 16]))))
-    monkeypatch.setenv("SSM_SCAN_TARGET_WAVES", "100000")
+    tune = {"path": "chunked", "min_chunk": int(rng.choice([8, 16])), "target_waves": 100000}
     x = to_device(workloads.make_scan_inputs(w, seed=seed))
     h0 = torch.randn((w.b, w.E, w.N), generator=torch.Generator().manual_seed(seed)).cuda()
     say(f"sweep chain seed={seed}: b{w.b} L{w.L} E{w.E} N{w.N} {w.dtype} "
-        f"plan={ssm.ssm_scan_plan(w.b, w.L, w.E, w.N, w.dtype)}")
+        f"plan={ssm.ssm_scan_plan(w.b, w.L, w.E, w.N, w.dtype, tuning=tune)}")
     y, last = ssm.ssm_scan_fwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
-                               x["softplus"], initial_state=h0)
+                               x["softplus"], initial_state=h0, tuning=tune)
     torch.cuda.synchronize()
     y_ref, last_ref = oracle.scan(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
                                   x["softplus"], h0=h0)
@@ -169,7 +167,7 @@ def test_backward_sweep(seed):
 
 
 @pytest.mark.parametrize("seed", range(8))
-def test_saved_states_sweep(seed, monkeypatch):
+def test_saved_states_sweep(seed):
     """ssm_scan_fwd_save then ssm_scan_bwd_saved on random shapes, the forward cut into random chunks."""
     import torch
 
@@ -181,8 +179,7 @@ def test_saved_states_sweep(seed, monkeypatch):
         N=int(rng.integers(1, 17)), dtype=str(rng.choice(["f32", "bf16"])), u=N01, delta=("normal", -1.0, 0.8),
         z=N01 if rng.integers(2) else None, B=N01, C=N01, D=N01 if rng.integers(2) else None,
         delta_bias=("normal", 0.0, 0.3) if rng.integers(2) else None, softplus=True)
-    monkeypatch.setenv("SSM_SCAN_MIN_CHUNK", str(int(rng.choice([8, 24, 40, 72, 136]))))
-    monkeypatch.setenv("SSM_SCAN_TARGET_WAVES", "100000")
+    tune = {"path": "chunked", "min_chunk": int(rng.choice([8, 24, 40, 72, 136])), "target_waves": 100000}
     x = to_device(workloads.make_scan_inputs(w, seed=seed))
     gen = torch.Generator().manual_seed(seed)
     dy = torch.randn(x["u"].shape, generator=gen).to(x["u"].dtype).cuda()
@@ -190,9 +187,9 @@ def test_saved_states_sweep(seed, monkeypatch):
     dlast = torch.randn((w.b, w.E, w.N), generator=gen).cuda() if rng.integers(2) else None
     say(f"sweep saved seed={seed}: b{w.b} L{w.L} E{w.E} N{w.N} {w.dtype} z={w.z is not None} D={w.D is not None} "
         f"bias={w.delta_bias is not None} h0={h0 is not None} dlast={dlast is not None} "
-        f"plan={ssm.ssm_scan_plan(w.b, w.L, w.E, w.N, w.dtype)}")
+        f"plan={ssm.ssm_scan_plan(w.b, w.L, w.E, w.N, w.dtype, tuning=tune)}")
     y, last, saved = ssm.ssm_scan_fwd_save(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"],
-                                           x["delta_bias"], True, initial_state=h0)
+                                           x["delta_bias"], True, initial_state=h0, tuning=tune)
     g = ssm.ssm_scan_bwd_saved(x["u"], x["delta"], x["A"], x["B"], x["C"], dy, saved, x["D"], x["z"],
                                x["delta_bias"], True, initial_state=h0, d_last_state=dlast)
     torch.cuda.synchronize()
