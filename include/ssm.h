@@ -12,6 +12,7 @@
  *                                     the training form: the forward keeps the state
  *                                     every SSM_SAVE_INTERVAL steps for the backward
  *   ssm_scan_fwd_tuned                the forward with its form and split chosen by the caller
+ *   ssm_scan_fwd_noalloc              the forward for callers that cannot allocate device memory
  *   ssm_ssd_fwd                       the scan with a scalar transition per head
  *   ssm_conv_fwd, ssm_conv_update     the causal depthwise convolution + SiLU before
  *                                     the scan, and its token step
@@ -90,7 +91,8 @@ typedef enum {
   SSM_ERR_UNSUPPORTED_N = -4, /* N outside the supported range (1..16; ssm_ssd_fwd: 16..128 in steps of 16) */
   SSM_ERR_ALIGN = -5,         /* an array is not aligned to its element size */
   SSM_ERR_HIP = -6,           /* HIP launch / allocation failure */
-  SSM_ERR_PLAN = -7           /* an ssm_scan_tuning value is invalid or does not apply to the call */
+  SSM_ERR_PLAN = -7,          /* an ssm_scan_tuning value is invalid or does not apply to the call */
+  SSM_ERR_SCRATCH = -8        /* ssm_scan_fwd_noalloc: the call needs more than SSM_NOALLOC_SCRATCH_BYTES */
 } ssm_status;
 
 /*
@@ -223,6 +225,37 @@ SSM_API int ssm_scan_fwd_tuned(const void* u, const void* delta, const float* A,
                                const float* initial_state, void* y, float* last_state, float* saved_states,
                                const ssm_scan_tuning* tuning, int64_t b, int64_t L, int64_t E, int64_t N, int dtype,
                                void* stream);
+
+/*
+ * Size of the fixed device buffer of ssm_scan_fwd_noalloc (128 MiB).
+ */
+#define SSM_NOALLOC_SCRATCH_BYTES (128ll << 20)
+
+/*
+ * ssm_scan_fwd_from for callers that cannot allocate device memory: code
+ * under HIP graph capture, serving loops, harnesses that forbid hipMalloc.
+ * It runs the same plan as ssm_scan_fwd_from (same kernels, same results),
+ * but a scan in the chunked form cut into several chunks takes its workspace
+ * (chunk aggregates, chunk step sums, float copies of bf16 B / C rows) from a
+ * buffer of SSM_NOALLOC_SCRATCH_BYTES that the library holds in device memory
+ * on every GPU it runs on until the process ends; no call allocates or frees
+ * device memory.  The single-pass form and one-chunk scans need no workspace.
+ *
+ * The buffer is shared by every call on one GPU and keeps the last call's
+ * contents (no call reads a part of it before writing that part): calls on one
+ * GPU whose executions overlap (different streams, or threads enqueueing
+ * concurrently without ordering their streams) race on it and must be
+ * serialised by the caller.
+ *
+ * Arguments, results and errors as ssm_scan_fwd_from, plus SSM_ERR_SCRATCH
+ * when the plan's workspace exceeds SSM_NOALLOC_SCRATCH_BYTES (then nothing
+ * is enqueued).  At the long-sequence size (b1 L65536 E5120 N16 bf16) the
+ * workspace is 98 MB.
+ */
+SSM_API int ssm_scan_fwd_noalloc(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                                 const float* D, const void* z, const float* delta_bias, int softplus,
+                                 const float* initial_state, void* y, float* last_state, int64_t b, int64_t L,
+                                 int64_t E, int64_t N, int dtype, void* stream);
 
 /*
  * One recurrent step for every (b, e) -- the SSM half of the decode step of

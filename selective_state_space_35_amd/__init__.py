@@ -15,6 +15,10 @@ Functions (same names as the C entry points):
   ``tuning`` (a dict with keys ``path`` in "auto" / "chunked" /
   "single_pass", ``min_chunk``, ``target_waves``) selects the C entry point
   ``ssm_scan_fwd_tuned``
+* ``ssm_scan_fwd_noalloc(u, delta, A, B, C, D=None, z=None, delta_bias=None,
+  softplus=False, initial_state=None, y=None, last_state=None)`` ->
+  ``(y, last_state)``: the same scan with the library's fixed workspace buffer
+  (no device allocation in the library)
 * ``ssm_scan_plan(b, L, E, N, dtype="bf16", tuning=None)`` ->
   ``(path, chunk_len, n_chunks)``: how the forward runs at that size
 * ``ssm_state_update(state, x, delta, A, B, C, D=None, z=None,
@@ -45,7 +49,7 @@ import ctypes
 import os
 
 __all__ = [
-    "ssm_scan_fwd", "ssm_scan_fwd_from", "ssm_scan_bwd", "ssm_ssd_fwd", "ssm_state_update", "ssm_conv_fwd", "ssm_conv_update", "ssm_scan_plan", "ssm_profile_enable", "ssm_profile_read",
+    "ssm_scan_fwd", "ssm_scan_fwd_from", "ssm_scan_fwd_noalloc", "ssm_scan_bwd", "ssm_ssd_fwd", "ssm_state_update", "ssm_conv_fwd", "ssm_conv_update", "ssm_scan_plan", "ssm_profile_enable", "ssm_profile_read",
     "ssm_status_string", "library_path", "SSMError", "ScanTuning", "SCAN_PATHS",
     "SSM_F32", "SSM_BF16", "load_library",
 ]
@@ -115,6 +119,8 @@ def load_library():
     lib.ssm_scan_fwd_from.argtypes = [_vp] * 8 + [_int, _vp, _vp, _vp] + [_i64] * 4 + [_int, _vp]
     lib.ssm_scan_fwd_save.restype = _int
     lib.ssm_scan_fwd_save.argtypes = [_vp] * 8 + [_int, _vp, _vp, _vp, _vp] + [_i64] * 4 + [_int, _vp]
+    lib.ssm_scan_fwd_noalloc.restype = _int
+    lib.ssm_scan_fwd_noalloc.argtypes = [_vp] * 8 + [_int, _vp, _vp, _vp] + [_i64] * 4 + [_int, _vp]
     lib.ssm_scan_fwd_tuned.restype = _int
     lib.ssm_scan_fwd_tuned.argtypes = ([_vp] * 8 + [_int, _vp, _vp, _vp, _vp, ctypes.POINTER(ScanTuning)] +
                                        [_i64] * 4 + [_int, _vp])
@@ -251,19 +257,9 @@ def saved_states_shape(b, L, E, N):
     return (b, max((L + SAVE_INTERVAL - 1) // SAVE_INTERVAL - 1, 0), E, N)
 
 
-def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=False, y=None,
-                 last_state=None, return_last_state=True, initial_state=None, saved_states=None, tuning=None):
-    """Selective scan forward on the GPU.  Returns ``(y, last_state)`` (last_state None if not requested).
-
-    ``initial_state`` [b, E, N] float32 continues the recurrence from that state
-    (the C entry point ``ssm_scan_fwd_from``); None starts from zero.  A given
-    ``saved_states`` buffer (``saved_states_shape``, float32) receives the state
-    every 64 steps (the C entry point ``ssm_scan_fwd_save``).  ``tuning`` (dict
-    or ScanTuning) fixes the form and split (the C entry point ``ssm_scan_fwd_tuned``).
-    """
-    import torch
-
-    lib = load_library()
+def _scan_outputs(torch, u, delta, A, B, C, D, z, delta_bias, y, last_state, return_last_state, initial_state,
+                  saved_states):
+    """Checks the forward's tensors; returns (b, L, E, N, dtype code, device, y, last_state)."""
     if not isinstance(u, torch.Tensor) or u.dim() != 3:
         raise ValueError("u must be a [b, L, E] tensor")
     device = u.device
@@ -296,6 +292,24 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=Fa
         raise ValueError("initial_state must not be the last_state buffer")
     if saved_states is not None:
         _check(torch, "saved_states", saved_states, saved_states_shape(b, L, E, N), torch.float32, device)
+    return b, L, E, N, code, device, y, last_state
+
+
+def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=False, y=None,
+                 last_state=None, return_last_state=True, initial_state=None, saved_states=None, tuning=None):
+    """Selective scan forward on the GPU.  Returns ``(y, last_state)`` (last_state None if not requested).
+
+    ``initial_state`` [b, E, N] float32 continues the recurrence from that state
+    (the C entry point ``ssm_scan_fwd_from``); None starts from zero.  A given
+    ``saved_states`` buffer (``saved_states_shape``, float32) receives the state
+    every 64 steps (the C entry point ``ssm_scan_fwd_save``).  ``tuning`` (dict
+    or ScanTuning) fixes the form and split (the C entry point ``ssm_scan_fwd_tuned``).
+    """
+    import torch
+
+    lib = load_library()
+    b, L, E, N, code, device, y, last_state = _scan_outputs(torch, u, delta, A, B, C, D, z, delta_bias, y, last_state,
+                                                            return_last_state, initial_state, saved_states)
     t = _tuning(tuning)
     if t is not None:
         with _on(torch, device):
@@ -323,6 +337,24 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=Fa
                                            _ptr(delta_bias), int(bool(softplus)), _ptr(initial_state), _ptr(y),
                                            _ptr(last_state), b, L, E, N, code, _stream_of(torch, device))
     _raise_on("ssm_scan_fwd" if initial_state is None else "ssm_scan_fwd_from", status)
+    return y, last_state
+
+
+def ssm_scan_fwd_noalloc(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=False, initial_state=None,
+                         y=None, last_state=None, return_last_state=True):
+    """``ssm_scan_fwd_from`` whose library side allocates no device memory (the C entry point
+    ``ssm_scan_fwd_noalloc``): a workspace comes from the library's fixed buffer.  The outputs y and
+    last_state are the caller's; pass them to keep this call free of allocations on the PyTorch side too."""
+    import torch
+
+    lib = load_library()
+    b, L, E, N, code, device, y, last_state = _scan_outputs(torch, u, delta, A, B, C, D, z, delta_bias, y, last_state,
+                                                            return_last_state, initial_state, None)
+    with _on(torch, device):
+        status = lib.ssm_scan_fwd_noalloc(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                          _ptr(delta_bias), int(bool(softplus)), _ptr(initial_state), _ptr(y),
+                                          _ptr(last_state), b, L, E, N, code, _stream_of(torch, device))
+    _raise_on("ssm_scan_fwd_noalloc", status)
     return y, last_state
 
 

@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libssm.so")
 CALIB_SRC = os.path.join(PKG, "calib", "ssm_calib.hip")
 CALIB_LIB = os.path.join(PKG, "libssm_calib.so")
-SOURCES = ["ssm_kernels.hip", "ssm_fused.hip", "ssm_conv.hip", "ssm_bwd.hip", "ssm_ssd.hip", "ssm_api.hip", "ssm_profile.hip"]
+SOURCES = ["ssm_kernels.hip", "ssm_fused.hip", "ssm_conv.hip", "ssm_bwd.hip", "ssm_ssd.hip", "ssm_api.hip", "ssm_profile.hip",
+           "ssm_noalloc.hip"]
 ARCH = os.environ.get("SSM_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

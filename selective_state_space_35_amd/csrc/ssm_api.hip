@@ -45,6 +45,10 @@ int64_t saved_count(int64_t b, int64_t L, int64_t E, int64_t N) {
   return b * ((L + ssm::kSaveEvery - 1) / ssm::kSaveEvery - 1) * E * N;
 }
 
+int prepare_scan(const void* u, const void* delta, const float* A, const void* B, const void* C, const float* D,
+                 const void* z, const float* delta_bias, int softplus, const float* initial_state, void* y,
+                 float* last_state, float* saved, const ssm_scan_tuning* tuning, int64_t b, int64_t L, int64_t E,
+                 int64_t N, int dtype, void* stream, ssm::ScanArgs* a, ssm::ScanPlan* pl);
 int scan_fwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C, const float* D,
                   const void* z, const float* delta_bias, int softplus, const float* initial_state, void* y,
                   float* last_state, float* saved, const ssm_scan_tuning* tuning, int64_t b, int64_t L, int64_t E,
@@ -98,6 +102,31 @@ int ssm_scan_fwd_tuned(const void* u, const void* delta, const float* A, const v
                        tuning, b, L, E, N, dtype, stream);
 }
 
+int ssm_scan_fwd_noalloc(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                         const float* D, const void* z, const float* delta_bias, int softplus,
+                         const float* initial_state, void* y, float* last_state, int64_t b, int64_t L, int64_t E,
+                         int64_t N, int dtype, void* stream) {
+  ssm::ScanArgs a{};
+  ssm::ScanPlan pl{};
+  int st = prepare_scan(u, delta, A, B, C, D, z, delta_bias, softplus, initial_state, y, last_state, nullptr, nullptr,
+                        b, L, E, N, dtype, stream, &a, &pl);
+  if (st != SSM_OK || b == 0 || E == 0) return st;
+  if (L == 0) return hip_status(ssm::launch_scan(a));  // no workspace: the last state only
+  int n_cu = 0;
+  hipError_t err = ssm::device_cu_count(&n_cu);
+  if (err != hipSuccess) return hip_status(err);
+  ssm::FusedPlan fp;
+  if (ssm::choose_path(a, pl, n_cu, &fp) == ssm::kPathSinglePass) return hip_status(ssm::launch_scan(a));
+  const size_t need = ssm::chunked_workspace_bytes(a, pl);
+  if (need > ssm::kScratchBytes) return SSM_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (need > 0) {
+    err = ssm::scratch_address(&ws);
+    if (err != hipSuccess) return hip_status(err);
+  }
+  return hip_status(ssm::launch_scan(a, ws, ssm::kScratchBytes));
+}
+
 }  // extern "C"
 
 namespace {
@@ -115,10 +144,11 @@ int to_tuning(const ssm_scan_tuning* t, ssm::ScanTuning* out) {
   return SSM_OK;
 }
 
-int scan_fwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C, const float* D,
-                  const void* z, const float* delta_bias, int softplus, const float* initial_state, void* y,
-                  float* last_state, float* saved, const ssm_scan_tuning* tuning, int64_t b, int64_t L, int64_t E,
-                  int64_t N, int dtype, void* stream) {
+// Checks the arguments of a forward scan and fills *a and *pl.  Enqueues nothing.
+int prepare_scan(const void* u, const void* delta, const float* A, const void* B, const void* C, const float* D,
+                 const void* z, const float* delta_bias, int softplus, const float* initial_state, void* y,
+                 float* last_state, float* saved, const ssm_scan_tuning* tuning, int64_t b, int64_t L, int64_t E,
+                 int64_t N, int dtype, void* stream, ssm::ScanArgs* a, ssm::ScanPlan* pl) {
   int st = check_sizes(b, L, E, N, dtype);
   if (st != SSM_OK) return st;
   ssm::ScanTuning tune;
@@ -134,18 +164,28 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A, const void* 
   for (const void* p : fl)
     if (p && !aligned(p, 4)) return SSM_ERR_ALIGN;
   // the grid of the chunked form is b * ceil(E / 64) * chunks workgroups
-  const ssm::ScanPlan pl = ssm::plan_scan(b, L, E, int(es), tune);
+  *pl = ssm::plan_scan(b, L, E, int(es), tune);
   int64_t grid = 0;
-  if (pl.chunk_len <= 0 || !mul_ok(b * pl.e_blocks, pl.n_chunks, &grid) || grid > INT32_MAX) return SSM_ERR_DIM;
+  if (pl->chunk_len <= 0 || !mul_ok(b * pl->e_blocks, pl->n_chunks, &grid) || grid > INT32_MAX) return SSM_ERR_DIM;
+  a->u = u; a->delta = delta; a->A = A; a->B = B; a->C = C; a->D = D; a->z = z; a->bias = delta_bias;
+  a->softplus = softplus ? 1 : 0; a->y = y; a->last_state = last_state; a->h0 = initial_state;
+  a->saved = saved_count(b, L, E, N) > 0 ? saved : nullptr;
+  a->b = b; a->L = L; a->E = E; a->N = N; a->dtype = dtype;
+  a->stream = static_cast<hipStream_t>(stream);
+  a->tune = tune;
+  return SSM_OK;
+}
 
-  ssm::ScanArgs a;
-  a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias;
-  a.softplus = softplus ? 1 : 0; a.y = y; a.last_state = last_state; a.h0 = initial_state;
-  a.saved = saved_count(b, L, E, N) > 0 ? saved : nullptr;
-  a.b = b; a.L = L; a.E = E; a.N = N; a.dtype = dtype;
-  a.stream = static_cast<hipStream_t>(stream);
-  a.tune = tune;
-  if (tune.path == ssm::kPathSinglePass && L > 0) {  // asked for explicitly: it has to apply
+int scan_fwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C, const float* D,
+                  const void* z, const float* delta_bias, int softplus, const float* initial_state, void* y,
+                  float* last_state, float* saved, const ssm_scan_tuning* tuning, int64_t b, int64_t L, int64_t E,
+                  int64_t N, int dtype, void* stream) {
+  ssm::ScanArgs a{};
+  ssm::ScanPlan pl{};
+  int st = prepare_scan(u, delta, A, B, C, D, z, delta_bias, softplus, initial_state, y, last_state, saved, tuning, b,
+                        L, E, N, dtype, stream, &a, &pl);
+  if (st != SSM_OK || b == 0 || E == 0) return st;
+  if (a.tune.path == ssm::kPathSinglePass && L > 0) {  // asked for explicitly: it has to apply
     int n_cu = 0;
     hipError_t err = ssm::device_cu_count(&n_cu);
     if (err != hipSuccess) return hip_status(err);
@@ -375,6 +415,9 @@ const char* ssm_status_string(int status) {
     case SSM_ERR_UNSUPPORTED_N:
       return "state size N outside the entry point's range (1..16; ssm_ssd_fwd: 16..128 in steps of 16)";
     case SSM_ERR_PLAN: return "the requested scan form or tuning does not apply to this call";
+    case SSM_ERR_SCRATCH:
+      return "the call needs more workspace than the fixed buffer of ssm_scan_fwd_noalloc holds "
+             "(SSM_NOALLOC_SCRATCH_BYTES)";
     case SSM_ERR_ALIGN: return "array not aligned to its element size";
     case SSM_ERR_HIP: return "HIP launch or allocation failed";
     default: return "unknown status";

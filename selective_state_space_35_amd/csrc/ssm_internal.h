@@ -189,6 +189,11 @@ hipError_t device_cu_count(int* n_cu);
 // Bytes of workspace the chunked form of this scan needs (0 for one chunk).
 size_t chunked_workspace_bytes(const ScanArgs& a, const ScanPlan& pl);
 
+// Size of the fixed device buffer of ssm_scan_fwd_noalloc (ssm_noalloc.hip).
+constexpr size_t kScratchBytes = size_t(128) << 20;
+// Device address of the current device's copy of that buffer (taken once per device).
+hipError_t scratch_address(void** out);
+
 // Both return hipSuccess or the first HIP error met while enqueueing.  A cut
 // chunked scan takes its workspace from `workspace` when given (at least
 // chunked_workspace_bytes), else from the stream-ordered pool.

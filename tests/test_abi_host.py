@@ -106,6 +106,20 @@ def test_scan_from_validation(lib):
     assert f(None, b=0) == OK
 
 
+def test_scan_noalloc_validation(lib):
+    f = lambda **kw: lib.ssm_scan_fwd_noalloc(kw.get("u", FAKE), FAKE, FAKE, FAKE, FAKE, None, None, None, 1,
+                                              kw.get("h0", None), kw.get("y", FAKE), None, kw.get("b", 1), 8, 64,
+                                              kw.get("N", 16), kw.get("dtype", 0), None)
+    assert f(dtype=5) == ERR_DTYPE
+    assert f(N=17) == ERR_N
+    assert f(u=None) == ERR_NULL
+    assert f(y=None) == ERR_NULL
+    assert f(h0=FAKE + 2) == ERR_ALIGN
+    assert f(b=-1) == ERR_DIM
+    assert f(b=0, u=None, y=None) == OK
+    assert "SSM_NOALLOC_SCRATCH_BYTES" in ssm.ssm_status_string(-8)
+
+
 def test_update_validation(lib):
     assert update(lib, dtype=7) == ERR_DTYPE
     assert update(lib, b=-2) == ERR_DIM
