@@ -12,12 +12,12 @@ SRC = os.path.join(HERE, "ssm_oracle.c")
 LIB = os.path.join(HERE, "libssm_oracle.so")
 
 
-def build(verbose: bool = False, out: str = LIB, mutation: int = 0) -> str:
-    """Build the oracle library.  ``mutation`` > 0 plants a numbered mistake (mutation tests only)."""
+def build(verbose: bool = False, out: str = LIB, src: str = SRC) -> str:
+    """Build the oracle library from ``src`` (another source only in the mutation tests)."""
     cmd = [
         "gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
-        "-ffp-contract=off", "-fno-fast-math", f"-DORACLE_MUTATION={int(mutation)}",
-        "-o", out + ".tmp", SRC, "-lm",
+        "-ffp-contract=off", "-fno-fast-math",
+        "-o", out + ".tmp", src, "-lm",
     ]
     if verbose:
         print(" ".join(cmd), flush=True)

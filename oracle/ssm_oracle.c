@@ -56,30 +56,18 @@
 #include <math.h>
 #include <pthread.h>
 
-/* ORACLE_MUTATION plants one deliberate mistake (test builds only; the
- * default 0 is the oracle).  The mutation test compiles each variant on the
- * CPU and requires every one of them to fail at least one pin. */
-#ifndef ORACLE_MUTATION
-#define ORACLE_MUTATION 0
-#endif
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
 /* softplus(x) = log(1 + e^x), written so neither branch overflows. */
 static double oracle_softplus(double x) {
-#if ORACLE_MUTATION == 9
-  if (x > 0.0) return x + log1p(exp(x));
-#endif
   if (x > 0.0) return x + log1p(exp(-x));
   return log1p(exp(x));
 }
 
 /* silu(z) = z * sigmoid(z) = z / (1 + e^{-z}). */
 static double oracle_silu(double z) {
-#if ORACLE_MUTATION == 6
-  return 1.0 / (1.0 + exp(-z));
-#endif
   return z / (1.0 + exp(-z));
 }
 
@@ -100,40 +88,15 @@ static void scan_chain(const scan_job* j, int64_t bi, int64_t e, double* h) {
     const double x = j->u[xe];
     double d = j->delta[xe] + (j->bias ? j->bias[e] : 0.0);
     if (j->softplus) d = oracle_softplus(d);
-#if ORACLE_MUTATION == 3
-    if (j->softplus && j->bias) d = oracle_softplus(j->delta[xe]) + j->bias[e];
-#endif
     double acc = 0.0;
     for (int64_t n = 0; n < N; n++) {
-#if ORACLE_MUTATION == 4
-      const double a = exp(-d * j->A[e * N + n]);
-#else
       const double a = exp(d * j->A[e * N + n]);
-#endif
-#if ORACLE_MUTATION == 5
-      const double w = j->B[xn + n] * x;
-#elif ORACLE_MUTATION == 7
-      const double w = d * j->B[xn + (N - 1 - n)] * x;
-#else
       const double w = d * j->B[xn + n] * x;
-#endif
-#if ORACLE_MUTATION == 1
-      acc += j->C[xn + n] * h[n];
-      h[n] = a * h[n] + w;
-#elif ORACLE_MUTATION == 8
-      h[n] = a * h[n] + w;
-      acc += j->C[(t > 0 ? xn - N : xn) + n] * h[n];
-#else
       h[n] = a * h[n] + w;
       acc += j->C[xn + n] * h[n];
-#endif
       if (j->states) j->states[((bi * L + t) * E + e) * N + n] = h[n];
     }
-#if ORACLE_MUTATION == 2
-    double yv = acc;
-#else
     double yv = acc + (j->D ? j->D[e] * x : 0.0);
-#endif
     if (j->z) yv *= oracle_silu(j->z[xe]);
     j->y[xe] = yv;
   }
@@ -213,13 +176,8 @@ static void* update_worker(void* arg) {
     double acc = 0.0;
     for (int64_t n = 0; n < N; n++) {
       double* s = &j->state[c * N + n];
-#if ORACLE_MUTATION == 10
-      *s = exp(d * j->A[e * N + n]) * *s + d * j->C[bi * N + n] * x;
-      acc += j->B[bi * N + n] * *s;
-#else
       *s = exp(d * j->A[e * N + n]) * *s + d * j->B[bi * N + n] * x;
       acc += j->C[bi * N + n] * *s;
-#endif
     }
     double yv = acc + (j->D ? j->D[e] * x : 0.0);
     if (j->z) yv *= oracle_silu(j->z[c]);
@@ -284,11 +242,7 @@ int oracle_conv_fwd(const double* v, const double* q, const double* cb, const do
           else sample = state_in ? state_in[(bi * E + c) * K + (K + s)] : 0.0;
           acc += q[c * K + k] * sample;
         }
-#if ORACLE_MUTATION == 11
-        x[(bi * L + t) * E + c] = acc;
-#else
         x[(bi * L + t) * E + c] = oracle_silu(acc);
-#endif
       }
       if (state_out) {
         for (int64_t k = 0; k < K; k++) {
@@ -315,11 +269,7 @@ int oracle_conv_update(double* state, const double* v, const double* q, const do
       for (int64_t k = 0; k + 1 < K; k++) st[k] = st[k + 1];
       st[K - 1] = v[bi * E + c];
       double acc = cb ? cb[c] : 0.0;
-#if ORACLE_MUTATION == 12
-      for (int64_t k = 0; k < K; k++) acc += q[c * K + (K - 1 - k)] * st[k];
-#else
       for (int64_t k = 0; k < K; k++) acc += q[c * K + k] * st[k];
-#endif
       x[bi * E + c] = oracle_silu(acc);
     }
   }
@@ -378,9 +328,6 @@ static void bwd_chain(const bwd_job* j, int64_t bi, int64_t e, double* hist, dou
   }
   /* backward */
   for (int64_t n = 0; n < N; n++) X[n] = j->dlast ? j->dlast[(bi * E + e) * N + n] : 0.0;
-#if ORACLE_MUTATION == 19
-  for (int64_t n = 0; n < N; n++) X[n] = 0.0;
-#endif
   for (int64_t t = L - 1; t >= 0; t--) {
     const int64_t xe = (bi * L + t) * E + e, xn = (bi * L + t) * N;
     const double x = j->u[xe];
@@ -389,11 +336,7 @@ static void bwd_chain(const bwd_job* j, int64_t bi, int64_t e, double* hist, dou
     double dq = j->dy[xe];
     if (j->z) {
       const double zz = j->z[xe], sg = oracle_sigmoid(zz);
-#if ORACLE_MUTATION == 17
-      j->dz[xe] = j->dy[xe] * q[t] * sg;
-#else
       j->dz[xe] = j->dy[xe] * q[t] * sg * (1.0 + zz * (1.0 - sg));
-#endif
       dq *= oracle_silu(zz);
     }
     double dut = 0.0, dd = 0.0;
@@ -405,36 +348,16 @@ static void bwd_chain(const bwd_job* j, int64_t bi, int64_t e, double* hist, dou
       const double G = X[n] + dq * j->C[xn + n];
       const double h_t = hist[(t + 1) * N + n], h_prev = hist[t * N + n];
       const double a = exp(d * j->A[e * N + n]);
-#if ORACLE_MUTATION == 16
-      j->dC[xn + n] += dq * h_prev;
-#else
       j->dC[xn + n] += dq * h_t;
-#endif
-#if ORACLE_MUTATION == 18
-      j->dB[xn + n] += G * x;
-#else
       j->dB[xn + n] += G * d * x;
-#endif
       dut += G * d * j->B[xn + n];
-#if ORACLE_MUTATION == 13
-      const double ha = h_t * a;
-#else
       const double ha = h_prev * a;
-#endif
       dd += G * x * j->B[xn + n] + G * ha * j->A[e * N + n];
       j->dA[e * N + n] += G * ha * d;
-#if ORACLE_MUTATION == 14
-      X[n] = G;
-#else
       X[n] = a * G;
-#endif
     }
     j->du[xe] = dut;
-#if ORACLE_MUTATION == 15
-    const double ddelta = dd;
-#else
     const double ddelta = j->softplus ? dd * oracle_sigmoid(raw) : dd;
-#endif
     j->ddelta[xe] = ddelta;
     if (j->bias) j->dbias[e] += ddelta;
   }
