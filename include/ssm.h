@@ -49,7 +49,7 @@
  *
  * Sizes.  b (batch), L (sequence length), E (expanded channels) and
  * N (state size per channel).  Supported: 1 <= N <= 16 (ssm_ssd_fwd: N a
- * multiple of 16 up to 128); b, L, E >= 0.  b == 0 or E == 0 is a no-op.
+ * multiple of 16 up to 128); 0 <= b, L, E <= 2^48.  b == 0 or E == 0 is a no-op.
  * L == 0 writes a zero last_state (or the incoming state, where one is given).
  *
  * Alignment.  Every array must be aligned to its element size; float arrays
@@ -86,7 +86,7 @@ typedef enum {
 typedef enum {
   SSM_OK = 0,
   SSM_ERR_NULL = -1,          /* a required pointer is NULL */
-  SSM_ERR_DIM = -2,           /* a negative size, or a size product that overflows */
+  SSM_ERR_DIM = -2,           /* a negative size, a size above 2^48, or a size product that overflows */
   SSM_ERR_DTYPE = -3,         /* dtype is not an ssm_dtype value */
   SSM_ERR_UNSUPPORTED_N = -4, /* N outside the supported range (1..16; ssm_ssd_fwd: 16..128 in steps of 16) */
   SSM_ERR_ALIGN = -5,         /* an array is not aligned to its element size */

@@ -87,10 +87,15 @@ def use_library(path=None):
 
 
 def default_threads() -> int:
-    """Host threads for the oracle: OMP_NUM_THREADS if set, else the CPU count, at most 16."""
+    """Host threads for the oracle: OMP_NUM_THREADS if set (the share of the host a job is given), else
+    every core this process may run on."""
     env = os.environ.get("OMP_NUM_THREADS")
-    n = int(env) if env and env.isdigit() else (os.cpu_count() or 1)
-    return max(1, min(n, 16))
+    if env and env.isdigit() and int(env) > 0:
+        return int(env)
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except (AttributeError, OSError):
+        return max(1, os.cpu_count() or 1)
 
 
 def to_f64(x):

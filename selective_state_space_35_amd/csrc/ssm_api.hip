@@ -27,10 +27,15 @@ bool aligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % 
 
 bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
 
+// Every size is at most 2^48 on its own (any real tensor is far smaller), so the plans' sums and
+// rounded divisions cannot overflow even where another size is zero and the products are.
+constexpr int64_t kMaxSize = int64_t(1) << 48;
+bool size_ok(int64_t v) { return v >= 0 && v <= kMaxSize; }
+
 // Common size / dtype checks.  `elems` receives b*L*E (or b*E).
 int check_sizes(int64_t b, int64_t L, int64_t E, int64_t N, int dtype) {
   if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_DTYPE;
-  if (b < 0 || L < 0 || E < 0 || N < 0) return SSM_ERR_DIM;
+  if (!size_ok(b) || !size_ok(L) || !size_ok(E) || N < 0) return SSM_ERR_DIM;
   if (N < 1 || N > 16) return SSM_ERR_UNSUPPORTED_N;
   int64_t t = 0;
   if (!mul_ok(b, L, &t) || !mul_ok(t, E, &t) || !mul_ok(t, 4, &t)) return SSM_ERR_DIM;
@@ -298,7 +303,7 @@ int ssm_ssd_fwd(const void* x, const void* delta, const float* A, const void* B,
                 float* last_state, int64_t b, int64_t L, int64_t H, int64_t P, int64_t N, int dtype, void* stream) {
   if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_DTYPE;
   if (dtype != SSM_BF16) return SSM_ERR_DTYPE;  // the matrix products take bf16 operands
-  if (b < 0 || L < 0 || H < 0 || P != ssm::ssd_head_dim()) return SSM_ERR_DIM;
+  if (!size_ok(b) || !size_ok(L) || !size_ok(H) || P != ssm::ssd_head_dim()) return SSM_ERR_DIM;
   if (H > ssm::ssd_max_channels() / P) return SSM_ERR_DIM;
   if (N < 16 || N > 128 || N % 16 != 0) return SSM_ERR_UNSUPPORTED_N;
   int64_t E = 0, t = 0;
@@ -363,7 +368,7 @@ int ssm_scan_plan(int64_t b, int64_t L, int64_t E, int64_t N, int dtype, const s
 int ssm_conv_fwd(const void* v, const float* q, const float* conv_bias, const void* state_in, void* x,
                  void* state_out, int64_t b, int64_t L, int64_t E, int64_t K, int dtype, void* stream) {
   if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_DTYPE;
-  if (b < 0 || L < 0 || E < 0 || K < 1 || K > ssm::kMaxConvK) return SSM_ERR_DIM;
+  if (!size_ok(b) || !size_ok(L) || !size_ok(E) || K < 1 || K > ssm::kMaxConvK) return SSM_ERR_DIM;
   int64_t t = 0;
   if (!mul_ok(b, L, &t) || !mul_ok(t, E, &t) || !mul_ok(t, 4, &t)) return SSM_ERR_DIM;
   if (!mul_ok(b, E, &t) || !mul_ok(t, K, &t) || !mul_ok(t, 4, &t)) return SSM_ERR_DIM;
@@ -388,7 +393,7 @@ int ssm_conv_fwd(const void* v, const float* q, const float* conv_bias, const vo
 int ssm_conv_update(void* conv_state, const void* v, const float* q, const float* conv_bias, void* x, int64_t b,
                     int64_t E, int64_t K, int dtype, void* stream) {
   if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_DTYPE;
-  if (b < 0 || E < 0 || K < 1 || K > ssm::kMaxConvK) return SSM_ERR_DIM;
+  if (!size_ok(b) || !size_ok(E) || K < 1 || K > ssm::kMaxConvK) return SSM_ERR_DIM;
   int64_t t = 0;
   if (!mul_ok(b, E, &t) || !mul_ok(t, K, &t) || !mul_ok(t, 4, &t)) return SSM_ERR_DIM;
   if (b == 0 || E == 0) return SSM_OK;
