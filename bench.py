@@ -14,13 +14,14 @@ backward on the long workload, and the scan with a scalar transition per head
 
 Prints ONE JSON line on stdout:
   value        b*L*E elements per second over the timed steps
-  roofline     ALU roofline of the dominant kernel (scan_main): algorithmic fp32
-               VALU lane-slots of one pass (a transcendental counts 4) over its
-               duration, measured with HIP events on the launch stream over the
-               timed region, against the 78.6e12 slot/s issue peak; traffic (HBM
-               bytes per launch) from the committed rocprofv3 PMC summary when it
-               was taken on the current kernel source, else null
-  roofline_hbm the same kernel's algorithmic bytes over its duration vs 8 TB/s
+  roofline     ALU roofline of the dominant kernel (the main pass of the chunked form, or the single-pass
+               kernel): algorithmic VALU issue slots of one pass (one non-packed fp32 lane-op per slot, a
+               transcendental included) over its duration, measured with HIP events on the launch stream
+               over the timed region, against 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 3.93e13 slot/s;
+               `hbm` holds the HBM view of the same kernel and of the whole call (algorithmic bytes over
+               time vs 8 TB/s); traffic (L2-to-fabric bytes per launch) and VALU busy per kernel come from
+               the committed rocprofv3 summaries in profiles/ when they were taken on the current kernel
+               sources, else null
   cpu_baseline the fp64 oracle on a bounded channel sample of the same inputs
                (channels are independent chains), timed on the host cores
   configs      the tiny (b1 L64 E16 N4 fp32), block (b32 L512 E512 N16 fp32) and
@@ -30,7 +31,10 @@ Prints ONE JSON line on stdout:
                against a measured 1 GiB copy, ALU-issue fraction; the oracle's
                rate on 1 and on all host threads, and parity of the timed outputs
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Other modes: --alu-calibration (issue rates of single instruction kinds), --copy-calibration (a 1 GiB copy
+for the byte counters), --summarize RUN_ROOT (no GPU: profiles/ summaries from rocprofv3 output).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--workload long]
 """
 import argparse
 import hashlib
@@ -43,11 +47,21 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
-# fp32 VALU issue peak in lane-slots/s: 157.3 TFLOP/s of fp32 vector FMA = 78.6e12 FMA lane-ops/s
-# (256 CUs x 4 SIMDs x 32 lanes x 2.4 GHz).  A transcendental (exp2, log2, rcp) issues at a quarter
-# of that rate, so it occupies 4 slots.
-VALU_SLOT_PEAK = 256 * 4 * 32 * 2.4e9
-TRANS_SLOTS = 4
+# VALU issue peak in lane-slots/s: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 3.93e13.  A wave64 VALU
+# instruction holds a SIMD for 4 cycles; one slot is one non-packed fp32 lane-op (78.6 TFLOP/s of FMA;
+# the library is built with packed FP32 disabled, so 157.3 TFLOP/s, the packed rate, is out of reach).
+VALU_SLOT_PEAK = 256 * 4 * 16 * 2.4e9
+# Slots a v_exp_f32 (and the other fp32 transcendentals) takes: one, like any VALU instruction.  In the scan
+# kernels' mix (a fifth of the instructions transcendental) the long scan's main pass issues 5.30e8 wave64
+# VALU instructions in 976 us, 4.52 cycles each at 2.4 GHz: 88% of one instruction per 4 cycles per SIMD
+# (profiles/sq_scan_long.txt); two slots per transcendental would put that kernel at 103% of the peak.  The
+# standalone calibration kinds (profiles/alu_issue_rates.txt) bound the cost from above: an exp alone takes
+# 9.4 cycles, and beside 4 dependent-free FMAs it added 8.1.
+TRANS_SLOTS = 1
+# profile kinds of ssm_profile_read() -> the kernel symbol they time
+KIND_SYMBOL = {"chunk_aggregate": "scan_chunk_agg_kernel", "chunk_carry": "chain_kernel", "scan_main": "scan_main_kernel",
+               "scan_fused": "scan_fused_kernel", "widen_rows": "widen_rows_kernel", "state_update": "state_update_kernel",
+               "bwd_main": "bwd_main_kernel", "ssd_scan": "ssd_scan_kernel", "ssd_state": "ssd_state_kernel"}
 
 
 def log(*a):
@@ -67,10 +81,10 @@ def scan_bytes(b, L, E, N, s, gate=True, last_state=True):
 def scan_slots(b, L, E, N, softplus=True, gate=True, has_d=True, has_bias=False, bf16=True):
     """Algorithmic fp32 VALU lane-slots of one scan pass (the minimal single pass).
 
-    Per (t, e, n): d*A2 (1), exp2 (4), du*B (1), a*h + w (1), C*h + acc (1)          -> 8
-    Per (t, e):    delta + bias (1); softplus: 2 transcendentals + 4 VALU (12);
-                   d*u (1); D*u (1); silu gate: 2 transcendentals + 3 VALU, and the
-                   product (12); bf16 widening of each streamed input and rounding of y (1 each)
+    Per (t, e, n): d*A2 (1), exp2 (TRANS_SLOTS), du*B (1), a*h + w (1), C*h + acc (1)     -> 4 + TRANS_SLOTS
+    Per (t, e):    delta + bias (1); softplus: 2 transcendentals + 4 VALU; d*u (1); D*u (1);
+                   silu gate: 2 transcendentals + 3 VALU, and the product; bf16 widening of each
+                   streamed input and rounding of y (1 each)
     """
     per_te = 1  # d * u
     per_te += 1 if has_bias else 0
@@ -78,7 +92,7 @@ def scan_slots(b, L, E, N, softplus=True, gate=True, has_d=True, has_bias=False,
     per_te += 1 if has_d else 0
     per_te += 2 * TRANS_SLOTS + 4 if gate else 0
     per_te += (3 if gate else 2) + 1 if bf16 else 0
-    return b * L * E * (8 * N + per_te)
+    return b * L * E * ((4 + TRANS_SLOTS) * N + per_te)
 
 
 def update_bytes(b, E, N, s, gate=True):
@@ -116,36 +130,56 @@ def conv_update_bytes(b, E, K, s, bias=True):
     return 2 * b * E * K * s + 2 * b * E * s + E * K * 4 + (E * 4 if bias else 0)
 
 
+HASH_EXCLUDES = ("ssm_api.hip",)  # the C ABI's argument checks: no kernel, no launch shape
+
+
 def source_hash():
+    """sha256[:16] of every library source that builds a kernel or plans a launch (all of csrc/ but the argument
+    checks): a profile taken on other sources is stale."""
     h = hashlib.sha256()
-    for f in ("ssm_kernels.hip", "ssm_device.h"):
-        with open(os.path.join(ROOT, "selective_state_space_35_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    csrc = os.path.join(ROOT, "selective_state_space_35_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")) and f not in HASH_EXCLUDES:
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel, workload):
-    """HBM traffic per launch from profiles/traffic_<kernel>_<workload>.json if taken on this source."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+def load_profile(name):
+    """A committed profile summary (profiles/<name>.json) and whether it was taken on the current sources."""
+    path = os.path.join(ROOT, "profiles", f"{name}.json")
     if not os.path.exists(path):
-        return None, "no PMC summary"
+        return None, "no summary in profiles/"
     with open(path) as f:
         doc = json.load(f)
     if doc.get("source_hash") != source_hash():
-        return None, "kernel changed since the PMC counters were taken"
-    return doc.get("hbm_bytes_per_launch"), doc.get("note", "")
+        return None, "kernel sources changed since the counters were taken"
+    return doc, ""
 
 
-def cpu_model():
-    """The host CPU's model name (first processor in /proc/cpuinfo), or None."""
+def cpu_facts():
+    """The host as the CPU baseline sees it: model strings from /proc/cpuinfo, nproc, the cores this
+    process may run on, and OMP_NUM_THREADS (the share of the host a job is given, where set)."""
+    fields = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if ":" not in line:
+                    if fields:
+                        break  # the first processor's block is enough
+                    continue
+                k, v = (t.strip() for t in line.split(":", 1))
+                if k in ("vendor_id", "model name", "cpu family", "model", "stepping", "cpu MHz", "cache size",
+                         "siblings", "cpu cores"):
+                    fields[k] = v
     except OSError:
         pass
-    return None
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
+    return {"cpuinfo": fields, "nproc": os.cpu_count(), "affinity_cores": affinity,
+            "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS")}
 
 
 def copy_bandwidth(torch, dev, stream, nbytes=1 << 30, reps=10):
@@ -287,6 +321,31 @@ def measure_decode(ssm, torch, workloads, dev, stream, seed):
               "bytes_per_call": ub,
               "note": "the 84 MB fp32 state fits in the 256 MB Infinity Cache, so carried-state traffic "
                       "can be served from it; GB/s is algorithmic bytes over kernel time"}
+    # where the carried state comes from: the same calls with a 1 GiB buffer written between them (outside
+    # each call's event pair), which evicts the state from the Infinity Cache, so every call reads it from HBM
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    res, evi = [], []
+    for k in range(wd.steps):
+        for evicted, acc in ((False, res), (True, evi)):
+            if evicted:
+                flush.fill_(k & 0x7F)
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            ssm.ssm_state_update(st, xd["x"][k], xd["delta"][k], xd["A"], xd["B"][k], xd["C"][k], xd["D"],
+                                 xd["z"][k], xd["delta_bias"], xd["softplus"], y=yd)
+            a1.record(stream)
+            acc.append((a0, a1))
+    torch.cuda.synchronize()
+    med = lambda ev: sorted(1e3 * a.elapsed_time(b) for a, b in ev)[len(ev) // 2]
+    r_us, e_us = med(res), med(evi)
+    update["state_source"] = {
+        "resident_us_median": round(r_us, 3), "evicted_us_median": round(e_us, 3),
+        "resident_GBps": round(ub / (r_us * 1e-6) / 1e9, 1), "evicted_GBps": round(ub / (e_us * 1e-6) / 1e9, 1),
+        "evicted_hbm_frac": round(ub / (e_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        "note": "each call timed alone with an event pair: right after the previous call (state in the Infinity "
+                "Cache) and after a 1 GiB write that evicts it (state from HBM); the evicted rate is the HBM "
+                "figure, the difference is what the cache serves"}
+    del flush
 
     # one generation step of the block's kernels per token: the convolution token step, then the state
     # update on its output; eager launches against the same T tokens captured once in a HIP graph
@@ -430,8 +489,9 @@ def measure_backward(ssm, torch, dev, stream, x, w, steps, seed):
     return bwd
 
 
-def measure_ssd(ssm, torch, workloads, dev, stream, seed):
-    """ssm_ssd_fwd on the scalar-per-head workload, with its per-kernel split."""
+def measure_ssd(ssm, torch, workloads, dev, stream, seed, cpu=True):
+    """ssm_ssd_fwd on the scalar-per-head workload, with its per-kernel split; with ``cpu``, the fp64 oracle
+    checks the timed outputs on a sample of heads."""
     ws = workloads.SSD_LONG
     xs = workloads.make_ssd_inputs(ws, seed=seed, device=dev, backend="torch")
     ys = torch.empty_like(xs["x"])
@@ -462,6 +522,24 @@ def measure_ssd(ssm, torch, workloads, dev, stream, seed):
            "GBps": round(sb / (ssd_ms * 1e-3) / 1e9, 1), "matrix_TFLOPs": round(sf / (ssd_ms * 1e-3) / 1e12, 2),
            "kernels": {k: {"avg_us": round(1e3 * v[0] / v[1], 2), "launches": v[1]}
                        for k, v in prof.items() if v[1]}}
+    if cpu:  # heads are independent: the oracle on a head sample is exactly that sample of the oracle
+        import numpy as np
+
+        import oracle
+
+        rng = np.random.default_rng(seed + 3)
+        heads = sorted({0, ws.H - 1, *rng.choice(ws.H, size=2, replace=False).tolist()})
+        hs = torch.tensor(heads, device=dev)
+        ch = (hs[:, None] * ws.P + torch.arange(ws.P, device=dev)[None, :]).reshape(-1)
+        sel = lambda t, idx, dim: None if t is None else t.index_select(dim, idx)
+        c0 = time.perf_counter()
+        y_ref, l_ref = oracle.ssd(sel(xs["x"], ch, 2), sel(xs["delta"], hs, 2), sel(xs["A"], hs, 0), xs["B"],
+                                  xs["C"], sel(xs["D"], hs, 0), sel(xs["z"], ch, 2), sel(xs["delta_bias"], hs, 0),
+                                  xs["softplus"])
+        err = lambda g, r: float(np.max(np.abs(g - r) / (1 + np.abs(r))))
+        ssd["parity"] = {"y_max_normalised_error": err(oracle.to_f64(ys.index_select(2, ch)), y_ref),
+                         "last_state_max_normalised_error": err(oracle.to_f64(ls.index_select(1, ch)), l_ref),
+                         "bound": 2e-2, "heads_checked": heads, "oracle_seconds": round(time.perf_counter() - c0, 2)}
     log(f"[bench] ssd {ssd}")
     del xs, ys, ls
     return ssd
@@ -541,7 +619,9 @@ def measure_cpu_baseline(torch, dev, x, w, y, last, cpu_seconds):
     y_ref, last_ref = oracle.scan(*a, softplus=x["softplus"], threads=threads)
     cpu_s = time.perf_counter() - c0
     cpu = {"value": w.b * w.L * nch / cpu_s, "unit": "elem/s", "cores": threads, "kind": "oracle",
-           "cpu_model": cpu_model(), "seconds": round(cpu_s, 2),
+           "host": cpu_facts(), "seconds": round(cpu_s, 2),
+           "threads_note": "threads = OMP_NUM_THREADS where set (the host share given to the job), else every core "
+                           "the process may run on",
            "sample": f"{nch} of {w.E} channels (independent chains), full L={w.L}, b={w.b}; "
                      "fp64 sequential oracle, same inputs"}
     yg = oracle.to_f64(y.index_select(2, ch))
@@ -551,6 +631,204 @@ def measure_cpu_baseline(torch, dev, x, w, y, last, cpu_seconds):
               "bound": 2e-2, "channels_checked": nch}
     log(f"[bench] cpu baseline {cpu['value']:.3e} elem/s on {threads} threads; parity {parity}")
     return cpu, parity
+
+
+# ---------------------------------------------------------------------------------------------------
+# summaries of rocprofv3 output (run on any host, after the GPU run): profiles/*.txt and *.json
+# ---------------------------------------------------------------------------------------------------
+def _split(name):
+    """(symbol, symbol with template arguments) of a demangled kernel name: no namespace, no parameters."""
+    n = name.replace("(anonymous namespace)::", "")
+    if n.startswith("void "):
+        n = n[5:]
+    depth, cut = 0, len(n)
+    for i, ch in enumerate(n):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            cut = i
+            break
+    q = n[:cut]
+    lt = q.find("<")
+    sym = (q if lt < 0 else q[:lt]).split("::")[-1].strip()
+    return sym, sym + (q[lt:] if lt >= 0 else "")
+
+
+def _short(name):
+    """Kernel symbol ("copy" for torch's copy kernels)."""
+    sym = _split(name)[0]
+    if sym not in LIB_KERNELS and "copy" in name:
+        return "copy"
+    return sym
+
+
+def _template(name):
+    return _split(name)[1]
+
+
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no *{suffix} under {d}")
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def _counters(d, only=None):
+    """{(symbol, grid, wg): {counter: mean value per dispatch}} from a rocprofv3 --pmc run."""
+    acc = {}
+    for r in _csv_rows(d, "counter_collection.csv"):
+        sym = _short(r["Kernel_Name"])
+        if only and sym not in only:
+            continue
+        key = (sym, int(r["Grid_Size"]), int(r["Workgroup_Size"]))
+        per = acc.setdefault(key, {})
+        per.setdefault(r["Counter_Name"], {})[r["Dispatch_Id"]] = float(r["Counter_Value"])
+    return {k: {c: sum(v.values()) / len(v) for c, v in per.items()} for k, per in acc.items()}
+
+
+LIB_KERNELS = ("scan_main_kernel", "scan_chunk_agg_kernel", "chain_kernel", "scan_fused_kernel", "widen_rows_kernel",
+               "fill_state_kernel", "state_update_kernel", "bwd_main_kernel", "bwd_agg_kernel", "bwd_rows_kernel",
+               "bwd_reduce_bc_kernel", "bwd_reduce_chan_kernel", "ssd_state_kernel", "ssd_scan_kernel",
+               "conv_fwd_kernel", "conv_update_kernel")
+
+
+def summarize(run_root, prefix, title, commands, profiled_hash=None):
+    """Write profiles/<prefix>_kernel_stats.txt, traffic_<prefix>.{txt,json} and sq_<prefix>.{txt,json} from the
+    rocprofv3 runs under run_root: trace/ (--kernel-trace --stats), fetch/ and write/ (FETCH_SIZE, WRITE_SIZE),
+    raw/ (TCC request counters), sq/ (SQ counters and VALUBusy), and copy_fetch/, copy_write/, copy_raw/ (the
+    same counters on `bench.py --copy-calibration`).  Missing runs are skipped."""
+    out_dir = os.path.join(ROOT, "profiles")
+    sh = profiled_hash or source_hash()
+    head = [f"# {title}", "# commands (from the repository root, on one MI355X; each --pmc set in a run of its own):"]
+    head += [f"#   {c}" for c in commands]
+    head += [f"# kernel source hash (bench.source_hash(): sha256[:16] of selective_state_space_35_amd/csrc/*.hip, *.h "
+             f"but ssm_api.hip): {sh}", "#"]
+    sub = lambda n: os.path.join(run_root, n)
+    # kernel trace: per launch shape
+    if os.path.isdir(sub("trace")):
+        import statistics
+
+        groups = {}
+        for r in _csv_rows(sub("trace"), "kernel_trace.csv"):
+            sym = _short(r["Kernel_Name"])
+            if sym not in LIB_KERNELS:
+                continue
+            grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+            wg = int(r["Workgroup_Size_X"]) * int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"])
+            us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
+            groups.setdefault((_template(r["Kernel_Name"]), grid, wg, int(r["LDS_Block_Size"]),
+                               int(r["VGPR_Count"])), []).append(us)
+        lines = head + ["# per launch shape (grid and workgroup in threads, LDS in bytes); med_us is the steady "
+                        "state, avg_us includes the first calls while the clocks ramp up",
+                        f"# {'kernel':<78} {'grid':>9} {'wg':>5} {'lds':>7} {'vgpr':>4} {'calls':>5} {'avg_us':>9} "
+                        f"{'med_us':>9} {'min_us':>9} {'max_us':>9}"]
+        for (name, grid, wg, lds, vg), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+            lines.append(f"  {name[:78]:<78} {grid:>9} {wg:>5} {lds:>7} {vg:>4} {len(v):>5} "
+                         f"{sum(v) / len(v):>9.2f} {statistics.median(v):>9.2f} {min(v):>9.2f} {max(v):>9.2f}")
+        with open(os.path.join(out_dir, f"{prefix}_kernel_stats.txt"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+    # traffic
+    if os.path.isdir(sub("fetch")) and os.path.isdir(sub("write")) and os.path.isdir(sub("copy_fetch")):
+        fe, wr = _counters(sub("fetch"), LIB_KERNELS), _counters(sub("write"), LIB_KERNELS)
+        cf, cw = _counters(sub("copy_fetch"), ("copy",)), _counters(sub("copy_write"), ("copy",))
+        big = lambda d, c: max((v for k, v in d.items() if k[0] == "copy"), key=lambda v: v.get(c, 0))
+        nbytes = 1 << 30
+        rf = nbytes / (big(cf, "FETCH_SIZE")["FETCH_SIZE"] * 1024)
+        wf = nbytes / (big(cw, "WRITE_SIZE")["WRITE_SIZE"] * 1024)
+        doc = {"source_hash": sh, "title": title, "commands": commands,
+               "copy_calibration": {"bytes": nbytes, "fetch_size_kib": big(cf, "FETCH_SIZE")["FETCH_SIZE"],
+                                    "write_size_kib": big(cw, "WRITE_SIZE")["WRITE_SIZE"], "read_factor": rf,
+                                    "write_factor": wf},
+               "kernels": {}}
+        if os.path.isdir(sub("copy_raw")):
+            raw = big(_counters(sub("copy_raw"), ("copy",)), "TCC_EA0_RDREQ_sum")
+            doc["copy_calibration"]["raw"] = raw
+        raw_k = _counters(sub("raw"), LIB_KERNELS) if os.path.isdir(sub("raw")) else {}
+        lines = head + [f"# copy calibration (1 GiB read + 1 GiB written): FETCH_SIZE "
+                        f"{doc['copy_calibration']['fetch_size_kib']:.0f} KiB -> read factor {rf:.3f}; WRITE_SIZE "
+                        f"{doc['copy_calibration']['write_size_kib']:.0f} KiB -> write factor {wf:.3f}"]
+        if "raw" in doc["copy_calibration"]:
+            r = doc["copy_calibration"]["raw"]
+            lines.append(f"# copy raw TCC requests: TCC_EA0_RDREQ_sum {r.get('TCC_EA0_RDREQ_sum', 0):.0f}, "
+                         f"TCC_EA0_RDREQ_32B_sum {r.get('TCC_EA0_RDREQ_32B_sum', 0):.0f}, TCC_BUBBLE_sum "
+                         f"{r.get('TCC_BUBBLE_sum', 0):.0f} (1 GiB / 128 B = {nbytes // 128})")
+        lines.append(f"# {'kernel':<24} {'grid':>9} {'wg':>5} {'FETCH_KiB':>12} {'WRITE_KiB':>12} {'read_GB':>9} "
+                     f"{'write_GB':>9} {'RDREQ':>12} {'RDREQ_32B':>10} {'BUBBLE':>10}")
+        for key in sorted(fe, key=lambda k: -fe[k].get("FETCH_SIZE", 0)):
+            if key not in wr:
+                continue
+            rd = fe[key]["FETCH_SIZE"] * 1024 * rf
+            wt = wr[key]["WRITE_SIZE"] * 1024 * wf
+            rk = raw_k.get(key, {})
+            rec = {"grid": key[1], "workgroup": key[2], "fetch_size_kib": fe[key]["FETCH_SIZE"],
+                   "write_size_kib": wr[key]["WRITE_SIZE"], "read_bytes_per_launch": rd,
+                   "write_bytes_per_launch": wt, "hbm_bytes_per_launch": rd + wt, "raw": rk}
+            name = key[0] if key[0] not in doc["kernels"] else f"{key[0]}@{key[1]}"
+            doc["kernels"][name] = rec
+            lines.append(f"  {key[0]:<24} {key[1]:>9} {key[2]:>5} {fe[key]['FETCH_SIZE']:>12.0f} "
+                         f"{wr[key]['WRITE_SIZE']:>12.0f} {rd / 1e9:>9.4f} {wt / 1e9:>9.4f} "
+                         f"{rk.get('TCC_EA0_RDREQ_sum', float('nan')):>12.0f} "
+                         f"{rk.get('TCC_EA0_RDREQ_32B_sum', float('nan')):>10.0f} "
+                         f"{rk.get('TCC_BUBBLE_sum', float('nan')):>10.0f}")
+        with open(os.path.join(out_dir, f"traffic_{prefix}.json"), "w") as f:
+            json.dump(doc, f, indent=1)
+        with open(os.path.join(out_dir, f"traffic_{prefix}.txt"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+    # issue rates of the calibration kernels
+    if os.path.exists(sub("alu.json")):
+        with open(sub("alu.json")) as f:
+            alu = json.loads(f.read().strip().splitlines()[-1])
+        lines = [f"# issue rates of single VALU instruction kinds on one MI355X ({alu['simds']} SIMDs, "
+                 f"{alu['clock_GHz_assumed']} GHz assumed)",
+                 "# command (from the repository root):", "#   python3 bench.py --alu-calibration",
+                 "# kernels: selective_state_space_35_amd/calib/ssm_calib.hip, built by build_calib() with the "
+                 "library's flags:", f"#   {alu['flags']}",
+                 "# each kind runs 8 independent chains per lane over 256 CUs x waves_per_simd x 4 waves",
+                 f"# {'kind':<46} {'waves/SIMD':>10} {'ms':>8} {'VALU lane-op/s':>15} {'trans lane-op/s':>15} "
+                 f"{'cyc/inst':>9} {'cyc/group':>9}"]
+        for k in alu["kinds"]:
+            lines.append(f"  {k['what']:<46} {k['waves_per_simd']:>10} {k['ms']:>8.3f} "
+                         f"{k['valu_lane_ops_per_s']:>15.4g} {k['trans_lane_ops_per_s']:>15.4g} "
+                         f"{k['cycles_per_wave_inst']:>9.3f} {k.get('cycles_per_group', float('nan')):>9.3f}")
+        fma = [k for k in alu["kinds"] if k["kind"] == 0 and k["waves_per_simd"] == 8][0]["cycles_per_wave_inst"]
+        mix4 = [k for k in alu["kinds"] if k["kind"] == 2 and k["waves_per_simd"] == 8][0]["cycles_per_group"]
+        mix2 = [k for k in alu["kinds"] if k["kind"] == 3][0]["cycles_per_group"]
+        lines += ["#", f"# reading: an fp32 FMA issues in {fma:.2f} cycles per wave64 instruction (4 at the "
+                  f"nominal 16 lanes/clock/SIMD: {4 / fma:.1%} of 3.93e13 lane-op/s); in these probes an exp next "
+                  f"to 4 FMAs adds {mix4 - 4 * fma:.2f} cycles and next to 2 FMAs {mix2 - 2 * fma:.2f} "
+                  f"({(mix4 - 4 * fma) / fma:.2f} / {(mix2 - 2 * fma) / fma:.2f} FMA slots), an upper bound: the "
+                  "scan kernels issue their mix (a fifth transcendental) at 4.5 cycles per instruction "
+                  "(sq_scan_long.txt), so the roofline counts every VALU instruction, a transcendental included, "
+                  "as one slot against 256 x 4 x 16 x 2.4e9 = 3.93e13 slot/s"]
+        with open(os.path.join(out_dir, "alu_issue_rates.txt"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+
+    # SQ counters and VALU busy
+    if os.path.isdir(sub("sq")):
+        sq = _counters(sub("sq"), LIB_KERNELS)
+        for extra in ("sq2", "sq3"):
+            if os.path.isdir(sub(extra)):
+                for k, v in _counters(sub(extra), LIB_KERNELS).items():
+                    sq.setdefault(k, {}).update(v)
+        doc = {"source_hash": sh, "title": title, "commands": commands, "kernels": {}}
+        lines = head + ["# per dispatch (mean over the run's dispatches of that launch shape); VALUBusy = 100 x "
+                        "SQ_ACTIVE_INST_VALU / CU_NUM / GRBM_GUI_ACTIVE (rocprofv3's derived counter)",
+                        f"# {'kernel':<24} {'grid':>9} {'counter':<26} {'value':>14}"]
+        for key in sorted(sq, key=lambda k: -sq[k].get("SQ_INSTS_VALU", 0)):
+            name = key[0] if key[0] not in doc["kernels"] else f"{key[0]}@{key[1]}"
+            doc["kernels"][name] = dict(sq[key], grid=key[1], workgroup=key[2])
+            for c in sorted(sq[key]):
+                lines.append(f"  {key[0]:<24} {key[1]:>9} {c:<26} {sq[key][c]:>14.4g}")
+        with open(os.path.join(out_dir, f"sq_{prefix}.json"), "w") as f:
+            json.dump(doc, f, indent=1)
+        with open(os.path.join(out_dir, f"sq_{prefix}.txt"), "w") as f:
+            f.write("\n".join(lines) + "\n")
 
 
 ALU_KINDS = {0: "v_fma_f32", 1: "v_exp_f32", 2: "4 v_fma_f32 + 1 v_exp_f32", 3: "2 v_fma_f32 + 1 v_exp_f32",
@@ -570,7 +848,8 @@ def alu_calibration(iters=20000, reps=3):
     lib.ssm_calib_alu.restype = ctypes.c_int
     d = ctypes.c_double
     lib.ssm_calib_alu.argtypes = [ctypes.c_int] * 4 + [ctypes.POINTER(d)] * 3
-    out = {"clock_GHz_assumed": 2.4, "simds": 1024, "flags": " ".join(lib_build.COMMON[:8]), "kinds": []}
+    flags = " ".join(f for f in lib_build.COMMON if not f.startswith("-I"))
+    out = {"clock_GHz_assumed": 2.4, "simds": 1024, "flags": flags, "kinds": []}
     for kind, wps in [(0, 1), (0, 2), (0, 4), (0, 8), (1, 8), (2, 8), (3, 8), (4, 8), (5, 8), (2, 4), (1, 4)]:
         ms, valu, trans = d(), d(), d()
         rc = lib.ssm_calib_alu(kind, 256 * wps, iters, reps, ctypes.byref(ms), ctypes.byref(valu), ctypes.byref(trans))
@@ -606,7 +885,28 @@ def main():
                     help="only time the issue-rate calibration kernels (libssm_calib.so) and print their rates")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
+    ap.add_argument("--workload", default="long", choices=["long", "mid", "block", "tiny", "long_e640"],
+                    help="the scan timed as the step (default: the long sequence, the headline; the others for "
+                         "profiling their kernels alone)")
+    ap.add_argument("--summarize", metavar="RUN_ROOT",
+                    help="no GPU: write profiles/ summaries from the rocprofv3 runs under RUN_ROOT")
+    ap.add_argument("--prefix", default="scan_long", help="--summarize: name of the summaries")
+    ap.add_argument("--title", default="", help="--summarize: first line of the summaries")
+    ap.add_argument("--commands", default="", help="--summarize: file with the commands that made the runs")
+    ap.add_argument("--source-hash", default="", help="--summarize: bench.source_hash() of the profiled tree")
+    ap.add_argument("--print-source-hash", action="store_true", help="print bench.source_hash() and exit")
     args = ap.parse_args()
+
+    if args.print_source_hash:
+        print(source_hash())
+        return
+    if args.summarize:
+        cmds = []
+        if args.commands:
+            with open(args.commands) as f:
+                cmds = [ln.rstrip("\n") for ln in f if ln.strip()]
+        summarize(args.summarize, args.prefix, args.title, cmds, args.source_hash or None)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -640,7 +940,8 @@ def main():
         print(json.dumps({"copy_calibration_bytes_read": nbytes, "bytes_written": nbytes, "launches": 3}))
         return
 
-    w = workloads.LONG
+    w = {"long": workloads.LONG, "mid": workloads.MID, "block": workloads.BLOCK, "tiny": workloads.TINY,
+         "long_e640": workloads.LONG_E640}[args.workload]
     log(f"[bench] generating {w.description} (seed {args.seed}) on {torch.cuda.get_device_name(dev)}")
     x = workloads.make_scan_inputs(w, seed=args.seed, device=dev, backend="torch")
     y = torch.empty_like(x["u"])
@@ -679,7 +980,6 @@ def main():
     main_ms, main_n = per_kernel[main_name]
     main_avg_s = main_ms / max(main_n, 1) * 1e-3
     achieved = algo / main_avg_s / 1e9
-    traffic, traffic_note = load_traffic("scan_main", w.name)
     log(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step, {value:.4e} elem/s, path {path_gbps:.1f} GB/s; "
         f"kernels {kernels}")
 
@@ -690,8 +990,31 @@ def main():
     path_tslots = slots / (ms_per_step * 1e-3) / 1e12
     alu = {"slots_per_step": slots, "path_Tslot_per_s": path_tslots,
            "path_frac": path_tslots * 1e12 / VALU_SLOT_PEAK,
-           "note": "one slot = one fp32 VALU lane-op issue; a transcendental takes 4. The sequence split runs a "
-                   "second (aggregate) pass over all but the last chunk; its slots are not algorithmic"}
+           "note": f"one slot = one non-packed fp32 VALU lane-op issue, a transcendental takes {TRANS_SLOTS} "
+                   "(profiles/alu_issue_rates.txt); peak 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz.  The chunked "
+                   "form runs a second (aggregate) pass over all but the last chunk; its slots are not "
+                   "algorithmic"}
+    # committed counter summaries of this workload, used when taken on the current sources
+    tr_doc, tr_note = load_profile(f"traffic_scan_{w.name}")
+    sq_doc, sq_note = load_profile(f"sq_scan_{w.name}")
+    main_sym = KIND_SYMBOL.get(main_name, main_name)
+    traffic = None
+    if tr_doc and main_sym in tr_doc["kernels"]:
+        traffic = tr_doc["kernels"][main_sym]["hbm_bytes_per_launch"]
+    valu_busy = ({k: v.get("VALUBusy") for k, v in sq_doc["kernels"].items()} if sq_doc else None)
+    roofline = {
+        "bound": "alu", "kernel": main_sym, "achieved": main_tslots, "peak": VALU_SLOT_PEAK / 1e12,
+        "unit": "Tslot/s", "frac": main_tslots * 1e12 / VALU_SLOT_PEAK, "traffic": traffic,
+        "traffic_note": tr_note or ("L2-to-fabric bytes per launch: FETCH_SIZE and WRITE_SIZE from two rocprofv3 "
+                                    "--pmc runs, each scaled by the same counter on a plain 1 GiB copy "
+                                    "(profiles/traffic_scan_long.txt)"),
+        "algorithmic_bytes": algo, "algorithmic_slots": slots, "kernel_avg_us": round(main_avg_s * 1e6, 2),
+        "hbm": {"kernel_GBps": achieved, "kernel_frac": achieved / HBM_PEAK_GBPS,
+                "call_GBps": path_gbps, "call_frac": path_gbps / HBM_PEAK_GBPS, "peak_GBps": HBM_PEAK_GBPS},
+        "valu_busy_pct": valu_busy, "valu_busy_note": sq_note or "rocprofv3 VALUBusy per kernel "
+                                                                 "(profiles/sq_scan_long.txt)",
+        "slot_model": f"one slot = one non-packed fp32 VALU lane-op; a transcendental = {TRANS_SLOTS} slots, "
+                      "measured by the calibration kernels (profiles/alu_issue_rates.txt)"}
 
     # state update (generation): 128 successive single-token updates, state carried in HBM
     update = None if args.no_decode else measure_decode(ssm, torch, workloads, dev, stream, args.seed)
@@ -700,7 +1023,8 @@ def main():
     bwd = None if args.no_bwd else measure_backward(ssm, torch, dev, stream, x, w, args.steps, args.seed)
 
     # the scan with a scalar transition per head, in chunks of MFMA matrix products
-    ssd = None if args.no_ssd else measure_ssd(ssm, torch, workloads, dev, stream, args.seed)
+    ssd = None if args.no_ssd else measure_ssd(ssm, torch, workloads, dev, stream, args.seed,
+                                               cpu=not args.no_cpu_baseline)
 
     # causal convolution in front of the scan (long workload) and its generation-time token step
     conv = None if args.no_conv else measure_conv(ssm, torch, workloads, dev, args.seed)
@@ -728,8 +1052,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
         "data": "synthetic",
+        "dtype_note": "bf16 inputs and outputs; state, exponentials and accumulation in fp32",
         "config": {"workload": "long-sequence selective scan b1 L65536 E5120 N16, bf16 I/O, fp32 state, "
                                "softplus step, silu gate, D skip",
                    "b": w.b, "L": w.L, "E": w.E, "N": w.N, "io_dtype": w.dtype,
@@ -738,12 +1063,7 @@ def main():
         "hbm_GBps": path_gbps,
         "hbm_frac": path_gbps / HBM_PEAK_GBPS,
         "algorithmic_bytes_per_step": algo,
-        "roofline": {"bound": "alu", "kernel": "scan_main", "achieved": main_tslots,
-                     "peak": VALU_SLOT_PEAK / 1e12, "unit": "Tslot/s", "frac": main_tslots * 1e12 / VALU_SLOT_PEAK,
-                     "traffic": traffic, "traffic_note": traffic_note, "algorithmic_bytes": algo,
-                     "algorithmic_slots": slots, "kernel_avg_us": round(main_avg_s * 1e6, 2)},
-        "roofline_hbm": {"bound": "hbm", "kernel": "scan_main", "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS},
+        "roofline": roofline,
         "kernels": kernels,
         "alu": alu,
         "state_update": update,

@@ -69,16 +69,20 @@ def test_scan_bytes_of_the_long_workload():
 
 
 def test_scan_slots_of_the_long_workload():
-    # per (t, e, n): step times A, exp2 (4), d u times B, the state update, the readout -> 8
-    # per (t, e): d u (1), softplus 2 exp/log (8) + 4, D u (1), silu gate 2 transcendentals (8) + 4,
+    # a transcendental takes one issue slot like any VALU instruction
+    assert bench.TRANS_SLOTS == 1
+    # per (t, e, n): step times A, exp2, d u times B, the state update, the readout -> 5
+    # per (t, e): d u (1), softplus 2 exp/log + 4, D u (1), silu gate 2 transcendentals + 4,
     #             bf16 widening of u, delta, z and rounding of y (4)
-    per_elem = 8 * 16 + 1 + 12 + 1 + 12 + 4
-    assert per_elem == 158
+    per_elem = 5 * 16 + 1 + 6 + 1 + 6 + 4
+    assert per_elem == 98
     got = bench.scan_slots(1, 65536, 5120, 16, softplus=True, gate=True, has_d=True, has_bias=False, bf16=True)
-    assert got == 158 * 65536 * 5120
+    assert got == 98 * 65536 * 5120
     # fp32 I/O drops the widening and rounding; a step bias adds one slot per (t, e)
     got = bench.scan_slots(1, 64, 16, 4, softplus=True, gate=False, has_d=True, has_bias=True, bf16=False)
-    assert got == 64 * 16 * (8 * 4 + 1 + 1 + 12 + 1)
+    assert got == 64 * 16 * (5 * 4 + 1 + 1 + 6 + 1)
+    # the peak: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (non-packed fp32)
+    assert bench.VALU_SLOT_PEAK == 256 * 4 * 16 * 2.4e9
 
 
 def test_update_bytes_of_the_decode_workload():
@@ -90,15 +94,31 @@ def test_update_bytes_of_the_decode_workload():
     assert bench.update_bytes(b, E, N, 2) == state + tokens + rows + params == 178_642_944
 
 
-def test_traffic_needs_the_current_kernel_source(monkeypatch):
-    path = os.path.join(ROOT, "profiles", "traffic_scan_main_long.json")
+def test_profiles_need_the_current_kernel_source(monkeypatch):
+    path = os.path.join(ROOT, "profiles", "traffic_scan_long.json")
     with open(path) as f:
         doc = json.load(f)
     monkeypatch.setattr(bench, "source_hash", lambda: doc["source_hash"])
-    value, note = bench.load_traffic("scan_main", "long")
-    assert value == doc["hbm_bytes_per_launch"] and value > 0
+    got, note = bench.load_profile("traffic_scan_long")
+    assert got == doc and note == ""
+    assert got["kernels"]["scan_main_kernel"]["hbm_bytes_per_launch"] > 0
     monkeypatch.setattr(bench, "source_hash", lambda: "0" * 16)
-    value, note = bench.load_traffic("scan_main", "long")
-    assert value is None and "changed" in note
-    value, note = bench.load_traffic("scan_main", "no_such_workload")
-    assert value is None and "no PMC summary" in note
+    got, note = bench.load_profile("traffic_scan_long")
+    assert got is None and "changed" in note
+    got, note = bench.load_profile("traffic_no_such_workload")
+    assert got is None and "no summary" in note
+
+
+def test_source_hash_covers_every_kernel_source():
+    csrc = os.path.join(ROOT, "selective_state_space_35_amd", "csrc")
+    names = {f for f in os.listdir(csrc) if f.endswith((".hip", ".h"))}
+    assert {"ssm_kernels.hip", "ssm_fused.hip", "ssm_chain.h", "ssm_device.h"} <= names
+    assert len(bench.source_hash()) == 16
+
+
+def test_kernel_names_of_the_profiles():
+    assert bench._split("void ssm::(anonymous namespace)::scan_fused_kernel<unsigned short, 4, true, true, false>"
+                        "(unsigned short const*, float)") == (
+        "scan_fused_kernel", "scan_fused_kernel<unsigned short, 4, true, true, false>")
+    assert bench._short("void ssm::chain_kernel<1, 32, false, false, false>(ssm::ChainArgs)") == "chain_kernel"
+    assert bench._short("void at::native::elementwise_kernel<128, 2, direct_copy_kernel_cuda>(int)") == "copy"
