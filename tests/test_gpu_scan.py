@@ -212,15 +212,17 @@ def test_full_mid_no_D_no_gate():
     check_scan(make(w, seed=1), "bf16", "mid full no D / no gate")
 
 
-def test_full_long_sampled_channels():
+def test_full_long_all_channels():
+    """b1 L65536 E5120 N16 bf16, the headline workload: every channel against the oracle (1024 per oracle call)."""
     import torch
 
     say("full long b1 L65536 E5120 N16 bf16 (torch generator on device)")
     x = make(workloads.LONG, seed=0, backend="torch")
     y, last = gpu_scan(x)
-    ch = sample_channels(workloads.LONG.E, "cuda", k=64, seed=0)
-    say(f"oracle on {ch.numel()} sampled channels")
-    check_scan(x, "bf16", "long full (sampled channels)", channels=ch, y=y, last=last)
+    for c0 in range(0, workloads.LONG.E, 1024):
+        ch = torch.arange(c0, c0 + 1024, device="cuda")
+        say(f"oracle on channels {c0}..{c0 + 1023}")
+        check_scan(x, "bf16", f"long full (channels {c0}..{c0 + 1023})", channels=ch, y=y, last=last)
     del x, y, last
     torch.cuda.empty_cache()
 

@@ -151,11 +151,13 @@ def test_mid_workload_full():
     check(make(w, 0), "ssd mid")
 
 
-def test_long_workload_sampled_heads():
+def test_long_workload_all_heads():
+    """b1 L65536 H80 P64 N64 bf16: every head against the oracle, 16 heads (1024 channels) per oracle call."""
     import torch
 
     w = workloads.SSD_LONG
     x = make(w, 0, backend="torch")
-    heads = torch.tensor([0, 1, 40, 79], device="cuda")
-    say(f"ssd {w.description}, heads {heads.tolist()}")
-    check(x, "ssd long (sampled heads)", heads=heads)
+    for h0 in range(0, w.H, 16):
+        heads = torch.arange(h0, min(h0 + 16, w.H), device="cuda")
+        say(f"ssd {w.description}, heads {h0}..{int(heads[-1])}")
+        check(x, f"ssd long (heads {h0}..{int(heads[-1])})", heads=heads)
