@@ -90,3 +90,47 @@ def test_token_steps_replay_exactly(b, E, N, K, T):
         assert torch.equal(ssm_g, ssm_e), f"replay {rep}: scan state differs"
         _ = (ys_g.float().sum() + 1).item()  # eager work between replays
     print(f"[parity] graph of {T} token steps b{b} E{E}: 3 replays equal to eager", flush=True)
+
+
+@pytest.mark.parametrize("name,b,L,E,N", [("chunked, cut into chunks", 1, 4096, 2560, 16),
+                                          ("single pass", 8, 512, 1536, 16)])
+def test_noalloc_scan_replays_exactly(name, b, L, E, N):
+    """ssm_scan_fwd_noalloc allocates nothing and issues no memset, so it can be captured: the replays of a
+    captured call equal the eager call bit for bit (the eager call is checked against ssm_scan_fwd_from and the
+    oracle in test_zz_no_alloc.py)."""
+    import torch
+
+    import selective_state_space_35_amd as ssm
+    import workloads
+    from tests.gpu_common import say
+
+    w = workloads.MID.with_shape(b=b, L=L, E=E, N=N)
+    path, _, n_chunks = ssm.ssm_scan_plan(b, L, E, N, "bf16")
+    assert (path == "chunked" and n_chunks > 1) if name.startswith("chunked") else path == "single_pass"
+    say(f"graph capture of ssm_scan_fwd_noalloc ({name}) b{b} L{L} E{E} N{N}")
+    x = workloads.make_scan_inputs(w, seed=L, device="cuda", backend="torch")
+    args = (x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"], x["softplus"])
+    y_e, last_e = ssm.ssm_scan_fwd_noalloc(*args)
+    torch.cuda.synchronize()
+    y_g, last_g = torch.empty_like(y_e), torch.empty_like(last_e)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ssm.ssm_scan_fwd_noalloc(*args, y=y_g, last_state=last_g)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ssm.ssm_scan_fwd_noalloc(*args, y=y_g, last_state=last_g)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        y_g.zero_()
+        last_g.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y_g, y_e), f"replay {rep}: y differs"
+        assert torch.equal(last_g, last_e), f"replay {rep}: last state differs"
+        ssm.ssm_scan_fwd_from(*args)  # eager work on the same buffer between replays
+        _ = (y_g.float().sum() + 1).item()
+    print(f"[parity] graph of ssm_scan_fwd_noalloc ({name}): 3 replays equal to eager", flush=True)
