@@ -203,8 +203,12 @@ def scan_configs(ssm, workloads, torch, dev, stream, seed, cpu=True):
     """Each scan configuration timed call by call, with the oracle beside it.
 
     The block and mid configurations are small enough to stay in the 256 MB
-    Infinity Cache between calls, so a 1 GiB buffer is written before every
-    timed call (outside its event pair).  The tiny one is launch-bound.  The
+    Infinity Cache between calls, so a 1 GiB buffer is read before every timed
+    call (outside its event pair): the call's inputs come from HBM.  The same
+    calls are also timed after a 1 GiB write instead; that flush leaves the
+    cache full of dirty lines, whose write-back to HBM then runs inside the
+    timed call, so it measures the call plus part of the flush's own cost
+    (reported beside, not as the figure).  The tiny one is launch-bound.  The
     long workload's share at E = 640 is what one GPU of 8 runs when the
     channels are split over them.  With ``cpu``, the fp64 oracle runs on the
     same inputs, on 1 thread and on the host's threads, and checks the
@@ -213,6 +217,7 @@ def scan_configs(ssm, workloads, torch, dev, stream, seed, cpu=True):
     import numpy as np
 
     copy_gbps, flush = copy_bandwidth(torch, dev, stream)
+    flush_words = flush.view(torch.int64)
     out = {"copy_GBps": round(copy_gbps, 1),
            "copy_note": "1 GiB device-to-device copy: bytes read + written over its time",
            "timing": "event pair around each call on the launch stream; median and min over the calls"}
@@ -233,29 +238,39 @@ def scan_configs(ssm, workloads, torch, dev, stream, seed, cpu=True):
         for _ in range(5):
             call()
         torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-        for k in range(reps):
-            if flushed:
-                flush.fill_(k & 0x7F)
-            ev[k][0].record(stream)
-            call()
-            ev[k][1].record(stream)
-        torch.cuda.synchronize()
-        us = sorted(1e3 * a.elapsed_time(b) for a, b in ev)
+
+        def timed(how):  # per-call event pairs; how: None, "read" or "write" flush before each call
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+            for k in range(reps):
+                if how == "read":
+                    flush_words.max()
+                elif how == "write":
+                    flush.fill_(k & 0x7F)
+                ev[k][0].record(stream)
+                call()
+                ev[k][1].record(stream)
+            torch.cuda.synchronize()
+            return sorted(1e3 * a.elapsed_time(b) for a, b in ev)
+
+        us = timed("read" if flushed else None)
         med, mn = us[len(us) // 2], us[0]
+        us_w = timed("write") if flushed else None
         s = 2 if wc.dtype == "bf16" else 4
         nb = scan_bytes(wc.b, wc.L, wc.E, wc.N, s, gate=wc.z is not None)
         sl = scan_slots(wc.b, wc.L, wc.E, wc.N, softplus=wc.softplus, gate=wc.z is not None,
                         has_d=wc.D is not None, has_bias=wc.delta_bias is not None, bf16=(wc.dtype == "bf16"))
         el = wc.b * wc.L * wc.E
         gbps = nb / (med * 1e-6) / 1e9
-        rec = {"workload": wc.description, "calls": reps, "cache_flushed": flushed,
+        rec = {"workload": wc.description, "calls": reps,
+               "cache_flushed": "1 GiB read before each call" if flushed else False,
                "us_median": round(med, 2), "us_min": round(mn, 2), "elem_per_s": el / (med * 1e-6),
                "algorithmic_bytes": nb, "GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
                "copy_frac": round(gbps / copy_gbps, 4),
                "alu_frac": round(sl / (med * 1e-6) / VALU_SLOT_PEAK, 4),
                "plan": dict(zip(("path", "chunk_len", "n_chunks"),
                                 ssm.ssm_scan_plan(wc.b, wc.L, wc.E, wc.N, wc.dtype)))}
+        if us_w is not None:
+            rec["after_write_flush"] = {"us_median": round(us_w[len(us_w) // 2], 2), "us_min": round(us_w[0], 2)}
         if cpu:
             a64 = [oracle.to_f64(xc[k]) for k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")]
             rates = {}
@@ -270,7 +285,7 @@ def scan_configs(ssm, workloads, torch, dev, stream, seed, cpu=True):
                              "bound": bound}
         out[wc.name] = rec
         del xc, yc, lc
-    del flush
+    del flush, flush_words
     if cpu:  # the decode workload on the host: a sample of its token steps (the GPU side is state_update)
         wd = workloads.DECODE.with_shape(steps=8)
         xd = workloads.make_decode_inputs(wd, seed=seed, device=dev, backend="torch")
@@ -324,11 +339,14 @@ def measure_decode(ssm, torch, workloads, dev, stream, seed):
     # where the carried state comes from: the same calls with a 1 GiB buffer written between them (outside
     # each call's event pair), which evicts the state from the Infinity Cache, so every call reads it from HBM
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    res, evi = [], []
+    flush_words = flush.view(torch.int64)
+    res, evi, evr = [], [], []
     for k in range(wd.steps):
-        for evicted, acc in ((False, res), (True, evi)):
-            if evicted:
+        for how, acc in ((None, res), ("write", evi), ("read", evr)):
+            if how == "write":
                 flush.fill_(k & 0x7F)
+            elif how == "read":
+                flush_words.max()
             a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a0.record(stream)
             ssm.ssm_state_update(st, xd["x"][k], xd["delta"][k], xd["A"], xd["B"][k], xd["C"][k], xd["D"],
@@ -337,15 +355,17 @@ def measure_decode(ssm, torch, workloads, dev, stream, seed):
             acc.append((a0, a1))
     torch.cuda.synchronize()
     med = lambda ev: sorted(1e3 * a.elapsed_time(b) for a, b in ev)[len(ev) // 2]
-    r_us, e_us = med(res), med(evi)
+    r_us, e_us, er_us = med(res), med(evi), med(evr)
     update["state_source"] = {
         "resident_us_median": round(r_us, 3), "evicted_us_median": round(e_us, 3),
+        "evicted_by_read_us_median": round(er_us, 3),
         "resident_GBps": round(ub / (r_us * 1e-6) / 1e9, 1), "evicted_GBps": round(ub / (e_us * 1e-6) / 1e9, 1),
         "evicted_hbm_frac": round(ub / (e_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
         "note": "each call timed alone with an event pair: right after the previous call (state in the Infinity "
                 "Cache) and after a 1 GiB write that evicts it (state from HBM); the evicted rate is the HBM "
-                "figure, the difference is what the cache serves"}
-    del flush
+                "figure, the difference is what the cache serves. evicted_by_read: the same after a 1 GiB read, "
+                "the flush the scan configurations use"}
+    del flush, flush_words
 
     # one generation step of the block's kernels per token: the convolution token step, then the state
     # update on its output; eager launches against the same T tokens captured once in a HIP graph
@@ -442,7 +462,8 @@ def measure_backward(ssm, torch, dev, stream, x, w, steps, seed):
            "algorithmic_bytes": bb, "GBps": round(bb / (bwd_ms * 1e-3) / 1e9, 1),
            "kernels": {k: {"avg_us": round(1e3 * v[0] / v[1], 2), "launches": v[1]}
                        for k, v in prof.items() if v[1]},
-           "note": "includes the workspace allocation and the forward chunk-state passes it reruns"}
+           "note": "includes the workspace allocation and the chunk maps it recomputes (bwd_aggregate: the "
+                   "forward and reverse maps of every chunk in one walk; chunk_carry and bwd_carry: their chains)"}
     log(f"[bench] backward {bwd}")
 
     # training form: the forward keeps the state every 64 steps, the backward starts its chunks from them

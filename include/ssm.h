@@ -414,7 +414,9 @@ SSM_API int ssm_scan_plan(int64_t b, int64_t L, int64_t E, int64_t N, int dtype,
  * (milliseconds) and launch counts for kinds 0 .. n_kinds-1 and clears the
  * record.  Kinds: 0 chunk_aggregate, 1 chunk_carry, 2 scan_main,
  * 3 fill_state, 4 state_update, 5 conv, 6 conv_update, 7 bwd_rows,
- * 8 bwd_aggregate, 9 bwd_carry, 10 bwd_main, 11 bwd_reduce, 12 ssd_state,
+ * 8 bwd_aggregate (the backward's per-chunk maps: with no saved states the
+ * forward and the reverse ones from one walk, whose forward chain is timed as
+ * chunk_carry), 9 bwd_carry, 10 bwd_main, 11 bwd_reduce, 12 ssd_state,
  * 13 ssd_carry, 14 ssd_scan, 15 scan_fused (the single-pass forward),
  * 16 widen_rows (float copies of the bf16 B / C rows of a cut forward); names
  * from ssm_profile_kind_name().  Off by default; the events add a few

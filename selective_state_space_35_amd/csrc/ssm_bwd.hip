@@ -14,10 +14,13 @@
 //   ddelta_t = dd_t * sigmoid(delta_t + bias) (softplus) ;  dz_t = dy_t * q_t * silu'(z_t)
 //
 // Passes (one call):
-//   1. forward chunk states: the forward's aggregate + carry passes over chunks
-//      of kBwdChunk steps give the state entering every chunk;
-//   2. bwd_chunk_agg_kernel: per chunk, the state gradient reached from zero
-//      walking the chunk backwards (the reverse-time aggregate);
+//   1. forward chunk states: per chunk of kBwdChunk steps the state reached
+//      from zero, then the forward chain of those maps gives the state entering
+//      every chunk (with saved states these are the saved states instead);
+//   2. per chunk, the state gradient its own steps send to its first step (the
+//      reverse-time aggregate).  Without saved states 1 and 2 come from one walk
+//      over each chunk (bwd_chunk_maps_kernel); with them, 2 alone
+//      (bwd_chunk_agg_kernel, walking the chunk backwards);
 //   3. chain_kernel (ssm_chain.h), in reverse: the chain of those aggregates
 //      from the last chunk to the first, started from dlast: the gradient
 //      entering every chunk from its end (the decay of a chunk is
@@ -120,6 +123,106 @@ __global__ __launch_bounds__(kWave) void bwd_chunk_agg_kernel(
 #pragma unroll
     for (int n = 0; n < kS; n++) dst[n] = X[n];
     xsum[(bi * n_chunks + c) * E + e] = float(dsum);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 1 and 2 in one walk (no saved states): chunk c walked once, first step to
+// last, gives both of its maps and its sum of steps, which both chains use:
+//   forward  h <- a_t * h + d_t * u_t * B_t from zero: the state leaving the
+//            chunk when it is entered with zero (written for c < n_chunks - 1);
+//   reverse  X = sum_t (a_t0 * .. * a_t) * dq_t * C_t: the state gradient that
+//            the chunk's own steps send to its first step, the same sum as the
+//            backward walk X <- a_t * (X + dq_t * C_t) above, with the running
+//            product of the retentions in place of the walk's order (written
+//            for c >= 1).
+// Each retention exp2(d * A * log2 e) is evaluated once for both maps and u,
+// delta, dy, z are read once.  One lane per channel, 16 states in registers;
+// the float B and C rows are wave-uniform (scalar loads).
+// ---------------------------------------------------------------------------
+template <typename T, bool SOFTPLUS, bool HAS_Z>
+__global__ __launch_bounds__(kWave) void bwd_chunk_maps_kernel(
+    const T* __restrict__ u, const T* __restrict__ delta, const T* __restrict__ dy, const T* __restrict__ z,
+    const float* __restrict__ A, const float* __restrict__ B16, const float* __restrict__ C16,
+    const float* __restrict__ bias, float* __restrict__ fagg, int fslots, float* __restrict__ xagg,
+    float* __restrict__ sums, int64_t L, int64_t E, int N, int n_chunks, int e_blocks) {
+  constexpr int kG = 4;  // steps whose loads are issued together
+  const int eb = blockIdx.x % e_blocks;
+  const int rest = blockIdx.x / e_blocks;
+  const int c = rest % n_chunks;
+  const int64_t bi = rest / n_chunks;
+  const int64_t e = int64_t(eb) * kWave + threadIdx.x;
+  const bool active = e < E;
+  const int64_t ec = active ? e : E - 1;
+  const int64_t t0 = int64_t(c) * kBwdChunk;
+  const int n_steps = int(std::min<int64_t>(L - t0, kBwdChunk));
+
+  float A2[kS];
+#pragma unroll
+  for (int n = 0; n < kS; n++) A2[n] = n < N ? A[ec * N + n] * kLog2e : 0.f;
+  const float bv = bias ? bias[ec] : 0.f;
+  float h[kS], X[kS], R[kS];
+#pragma unroll
+  for (int n = 0; n < kS; n++) {
+    h[n] = 0.f;
+    X[n] = 0.f;
+    R[n] = 1.f;
+  }
+  double dsum = 0.0;
+
+  const int64_t row0 = (bi * L + t0) * E + int64_t(eb) * kWave;
+  const __amdgpu_buffer_rsrc_t ru = make_rsrc(u + row0);
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(delta + row0);
+  const __amdgpu_buffer_rsrc_t ry = make_rsrc(dy + row0);
+  const __amdgpu_buffer_rsrc_t rz = make_rsrc(HAS_Z ? z + row0 : delta + row0);
+  const int voff = int(ec - int64_t(eb) * kWave) * int(sizeof(T));
+  const int row_bytes = int(E * int64_t(sizeof(T)));  // kBwdChunk * row_bytes < 2^31 is checked by the caller
+  const float* brow0 = B16 + (bi * L + t0) * kS;
+  const float* crow0 = C16 + (bi * L + t0) * kS;
+
+  for (int k0 = 0; k0 < n_steps; k0 += kG) {
+    float rd_[kG], ru_[kG], ry_[kG], rz_[kG];
+#pragma unroll
+    for (int g = 0; g < kG; g++) {  // rows past the chunk's end re-read its last row, unused
+      const int so = std::min(k0 + g, n_steps - 1) * row_bytes;
+      rd_[g] = buf_load(rd, voff, so, (T*)nullptr);
+      ru_[g] = buf_load(ru, voff, so, (T*)nullptr);
+      ry_[g] = buf_load(ry, voff, so, (T*)nullptr);
+      rz_[g] = HAS_Z ? buf_load(rz, voff, so, (T*)nullptr) : 0.f;
+    }
+#pragma unroll
+    for (int g = 0; g < kG; g++) {
+      const int k = k0 + g;
+      if (k < n_steps) {
+        float d = rd_[g] + bv;
+        if (SOFTPLUS) d = softplus(d);
+        const float dx = d * ru_[g];
+        const float dq = HAS_Z ? ry_[g] * silu(rz_[g]) : ry_[g];
+        const float* br = brow0 + k * kS;  // wave-uniform: scalar loads
+        const float* cr = crow0 + k * kS;
+#pragma unroll
+        for (int n = 0; n < kS; n++) {
+          const float a = exp2_fast(d * A2[n]);
+          h[n] = fmaf(a, h[n], dx * br[n]);
+          R[n] *= a;
+          X[n] = fmaf(R[n], dq * cr[n], X[n]);
+        }
+        dsum += double(d);
+      }
+    }
+  }
+  if (active) {
+    const int64_t slot = (bi * n_chunks + c) * E + e;
+    if (c < n_chunks - 1) {
+#pragma unroll
+      for (int n = 0; n < kS; n++)
+        if (n < fslots) fagg[slot * fslots + n] = h[n];
+    }
+    if (c >= 1) {
+#pragma unroll
+      for (int n = 0; n < kS; n++) xagg[slot * kS + n] = X[n];
+    }
+    sums[slot] = float(dsum);
   }
 }
 
@@ -534,14 +637,37 @@ hipError_t run_main(const BwdArgs& a, int n_chunks, int e_blocks, const float* B
                      dA_part, dDb_part, dbc_part, a.L, a.E, int(a.N), n_chunks, e_blocks);
 }
 
+// The forward and reverse chunk maps of a call without saved states, in one walk.
+template <typename T>
+hipError_t run_maps(const BwdArgs& a, int n_chunks, const float* B16, const float* C16, float* fagg, int fslots,
+                    float* xagg, float* sums) {
+  const int eb = int((a.E + kWave - 1) / kWave);
+  const int64_t blocks = a.b * n_chunks * eb;
+  const T* u = static_cast<const T*>(a.u);
+  const T* dl = static_cast<const T*>(a.delta);
+  const T* dyp = static_cast<const T*>(a.dy);
+  const T* zp = static_cast<const T*>(a.z);
+#define SSM_BWD_MAPS(SP, HZ)                                                                                     \
+  return launch_kind(kKindBwdAgg, bwd_chunk_maps_kernel<T, SP, HZ>, blocks, kWave, a.stream, u, dl, dyp, zp, a.A, \
+                     B16, C16, a.bias, fagg, fslots, xagg, sums, a.L, a.E, int(a.N), n_chunks, eb)
+  if (a.softplus) {
+    if (a.z) SSM_BWD_MAPS(true, true);
+    SSM_BWD_MAPS(true, false);
+  }
+  if (a.z) SSM_BWD_MAPS(false, true);
+  SSM_BWD_MAPS(false, false);
+#undef SSM_BWD_MAPS
+}
+
+// rev_done: the reverse chunk maps and sums are already in xagg / xsum (run_maps)
 template <typename T>
 hipError_t bwd_typed(const BwdArgs& a, int n_chunks, const float* B16, const float* C16, const float* fcarry,
                      int fslots, int fchunks, float* xagg, float* xsum, float* dA_part, float* dDb_part,
-                     float* dbc_part) {
+                     float* dbc_part, bool rev_done) {
   const int N = int(a.N);
   const int eb_agg = int((a.E + kWave - 1) / kWave);
   hipError_t err = hipSuccess;
-  if (n_chunks > 1) {
+  if (n_chunks > 1 && !rev_done) {
     const int64_t blocks = a.b * (n_chunks - 1) * eb_agg;
     const T* dl = static_cast<const T*>(a.delta);
     const T* dyp = static_cast<const T*>(a.dy);
@@ -603,12 +729,13 @@ hipError_t launch_scan_bwd(const BwdArgs& a) {
   const bool saved = a.saved != nullptr;
   const int fslots = saved ? int(N) : chunk_state_slots(N);
   const int fchunks = saved ? n_chunks - 1 : n_chunks;  // chunk slots per batch row
-  // workspace (floats): [B16 | C16 | forward carries | forward sums | reverse carries |
-  //                      reverse sums | dB/dC partials | dA partials | dD/dbias partials]
+  // workspace (floats): [B16 | C16 | forward carries | (unused) | reverse carries |
+  //                      chunk sums | dB/dC partials | dA partials | dD/dbias partials]
+  // (without saved states one walk per chunk gives both carries' maps and the sums both chains use)
   const size_t nb = size_t(b), nL = size_t(L), nE = size_t(E), nc = size_t(n_chunks);
   const size_t n_row16 = nb * nL * kS;
   const size_t n_fc = n_chunks > 1 && !saved ? nb * nc * nE * size_t(fslots) : 0;
-  const size_t n_fs = n_chunks > 1 && !saved ? nb * nc * nE : 0;
+  const size_t n_fs = 0;
   const size_t n_xa = nb * nc * nE * kS;
   const size_t n_xs = nb * nc * nE;
   const size_t n_bc = nb * nL * size_t(e_blocks) * kRed;
@@ -628,7 +755,6 @@ hipError_t launch_scan_bwd(const BwdArgs& a) {
   float* B16 = f + offs[0];
   float* C16 = f + offs[1];
   const float* fcarry = saved ? a.saved : f + offs[2];
-  float* fsum = f + offs[3];
   float* xagg = f + offs[4];
   float* xsum = f + offs[5];
   float* dbc = f + offs[6];
@@ -642,22 +768,21 @@ hipError_t launch_scan_bwd(const BwdArgs& a) {
                      : launch_kind(kKindBwdRows, bwd_rows_kernel<bf16_bits>, (nr16 + 255) / 256, 256, a.stream,
                                    static_cast<const bf16_bits*>(a.B), static_cast<const bf16_bits*>(a.C), B16, C16,
                                    b * L, int(N));
-  if (err == hipSuccess && n_chunks > 1 && !saved) {
-    ScanArgs s{};
-    s.u = a.u; s.delta = a.delta; s.A = a.A; s.B = a.B; s.C = a.C; s.D = a.D; s.z = a.z; s.bias = a.bias;
-    s.softplus = a.softplus; s.y = nullptr; s.last_state = nullptr; s.h0 = a.h0;
-    s.b = b; s.L = L; s.E = E; s.N = N; s.dtype = a.dtype; s.stream = a.stream;
-    ScanPlan pl;
-    pl.chunk_len = kBwdChunk;
-    pl.n_chunks = n_chunks;
-    pl.e_blocks = int((E + kWave - 1) / kWave);
-    err = launch_chunk_states(s, pl, f + offs[2], fsum);
+  const bool maps = n_chunks > 1 && !saved;
+  if (err == hipSuccess && maps) {
+    // both chunk maps and the sums, then the forward chain: slot c <- the state leaving chunk c
+    err = a.dtype == 0 ? run_maps<float>(a, n_chunks, B16, C16, f + offs[2], fslots, xagg, xsum)
+                       : run_maps<bf16_bits>(a, n_chunks, B16, C16, f + offs[2], fslots, xagg, xsum);
+    if (err == hipSuccess) {
+      const ChainArgs fc{f + offs[2], xsum, a.A, a.h0, nullptr, b, E, fslots, int(N), n_chunks, n_chunks - 1};
+      err = launch_chain<false, false, false>(kKindCarry, fc, a.stream);
+    }
   }
   if (err == hipSuccess)
     err = a.dtype == 0 ? bwd_typed<float>(a, n_chunks, B16, C16, fcarry, fslots, fchunks, xagg, xsum, dA_part,
-                                          dDb_part, dbc)
+                                          dDb_part, dbc, maps)
                        : bwd_typed<bf16_bits>(a, n_chunks, B16, C16, fcarry, fslots, fchunks, xagg, xsum, dA_part,
-                                              dDb_part, dbc);
+                                              dDb_part, dbc, maps);
   if (err == hipSuccess) {
     const int64_t n = b * L * kRed;
     err = launch_kind(kKindBwdReduce, bwd_reduce_bc_kernel, (n + 255) / 256, 256, a.stream, (const float*)dbc, a.dB,

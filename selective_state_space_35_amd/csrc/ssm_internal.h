@@ -88,11 +88,6 @@ ScanPlan plan_scan(int64_t b, int64_t L, int64_t E, int elem_bytes, const ScanTu
 
 // State slots per channel in the chunk-state buffers (N, or 16 when N is not 4, 8 or 16).
 int chunk_state_slots(int64_t N);
-// Incoming state of every chunk of the scan described by `a` cut as `pl` says:
-// afterwards carry[(b * n_chunks + c) * E + e][slots] holds the state at the end
-// of chunk c (c < n_chunks - 1) and csum the sum of steps of chunk c.  y /
-// last_state are not touched.
-hipError_t launch_chunk_states(const ScanArgs& a, const ScanPlan& pl, float* carry, float* csum);
 
 // Backward of the scan (gradients of every input).
 struct BwdArgs {

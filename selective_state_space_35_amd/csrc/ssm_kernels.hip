@@ -671,17 +671,6 @@ hipError_t scan_typed(const ScanArgs& a, const ScanPlan& pl, const ScanBufs& w) 
   return scan_full<T, R, 16, false>(a, pl, w);
 }
 
-template <typename T>
-hipError_t carries_typed(const ScanArgs& a, const ScanPlan& pl, const ScanBufs& w) {
-#define SSM_CARRIES(NS, EX) \
-  return a.softplus ? run_carries<T, T, NS, EX, true>(a, pl, w) : run_carries<T, T, NS, EX, false>(a, pl, w)
-  if (a.N == 16) { SSM_CARRIES(16, true); }
-  if (a.N == 8) { SSM_CARRIES(8, true); }
-  if (a.N == 4) { SSM_CARRIES(4, true); }
-  SSM_CARRIES(16, false);
-#undef SSM_CARRIES
-}
-
 template <typename T, int NS, bool VEC, bool STAGE>
 hipError_t update_launch(const UpdateArgs& a) {
   const T* x = static_cast<const T*>(a.x);
@@ -867,17 +856,6 @@ hipError_t launch_scan(const ScanArgs& a, void* workspace, size_t workspace_byte
 }
 
 int chunk_state_slots(int64_t N) { return scan_states(N); }
-
-hipError_t launch_chunk_states(const ScanArgs& a, const ScanPlan& pl, float* carry, float* csum) {
-  if (a.b == 0 || a.E == 0 || pl.n_chunks <= 1) return hipSuccess;
-  ScanBufs w;
-  w.carry = carry;
-  w.csum = csum;
-  w.B = a.B;
-  w.C = a.C;
-  w.rows_odd = a.dtype == 0 ? 0 : bf16_rows_odd(a.B);
-  return a.dtype == 0 ? carries_typed<float>(a, pl, w) : carries_typed<bf16_bits>(a, pl, w);
-}
 
 hipError_t launch_state_update(const UpdateArgs& a) {
   if (a.b == 0 || a.E == 0) return hipSuccess;

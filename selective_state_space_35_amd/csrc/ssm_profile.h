@@ -15,7 +15,7 @@ enum : int {
   kKindConv = 5,        // causal depthwise convolution over a sequence
   kKindConvUpdate = 6,  // single-token convolution-state update
   kKindBwdRows = 7,     // backward: B / C rows padded to 16 states
-  kKindBwdAgg = 8,      // backward: per-chunk aggregate of the state gradient (reverse in time)
+  kKindBwdAgg = 8,      // backward: per-chunk maps (reverse in time; without saved states also the forward ones)
   kKindBwdCarry = 9,    // backward: chain of the state gradient across chunks
   kKindBwdMain = 10,    // backward: recompute states, gradients of every input
   kKindBwdReduce = 11,  // backward: sums of the per-chunk / per-block partial gradients
