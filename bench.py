@@ -203,12 +203,12 @@ def scan_configs(ssm, workloads, torch, dev, stream, seed, cpu=True):
     """Each scan configuration timed call by call, with the oracle beside it.
 
     The block and mid configurations are small enough to stay in the 256 MB
-    Infinity Cache between calls, so a 1 GiB buffer is read before every timed
-    call (outside its event pair): the call's inputs come from HBM.  The same
-    calls are also timed after a 1 GiB write instead; that flush leaves the
-    cache full of dirty lines, whose write-back to HBM then runs inside the
-    timed call, so it measures the call plus part of the flush's own cost
-    (reported beside, not as the figure).  The tiny one is launch-bound.  The
+    Infinity Cache between calls, so a 1 GiB buffer is written before every
+    timed call (outside its event pair).  A 1 GiB read does not do it: it
+    leaves a state of 84 MB in the cache (the decode leg's evicted_by_read
+    figure equals its resident one).  The written lines are dirty, so part of
+    their write-back to HBM runs inside the timed call.  The tiny one is
+    launch-bound.  The
     long workload's share at E = 640 is what one GPU of 8 runs when the
     channels are split over them.  With ``cpu``, the fp64 oracle runs on the
     same inputs, on 1 thread and on the host's threads, and checks the
@@ -217,7 +217,6 @@ def scan_configs(ssm, workloads, torch, dev, stream, seed, cpu=True):
     import numpy as np
 
     copy_gbps, flush = copy_bandwidth(torch, dev, stream)
-    flush_words = flush.view(torch.int64)
     out = {"copy_GBps": round(copy_gbps, 1),
            "copy_note": "1 GiB device-to-device copy: bytes read + written over its time",
            "timing": "event pair around each call on the launch stream; median and min over the calls"}
@@ -238,23 +237,16 @@ def scan_configs(ssm, workloads, torch, dev, stream, seed, cpu=True):
         for _ in range(5):
             call()
         torch.cuda.synchronize()
-
-        def timed(how):  # per-call event pairs; how: None, "read" or "write" flush before each call
-            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-            for k in range(reps):
-                if how == "read":
-                    flush_words.max()
-                elif how == "write":
-                    flush.fill_(k & 0x7F)
-                ev[k][0].record(stream)
-                call()
-                ev[k][1].record(stream)
-            torch.cuda.synchronize()
-            return sorted(1e3 * a.elapsed_time(b) for a, b in ev)
-
-        us = timed("read" if flushed else None)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for k in range(reps):
+            if flushed:
+                flush.fill_(k & 0x7F)
+            ev[k][0].record(stream)
+            call()
+            ev[k][1].record(stream)
+        torch.cuda.synchronize()
+        us = sorted(1e3 * a.elapsed_time(b) for a, b in ev)
         med, mn = us[len(us) // 2], us[0]
-        us_w = timed("write") if flushed else None
         s = 2 if wc.dtype == "bf16" else 4
         nb = scan_bytes(wc.b, wc.L, wc.E, wc.N, s, gate=wc.z is not None)
         sl = scan_slots(wc.b, wc.L, wc.E, wc.N, softplus=wc.softplus, gate=wc.z is not None,
@@ -262,15 +254,13 @@ def scan_configs(ssm, workloads, torch, dev, stream, seed, cpu=True):
         el = wc.b * wc.L * wc.E
         gbps = nb / (med * 1e-6) / 1e9
         rec = {"workload": wc.description, "calls": reps,
-               "cache_flushed": "1 GiB read before each call" if flushed else False,
+               "cache_flushed": "1 GiB written before each call" if flushed else False,
                "us_median": round(med, 2), "us_min": round(mn, 2), "elem_per_s": el / (med * 1e-6),
                "algorithmic_bytes": nb, "GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
                "copy_frac": round(gbps / copy_gbps, 4),
                "alu_frac": round(sl / (med * 1e-6) / VALU_SLOT_PEAK, 4),
                "plan": dict(zip(("path", "chunk_len", "n_chunks"),
                                 ssm.ssm_scan_plan(wc.b, wc.L, wc.E, wc.N, wc.dtype)))}
-        if us_w is not None:
-            rec["after_write_flush"] = {"us_median": round(us_w[len(us_w) // 2], 2), "us_min": round(us_w[0], 2)}
         if cpu:
             a64 = [oracle.to_f64(xc[k]) for k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")]
             rates = {}
@@ -285,7 +275,7 @@ def scan_configs(ssm, workloads, torch, dev, stream, seed, cpu=True):
                              "bound": bound}
         out[wc.name] = rec
         del xc, yc, lc
-    del flush, flush_words
+    del flush
     if cpu:  # the decode workload on the host: a sample of its token steps (the GPU side is state_update)
         wd = workloads.DECODE.with_shape(steps=8)
         xd = workloads.make_decode_inputs(wd, seed=seed, device=dev, backend="torch")
@@ -363,8 +353,8 @@ def measure_decode(ssm, torch, workloads, dev, stream, seed):
         "evicted_hbm_frac": round(ub / (e_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
         "note": "each call timed alone with an event pair: right after the previous call (state in the Infinity "
                 "Cache) and after a 1 GiB write that evicts it (state from HBM); the evicted rate is the HBM "
-                "figure, the difference is what the cache serves. evicted_by_read: the same after a 1 GiB read, "
-                "the flush the scan configurations use"}
+                "figure, the difference is what the cache serves. evicted_by_read: the same after a 1 GiB read "
+                "instead, which does not evict the state (a read flush is not used anywhere)"}
     del flush, flush_words
 
     # one generation step of the block's kernels per token: the convolution token step, then the state
@@ -714,9 +704,10 @@ def _counters(d, only=None):
 
 
 LIB_KERNELS = ("scan_main_kernel", "scan_chunk_agg_kernel", "chain_kernel", "scan_fused_kernel", "widen_rows_kernel",
-               "fill_state_kernel", "state_update_kernel", "bwd_main_kernel", "bwd_agg_kernel", "bwd_rows_kernel",
-               "bwd_reduce_bc_kernel", "bwd_reduce_chan_kernel", "ssd_state_kernel", "ssd_scan_kernel",
-               "conv_fwd_kernel", "conv_update_kernel")
+               "fill_state_kernel", "state_update_kernel", "bwd_main_kernel", "bwd_chunk_maps_kernel",
+               "bwd_chunk_agg_kernel", "bwd_rows_kernel", "bwd_reduce_bc_kernel", "bwd_reduce_chan_kernel",
+               "bwd_fill_kernel", "ssd_state_kernel", "ssd_scan_kernel", "ssd_fill_kernel", "conv_fwd_kernel",
+               "conv_fwd_vec_kernel", "conv_update_kernel", "conv_state_copy_kernel")
 
 
 def summarize(run_root, prefix, title, commands, profiled_hash=None):

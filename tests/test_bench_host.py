@@ -122,3 +122,17 @@ def test_kernel_names_of_the_profiles():
         "scan_fused_kernel", "scan_fused_kernel<unsigned short, 4, true, true, false>")
     assert bench._short("void ssm::chain_kernel<1, 32, false, false, false>(ssm::ChainArgs)") == "chain_kernel"
     assert bench._short("void at::native::elementwise_kernel<128, 2, direct_copy_kernel_cuda>(int)") == "copy"
+
+
+def test_profile_summaries_keep_every_library_kernel():
+    """Every __global__ kernel of the library is one the profile summaries keep (none is dropped as foreign)."""
+    import re
+
+    csrc = os.path.join(ROOT, "selective_state_space_35_amd", "csrc")
+    found = set()
+    for f in os.listdir(csrc):
+        if f.endswith((".hip", ".h")):
+            text = open(os.path.join(csrc, f)).read()
+            found |= set(re.findall(r"__global__.{0,200}?\bvoid\s+(\w+)\s*\(", text, flags=re.S))
+    assert "bwd_chunk_maps_kernel" in found and "scan_main_kernel" in found
+    assert found <= set(bench.LIB_KERNELS), found - set(bench.LIB_KERNELS)
